@@ -1,0 +1,26 @@
+"""Build the CPU oracle (TEST INFRASTRUCTURE) into oracle/liboracle.so with gcc.
+
+Plain C99, -O2, no fast-math (the oracle's arithmetic must stay IEEE fp64),
+OpenMP over rows / heads.  Run as `python oracle/build.py`.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "ncgpt_oracle.c")
+OUT = os.path.join(HERE, "liboracle.so")
+
+
+def build(verbose: bool = False) -> str:
+    cmd = ["gcc", "-std=c99", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+           "-Wall", "-Wextra", "-o", OUT + ".tmp", SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.check_call(cmd)
+    os.replace(OUT + ".tmp", OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    print(build(verbose="-q" not in sys.argv))
