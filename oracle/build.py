@@ -1,6 +1,7 @@
 """Build the CPU oracle (TEST INFRASTRUCTURE) into oracle/liboracle.so with gcc.
 
-Plain C99, -O2, no fast-math (the oracle's arithmetic must stay IEEE fp64),
+Plain C99, -O2 with loop vectorisation but no fast-math and no FMA contraction
+(the oracle's arithmetic stays IEEE fp64, in the order the source states),
 OpenMP over rows / heads.  Run as `python oracle/build.py`.
 """
 import os
@@ -13,7 +14,7 @@ OUT = os.path.join(HERE, "liboracle.so")
 
 
 def build(verbose: bool = False) -> str:
-    cmd = ["gcc", "-std=c99", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+    cmd = ["gcc", "-std=c99", "-O2", "-ftree-vectorize", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
            "-Wall", "-Wextra", "-o", OUT + ".tmp", SRC, "-lm"]
     if verbose:
         print(" ".join(cmd))

@@ -93,40 +93,79 @@ int orc_param_slice(const orc_config* c, int layer, int which, int64_t* offset, 
 /* ------------------------------------------------------------------ */
 /* primitives                                                          */
 
-/* y = x W^T for x [rows, in], W [out, in]. */
+/* y = x W^T for x [rows, in], W [out, in].  Each output is one dot product
+ * summed over i in increasing order; four outputs are formed side by side
+ * only to keep the CPU's adders busy (the sum order of each is unchanged). */
 void orc_linear_fwd(const double* x, const double* W, int64_t rows, int64_t in, int64_t out, double* y)
 {
 #pragma omp parallel for schedule(static)
-    for (int64_t n = 0; n < rows; ++n)
-        for (int64_t o = 0; o < out; ++o) {
+    for (int64_t n = 0; n < rows; ++n) {
+        const double* xr = x + n * in;
+        int64_t o = 0;
+        for (; o + 4 <= out; o += 4) {
+            const double *w0 = W + o * in, *w1 = w0 + in, *w2 = w1 + in, *w3 = w2 + in;
+            double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+            for (int64_t i = 0; i < in; ++i) {
+                s0 += xr[i] * w0[i];
+                s1 += xr[i] * w1[i];
+                s2 += xr[i] * w2[i];
+                s3 += xr[i] * w3[i];
+            }
+            y[n * out + o] = s0; y[n * out + o + 1] = s1; y[n * out + o + 2] = s2; y[n * out + o + 3] = s3;
+        }
+        for (; o < out; ++o) {
             double s = 0.0;
-            for (int64_t i = 0; i < in; ++i) s += x[n * in + i] * W[o * in + i];
+            for (int64_t i = 0; i < in; ++i) s += xr[i] * W[o * in + i];
             y[n * out + o] = s;
         }
+    }
 }
 
 /* dx = dy W  (dx [rows,in], overwritten);  dW (+)= dy^T x  (dW [out,in], added to
- * when acc_dw = 1, overwritten when 0).  Either output may be NULL. */
+ * when acc_dw = 1, overwritten when 0).  Either output may be NULL.
+ * dx[n,i] sums over o in increasing order, dW[o,i] over n in increasing
+ * order; the partial sums run along rows of W and x so memory is read
+ * contiguously. */
 void orc_linear_bwd(const double* x, const double* W, const double* dy, int64_t rows, int64_t in, int64_t out,
                     double* dx, double* dW, int acc_dw)
 {
     if (dx) {
 #pragma omp parallel for schedule(static)
-        for (int64_t n = 0; n < rows; ++n)
-            for (int64_t i = 0; i < in; ++i) {
-                double s = 0.0;
-                for (int64_t o = 0; o < out; ++o) s += dy[n * out + o] * W[o * in + i];
-                dx[n * in + i] = s;
+        for (int64_t n = 0; n < rows; ++n) {
+            double* d = dx + n * in;
+            for (int64_t i = 0; i < in; ++i) d[i] = 0.0;
+            for (int64_t o = 0; o < out; ++o) {
+                const double a = dy[n * out + o];
+                const double* w = W + o * in;
+                for (int64_t i = 0; i < in; ++i) d[i] += a * w[i];
             }
+        }
     }
     if (dW) {
-#pragma omp parallel for schedule(static)
-        for (int64_t o = 0; o < out; ++o)
-            for (int64_t i = 0; i < in; ++i) {
-                double s = 0.0;
-                for (int64_t n = 0; n < rows; ++n) s += dy[n * out + o] * x[n * in + i];
-                dW[o * in + i] = acc_dw ? dW[o * in + i] + s : s;
+        const int64_t OB = 8;
+#pragma omp parallel
+        {
+            double* acc = (double*)malloc(sizeof(double) * (size_t)(OB * in));
+#pragma omp for schedule(static)
+            for (int64_t o0 = 0; o0 < out; o0 += OB) {
+                const int64_t ob = out - o0 < OB ? out - o0 : OB;
+                for (int64_t k = 0; k < ob * in; ++k) acc[k] = 0.0;
+                for (int64_t n = 0; n < rows; ++n) {
+                    const double* xr = x + n * in;
+                    for (int64_t k = 0; k < ob; ++k) {
+                        const double a = dy[n * out + o0 + k];
+                        double* t = acc + k * in;
+                        for (int64_t i = 0; i < in; ++i) t[i] += a * xr[i];
+                    }
+                }
+                for (int64_t k = 0; k < ob; ++k)
+                    for (int64_t i = 0; i < in; ++i) {
+                        double* g = dW + (o0 + k) * in + i;
+                        *g = acc_dw ? *g + acc[k * in + i] : acc[k * in + i];
+                    }
             }
+            free(acc);
+        }
     }
 }
 
