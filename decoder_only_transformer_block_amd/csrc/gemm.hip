@@ -1,0 +1,449 @@
+// GEMMs of the block stack: the bias-free linears y = x W^T (forward), their
+// input gradients dx = dy W and weight gradients dW = dy^T x (backward).
+//
+// bf16 path: one MFMA kernel (v_mfma_f32_32x32x16_bf16, fp32 accumulation)
+// for all three operand layouts.  Tiles of BM x BN x 64 are staged through
+// LDS (two stages, XOR-swizzled 16-byte chunks), 4 waves per workgroup in a
+// 2 x 2 grid.  Operands whose K index is not contiguous in memory (the
+// token-major activations of a weight gradient, the [out,in] weight of an
+// input gradient) are transposed 8x8 in registers with v_perm_b32 on their
+// way into LDS, so every MFMA fragment is one 16-byte LDS read.
+//
+// The MFMA is issued with the two operands swapped (it computes C^T), which
+// leaves each lane holding 4 consecutive columns of one output row: the
+// epilogues get (row, col..col+3) and row-wise work stays inside a lane.
+//
+// fp32 path: a plain LDS-tiled SIMT kernel with the same epilogues (the fp32
+// compute mode of the precision scheme is a correctness path).
+#include "common.h"
+#include "kernels.h"
+
+namespace ncgpt {
+
+// ------------------------------------------------------------------ epilogues
+template <typename T> struct EStoreCd {
+    T* out; int ldo;
+    __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
+        Vec4<T>::store(out + (size_t)m * ldo + n, v);
+    }
+};
+struct EStoreF32 {
+    float* out; int ldo;
+    __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
+        Vec4<float>::store(out + (size_t)m * ldo + n, v);
+    }
+};
+template <typename T> struct EResidual {
+    T* out; const T* in; int ldo;
+    __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
+        size_t o = (size_t)m * ldo + n;
+        float x[4];
+        Vec4<T>::load(in + o, x);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] += v[i];
+        Vec4<T>::store(out + o, x);
+    }
+};
+// a = relu(v) is stored for the backward; act = a^2 (of the stored, rounded a) feeds the next GEMM
+template <typename T> struct EReluSq {
+    T* a; T* act; int ldo;
+    __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
+        size_t o = (size_t)m * ldo + n;
+        float r[4], s[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            r[i] = to_f32(from_f32<T>(fmaxf(v[i], 0.0f)));
+            s[i] = r[i] * r[i];
+        }
+        Vec4<T>::store(a + o, r);
+        Vec4<T>::store(act + o, s);
+    }
+};
+// dh = dact * d(relu(h)^2)/dh = dact * 2 * relu(h)
+template <typename T> struct EReluSqBwd {
+    T* out; const T* a; int ldo;
+    __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
+        size_t o = (size_t)m * ldo + n;
+        float x[4];
+        Vec4<T>::load(a + o, x);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = v[i] * 2.0f * x[i];
+        Vec4<T>::store(out + o, x);
+    }
+};
+struct EGrad {
+    float* out; int ldo; int acc;
+    __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
+        float* p = out + (size_t)m * ldo + n;
+        float x[4] = {v[0], v[1], v[2], v[3]};
+        if (acc) {
+            float o[4];
+            Vec4<float>::load(p, o);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] += o[i];
+        }
+        Vec4<float>::store(p, x);
+    }
+};
+struct ESplitK {
+    float* out; int ldo; size_t stride;
+    __device__ void operator()(int m, int n, int split, const float (&v)[4]) const {
+        Vec4<float>::store(out + (size_t)split * stride + (size_t)m * ldo + n, v);
+    }
+};
+
+// ------------------------------------------------------------------ tile order
+// Workgroups are dealt round-robin to the 8 XCDs; renumber them so each XCD
+// gets a contiguous range of tiles (shared A / B tiles stay in one L2), then
+// walk tiles in bands of GROUP_M tile-rows.
+__device__ __forceinline__ int xcd_remap(int wg, int nwg) {
+    constexpr int NX = 8;
+    int per = (nwg + NX - 1) / NX;
+    int xcd = wg % NX, local = wg / NX;
+    int tall = nwg % NX;
+    if (tall == 0) tall = NX;
+    if (xcd < tall) return xcd * per + local;
+    return tall * per + (xcd - tall) * (per - 1) + local;
+}
+
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+    constexpr int GROUP_M = 8;
+    int in_group = GROUP_M * tiles_n;
+    int gid = t / in_group;
+    int first_m = gid * GROUP_M;
+    int gsz = min(tiles_m - first_m, GROUP_M);
+    int r = t % in_group;
+    tm = first_m + r % gsz;
+    tn = r / gsz;
+}
+
+// ------------------------------------------------------------------ LDS staging (bf16)
+// An LDS tile holds R rows x 64 k (bf16): 8 chunks of 16 bytes per row, the
+// chunk index XOR-ed with (row & 7) so that the 8 lanes served together by a
+// 16-byte LDS access hit 8 different bank groups.
+__device__ __forceinline__ int lds_chunk(int row, int ch) { return row * 8 + (ch ^ (row & 7)); }
+
+// K-contiguous operand: element (r, k) at P[r*ld + k].
+template <int R> struct StageK {
+    static constexpr int NC = R / 32;  // 16-byte chunks per thread
+    u32x4 v[NC];
+    __device__ __forceinline__ void load(const bf16* __restrict__ P, int ld, int r0, int rmax, int k0, int tid) {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            int u = tid + 256 * i;
+            int row = u >> 3, ch = u & 7;
+            int gr = min(r0 + row, rmax - 1);
+            v[i] = *reinterpret_cast<const u32x4*>(P + (size_t)gr * ld + k0 + ch * 8);
+        }
+    }
+    __device__ __forceinline__ void store(bf16* S, int tid) const {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            int u = tid + 256 * i;
+            int row = u >> 3, ch = u & 7;
+            *reinterpret_cast<u32x4*>(S + lds_chunk(row, ch) * 8) = v[i];
+        }
+    }
+};
+
+// MN-contiguous operand: element (r, k) at P[k*ld + r].  Each active thread
+// moves one 8 (k) x 8 (r) block: eight 16-byte row loads, a register
+// transpose (32 v_perm_b32), eight 16-byte LDS stores of 8 consecutive k.
+template <int R> struct StageMN {
+    u32x4 v[8];
+    __device__ __forceinline__ void load(const bf16* __restrict__ P, int ld, int r0, int rmax, int k0, int tid) {
+        if (tid >= R) return;
+        int kb = tid & 7, rb = tid >> 3;
+        int gr = min(r0 + rb * 8, rmax - 8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = *reinterpret_cast<const u32x4*>(P + (size_t)(k0 + kb * 8 + i) * ld + gr);
+    }
+    __device__ __forceinline__ void store(bf16* S, int tid) const {
+        if (tid >= R) return;
+        int kb = tid & 7, rb = tid >> 3;
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+            const uint32_t sel = (rr & 1) ? 0x07060302u : 0x05040100u;
+            u32x4 o;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) o[p] = __builtin_amdgcn_perm(v[2 * p + 1][rr >> 1], v[2 * p][rr >> 1], sel);
+            int row = rb * 8 + rr;
+            *reinterpret_cast<u32x4*>(S + lds_chunk(row, kb) * 8) = o;
+        }
+    }
+};
+
+template <int R, bool KC> struct Stage;
+template <int R> struct Stage<R, true> : StageK<R> {};
+template <int R> struct Stage<R, false> : StageMN<R> {};
+
+// ------------------------------------------------------------------ bf16 MFMA kernel
+template <int BM, int BN, bool AK, bool BK, class E>
+__global__ void __launch_bounds__(256, 1)
+gemm_bf16_mfma(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
+               int k_split, E epi)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    constexpr int TA = BM * 64, TB = BN * 64;
+    constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+    bf16* base = reinterpret_cast<bf16*>(smem);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1, h = lane >> 5, l32 = lane & 31;
+
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    int tm, tn;
+    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int split = blockIdx.y;
+    const int kbeg = split * k_split;
+    const int nk = min(k_split, K - kbeg) / 64;
+
+    Stage<BM, AK> sa;
+    Stage<BN, BK> sb;
+    auto gload = [&](int k0) {
+        sa.load(A, lda, m0, M, k0, tid);
+        sb.load(B, ldb, n0, N, k0, tid);
+    };
+    auto lstore = [&](int st) {
+        sa.store(base + st * (TA + TB), tid);
+        sb.store(base + st * (TA + TB) + TA, tid);
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    if (nk > 0) {
+        gload(kbeg);
+        lstore(0);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) gload(kbeg + (kt + 1) * 64);
+        const bf16* sA = base + cur * (TA + TB);
+        const bf16* sB = sA + TA;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            bf16x8 af[FM], bfr[FN];
+            const int ch = kk * 2 + h;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                int row = wm * WM + 32 * i + l32;
+                af[i] = *reinterpret_cast<const bf16x8*>(sA + lds_chunk(row, ch) * 8);
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                int row = wn * WN + 32 * j + l32;
+                bfr[j] = *reinterpret_cast<const bf16x8*>(sB + lds_chunk(row, ch) * 8);
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < nk) lstore(cur ^ 1);
+        __syncthreads();
+    }
+
+    // lane holds C[m0 + wm*WM + 32i + l32][n0 + wn*WN + 32j + 8g + 4h + (0..3)] = acc[i][j][4g + (0..3)]
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wm * WM + 32 * i + l32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * WN + 32 * j + 8 * g + 4 * h;
+                if (n < N) {
+                    float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    epi(m, n, split, v);
+                }
+            }
+    }
+}
+
+// ------------------------------------------------------------------ fp32 SIMT kernel
+template <bool AK, bool BK, class E>
+__global__ void __launch_bounds__(256)
+gemm_f32_simt(const float* __restrict__ A, const float* __restrict__ B, int M, int N, int K, int lda, int ldb,
+              int k_split, E epi)
+{
+    __shared__ float sA[16][68];
+    __shared__ float sB[16][68];
+    const int tid = threadIdx.x;
+    const int tiles_m = (M + 63) / 64;
+    const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+    const int m0 = tm * 64, n0 = tn * 64;
+    const int split = blockIdx.y;
+    const int kbeg = split * k_split, kend = min(K, kbeg + k_split);
+    const int tr = tid >> 4, tc = tid & 15;
+    float acc[4][4] = {};
+
+    for (int k0 = kbeg; k0 < kend; k0 += 16) {
+        if (AK) {
+            int row = tid >> 2, kq = (tid & 3) * 4;
+            int gm = min(m0 + row, M - 1);
+            float4 t = *reinterpret_cast<const float4*>(A + (size_t)gm * lda + k0 + kq);
+            sA[kq][row] = t.x; sA[kq + 1][row] = t.y; sA[kq + 2][row] = t.z; sA[kq + 3][row] = t.w;
+        } else {
+            int kr = tid >> 4, mq = (tid & 15) * 4;
+            int gm = min(m0 + mq, M - 4);
+            float4 t = *reinterpret_cast<const float4*>(A + (size_t)(k0 + kr) * lda + gm);
+            sA[kr][mq] = t.x; sA[kr][mq + 1] = t.y; sA[kr][mq + 2] = t.z; sA[kr][mq + 3] = t.w;
+        }
+        if (BK) {
+            int row = tid >> 2, kq = (tid & 3) * 4;
+            int gn = min(n0 + row, N - 1);
+            float4 t = *reinterpret_cast<const float4*>(B + (size_t)gn * ldb + k0 + kq);
+            sB[kq][row] = t.x; sB[kq + 1][row] = t.y; sB[kq + 2][row] = t.z; sB[kq + 3][row] = t.w;
+        } else {
+            int kr = tid >> 4, nq = (tid & 15) * 4;
+            int gn = min(n0 + nq, N - 4);
+            float4 t = *reinterpret_cast<const float4*>(B + (size_t)(k0 + kr) * ldb + gn);
+            sB[kr][nq] = t.x; sB[kr][nq + 1] = t.y; sB[kr][nq + 2] = t.z; sB[kr][nq + 3] = t.w;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { a[i] = sA[kk][tr * 4 + i]; b[i] = sB[kk][tc * 4 + i]; }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int m = m0 + tr * 4 + i, n = n0 + tc * 4;
+        if (m < M && n < N) epi(m, n, split, acc[i]);
+    }
+}
+
+// ------------------------------------------------------------------ host side
+template <int BM, int BN, bool AK, bool BK, class E>
+static hipError_t run_mfma(const GemmDesc& d, E e, hipStream_t s) {
+    constexpr size_t lds = 2 * (size_t)(BM + BN) * 64 * sizeof(bf16);
+    auto kern = gemm_bf16_mfma<BM, BN, AK, BK, E>;
+    static bool attr_done = false;
+    if (!attr_done) {
+        hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (st != hipSuccess) return st;
+        attr_done = true;
+    }
+    int tiles = ((d.M + BM - 1) / BM) * ((d.N + BN - 1) / BN);
+    dim3 grid(tiles, (d.K + d.k_split - 1) / d.k_split);
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, d.K, d.lda,
+                       d.ldb, d.k_split, e);
+    return hipGetLastError();
+}
+
+template <bool AK, bool BK, class E>
+static hipError_t run_bf16(const GemmDesc& d, E e, hipStream_t s) {
+    switch (d.tile) {
+    case 0: return run_mfma<256, 256, AK, BK>(d, e, s);
+    case 1: return run_mfma<256, 128, AK, BK>(d, e, s);
+    default: return run_mfma<128, 128, AK, BK>(d, e, s);
+    }
+}
+
+template <bool AK, bool BK, class E>
+static hipError_t run_f32(const GemmDesc& d, E e, hipStream_t s) {
+    int tiles = ((d.M + 63) / 64) * ((d.N + 63) / 64);
+    dim3 grid(tiles, (d.K + d.k_split - 1) / d.k_split);
+    hipLaunchKernelGGL((gemm_f32_simt<AK, BK, E>), grid, dim3(256), 0, s, (const float*)d.A, (const float*)d.B,
+                       d.M, d.N, d.K, d.lda, d.ldb, d.k_split, e);
+    return hipGetLastError();
+}
+
+template <typename T, bool AK, bool BK>
+static hipError_t dispatch_epi(const GemmDesc& d, hipStream_t s) {
+    auto run = [&](auto e) -> hipError_t {
+        if constexpr (sizeof(T) == 2) return run_bf16<AK, BK>(d, e, s);
+        else return run_f32<AK, BK>(d, e, s);
+    };
+    switch (d.epi) {
+    case Epi::StoreCd: return run(EStoreCd<T>{(T*)d.out, d.ldo});
+    case Epi::StoreF32: return run(EStoreF32{(float*)d.out, d.ldo});
+    case Epi::ResidualCd: return run(EResidual<T>{(T*)d.out, (const T*)d.in, d.ldo});
+    case Epi::ReluSq: return run(EReluSq<T>{(T*)d.out, (T*)d.out2, d.ldo});
+    case Epi::ReluSqBwd: return run(EReluSqBwd<T>{(T*)d.out, (const T*)d.in, d.ldo});
+    case Epi::Grad: return run(EGrad{(float*)d.out, d.ldo, d.accumulate});
+    case Epi::SplitK: return run(ESplitK{(float*)d.out, d.ldo, d.split_stride});
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t dispatch_layout(const GemmDesc& d, hipStream_t s) {
+    if (d.a_kcontig && d.b_kcontig) return dispatch_epi<T, true, true>(d, s);
+    if (d.a_kcontig && !d.b_kcontig) return dispatch_epi<T, true, false>(d, s);
+    if (!d.a_kcontig && !d.b_kcontig) return dispatch_epi<T, false, false>(d, s);
+    return dispatch_epi<T, false, true>(d, s);
+}
+
+hipError_t launch_gemm(const GemmDesc& in, hipStream_t s) {
+    GemmDesc d = in;
+    if (d.K <= 0 || d.K % 64 || d.M % 8 || d.N % 8 || d.M <= 0 || d.N <= 0 || d.splits < 1) return hipErrorInvalidValue;
+    if (d.k_split <= 0) {
+        if (d.K % d.splits || (d.K / d.splits) % 64) return hipErrorInvalidValue;
+        d.k_split = d.K / d.splits;
+    }
+    if (d.k_split % 64) return hipErrorInvalidValue;
+    if (d.epi != Epi::SplitK && d.k_split < d.K) return hipErrorInvalidValue;  // only SplitK writes partials
+    if (d.dt == Dt::BF16) return dispatch_layout<bf16>(d, s);
+    return dispatch_layout<float>(d, s);
+}
+
+const char* gemm_kernel_name(const GemmDesc& d) {
+    static const char* lay[4] = {"tn", "tk", "nt_mn", "nt"};
+    int li = (d.a_kcontig ? 2 : 0) + (d.b_kcontig ? 1 : 0);
+    (void)lay;
+    if (d.dt == Dt::F32) return li == 3 ? "gemm_f32_nt" : (li == 2 ? "gemm_f32_nn" : "gemm_f32_tn");
+    static const char* names[3][3] = {
+        {"gemm_bf16_nt_256x256", "gemm_bf16_nt_256x128", "gemm_bf16_nt_128x128"},
+        {"gemm_bf16_nn_256x256", "gemm_bf16_nn_256x128", "gemm_bf16_nn_128x128"},
+        {"gemm_bf16_tn_256x256", "gemm_bf16_tn_256x128", "gemm_bf16_tn_128x128"}};
+    int r = li == 3 ? 0 : (li == 2 ? 1 : 2);
+    int t = d.tile < 0 ? 0 : (d.tile > 2 ? 2 : d.tile);
+    return names[r][t];
+}
+
+hipError_t gemm_init_attributes() { return hipSuccess; }
+
+// ------------------------------------------------------------------ split-K reduction
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const float* __restrict__ part, int splits, size_t stride, float* __restrict__ g, size_t n4,
+                     int accumulate)
+{
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n4) return;
+    float4 acc = accumulate ? reinterpret_cast<const float4*>(g)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sidx = 0; sidx < splits; ++sidx) {
+        float4 p = reinterpret_cast<const float4*>(part + (size_t)sidx * stride)[i];
+        acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+    }
+    reinterpret_cast<float4*>(g)[i] = acc;
+}
+
+hipError_t launch_splitk_reduce(const float* part, int splits, size_t stride, float* grads, size_t n,
+                                int accumulate, hipStream_t s) {
+    size_t n4 = n / 4;
+    dim3 grid((unsigned)((n4 + 255) / 256));
+    hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(256), 0, s, part, splits, stride, grads, n4, accumulate);
+    return hipGetLastError();
+}
+
+}  // namespace ncgpt

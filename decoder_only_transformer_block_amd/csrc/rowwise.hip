@@ -1,0 +1,536 @@
+// Bandwidth-bound kernels of the step: weight cast, embedding gather and its
+// gradient, parameter-free RMSNorm, RoPE + QK-norm, and the cross-entropy
+// pieces.  Storage type T is the compute dtype (float or bf16); all
+// arithmetic is fp32.
+#include "common.h"
+#include "kernels.h"
+
+namespace ncgpt {
+
+// ------------------------------------------------------------------ fp32 master -> bf16 (RNE)
+// The precision scheme keeps fp32 master weights and casts them to the compute
+// dtype inside each linear ("nanochat：低成本跑通大模型训练全流程", precision paragraph).
+__global__ void __launch_bounds__(256) cast_bf16_kernel(const float* __restrict__ src, bf16* __restrict__ dst, size_t n4)
+{
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (; i < n4; i += stride) {
+        float v[4];
+        Vec4<float>::load(src + 4 * i, v);
+        Vec4<bf16>::store(dst + 4 * i, v);
+    }
+}
+
+hipError_t launch_cast_bf16(const float* src, void* dst, size_t n, hipStream_t s) {
+    size_t n4 = n / 4;
+    unsigned blocks = (unsigned)std::min<size_t>((n4 + 255) / 256, 256 * 64);
+    hipLaunchKernelGGL(cast_bf16_kernel, dim3(blocks), dim3(256), 0, s, src, (bf16*)dst, n4);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ embedding gather
+// x[n] = cd(wte[ids[n]]); an id outside [0, V) raises kErrBadToken and yields a zero row.
+template <typename T>
+__global__ void __launch_bounds__(256)
+embed_fwd_kernel(const int32_t* __restrict__ ids, const float* __restrict__ wte, T* __restrict__ x, int N, int C, int V,
+                 uint32_t* err)
+{
+    const int n = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (n >= N) return;
+    const int id = ids[n];
+    const bool ok = id >= 0 && id < V;
+    if (!ok && lane == 0) raise_error(err, kErrBadToken);
+    for (int c = lane * 4; c < C; c += 256) {
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (ok) Vec4<float>::load(wte + (size_t)id * C + c, v);
+        Vec4<T>::store(x + (size_t)n * C + c, v);
+    }
+}
+
+hipError_t launch_embed_fwd(Dt dt, const int32_t* ids, const float* wte, void* x, int N, int C, int V, uint32_t* err,
+                            hipStream_t s) {
+    dim3 grid((N + 3) / 4);
+    if (dt == Dt::BF16)
+        hipLaunchKernelGGL(embed_fwd_kernel<bf16>, grid, dim3(256), 0, s, ids, wte, (bf16*)x, N, C, V, err);
+    else
+        hipLaunchKernelGGL(embed_fwd_kernel<float>, grid, dim3(256), 0, s, ids, wte, (float*)x, N, C, V, err);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ RMSNorm (one wave per row)
+// y = x / sqrt(mean(x^2) + eps), no weight ("nanochat 项目深度分析" §2.1 item 5).
+template <typename T>
+__global__ void __launch_bounds__(256)
+rmsnorm_fwd_kernel(const T* __restrict__ x, T* __restrict__ y, float* __restrict__ rstd, int rows, int C, float eps)
+{
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const T* xr = x + (size_t)row * C;
+    float ss = 0.0f;
+    for (int c = lane * 4; c < C; c += 256) {
+        float v[4];
+        Vec4<T>::load(xr + c, v);
+        ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    }
+    ss = wave_sum(ss);
+    const float rs = 1.0f / sqrtf(ss / (float)C + eps);
+    T* yr = y + (size_t)row * C;
+    for (int c = lane * 4; c < C; c += 256) {
+        float v[4];
+        Vec4<T>::load(xr + c, v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] *= rs;
+        Vec4<T>::store(yr + c, v);
+    }
+    if (lane == 0) rstd[row] = rs;
+}
+
+hipError_t launch_rmsnorm_fwd(Dt dt, const void* x, void* y, float* rstd, int rows, int C, float eps, hipStream_t s) {
+    dim3 grid((rows + 3) / 4);
+    if (dt == Dt::BF16)
+        hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)x, (bf16*)y, rstd, rows, C, eps);
+    else
+        hipLaunchKernelGGL(rmsnorm_fwd_kernel<float>, grid, dim3(256), 0, s, (const float*)x, (float*)y, rstd, rows, C,
+                           eps);
+    return hipGetLastError();
+}
+
+// Derivative of the map above, from its saved output y and scale rstd:
+// dx = rstd * (dy - y * mean(dy * y)).
+template <typename T>
+__global__ void __launch_bounds__(256)
+rmsnorm_bwd_kernel(const T* __restrict__ y, const float* __restrict__ rstd, const float* __restrict__ dy,
+                   float* __restrict__ dx, T* __restrict__ dx_cd, int rows, int C, int accumulate)
+{
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const size_t base = (size_t)row * C;
+    float dot = 0.0f;
+    for (int c = lane * 4; c < C; c += 256) {
+        float a[4], b[4];
+        Vec4<T>::load(y + base + c, a);
+        Vec4<float>::load(dy + base + c, b);
+        dot += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+    }
+    dot = wave_sum(dot) / (float)C;
+    const float rs = rstd[row];
+    for (int c = lane * 4; c < C; c += 256) {
+        float a[4], b[4], o[4] = {0.f, 0.f, 0.f, 0.f};
+        Vec4<T>::load(y + base + c, a);
+        Vec4<float>::load(dy + base + c, b);
+        if (accumulate) Vec4<float>::load(dx + base + c, o);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] += rs * (b[i] - a[i] * dot);
+        Vec4<float>::store(dx + base + c, o);
+        if (dx_cd) Vec4<T>::store(dx_cd + base + c, o);
+    }
+}
+
+hipError_t launch_rmsnorm_bwd(Dt dt, const void* y, const float* rstd, const float* dy, float* dx, void* dx_cd,
+                              int rows, int C, int accumulate, hipStream_t s) {
+    dim3 grid((rows + 3) / 4);
+    if (dt == Dt::BF16)
+        hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)y, rstd, dy, dx, (bf16*)dx_cd,
+                           rows, C, accumulate);
+    else
+        hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, grid, dim3(256), 0, s, (const float*)y, rstd, dy, dx,
+                           (float*)dx_cd, rows, C, accumulate);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ RoPE + QK-norm
+// For each token n (position t = n mod T) and each q and k head: rotate pair
+// (i, i + D/2) as y_i = x_i cos + x_{i+D/2} sin, y_{i+D/2} = -x_i sin +
+// x_{i+D/2} cos ("nanochat 项目深度分析" §2.1 item 1, §5.3), then RMS-normalise
+// the head (item 2).  One group of D/2 lanes per head, lane i owning pair i.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+rope_qknorm_fwd_kernel(T* __restrict__ qkv, float* __restrict__ rstdq, float* __restrict__ rstdk,
+                       const float* __restrict__ cosv, const float* __restrict__ sinv, int N, int T_, int H, int Hkv,
+                       float eps)
+{
+    constexpr int G = D / 2;               // lanes per head
+    const int gid = blockIdx.x * (256 / G) + threadIdx.x / G;  // (n, head) with head in [0, H+Hkv)
+    const int i = threadIdx.x % G;
+    const int nh = H + Hkv;
+    if (gid >= N * nh) return;
+    const int n = gid / nh, hd = gid % nh;
+    const int t = n % T_;
+    const int QKV = (H + 2 * Hkv) * D;
+    T* v = qkv + (size_t)n * QKV + hd * D;   // k heads follow the q heads
+    const float x1 = to_f32(v[i]), x2 = to_f32(v[i + G]);
+    const float c = cosv[t * G + i], s = sinv[t * G + i];
+    const float y1 = x1 * c + x2 * s, y2 = -x1 * s + x2 * c;
+    const float ss = group_sum<G>(y1 * y1 + y2 * y2);
+    const float rs = 1.0f / sqrtf(ss / (float)D + eps);
+    v[i] = from_f32<T>(y1 * rs);
+    v[i + G] = from_f32<T>(y2 * rs);
+    if (i == 0) {
+        if (hd < H) rstdq[(size_t)n * H + hd] = rs;
+        else rstdk[(size_t)n * Hkv + hd - H] = rs;
+    }
+}
+
+// Backward: QK-norm derivative from the saved normalised output y = qkv and
+// rstd, then the transposed rotation.  In place on dqkv's q and k columns.
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+rope_qknorm_bwd_kernel(T* __restrict__ dqkv, const T* __restrict__ qkv, const float* __restrict__ rstdq,
+                       const float* __restrict__ rstdk, const float* __restrict__ cosv, const float* __restrict__ sinv,
+                       int N, int T_, int H, int Hkv)
+{
+    constexpr int G = D / 2;
+    const int gid = blockIdx.x * (256 / G) + threadIdx.x / G;
+    const int i = threadIdx.x % G;
+    const int nh = H + Hkv;
+    if (gid >= N * nh) return;
+    const int n = gid / nh, hd = gid % nh;
+    const int t = n % T_;
+    const int QKV = (H + 2 * Hkv) * D;
+    const size_t o = (size_t)n * QKV + hd * D;
+    const float y1 = to_f32(qkv[o + i]), y2 = to_f32(qkv[o + i + G]);
+    const float g1 = to_f32(dqkv[o + i]), g2 = to_f32(dqkv[o + i + G]);
+    const float rs = hd < H ? rstdq[(size_t)n * H + hd] : rstdk[(size_t)n * Hkv + hd - H];
+    const float dot = group_sum<G>(g1 * y1 + g2 * y2) / (float)D;
+    const float r1 = rs * (g1 - y1 * dot), r2 = rs * (g2 - y2 * dot);
+    const float c = cosv[t * G + i], s = sinv[t * G + i];
+    dqkv[o + i] = from_f32<T>(r1 * c - r2 * s);
+    dqkv[o + i + G] = from_f32<T>(r1 * s + r2 * c);
+}
+
+template <typename T>
+static hipError_t rope_fwd_t(T* qkv, float* rq, float* rk, const float* c, const float* sn, int N, int T_, int H,
+                             int Hkv, int D, float eps, hipStream_t s) {
+    const size_t heads = (size_t)N * (H + Hkv);
+    if (D == 128) {
+        hipLaunchKernelGGL((rope_qknorm_fwd_kernel<T, 128>), dim3((unsigned)((heads + 3) / 4)), dim3(256), 0, s, qkv, rq,
+                           rk, c, sn, N, T_, H, Hkv, eps);
+    } else if (D == 64) {
+        hipLaunchKernelGGL((rope_qknorm_fwd_kernel<T, 64>), dim3((unsigned)((heads + 7) / 8)), dim3(256), 0, s, qkv, rq,
+                           rk, c, sn, N, T_, H, Hkv, eps);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t rope_bwd_t(T* dqkv, const T* qkv, const float* rq, const float* rk, const float* c, const float* sn,
+                             int N, int T_, int H, int Hkv, int D, hipStream_t s) {
+    const size_t heads = (size_t)N * (H + Hkv);
+    if (D == 128) {
+        hipLaunchKernelGGL((rope_qknorm_bwd_kernel<T, 128>), dim3((unsigned)((heads + 3) / 4)), dim3(256), 0, s, dqkv,
+                           qkv, rq, rk, c, sn, N, T_, H, Hkv);
+    } else if (D == 64) {
+        hipLaunchKernelGGL((rope_qknorm_bwd_kernel<T, 64>), dim3((unsigned)((heads + 7) / 8)), dim3(256), 0, s, dqkv,
+                           qkv, rq, rk, c, sn, N, T_, H, Hkv);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_qknorm_fwd(Dt dt, void* qkv, float* rstdq, float* rstdk, const float* cosv, const float* sinv,
+                                  int N, int T, int H, int Hkv, int D, float eps, hipStream_t s) {
+    if (dt == Dt::BF16) return rope_fwd_t((bf16*)qkv, rstdq, rstdk, cosv, sinv, N, T, H, Hkv, D, eps, s);
+    return rope_fwd_t((float*)qkv, rstdq, rstdk, cosv, sinv, N, T, H, Hkv, D, eps, s);
+}
+
+hipError_t launch_rope_qknorm_bwd(Dt dt, void* dqkv, const void* qkv, const float* rstdq, const float* rstdk,
+                                  const float* cosv, const float* sinv, int N, int T, int H, int Hkv, int D,
+                                  hipStream_t s) {
+    if (dt == Dt::BF16)
+        return rope_bwd_t((bf16*)dqkv, (const bf16*)qkv, rstdq, rstdk, cosv, sinv, N, T, H, Hkv, D, s);
+    return rope_bwd_t((float*)dqkv, (const float*)qkv, rstdq, rstdk, cosv, sinv, N, T, H, Hkv, D, s);
+}
+
+// ------------------------------------------------------------------ cross-entropy
+// Per row of logits z: lse = log sum exp z, loss_row = lse - z[target] (0
+// when target < 0, i.e. ignored).  One workgroup per row.
+template <typename T>
+__global__ void __launch_bounds__(256)
+ce_fwd_rows_kernel(const T* __restrict__ z, const int32_t* __restrict__ targets, float* __restrict__ lse,
+                   float* __restrict__ loss_rows, int V, uint32_t* err)
+{
+    __shared__ float red_m[4], red_s[4];
+    const int n = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const T* zr = z + (size_t)n * V;
+    float m = -INFINITY, s = 0.0f;
+    for (int c = tid * 4; c < V; c += 1024) {
+        float v[4];
+        Vec4<T>::load(zr + c, v);
+        float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+        float mn = fmaxf(m, mx);
+        s = s * expf(m - mn) + expf(v[0] - mn) + expf(v[1] - mn) + expf(v[2] - mn) + expf(v[3] - mn);
+        m = mn;
+    }
+    // combine (m, s) across the wave, then across the 4 waves
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        float mo = __shfl_xor(m, o, kWave), so = __shfl_xor(s, o, kWave);
+        float mn = fmaxf(m, mo);
+        s = (m == -INFINITY ? 0.0f : s * expf(m - mn)) + (mo == -INFINITY ? 0.0f : so * expf(mo - mn));
+        m = mn;
+    }
+    if (lane == 0) { red_m[w] = m; red_s[w] = s; }
+    __syncthreads();
+    if (tid == 0) {
+        float M = red_m[0];
+        for (int i = 1; i < 4; ++i) M = fmaxf(M, red_m[i]);
+        float S = 0.0f;
+        for (int i = 0; i < 4; ++i) S += red_s[i] * expf(red_m[i] - M);
+        const float l = M + logf(S);
+        lse[n] = l;
+        const int t = targets[n];
+        float lr = 0.0f;
+        if (t >= V) raise_error(err, kErrBadTarget);
+        else if (t >= 0) lr = l - to_f32(zr[t]);
+        loss_rows[n] = lr;
+    }
+}
+
+hipError_t launch_ce_fwd_rows(Dt dt, const void* logits, const int32_t* targets, float* lse, float* loss_rows, int N,
+                              int V, uint32_t* err, hipStream_t s) {
+    if (dt == Dt::BF16)
+        hipLaunchKernelGGL(ce_fwd_rows_kernel<bf16>, dim3(N), dim3(256), 0, s, (const bf16*)logits, targets, lse,
+                           loss_rows, V, err);
+    else
+        hipLaunchKernelGGL(ce_fwd_rows_kernel<float>, dim3(N), dim3(256), 0, s, (const float*)logits, targets, lse,
+                           loss_rows, V, err);
+    return hipGetLastError();
+}
+
+// loss = sum(loss_rows over valid targets) / #valid, in a fixed order (one
+// workgroup); inv_valid = 1/#valid is kept for the backward.  No valid
+// target raises kErrNoTargets and yields loss = NaN, inv_valid = 0.
+__global__ void __launch_bounds__(1024)
+loss_reduce_kernel(const float* __restrict__ loss_rows, const int32_t* __restrict__ targets, int N, int V,
+                   float* __restrict__ loss, float* __restrict__ inv_valid, uint32_t* err)
+{
+    __shared__ double ssum[1024];
+    __shared__ int scnt[1024];
+    const int tid = threadIdx.x;
+    double acc = 0.0;
+    int cnt = 0;
+    for (int i = tid; i < N; i += 1024) {
+        int t = targets[i];
+        if (t >= 0 && t < V) { acc += (double)loss_rows[i]; ++cnt; }
+    }
+    ssum[tid] = acc;
+    scnt[tid] = cnt;
+    __syncthreads();
+    for (int o = 512; o > 0; o >>= 1) {
+        if (tid < o) { ssum[tid] += ssum[tid + o]; scnt[tid] += scnt[tid + o]; }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        if (scnt[0] == 0) {
+            raise_error(err, kErrNoTargets);
+            *loss = NAN;
+            *inv_valid = 0.0f;
+        } else {
+            *loss = (float)(ssum[0] / (double)scnt[0]);
+            *inv_valid = (float)(1.0 / (double)scnt[0]);
+        }
+    }
+}
+
+hipError_t launch_loss_reduce(const float* loss_rows, const int32_t* targets, int N, int V, float* loss,
+                              float* inv_valid, uint32_t* err, hipStream_t s) {
+    hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(1024), 0, s, loss_rows, targets, N, V, loss, inv_valid, err);
+    return hipGetLastError();
+}
+
+// dz = grad_scale * inv_valid * (exp(z - lse) - onehot(target)) on valid rows,
+// 0 on ignored rows; written over the logits.
+template <typename T>
+__global__ void __launch_bounds__(256)
+ce_bwd_kernel(T* __restrict__ z, const float* __restrict__ lse, const int32_t* __restrict__ targets,
+              const float* __restrict__ inv_valid, float grad_scale, size_t total4, int V4)
+{
+    const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;  // one group of 4 logits
+    if (q >= total4) return;
+    const int n = (int)(q / V4);
+    const int c = (int)(q % V4) * 4;
+    const int V = V4 * 4;
+    const int t = targets[n];
+    T* zr = z + (size_t)n * V + c;
+    float v[4];
+    if (t < 0 || t >= V) {
+        v[0] = v[1] = v[2] = v[3] = 0.0f;
+    } else {
+        const float k = grad_scale * (*inv_valid), l = lse[n];
+        Vec4<T>::load(zr, v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = k * (expf(v[i] - l) - (c + i == t ? 1.0f : 0.0f));
+    }
+    Vec4<T>::store(zr, v);
+}
+
+hipError_t launch_ce_bwd(Dt dt, void* logits, const float* lse, const int32_t* targets, const float* inv_valid,
+                         float grad_scale, int N, int V, hipStream_t s) {
+    const size_t total4 = (size_t)N * (V / 4);
+    dim3 grid((unsigned)((total4 + 255) / 256));
+    if (dt == Dt::BF16)
+        hipLaunchKernelGGL(ce_bwd_kernel<bf16>, grid, dim3(256), 0, s, (bf16*)logits, lse, targets, inv_valid,
+                           grad_scale, total4, V / 4);
+    else
+        hipLaunchKernelGGL(ce_bwd_kernel<float>, grid, dim3(256), 0, s, (float*)logits, lse, targets, inv_valid,
+                           grad_scale, total4, V / 4);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ embedding backward
+// dwte[v] = sum of dx rows of the tokens with id v, summed in a fixed order so
+// the result is bitwise reproducible (no float atomics):
+//   1. stable LSD radix sort of (id, position) pairs by id (one workgroup);
+//   2. the sorted array is cut into fixed chunks of 64; each chunk sums the
+//      rows of every run of equal ids inside it and writes the partial sum at
+//      the run's first sorted index;
+//   3. each vocab row sums its runs' partials (its sorted range [a, b) has
+//      partials at a and at every chunk start inside it), in order.
+constexpr int kSortThreads = 512;
+constexpr int kChunk = 64;
+
+__global__ void __launch_bounds__(kSortThreads)
+radix_sort_ids_kernel(const int32_t* __restrict__ ids, int N, int V, int32_t* __restrict__ keys_a,
+                      int32_t* __restrict__ vals_a, int32_t* __restrict__ keys_b, int32_t* __restrict__ vals_b)
+{
+    __shared__ uint32_t cnt[16][kSortThreads];
+    __shared__ uint32_t tot[16];
+    const int tid = threadIdx.x;
+    const int per = (N + kSortThreads - 1) / kSortThreads;
+    const int beg = min(N, tid * per), end = min(N, beg + per);
+    for (int i = beg; i < end; ++i) {
+        int id = ids[i];
+        keys_a[i] = (id >= 0 && id < V) ? id : 0;  // bad ids were reported by the forward
+        vals_a[i] = i;
+    }
+    int bits = 1;
+    while ((1 << bits) < V) ++bits;
+    __syncthreads();
+    int32_t *ks = keys_a, *vs = vals_a, *kd = keys_b, *vd = vals_b;
+    for (int shift = 0; shift < bits; shift += 4) {
+        for (int d = 0; d < 16; ++d) cnt[d][tid] = 0;
+        for (int i = beg; i < end; ++i) cnt[(ks[i] >> shift) & 15][tid]++;
+        __syncthreads();
+        if (tid < 16) {  // exclusive scan along threads for digit tid
+            uint32_t run = 0;
+            for (int t = 0; t < kSortThreads; ++t) { uint32_t c = cnt[tid][t]; cnt[tid][t] = run; run += c; }
+            tot[tid] = run;
+        }
+        __syncthreads();
+        if (tid == 0) {  // digit offsets
+            uint32_t run = 0;
+            for (int d = 0; d < 16; ++d) { uint32_t c = tot[d]; tot[d] = run; run += c; }
+        }
+        __syncthreads();
+        for (int i = beg; i < end; ++i) {
+            int k = ks[i], d = (k >> shift) & 15;
+            uint32_t pos = tot[d] + cnt[d][tid]++;
+            kd[pos] = k;
+            vd[pos] = vs[i];
+        }
+        __syncthreads();
+        int32_t* t0 = ks; ks = kd; kd = t0;
+        int32_t* t1 = vs; vs = vd; vd = t1;
+    }
+    // result must end in (keys_a, vals_a)
+    if (ks != keys_a) {
+        for (int i = beg; i < end; ++i) { keys_a[i] = ks[i]; vals_a[i] = vs[i]; }
+    }
+}
+
+__global__ void __launch_bounds__(256)
+embed_bwd_chunks_kernel(const int32_t* __restrict__ skeys, const int32_t* __restrict__ spos, const float* __restrict__ dx,
+                        float* __restrict__ partial, int N, int C)
+{
+    const int c0 = blockIdx.x * kChunk, c1 = min(N, c0 + kChunk);
+    for (int c = threadIdx.x * 4; c < C; c += 1024) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        int start = c0;
+        for (int i = c0; i < c1; ++i) {
+            float v[4];
+            Vec4<float>::load(dx + (size_t)spos[i] * C + c, v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += v[e];
+            if (i + 1 == c1 || skeys[i + 1] != skeys[i]) {
+                Vec4<float>::store(partial + (size_t)start * C + c, acc);
+                acc[0] = acc[1] = acc[2] = acc[3] = 0.0f;
+                start = i + 1;
+            }
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256)
+embed_bwd_combine_kernel(const int32_t* __restrict__ skeys, const float* __restrict__ partial, float* __restrict__ dwte,
+                         int N, int C, int accumulate)
+{
+    const int v = blockIdx.x;
+    // [a, b) = sorted range of id v
+    int lo = 0, hi = N;
+    while (lo < hi) { int mid = (lo + hi) >> 1; if (skeys[mid] < v) lo = mid + 1; else hi = mid; }
+    const int a = lo;
+    hi = N;
+    while (lo < hi) { int mid = (lo + hi) >> 1; if (skeys[mid] <= v) lo = mid + 1; else hi = mid; }
+    const int b = lo;
+    for (int c = threadIdx.x * 4; c < C; c += 1024) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        if (accumulate) Vec4<float>::load(dwte + (size_t)v * C + c, acc);
+        if (a < b) {
+            float s[4];
+            Vec4<float>::load(partial + (size_t)a * C + c, s);
+            for (int p = (a / kChunk + 1) * kChunk; p < b; p += kChunk) {
+                float q[4];
+                Vec4<float>::load(partial + (size_t)p * C + c, q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[e] += q[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += s[e];
+        }
+        Vec4<float>::store(dwte + (size_t)v * C + c, acc);
+    }
+}
+
+hipError_t launch_embed_bwd(const int32_t* ids, const float* dx, float* dwte, int N, int C, int V, int accumulate,
+                            int32_t* iscratch, float* partial, hipStream_t s) {
+    int32_t* ka = iscratch;
+    int32_t* va = iscratch + N;
+    int32_t* kb = iscratch + 2 * (size_t)N;
+    int32_t* vb = iscratch + 3 * (size_t)N;
+    hipLaunchKernelGGL(radix_sort_ids_kernel, dim3(1), dim3(kSortThreads), 0, s, ids, N, V, ka, va, kb, vb);
+    hipLaunchKernelGGL(embed_bwd_chunks_kernel, dim3((N + kChunk - 1) / kChunk), dim3(256), 0, s, ka, va, dx, partial,
+                       N, C);
+    hipLaunchKernelGGL(embed_bwd_combine_kernel, dim3(V), dim3(256), 0, s, ka, partial, dwte, N, C, accumulate);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ probe helper
+template <typename T>
+__global__ void __launch_bounds__(256) to_f32_kernel(const T* __restrict__ src, float* __restrict__ dst, size_t n)
+{
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (; i < n; i += stride) dst[i] = to_f32(src[i]);
+}
+
+hipError_t launch_to_f32(Dt dt, const void* src, float* dst, size_t n, hipStream_t s) {
+    unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 65536);
+    if (blocks == 0) return hipSuccess;
+    if (dt == Dt::BF16)
+        hipLaunchKernelGGL(to_f32_kernel<bf16>, dim3(blocks), dim3(256), 0, s, (const bf16*)src, dst, n);
+    else
+        hipLaunchKernelGGL(to_f32_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)src, dst, n);
+    return hipGetLastError();
+}
+
+}  // namespace ncgpt

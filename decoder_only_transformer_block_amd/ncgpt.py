@@ -1,0 +1,220 @@
+"""Python binding of libncgpt.so (include/ncgpt.h).
+
+Argument marshalling only: every step of the forward, loss and backward runs
+in the library's HIP kernels.  PyTorch supplies device memory (parameters,
+gradients, token ids, the workspace) and the HIP stream.  Importing this
+module loads the library and raises if it has not been built.
+"""
+import ctypes as ct
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libncgpt.so")
+
+OK, EINVAL, EUNSUPPORTED, ENOMEM, EHIP, ESTATE, EDEVICE = 0, -1, -2, -3, -4, -5, -6
+F32, BF16 = 0, 1
+_STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "ENOMEM", -4: "EHIP", -5: "ESTATE", -6: "EDEVICE"}
+
+# probe ids (ncgpt_probe)
+PROBE = {"x0": 0, "xn1": 1, "qkv": 2, "y": 3, "lse_att": 4, "xn2": 5, "a": 6, "xf": 7, "lse": 8, "loss_rows": 9,
+         "dx0": 10}
+WQ, WK, WV, WO, WFC, WPROJ = range(6)
+
+
+class NcgptError(RuntimeError):
+    def __init__(self, status, msg=""):
+        super().__init__(f"ncgpt {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class _Config(ct.Structure):
+    _fields_ = [(n, ct.c_int32) for n in ("n_layer", "n_embd", "n_head", "n_kv_head", "head_dim", "mlp_dim",
+                                           "vocab_size", "batch", "seq_len")] + \
+               [("rope_base", ct.c_float), ("norm_eps", ct.c_float)]
+
+
+@dataclass(frozen=True)
+class Config:
+    n_layer: int
+    n_embd: int
+    n_head: int
+    n_kv_head: int
+    head_dim: int
+    mlp_dim: int
+    vocab_size: int
+    batch: int
+    seq_len: int
+    rope_base: float = 10000.0
+    norm_eps: float = 2.0 ** -23
+
+    @classmethod
+    def from_workload(cls, w, **kw):
+        d = dict(n_layer=w.n_layer, n_embd=w.n_embd, n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim,
+                 mlp_dim=w.mlp_dim, vocab_size=w.vocab_size, batch=w.batch, seq_len=w.seq_len)
+        d.update(kw)
+        return cls(**d)
+
+    def _c(self):
+        return _Config(self.n_layer, self.n_embd, self.n_head, self.n_kv_head, self.head_dim, self.mlp_dim,
+                       self.vocab_size, self.batch, self.seq_len, self.rope_base, self.norm_eps)
+
+
+_lib = None
+
+EXPORTS = ["ncgpt_num_params", "ncgpt_param_slice", "ncgpt_create", "ncgpt_workspace_size", "ncgpt_bind",
+           "ncgpt_forward", "ncgpt_loss", "ncgpt_backward", "ncgpt_check", "ncgpt_probe_numel", "ncgpt_probe",
+           "ncgpt_timing_enable", "ncgpt_timing_reset", "ncgpt_timing_count", "ncgpt_timing_get",
+           "ncgpt_last_error", "ncgpt_destroy"]
+
+
+def lib():
+    """The loaded library; raises if it is missing (there is no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m decoder_only_transformer_block_amd.build`")
+        L = ct.CDLL(LIB_PATH)
+        P, vp = ct.POINTER, ct.c_void_p
+        L.ncgpt_num_params.argtypes = [P(_Config)]
+        L.ncgpt_num_params.restype = ct.c_size_t
+        L.ncgpt_param_slice.argtypes = [P(_Config), ct.c_int, ct.c_int, P(ct.c_size_t), P(ct.c_int64),
+                                        P(ct.c_int64)]
+        L.ncgpt_create.argtypes = [P(_Config), ct.c_int, P(vp)]
+        L.ncgpt_workspace_size.argtypes = [vp, P(ct.c_size_t)]
+        L.ncgpt_bind.argtypes = [vp, vp, ct.c_size_t, vp]
+        L.ncgpt_forward.argtypes = [vp, vp, vp]
+        L.ncgpt_loss.argtypes = [vp, vp, vp]
+        L.ncgpt_backward.argtypes = [vp, vp, ct.c_int, ct.c_float]
+        L.ncgpt_check.argtypes = [vp]
+        L.ncgpt_probe_numel.argtypes = [vp, ct.c_int, P(ct.c_size_t)]
+        L.ncgpt_probe.argtypes = [vp, ct.c_int, ct.c_int, vp]
+        L.ncgpt_timing_enable.argtypes = [vp, ct.c_int]
+        L.ncgpt_timing_reset.argtypes = [vp]
+        L.ncgpt_timing_count.argtypes = [vp, P(ct.c_int)]
+        L.ncgpt_timing_get.argtypes = [vp, ct.c_int, ct.c_char_p, ct.c_size_t, P(ct.c_int64), P(ct.c_double),
+                                       P(ct.c_double), P(ct.c_double)]
+        L.ncgpt_last_error.argtypes = [vp]
+        L.ncgpt_last_error.restype = ct.c_char_p
+        L.ncgpt_destroy.argtypes = [vp]
+        L.ncgpt_destroy.restype = None
+        for name in EXPORTS:
+            if name not in ("ncgpt_num_params", "ncgpt_last_error", "ncgpt_destroy"):
+                getattr(L, name).restype = ct.c_int
+        _lib = L
+    return _lib
+
+
+def num_params(cfg: Config) -> int:
+    return int(lib().ncgpt_num_params(ct.byref(cfg._c())))
+
+
+def param_slice(cfg: Config, layer: int, which: int):
+    o, r, c = ct.c_size_t(), ct.c_int64(), ct.c_int64()
+    st = lib().ncgpt_param_slice(ct.byref(cfg._c()), layer, which, ct.byref(o), ct.byref(r), ct.byref(c))
+    if st != OK:
+        raise NcgptError(st, "bad tensor selector")
+    return o.value, r.value, c.value
+
+
+def _ptr(t: torch.Tensor, dtype, numel, name):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype or not t.is_contiguous() or t.numel() != numel:
+        raise ValueError(f"{name}: expected contiguous {dtype} with {numel} elements, got {t.dtype} {tuple(t.shape)}")
+    return ct.c_void_p(t.data_ptr())
+
+
+class Model:
+    """One context of the library bound to a workspace and a stream.
+
+    dtype: "bf16" (bf16 compute, fp32 master weights) or "f32"."""
+
+    def __init__(self, cfg: Config, dtype: str = "bf16", stream: torch.cuda.Stream = None):
+        self.cfg = cfg
+        self.dtype = {"bf16": BF16, "f32": F32}[dtype]
+        self._ctx = ct.c_void_p()
+        st = lib().ncgpt_create(ct.byref(cfg._c()), self.dtype, ct.byref(self._ctx))
+        if st != OK:
+            raise NcgptError(st, f"ncgpt_create rejected {cfg} ({dtype})")
+        self.n_params = num_params(cfg)
+        self.n_tokens = cfg.batch * cfg.seq_len
+        nbytes = ct.c_size_t()
+        self._check(lib().ncgpt_workspace_size(self._ctx, ct.byref(nbytes)))
+        self.workspace_bytes = nbytes.value
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+        self.workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device="cuda")
+        self._check(lib().ncgpt_bind(self._ctx, ct.c_void_p(self.workspace.data_ptr()), self.workspace_bytes,
+                                     ct.c_void_p(self.stream.cuda_stream)))
+        self._keep = {}
+
+    def _check(self, st):
+        if st != OK:
+            raise NcgptError(st, lib().ncgpt_last_error(self._ctx).decode())
+
+    # -- the three calls of a training step -------------------------------------------------
+    def forward(self, ids: torch.Tensor, params: torch.Tensor):
+        pi = _ptr(ids, torch.int32, self.n_tokens, "ids")
+        pp = _ptr(params, torch.float32, self.n_params, "params")
+        self._keep = {"ids": ids, "params": params}   # the library reads them again in backward
+        self._check(lib().ncgpt_forward(self._ctx, pi, pp))
+
+    def loss(self, targets: torch.Tensor, out: torch.Tensor = None) -> torch.Tensor:
+        if out is None:
+            out = torch.empty(1, dtype=torch.float32, device="cuda")
+        pt = _ptr(targets, torch.int32, self.n_tokens, "targets")
+        po = _ptr(out, torch.float32, 1, "loss")
+        self._keep["targets"] = targets
+        self._check(lib().ncgpt_loss(self._ctx, pt, po))
+        return out
+
+    def backward(self, grads: torch.Tensor, accumulate: bool = False, grad_scale: float = 1.0):
+        pg = _ptr(grads, torch.float32, self.n_params, "grads")
+        self._check(lib().ncgpt_backward(self._ctx, pg, 1 if accumulate else 0, float(grad_scale)))
+
+    def check(self):
+        self._check(lib().ncgpt_check(self._ctx))
+
+    def check_status(self) -> int:
+        return int(lib().ncgpt_check(self._ctx))
+
+    # -- readouts ------------------------------------------------------------------------------
+    def probe(self, what: str, layer: int = 0) -> torch.Tensor:
+        w = PROBE[what]
+        n = ct.c_size_t()
+        self._check(lib().ncgpt_probe_numel(self._ctx, w, ct.byref(n)))
+        dst = torch.empty(n.value, dtype=torch.float32, device="cuda")
+        self._check(lib().ncgpt_probe(self._ctx, w, layer, ct.c_void_p(dst.data_ptr())))
+        return dst
+
+    def timing(self, enable: bool = True):
+        self._check(lib().ncgpt_timing_enable(self._ctx, 1 if enable else 0))
+
+    def timing_reset(self):
+        self._check(lib().ncgpt_timing_reset(self._ctx))
+
+    def timing_read(self):
+        """{name: (launches, total_ms, flops, bytes)} since the last reset."""
+        cnt = ct.c_int()
+        self._check(lib().ncgpt_timing_count(self._ctx, ct.byref(cnt)))
+        out = {}
+        buf = ct.create_string_buffer(256)
+        for i in range(cnt.value):
+            n, ms, fl, by = ct.c_int64(), ct.c_double(), ct.c_double(), ct.c_double()
+            self._check(lib().ncgpt_timing_get(self._ctx, i, buf, 256, ct.byref(n), ct.byref(ms), ct.byref(fl),
+                                               ct.byref(by)))
+            out[buf.value.decode()] = (n.value, ms.value, fl.value, by.value)
+        return out
+
+    def close(self):
+        if self._ctx:
+            lib().ncgpt_destroy(self._ctx)
+            self._ctx = ct.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
