@@ -26,25 +26,43 @@ namespace ncgpt {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// 16-byte chunk c of row r in a [rows][128] bf16 tile
-__device__ __forceinline__ int kchunk(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 3); }
-// 8-byte unit u (4 keys) of row d in a [128][64] bf16 transposed tile
-__device__ __forceinline__ int tunit(int d, int u) { return d * 64 + ((u ^ (d & 15)) << 2); }
+// ---------------------------------------------------------------- LDS tiles
+// Every tile is [64 rows][128] bf16 in its natural memory layout (256-byte
+// rows of 16 chunks of 16 bytes).  Two kinds of reads hit it:
+//  - row fragments: 16 consecutive rows at one chunk per 16-lane group
+//    (ds_read_b128), the MFMA operand whose K index runs along the row;
+//  - transposed fragments: ds_read_b64_tr_b16, 4 consecutive rows x 4
+//    consecutive chunks per 32 lanes, the operand whose K index runs down
+//    the rows (V for P.V, dO and Q for dV and dK, K for dQ).
+// The chunk index is XOR-ed with swz(row) = ((row & 3) << 2) | ((row >> 2) & 3):
+// a bijection over 16 consecutive rows (row reads hit 16 distinct chunks) whose
+// high bits differ across 4 consecutive rows (transposed reads hit 4 distinct
+// 64-byte bank groups), so neither read conflicts on the 64-bank LDS.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// 8x8 bf16 transpose in registers: in[i] holds row i (8 values); out[rr] gets column rr.
-__device__ __forceinline__ u32x4 tcol(const u32x4 (&in)[8], int rr) {
-    const uint32_t sel = (rr & 1) ? 0x07060302u : 0x05040100u;
-    u32x4 o;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) o[p] = __builtin_amdgcn_perm(in[2 * p + 1][rr >> 1], in[2 * p][rr >> 1], sel);
-    return o;
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int toff(int r, int c) { return r * 128 + ((c ^ swz(r)) << 3); }
+
+__device__ __forceinline__ bf16x8 rfrag(const bf16* S, int r, int c) {
+    return *reinterpret_cast<const bf16x8*>(S + toff(r, c));
 }
 
-// Transposed-tile fragment: 4 keys at unit u0 and 4 at unit u0 + 2 of row d.
-__device__ __forceinline__ bf16x8 tfrag(const bf16* S, int d, int u0) {
-    u32x2 a = *reinterpret_cast<const u32x2*>(S + tunit(d, u0));
-    u32x2 b = *reinterpret_cast<const u32x2*>(S + tunit(d, u0 + 2));
-    u32x4 v = {a[0], a[1], b[0], b[1]};
+// Transposed fragment for MFMA lane l: X[row = d0 + (l & 31)][k] with the 8 k
+// slots of lane half hh = l >> 5 being tile rows kbase + 4hh + (0..3) and
+// kbase + 8 + 4hh + (0..3) -- the order in which an operand-swapped MFMA
+// accumulator holds its 32 columns, so P and dS feed back from registers.
+// ds_read_b64_tr_b16 gives lane i of a 16-lane group element e of the 4-value
+// row addressed by lane 4e + i/4, at position i % 4.
+__device__ __forceinline__ bf16x8 trfrag(const bf16* S, int d0, int kbase, int lane) {
+    const int s = lane & 15, hh = lane >> 5;
+    const int d = d0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+    const int c = d >> 3, o = d & 7;
+    const int r = kbase + 4 * hh + (s >> 2);
+    s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(S + toff(r, c) + o));
+    s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(S + toff(r + 8, c) + o));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v);
 }
 
@@ -55,139 +73,147 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
     return r;
 }
 
-// ======================================================================== bf16 forward
-struct FwdSmem {
-    bf16 K[2][64 * 128];
-    bf16 Vt[2][128 * 64];
+__device__ __forceinline__ void zero16(f32x16& a) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) a[r] = 0.0f;
+}
+
+// Copies two [64][128] tiles (e.g. K and V) from global to LDS through
+// registers: 8 16-byte chunks per thread.
+struct TilePair {
+    u32x4 v[8];
+    __device__ __forceinline__ void load(const bf16* __restrict__ p0, const bf16* __restrict__ p1, size_t ld, int tid) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int u = tid + 256 * i, row = (u >> 4) & 63, c = u & 15;
+            const bf16* src = (i < 4 ? p0 : p1) + row * ld + c * 8;
+            v[i] = *reinterpret_cast<const u32x4*>(src);
+        }
+    }
+    __device__ __forceinline__ void store(bf16* t0, bf16* t1, int tid) const {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int u = tid + 256 * i, row = (u >> 4) & 63, c = u & 15;
+            *reinterpret_cast<u32x4*>((i < 4 ? t0 : t1) + toff(row, c)) = v[i];
+        }
+    }
 };
 
-__global__ void __launch_bounds__(256, 2)
+// ======================================================================== bf16 forward
+// Workgroup: 256 queries of one head (4 waves x 64); K/V tiles of 64 keys,
+// double-buffered.  Each wave's 64 queries are two 32-row MFMA blocks sharing
+// every K and V fragment read.
+constexpr int kFwdLds = 2 * 2 * 64 * 128 * 2;  // 64 KB
+
+__global__ void __launch_bounds__(256, 1)
 attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restrict__ lse, int T, int H, int Hkv)
 {
     constexpr int D = 128;
-    __shared__ FwdSmem sm;
+    __shared__ __attribute__((aligned(16))) bf16 smK[2][64 * 128];
+    __shared__ __attribute__((aligned(16))) bf16 smV[2][64 * 128];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
     const int qb = gridDim.x - 1 - blockIdx.x;  // heavy (late) query blocks first
     const int hq = blockIdx.y, b = blockIdx.z;
     const int g = hq / (H / Hkv);
     const int QKV = (H + 2 * Hkv) * D, HD = H * D, KD = Hkv * D;
-    const int q0 = qb * 128;
-    const int qrow = q0 + 32 * w + l32;
+    const int q0 = qb * 256;
+    const int qw = q0 + 64 * w;                 // first query of this wave
+    const bool active = qw < T;
     const size_t rowbase = (size_t)b * T;
 
-    bf16x8 qf[8];
-    {
-        const bf16* qp = qkv + (rowbase + qrow) * QKV + hq * D + 8 * hh;
+    bf16x8 qf[2][8];
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
+    for (int qq = 0; qq < 2; ++qq) {
+        const int q = active ? qw + 32 * qq + l32 : 0;
+        const bf16* qp = qkv + (rowbase + q) * QKV + hq * D + 8 * hh;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) qf[qq][kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
     }
-    f32x16 o[4];
+    f32x16 o[2][4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-    float lsum = 0.0f;
+        for (int db = 0; db < 4; ++db) zero16(o[qq][db]);
+    float lsum[2] = {0.0f, 0.0f};
     const float c1 = kLog2e * rsqrtf((float)D), c2 = sqrtf((float)D) * kLog2e;
 
-    // tile loader: threads 0..127 transpose one 8x8 block of V, threads 128..255 copy 8 chunks of K
-    u32x4 st[8];
-    auto gload = [&](int kv0) {
-        if (tid < 128) {
-            int kb = tid & 7, db = tid >> 3;
-            const bf16* vp = qkv + (rowbase + kv0 + kb * 8) * QKV + HD + KD + g * D + db * 8;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) st[i] = *reinterpret_cast<const u32x4*>(vp + (size_t)i * QKV);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                int u = (tid - 128) + 128 * i, row = u >> 4, c = u & 15;
-                st[i] = *reinterpret_cast<const u32x4*>(qkv + (rowbase + kv0 + row) * QKV + HD + g * D + c * 8);
-            }
-        }
-    };
-    auto lstore = [&](int s) {
-        if (tid < 128) {
-            int kb = tid & 7, db = tid >> 3;
-#pragma unroll
-            for (int rr = 0; rr < 8; ++rr) {
-                u32x4 c = tcol(st, rr);
-                int d = db * 8 + rr;
-                *reinterpret_cast<u32x2*>(sm.Vt[s] + tunit(d, 2 * kb)) = u32x2{c[0], c[1]};
-                *reinterpret_cast<u32x2*>(sm.Vt[s] + tunit(d, 2 * kb + 1)) = u32x2{c[2], c[3]};
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                int u = (tid - 128) + 128 * i, row = u >> 4, c = u & 15;
-                *reinterpret_cast<u32x4*>(sm.K[s] + kchunk(row, c)) = st[i];
-            }
-        }
-    };
-
-    const int nkv = (q0 + 128) / 64;
-    gload(0);
-    lstore(0);
+    const bf16* kbase = qkv + rowbase * QKV + HD + g * D;
+    TilePair st;
+    const int nkv = min(q0 + 256, T) / 64;
+    st.load(kbase, kbase + KD, QKV, tid);
+    st.store(smK[0], smV[0], tid);
     __syncthreads();
     for (int t = 0; t < nkv; ++t) {
         const int cur = t & 1, kv0 = t * 64;
-        if (t + 1 < nkv) gload(kv0 + 64);
-        if (kv0 <= q0 + 32 * w + 31) {  // wave-uniform: some key of the tile is visible to this wave
-            const bf16* Ks = sm.K[cur];
-            const bf16* Vs = sm.Vt[cur];
-            f32x16 s[2];
+        if (t + 1 < nkv) st.load(kbase + (size_t)(kv0 + 64) * QKV, kbase + (size_t)(kv0 + 64) * QKV + KD, QKV, tid);
+        if (active && kv0 <= qw + 63) {
+            const bf16* Ks = smK[cur];
+            const bf16* Vs = smV[cur];
+            const bool diag = kv0 + 63 > qw;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-                const int krow = 32 * kb + l32;
+                f32x16 s[2];
+                zero16(s[0]);
+                zero16(s[1]);
 #pragma unroll
                 for (int kk = 0; kk < 8; ++kk) {
-                    bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + kchunk(krow, 2 * kk + hh));
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[kb], 0, 0, 0);
+                    const bf16x8 kf = rfrag(Ks, 32 * kb + l32, 2 * kk + hh);
+                    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0][kk], s[0], 0, 0, 0);
+                    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[1][kk], s[1], 0, 0, 0);
                 }
-            }
-            // lane holds S[qrow][kv0 + 32kb + 8(r>>2) + 4hh + (r&3)] in s[kb][r]
-            const bool diag = kv0 + 63 > q0 + 32 * w;
+                // lane holds S[q = qw + 32qq + l32][key = kv0 + 32kb + 8(r>>2) + 4hh + (r&3)] in s[qq][r]
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int qq = 0; qq < 2; ++qq) {
+                    if (diag) {
+                        const int q = qw + 32 * qq + l32;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    float p = exp2f(s[kb][r] * c1 - c2);
-                    p = (diag && key > qrow) ? 0.0f : p;
-                    s[kb][r] = p;
-                    lsum += p;
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+                            const float p = exp2f(s[qq][r] * c1 - c2);
+                            s[qq][r] = key > q ? 0.0f : p;
+                        }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) s[qq][r] = exp2f(s[qq][r] * c1 - c2);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) lsum[qq] += s[qq][r];
                 }
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    bf16x8 pf = pack8(s[kb], 8 * j);
-                    const int u0 = 8 * kb + 4 * j + hh;
+                    const bf16x8 p0 = pack8(s[0], 8 * j), p1 = pack8(s[1], 8 * j);
 #pragma unroll
                     for (int db = 0; db < 4; ++db) {
-                        bf16x8 vf = tfrag(Vs, 32 * db + l32, u0);
-                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
+                        const bf16x8 vf = trfrag(Vs, 32 * db, 32 * kb + 16 * j, lane);
+                        o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p0, o[0][db], 0, 0, 0);
+                        o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p1, o[1][db], 0, 0, 0);
                     }
                 }
+            }
         }
-        if (t + 1 < nkv) lstore(cur ^ 1);
+        if (t + 1 < nkv) st.store(smK[cur ^ 1], smV[cur ^ 1], tid);
         __syncthreads();
     }
-    const float ltot = lsum + __shfl_xor(lsum, 32, kWave);
-    const float inv = 1.0f / ltot;
-    bf16* yp = y + (rowbase + qrow) * HD + hq * D;
+    if (!active) return;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int qq = 0; qq < 2; ++qq) {
+        const int q = qw + 32 * qq + l32;
+        const float ltot = lsum[qq] + __shfl_xor(lsum[qq], 32, kWave);
+        const float inv = 1.0f / ltot;
+        bf16* yp = y + (rowbase + q) * HD + hq * D;
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-            float v[4] = {o[db][4 * gg] * inv, o[db][4 * gg + 1] * inv, o[db][4 * gg + 2] * inv, o[db][4 * gg + 3] * inv};
-            Vec4<bf16>::store(yp + 32 * db + 8 * gg + 4 * hh, v);
-        }
-    if (hh == 0) lse[((size_t)b * H + hq) * T + qrow] = sqrtf((float)D) + logf(ltot);
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                float v[4] = {o[qq][db][4 * gg] * inv, o[qq][db][4 * gg + 1] * inv, o[qq][db][4 * gg + 2] * inv,
+                              o[qq][db][4 * gg + 3] * inv};
+                Vec4<bf16>::store(yp + 32 * db + 8 * gg + 4 * hh, v);
+            }
+        if (hh == 0) lse[((size_t)b * H + hq) * T + q] = sqrtf((float)D) + logf(ltot);
+    }
 }
 
-// ======================================================================== delta = rowsum(dO * O)
+// ======================================================================== delta = rowsum(dO * O) (fp32 path)
 template <typename T>
 __global__ void __launch_bounds__(256)
 attn_delta(const T* __restrict__ dy, const T* __restrict__ y, float* __restrict__ delta, int N, int T_, int H, int D)
@@ -208,14 +234,141 @@ attn_delta(const T* __restrict__ dy, const T* __restrict__ y, float* __restrict_
     delta[((size_t)b * H + h) * T_ + t] = acc;
 }
 
+// ======================================================================== bf16 backward: dQ (and delta)
+// Workgroup: 4 waves x 32*QB queries of one head, K/V tiles of 64 keys.  Each
+// lane first forms delta = rowsum(dO * O) of its query rows (the key-outer
+// kernel reads it afterwards), then for every tile recomputes S and dP, forms
+// dS = P (dP - delta) / sqrt(D) and accumulates dQ = dS K.
+template <int QB>
+__global__ void __launch_bounds__(256, 1)
+attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const bf16* __restrict__ dy,
+                 const float* __restrict__ lse, float* __restrict__ delta, bf16* __restrict__ dqkv, int T, int H,
+                 int Hkv)
+{
+    constexpr int D = 128, QW = 32 * QB, QBLK = 4 * QW;
+    __shared__ __attribute__((aligned(16))) bf16 smK[2][64 * 128];
+    __shared__ __attribute__((aligned(16))) bf16 smV[2][64 * 128];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
+    const int qb = gridDim.x - 1 - blockIdx.x;
+    const int hq = blockIdx.y, b = blockIdx.z;
+    const int g = hq / (H / Hkv);
+    const int QKV = (H + 2 * Hkv) * D, HD = H * D, KD = Hkv * D;
+    const int q0 = qb * QBLK;
+    const int qw = q0 + QW * w;
+    const bool active = qw < T;
+    const size_t rowbase = (size_t)b * T;
+    const float scale = rsqrtf((float)D), c1 = kLog2e * scale;
+
+    bf16x8 qf[QB][8], dof[QB][8];
+    float l2[QB], dl[QB];
+#pragma unroll
+    for (int qq = 0; qq < QB; ++qq) {
+        const int q = active ? qw + 32 * qq + l32 : 0;
+        const bf16* qp = qkv + (rowbase + q) * QKV + hq * D + 8 * hh;
+        const bf16* gp = dy + (rowbase + q) * HD + hq * D + 8 * hh;
+        const bf16* yp = y + (rowbase + q) * HD + hq * D + 8 * hh;
+        float part = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            qf[qq][kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
+            dof[qq][kk] = *reinterpret_cast<const bf16x8*>(gp + 16 * kk);
+            const bf16x8 yv = *reinterpret_cast<const bf16x8*>(yp + 16 * kk);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part += (float)dof[qq][kk][e] * (float)yv[e];
+        }
+        dl[qq] = part + __shfl_xor(part, 32, kWave);
+        const size_t li = ((size_t)b * H + hq) * T + q;
+        l2[qq] = lse[li] * kLog2e;
+        if (active && hh == 0) delta[li] = dl[qq];
+    }
+    f32x16 dq[QB][4];
+#pragma unroll
+    for (int qq = 0; qq < QB; ++qq)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) zero16(dq[qq][db]);
+
+    const bf16* kbase = qkv + rowbase * QKV + HD + g * D;
+    TilePair st;
+    const int nkv = min(q0 + QBLK, T) / 64;
+    st.load(kbase, kbase + KD, QKV, tid);
+    st.store(smK[0], smV[0], tid);
+    __syncthreads();
+    for (int t = 0; t < nkv; ++t) {
+        const int cur = t & 1, kv0 = t * 64;
+        if (t + 1 < nkv) st.load(kbase + (size_t)(kv0 + 64) * QKV, kbase + (size_t)(kv0 + 64) * QKV + KD, QKV, tid);
+        if (active && kv0 <= qw + QW - 1) {
+            const bf16* Ks = smK[cur];
+            const bf16* Vs = smV[cur];
+            const bool diag = kv0 + 63 > qw;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                f32x16 s[QB], dp[QB];
+#pragma unroll
+                for (int qq = 0; qq < QB; ++qq) { zero16(s[qq]); zero16(dp[qq]); }
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    const bf16x8 kf = rfrag(Ks, 32 * kb + l32, 2 * kk + hh);
+                    const bf16x8 vf = rfrag(Vs, 32 * kb + l32, 2 * kk + hh);
+#pragma unroll
+                    for (int qq = 0; qq < QB; ++qq) {
+                        s[qq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qq][kk], s[qq], 0, 0, 0);
+                        dp[qq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[qq][kk], dp[qq], 0, 0, 0);
+                    }
+                }
+                bf16x8 dsf[QB][2];
+#pragma unroll
+                for (int qq = 0; qq < QB; ++qq) {
+                    const int q = qw + 32 * qq + l32;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float p = exp2f(s[qq][r] * c1 - l2[qq]);
+                        if (diag) {
+                            const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+                            p = key > q ? 0.0f : p;
+                        }
+                        dp[qq][r] = p * (dp[qq][r] - dl[qq]) * scale;
+                    }
+                    dsf[qq][0] = pack8(dp[qq], 0);
+                    dsf[qq][1] = pack8(dp[qq], 8);
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int db = 0; db < 4; ++db) {
+                        const bf16x8 kt = trfrag(Ks, 32 * db, 32 * kb + 16 * j, lane);
+#pragma unroll
+                        for (int qq = 0; qq < QB; ++qq)
+                            dq[qq][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsf[qq][j], dq[qq][db], 0, 0, 0);
+                    }
+            }
+        }
+        if (t + 1 < nkv) st.store(smK[cur ^ 1], smV[cur ^ 1], tid);
+        __syncthreads();
+    }
+    if (!active) return;
+#pragma unroll
+    for (int qq = 0; qq < QB; ++qq) {
+        bf16* qout = dqkv + (rowbase + qw + 32 * qq + l32) * QKV + hq * D;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                float a[4] = {dq[qq][db][4 * gg], dq[qq][db][4 * gg + 1], dq[qq][db][4 * gg + 2], dq[qq][db][4 * gg + 3]};
+                Vec4<bf16>::store(qout + 32 * db + 8 * gg + 4 * hh, a);
+            }
+    }
+}
+
 // ======================================================================== bf16 backward: dK, dV
+// Workgroup: 128 keys of one kv head (4 waves x 32 keys, K and V fragments
+// held in registers), looping over the r query heads of the group and over
+// the query tiles (64 rows) at or after the keys.  Q and dO tiles are
+// double-buffered in LDS with their log-sum-exp and delta rows.
 struct DkvSmem {
-    bf16 Q[64 * 128];
-    bf16 Qt[128 * 64];
-    bf16 dO[64 * 128];
-    bf16 dOt[128 * 64];
-    float lse2[64];
-    float dlt[64];
+    bf16 Q[2][64 * 128];
+    bf16 dO[2][64 * 128];
+    float lse2[2][64];
+    float dlt[2][64];
 };
 
 __global__ void __launch_bounds__(256, 1)
@@ -226,12 +379,13 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
     extern __shared__ __attribute__((aligned(16))) unsigned char smraw[];
     DkvSmem& sm = *reinterpret_cast<DkvSmem*>(smraw);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
-    const int kblk = gridDim.x - 1 - blockIdx.x;  // keys late in the sequence see the fewest queries
+    const int kblk = blockIdx.x;  // keys early in the sequence see the most queries: schedule them first
     const int g = blockIdx.y, b = blockIdx.z;
     const int r = H / Hkv;
     const int QKV = (H + 2 * Hkv) * D, HD = H * D, KD = Hkv * D;
     const int k0 = kblk * 128;
-    const int key = k0 + 32 * w + l32;
+    const int kw = k0 + 32 * w;
+    const int key = kw + l32;
     const size_t rowbase = (size_t)b * T;
     const float scale = rsqrtf((float)D), c1 = kLog2e * scale;
 
@@ -246,106 +400,82 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
     }
     f32x16 dk[4], dv[4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) { dk[db][e] = 0.0f; dv[db][e] = 0.0f; }
+    for (int db = 0; db < 4; ++db) { zero16(dk[db]); zero16(dv[db]); }
 
-    // tile loader: threads 0..127 one 8x8 block of Q, threads 128..255 one of dO
-    u32x4 st[8];
-    auto gload = [&](int hq, int q0) {
-        int u = tid & 127, qb = u & 7, db = u >> 3;
-        const bf16* src = tid < 128 ? qkv + (rowbase + q0 + qb * 8) * QKV + hq * D + db * 8
-                                    : dy + (rowbase + q0 + qb * 8) * HD + hq * D + db * 8;
-        const size_t ld = tid < 128 ? (size_t)QKV : (size_t)HD;
+    TilePair st;
+    float srow = 0.0f;
+    // Q and dO rows have different strides: each half of the chunks uses its own
+    auto gload2 = [&](int hq, int q0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) st[i] = *reinterpret_cast<const u32x4*>(src + i * ld);
-    };
-    float stl = 0.0f, std_ = 0.0f;
-    auto gload_rows = [&](int hq, int q0) {
-        if (tid < 64) {
-            stl = lse[((size_t)b * H + hq) * T + q0 + tid] * kLog2e;
-            std_ = delta[((size_t)b * H + hq) * T + q0 + tid];
+        for (int i = 0; i < 8; ++i) {
+            const int u = tid + 256 * i, row = (u >> 4) & 63, c = u & 15;
+            const bf16* src = i < 4 ? qkv + (rowbase + q0 + row) * QKV + hq * D + c * 8
+                                    : dy + (rowbase + q0 + row) * HD + hq * D + c * 8;
+            st.v[i] = *reinterpret_cast<const u32x4*>(src);
         }
+        if (tid < 64) srow = lse[((size_t)b * H + hq) * T + q0 + tid] * kLog2e;
+        else if (tid < 128) srow = delta[((size_t)b * H + hq) * T + q0 + tid - 64];
     };
-    auto lstore = [&]() {
-        int u = tid & 127, qb = u & 7, db = u >> 3;
-        bf16* S = tid < 128 ? sm.Q : sm.dO;
-        bf16* St = tid < 128 ? sm.Qt : sm.dOt;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(S + kchunk(qb * 8 + i, db)) = st[i];
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-            u32x4 c = tcol(st, rr);
-            int d = db * 8 + rr;
-            *reinterpret_cast<u32x2*>(St + tunit(d, 2 * qb)) = u32x2{c[0], c[1]};
-            *reinterpret_cast<u32x2*>(St + tunit(d, 2 * qb + 1)) = u32x2{c[2], c[3]};
-        }
-        if (tid < 64) { sm.lse2[tid] = stl; sm.dlt[tid] = std_; }
+    auto lstore = [&](int sidx) {
+        st.store(sm.Q[sidx], sm.dO[sidx], tid);
+        if (tid < 64) sm.lse2[sidx][tid] = srow;
+        else if (tid < 128) sm.dlt[sidx][tid - 64] = srow;
     };
 
     const int qt0 = k0 / 64, nqt = T / 64 - qt0;
     const int total = r * nqt;
-    gload(g * r, k0);
-    gload_rows(g * r, k0);
+    gload2(g * r, k0);
+    lstore(0);
+    __syncthreads();
     for (int it = 0; it < total; ++it) {
-        const int hq = g * r + it / nqt;
+        const int cur = it & 1;
         const int q0 = (qt0 + it % nqt) * 64;
-        __syncthreads();  // previous tile fully consumed
-        lstore();
+        if (it + 1 < total) gload2(g * r + (it + 1) / nqt, (qt0 + (it + 1) % nqt) * 64);
+        if (q0 + 63 >= kw) {  // wave-uniform: some query of the tile sees some key of the wave
+            const bf16* Qs = sm.Q[cur];
+            const bf16* Gs = sm.dO[cur];
+            const bool diag = q0 < kw + 31;
+#pragma unroll
+            for (int qb2 = 0; qb2 < 2; ++qb2) {
+                f32x16 s, dp;
+                zero16(s);
+                zero16(dp);
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(Qs, 32 * qb2 + l32, 2 * kk + hh), kf[kk], s, 0, 0, 0);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(Gs, 32 * qb2 + l32, 2 * kk + hh), vf[kk], dp, 0, 0, 0);
+                }
+                // lane holds S[q = q0 + 32qb2 + 8(e>>2) + 4hh + (e&3)][key] in s[e]
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg) {
+                    const int ql = 32 * qb2 + 8 * gg + 4 * hh;
+                    const float4 l4 = *reinterpret_cast<const float4*>(&sm.lse2[cur][ql]);
+                    const float4 d4 = *reinterpret_cast<const float4*>(&sm.dlt[cur][ql]);
+                    const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int idx = 4 * gg + e;
+                        float p = exp2f(s[idx] * c1 - lv[e]);
+                        if (diag) p = q0 + ql + e < key ? 0.0f : p;
+                        s[idx] = p;
+                        dp[idx] = p * (dp[idx] - dv4[e]) * scale;
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const bf16x8 pf = pack8(s, 8 * j), dsf = pack8(dp, 8 * j);
+#pragma unroll
+                    for (int db = 0; db < 4; ++db) {
+                        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(Gs, 32 * db, 32 * qb2 + 16 * j, lane), pf,
+                                                                          dv[db], 0, 0, 0);
+                        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(Qs, 32 * db, 32 * qb2 + 16 * j, lane), dsf,
+                                                                          dk[db], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        if (it + 1 < total) lstore(cur ^ 1);
         __syncthreads();
-        if (it + 1 < total) {
-            const int hn = g * r + (it + 1) / nqt, qn = (qt0 + (it + 1) % nqt) * 64;
-            gload(hn, qn);
-            gload_rows(hn, qn);
-        }
-        if (q0 + 63 < k0 + 32 * w) continue;  // wave-uniform: every query of the tile precedes every key
-        f32x16 s[2], dp[2];
-#pragma unroll
-        for (int qb2 = 0; qb2 < 2; ++qb2) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) { s[qb2][e] = 0.0f; dp[qb2][e] = 0.0f; }
-            const int qr = 32 * qb2 + l32;
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                bf16x8 qfr = *reinterpret_cast<const bf16x8*>(sm.Q + kchunk(qr, 2 * kk + hh));
-                bf16x8 dof = *reinterpret_cast<const bf16x8*>(sm.dO + kchunk(qr, 2 * kk + hh));
-                s[qb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr, kf[kk], s[qb2], 0, 0, 0);
-                dp[qb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dof, vf[kk], dp[qb2], 0, 0, 0);
-            }
-        }
-        // lane holds S[q0 + 32qb2 + 8(e>>2) + 4hh + (e&3)][key] in s[qb2][e]
-        const bool diag = q0 < k0 + 32 * w + 31;
-#pragma unroll
-        for (int qb2 = 0; qb2 < 2; ++qb2)
-#pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                const int ql = 32 * qb2 + 8 * gg + 4 * hh;
-                float4 l2 = *reinterpret_cast<const float4*>(sm.lse2 + ql);
-                float4 dl = *reinterpret_cast<const float4*>(sm.dlt + ql);
-                float l2v[4] = {l2.x, l2.y, l2.z, l2.w}, dlv[4] = {dl.x, dl.y, dl.z, dl.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int idx = 4 * gg + e;
-                    float p = exp2f(s[qb2][idx] * c1 - l2v[e]);
-                    p = (diag && q0 + ql + e < key) ? 0.0f : p;
-                    s[qb2][idx] = p;
-                    dp[qb2][idx] = p * (dp[qb2][idx] - dlv[e]) * scale;
-                }
-            }
-#pragma unroll
-        for (int qb2 = 0; qb2 < 2; ++qb2)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                bf16x8 pf = pack8(s[qb2], 8 * j);
-                bf16x8 dsf = pack8(dp[qb2], 8 * j);
-                const int u0 = 8 * qb2 + 4 * j + hh;
-#pragma unroll
-                for (int db = 0; db < 4; ++db) {
-                    const int d = 32 * db + l32;
-                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag(sm.dOt, d, u0), pf, dv[db], 0, 0, 0);
-                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag(sm.Qt, d, u0), dsf, dk[db], 0, 0, 0);
-                }
-            }
     }
     bf16* kout = dqkv + (rowbase + key) * QKV + HD + g * D;
 #pragma unroll
@@ -356,138 +486,6 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
             float c[4] = {dv[db][4 * gg], dv[db][4 * gg + 1], dv[db][4 * gg + 2], dv[db][4 * gg + 3]};
             Vec4<bf16>::store(kout + 32 * db + 8 * gg + 4 * hh, a);
             Vec4<bf16>::store(kout + KD + 32 * db + 8 * gg + 4 * hh, c);
-        }
-}
-
-// ======================================================================== bf16 backward: dQ
-struct DqSmem {
-    bf16 K[64 * 128];
-    bf16 V[64 * 128];
-    bf16 Kt[128 * 64];
-};
-
-__global__ void __launch_bounds__(256, 1)
-attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, const float* __restrict__ lse,
-                 const float* __restrict__ delta, bf16* __restrict__ dqkv, int T, int H, int Hkv)
-{
-    constexpr int D = 128;
-    __shared__ DqSmem sm;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
-    const int qb = gridDim.x - 1 - blockIdx.x;
-    const int hq = blockIdx.y, b = blockIdx.z;
-    const int g = hq / (H / Hkv);
-    const int QKV = (H + 2 * Hkv) * D, HD = H * D, KD = Hkv * D;
-    const int q0 = qb * 128;
-    const int qrow = q0 + 32 * w + l32;
-    const size_t rowbase = (size_t)b * T;
-    const float scale = rsqrtf((float)D), c1 = kLog2e * scale;
-
-    bf16x8 qf[8], dof[8];
-    {
-        const bf16* qp = qkv + (rowbase + qrow) * QKV + hq * D + 8 * hh;
-        const bf16* dp_ = dy + (rowbase + qrow) * HD + hq * D + 8 * hh;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
-            dof[kk] = *reinterpret_cast<const bf16x8*>(dp_ + 16 * kk);
-        }
-    }
-    const float l2 = lse[((size_t)b * H + hq) * T + qrow] * kLog2e;
-    const float dl = delta[((size_t)b * H + hq) * T + qrow];
-    f32x16 dq[4];
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) dq[db][e] = 0.0f;
-
-    // loader: threads 0..127 one 8x8 block of K (row-major + transposed), 128..255 eight chunks of V
-    u32x4 st[8];
-    auto gload = [&](int kv0) {
-        if (tid < 128) {
-            int kb = tid & 7, db = tid >> 3;
-            const bf16* kp = qkv + (rowbase + kv0 + kb * 8) * QKV + HD + g * D + db * 8;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) st[i] = *reinterpret_cast<const u32x4*>(kp + (size_t)i * QKV);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                int u = (tid - 128) + 128 * i, row = u >> 4, c = u & 15;
-                st[i] = *reinterpret_cast<const u32x4*>(qkv + (rowbase + kv0 + row) * QKV + HD + KD + g * D + c * 8);
-            }
-        }
-    };
-    auto lstore = [&]() {
-        if (tid < 128) {
-            int kb = tid & 7, db = tid >> 3;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(sm.K + kchunk(kb * 8 + i, db)) = st[i];
-#pragma unroll
-            for (int rr = 0; rr < 8; ++rr) {
-                u32x4 c = tcol(st, rr);
-                int d = db * 8 + rr;
-                *reinterpret_cast<u32x2*>(sm.Kt + tunit(d, 2 * kb)) = u32x2{c[0], c[1]};
-                *reinterpret_cast<u32x2*>(sm.Kt + tunit(d, 2 * kb + 1)) = u32x2{c[2], c[3]};
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                int u = (tid - 128) + 128 * i, row = u >> 4, c = u & 15;
-                *reinterpret_cast<u32x4*>(sm.V + kchunk(row, c)) = st[i];
-            }
-        }
-    };
-
-    const int nkv = (q0 + 128) / 64;
-    gload(0);
-    for (int t = 0; t < nkv; ++t) {
-        const int kv0 = t * 64;
-        __syncthreads();
-        lstore();
-        __syncthreads();
-        if (t + 1 < nkv) gload(kv0 + 64);
-        if (kv0 > q0 + 32 * w + 31) continue;
-        f32x16 s[2], dp[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) { s[kb][e] = 0.0f; dp[kb][e] = 0.0f; }
-            const int kr = 32 * kb + l32;
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                bf16x8 kfr = *reinterpret_cast<const bf16x8*>(sm.K + kchunk(kr, 2 * kk + hh));
-                bf16x8 vfr = *reinterpret_cast<const bf16x8*>(sm.V + kchunk(kr, 2 * kk + hh));
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf[kk], s[kb], 0, 0, 0);
-                dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr, dof[kk], dp[kb], 0, 0, 0);
-            }
-        }
-        const bool diag = kv0 + 63 > q0 + 32 * w;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int keyi = kv0 + 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
-                float p = exp2f(s[kb][e] * c1 - l2);
-                p = (diag && keyi > qrow) ? 0.0f : p;
-                dp[kb][e] = p * (dp[kb][e] - dl) * scale;
-            }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                bf16x8 dsf = pack8(dp[kb], 8 * j);
-                const int u0 = 8 * kb + 4 * j + hh;
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-                    dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag(sm.Kt, 32 * db + l32, u0), dsf, dq[db], 0, 0, 0);
-            }
-    }
-    bf16* qout = dqkv + (rowbase + qrow) * QKV + hq * D;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-            float a[4] = {dq[db][4 * gg], dq[db][4 * gg + 1], dq[db][4 * gg + 2], dq[db][4 * gg + 3]};
-            Vec4<bf16>::store(qout + 32 * db + 8 * gg + 4 * hh, a);
         }
 }
 
@@ -612,7 +610,7 @@ hipError_t attn_init_attributes() {
 hipError_t launch_attn_fwd(const AttnDesc& a, hipStream_t s) {
     if (a.dt == Dt::BF16) {
         if (a.D != 128 || a.T % 128) return hipErrorInvalidValue;
-        dim3 grid(a.T / 128, a.H, a.B);
+        dim3 grid((a.T + 255) / 256, a.H, a.B);
         hipLaunchKernelGGL(attn_fwd_bf16, grid, dim3(256), 0, s, (const bf16*)a.qkv, (bf16*)a.y, a.lse, a.T, a.H,
                            a.Hkv);
         return hipGetLastError();
@@ -629,36 +627,41 @@ hipError_t launch_attn_fwd(const AttnDesc& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd(const AttnDesc& a, hipStream_t s) {
+hipError_t launch_attn_bwd(const AttnDesc& a, hipStream_t s, int part) {
     const int N = a.B * a.T;
-    dim3 dg((unsigned)(((size_t)N * a.H + 255) / 256));
-    if (a.dt == Dt::BF16) {
-        if (a.D != 128 || a.T % 128) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(attn_delta<bf16>, dg, dim3(256), 0, s, (const bf16*)a.dy, (const bf16*)a.y, a.delta, N,
-                           a.T, a.H, a.D);
-        hipLaunchKernelGGL(attn_bwd_dkdv_bf16, dim3(a.T / 128, a.Hkv, a.B), dim3(256), sizeof(DkvSmem), s,
-                           (const bf16*)a.qkv, (const bf16*)a.dy, (const float*)a.lse, (const float*)a.delta,
-                           (bf16*)a.dqkv, a.T, a.H, a.Hkv);
-        hipLaunchKernelGGL(attn_bwd_dq_bf16, dim3(a.T / 128, a.H, a.B), dim3(256), 0, s, (const bf16*)a.qkv,
-                           (const bf16*)a.dy, (const float*)a.lse, (const float*)a.delta, (bf16*)a.dqkv, a.T, a.H,
-                           a.Hkv);
+    const bool bf = a.dt == Dt::BF16;
+    if (bf ? (a.D != 128 || a.T % 128) : (a.D != 128 && a.D != 64)) return hipErrorInvalidValue;
+    if (bf) {
+        if (part == 0)
+            hipLaunchKernelGGL(attn_bwd_dq_bf16<1>, dim3(a.T / 128, a.H, a.B), dim3(256), 0, s, (const bf16*)a.qkv,
+                               (const bf16*)a.y, (const bf16*)a.dy, (const float*)a.lse, a.delta, (bf16*)a.dqkv, a.T,
+                               a.H, a.Hkv);
+        else
+            hipLaunchKernelGGL(attn_bwd_dkdv_bf16, dim3(a.T / 128, a.Hkv, a.B), dim3(256), sizeof(DkvSmem), s,
+                               (const bf16*)a.qkv, (const bf16*)a.dy, (const float*)a.lse, (const float*)a.delta,
+                               (bf16*)a.dqkv, a.T, a.H, a.Hkv);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(attn_delta<float>, dg, dim3(256), 0, s, (const float*)a.dy, (const float*)a.y, a.delta, N,
-                       a.T, a.H, a.D);
     dim3 gq((unsigned)(((size_t)N * a.H + 3) / 4)), gk((unsigned)(((size_t)N * a.Hkv + 3) / 4));
-    if (a.D == 128) {
-        hipLaunchKernelGGL(attn_bwd_dq_f32<128>, gq, dim3(256), 0, s, (const float*)a.qkv, (const float*)a.dy,
-                           (const float*)a.lse, (const float*)a.delta, (float*)a.dqkv, a.B, a.T, a.H, a.Hkv);
-        hipLaunchKernelGGL(attn_bwd_dkdv_f32<128>, gk, dim3(256), 0, s, (const float*)a.qkv, (const float*)a.dy,
-                           (const float*)a.lse, (const float*)a.delta, (float*)a.dqkv, a.B, a.T, a.H, a.Hkv);
-    } else if (a.D == 64) {
-        hipLaunchKernelGGL(attn_bwd_dq_f32<64>, gq, dim3(256), 0, s, (const float*)a.qkv, (const float*)a.dy,
-                           (const float*)a.lse, (const float*)a.delta, (float*)a.dqkv, a.B, a.T, a.H, a.Hkv);
-        hipLaunchKernelGGL(attn_bwd_dkdv_f32<64>, gk, dim3(256), 0, s, (const float*)a.qkv, (const float*)a.dy,
-                           (const float*)a.lse, (const float*)a.delta, (float*)a.dqkv, a.B, a.T, a.H, a.Hkv);
+    const float* q = (const float*)a.qkv;
+    const float* dy = (const float*)a.dy;
+    float* dq = (float*)a.dqkv;
+    if (part == 0) {
+        dim3 dg((unsigned)(((size_t)N * a.H + 255) / 256));
+        hipLaunchKernelGGL(attn_delta<float>, dg, dim3(256), 0, s, dy, (const float*)a.y, a.delta, N, a.T, a.H, a.D);
+        if (a.D == 128)
+            hipLaunchKernelGGL(attn_bwd_dq_f32<128>, gq, dim3(256), 0, s, q, dy, (const float*)a.lse,
+                               (const float*)a.delta, dq, a.B, a.T, a.H, a.Hkv);
+        else
+            hipLaunchKernelGGL(attn_bwd_dq_f32<64>, gq, dim3(256), 0, s, q, dy, (const float*)a.lse,
+                               (const float*)a.delta, dq, a.B, a.T, a.H, a.Hkv);
     } else {
-        return hipErrorInvalidValue;
+        if (a.D == 128)
+            hipLaunchKernelGGL(attn_bwd_dkdv_f32<128>, gk, dim3(256), 0, s, q, dy, (const float*)a.lse,
+                               (const float*)a.delta, dq, a.B, a.T, a.H, a.Hkv);
+        else
+            hipLaunchKernelGGL(attn_bwd_dkdv_f32<64>, gk, dim3(256), 0, s, q, dy, (const float*)a.lse,
+                               (const float*)a.delta, dq, a.B, a.T, a.H, a.Hkv);
     }
     return hipGetLastError();
 }

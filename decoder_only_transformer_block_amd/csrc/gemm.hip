@@ -118,10 +118,13 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
 }
 
 // ------------------------------------------------------------------ LDS staging (bf16)
-// An LDS tile holds R rows x 64 k (bf16): 8 chunks of 16 bytes per row, the
-// chunk index XOR-ed with (row & 7) so that the 8 lanes served together by a
-// 16-byte LDS access hit 8 different bank groups.
-__device__ __forceinline__ int lds_chunk(int row, int ch) { return row * 8 + (ch ^ (row & 7)); }
+// An LDS tile holds R rows x 64 k (bf16): 8 chunks of 16 bytes per row.  The
+// gfx950 LDS serves 16 lanes of a 16-byte access per cycle from 64 banks, so
+// the 16 consecutive rows read together must cover all (row parity, chunk)
+// pairs: the chunk index is XOR-ed with (row & 7) ^ ((row >> 3) & 1), which
+// gives the even rows of a 16-row group 8 distinct chunks and the odd rows 8
+// distinct chunks (bank-conflict counter reads 0 on the MFMA reads).
+__device__ __forceinline__ int lds_chunk(int row, int ch) { return row * 8 + (ch ^ ((row & 7) ^ ((row >> 3) & 1))); }
 
 // K-contiguous operand: element (r, k) at P[r*ld + k].
 template <int R> struct StageK {
@@ -271,6 +274,257 @@ gemm_bf16_mfma(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, in
     }
 }
 
+// ------------------------------------------------------------------ bf16 MFMA kernel, software-pipelined
+// Same tiling as above, with the LDS fragment reads of k-step kk+1 issued
+// while the MFMAs of k-step kk run (two fragment register sets), one
+// branch-free basic block per 64-deep stage (the prefetch of the stage after
+// the last one is clamped to a valid address and never stored), and
+// scheduling-group hints that interleave MFMAs with LDS reads and global loads.
+template <int BM, int BN, bool AK, bool BK, class E>
+__global__ void __launch_bounds__(256, 1)
+gemm_bf16_mfma_pipe(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
+                    int k_split, E epi)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    constexpr int TA = BM * 64, TB = BN * 64;
+    constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+    bf16* base = reinterpret_cast<bf16*>(smem);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1, h = lane >> 5, l32 = lane & 31;
+
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    int tm, tn;
+    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int split = blockIdx.y;
+    const int kbeg = split * k_split;
+    const int nk = min(k_split, K - kbeg) / 64;
+
+    Stage<BM, AK> sa;
+    Stage<BN, BK> sb;
+    auto gload = [&](int k0) {
+        sa.load(A, lda, m0, M, k0, tid);
+        sb.load(B, ldb, n0, N, k0, tid);
+    };
+    auto lstore = [&](int st) {
+        sa.store(base + st * (TA + TB), tid);
+        sb.store(base + st * (TA + TB) + TA, tid);
+    };
+    bf16x8 fa[2][FM], fb[2][FN];
+    auto lfrag = [&](int buf, int st, int kk) {
+        const bf16* sA = base + st * (TA + TB);
+        const bf16* sB = sA + TA;
+        const int ch = kk * 2 + h;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            int row = wm * WM + 32 * i + l32;
+            fa[buf][i] = *reinterpret_cast<const bf16x8*>(sA + lds_chunk(row, ch) * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            int row = wn * WN + 32 * j + l32;
+            fb[buf][j] = *reinterpret_cast<const bf16x8*>(sB + lds_chunk(row, ch) * 8);
+        }
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    if (nk > 0) {
+        gload(kbeg);
+        lstore(0);
+    }
+    __syncthreads();
+    if (nk > 0) lfrag(0, 0, 0);
+    const int klast = kbeg + (nk - 1) * 64;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        gload(min(kbeg + (kt + 1) * 64, klast));  // past the end: a harmless reload of the last stage
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int fc = kk & 1;
+            if (kk < 3) lfrag(fc ^ 1, cur, kk + 1);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fc][j], fa[fc][i], acc[i][j], 0, 0, 0);
+            if (kk == 0) {
+                // spread this stage's global loads over the first k-step's MFMAs
+#pragma unroll
+                for (int q = 0; q < FM + FN; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+                }
+#pragma unroll
+                for (int q = 0; q < FM * FN - (FM + FN); ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 global load
+                }
+            } else if (kk < 3) {
+#pragma unroll
+                for (int q = 0; q < FM + FN; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
+        }
+        lstore(cur ^ 1);
+        __syncthreads();
+        lfrag(0, cur ^ 1, 0);
+    }
+
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wm * WM + 32 * i + l32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * WN + 32 * j + 8 * g + 4 * h;
+                if (n < N) {
+                    float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    epi(m, n, split, v);
+                }
+            }
+    }
+}
+
+// ------------------------------------------------------------------ bf16 MFMA kernel, two register stages
+// The global loads of stage k+2 are issued while stage k is computed and
+// written to LDS only at the end of stage k+1, so every load has two stages of
+// MFMA work (~4k cycles) to arrive: the single-stage prefetch above leaves the
+// one wave per SIMD waiting on memory.  Two register sets alternate, so the
+// stage loop is unrolled by two.
+template <int BM, int BN, bool AK, bool BK, class E>
+__global__ void __launch_bounds__(256, 1)
+gemm_bf16_mfma_db(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
+                  int k_split, E epi)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    constexpr int TA = BM * 64, TB = BN * 64;
+    constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+    bf16* base = reinterpret_cast<bf16*>(smem);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1, h = lane >> 5, l32 = lane & 31;
+
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    int tm, tn;
+    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int split = blockIdx.y;
+    const int kbeg = split * k_split;
+    const int nk = min(k_split, K - kbeg) / 64;
+    const int klast = kbeg + (nk - 1) * 64;
+
+    Stage<BM, AK> sa0, sa1;
+    Stage<BN, BK> sb0, sb1;
+    bf16x8 fa[2][FM], fb[2][FN];
+    auto lfrag = [&](int buf, int st, int kk) {
+        const bf16* sA = base + st * (TA + TB);
+        const bf16* sB = sA + TA;
+        const int ch = kk * 2 + h;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            int row = wm * WM + 32 * i + l32;
+            fa[buf][i] = *reinterpret_cast<const bf16x8*>(sA + lds_chunk(row, ch) * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            int row = wn * WN + 32 * j + l32;
+            fb[buf][j] = *reinterpret_cast<const bf16x8*>(sB + lds_chunk(row, ch) * 8);
+        }
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // one 64-deep stage out of LDS buffer st, with the fragment reads of the
+    // next k-step overlapping the MFMAs of the current one
+    auto compute = [&](int st) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int fc = kk & 1;
+            if (kk < 3) lfrag(fc ^ 1, st, kk + 1);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fc][j], fa[fc][i], acc[i][j], 0, 0, 0);
+            if (kk < 3) {
+#pragma unroll
+                for (int q = 0; q < FM + FN; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+                }
+            }
+        }
+    };
+
+    if (nk > 0) {
+        sa0.load(A, lda, m0, M, kbeg, tid);
+        sb0.load(B, ldb, n0, N, kbeg, tid);
+        sa0.store(base, tid);
+        sb0.store(base + TA, tid);
+        sa1.load(A, lda, m0, M, min(kbeg + 64, klast), tid);
+        sb1.load(B, ldb, n0, N, min(kbeg + 64, klast), tid);
+    }
+    __syncthreads();
+    if (nk > 0) lfrag(0, 0, 0);
+    for (int kt = 0; kt < nk; kt += 2) {
+        // even stage: buffer 0; prefetch stage kt+2 into set 0; publish stage kt+1 (set 1) to buffer 1
+        {
+            const int kn = min(kbeg + (kt + 2) * 64, klast);
+            sa0.load(A, lda, m0, M, kn, tid);
+            sb0.load(B, ldb, n0, N, kn, tid);
+            compute(0);
+            sa1.store(base + (TA + TB), tid);
+            sb1.store(base + (TA + TB) + TA, tid);
+            __syncthreads();
+            lfrag(0, 1, 0);
+        }
+        if (kt + 1 < nk) {
+            const int kn = min(kbeg + (kt + 3) * 64, klast);
+            sa1.load(A, lda, m0, M, kn, tid);
+            sb1.load(B, ldb, n0, N, kn, tid);
+            compute(1);
+            sa0.store(base, tid);
+            sb0.store(base + TA, tid);
+            __syncthreads();
+            lfrag(0, 0, 0);
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wm * WM + 32 * i + l32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * WN + 32 * j + 8 * g + 4 * h;
+                if (n < N) {
+                    float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    epi(m, n, split, v);
+                }
+            }
+    }
+}
+
 // ------------------------------------------------------------------ fp32 SIMT kernel
 template <bool AK, bool BK, class E>
 __global__ void __launch_bounds__(256)
@@ -332,16 +586,22 @@ gemm_f32_simt(const float* __restrict__ A, const float* __restrict__ B, int M, i
 }
 
 // ------------------------------------------------------------------ host side
+static int g_variant = 1;
+void gemm_set_variant(int v) { g_variant = v; }
+
 template <int BM, int BN, bool AK, bool BK, class E>
 static hipError_t run_mfma(const GemmDesc& d, E e, hipStream_t s) {
     constexpr size_t lds = 2 * (size_t)(BM + BN) * 64 * sizeof(bf16);
-    auto kern = gemm_bf16_mfma<BM, BN, AK, BK, E>;
-    static bool attr_done = false;
-    if (!attr_done) {
+    const int v = d.variant >= 0 && d.variant <= 2 ? d.variant : g_variant;
+    auto kern = v == 2   ? gemm_bf16_mfma_db<BM, BN, AK, BK, E>
+                : v == 1 ? gemm_bf16_mfma_pipe<BM, BN, AK, BK, E>
+                         : gemm_bf16_mfma<BM, BN, AK, BK, E>;
+    static bool attr_done[3] = {false, false, false};
+    if (!attr_done[v]) {
         hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (st != hipSuccess) return st;
-        attr_done = true;
+        attr_done[v] = true;
     }
     int tiles = ((d.M + BM - 1) / BM) * ((d.N + BN - 1) / BN);
     dim3 grid(tiles, (d.K + d.k_split - 1) / d.k_split);

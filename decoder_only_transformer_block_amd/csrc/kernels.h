@@ -45,7 +45,9 @@ struct GemmDesc {
     int splits = 1;         // split-K: K is cut into ceil(K / k_split) ranges of k_split (grid.y)
     int k_split = 0;        // multiple of 64; 0 = K / splits
     size_t split_stride = 0;
-    int tile = 0;  // MFMA tile: 0 = 256x256, 1 = 256x128, 2 = 128x128
+    int tile = 0;     // MFMA tile: 0 = 256x256, 1 = 256x128, 2 = 128x128
+    int variant = -1; // MFMA main loop: 0 = plain two-stage, 1 = software-pipelined, 2 = two register stages;
+                      // -1 = the default (gemm_set_variant)
 };
 
 const char* gemm_kernel_name(const GemmDesc& d);
@@ -55,6 +57,8 @@ hipError_t launch_splitk_reduce(const float* part, int splits, size_t stride, fl
                                 int accumulate, hipStream_t s);
 // MFMA kernels need more than the default 64 KB of dynamic LDS; call once per device.
 hipError_t gemm_init_attributes();
+// kernel variant of the bf16 GEMM: 1 = software-pipelined (default), 0 = plain two-stage
+void gemm_set_variant(int v);
 
 // ---------------------------------------------------------------- attention
 struct AttnDesc {
@@ -68,7 +72,8 @@ struct AttnDesc {
     float* delta = nullptr;     // [B, H, T] scratch (backward)
 };
 hipError_t launch_attn_fwd(const AttnDesc& a, hipStream_t s);
-hipError_t launch_attn_bwd(const AttnDesc& a, hipStream_t s);
+// part 0: dQ (and delta = rowsum(dy * y), which part 1 reads); part 1: dK, dV -- in this order
+hipError_t launch_attn_bwd(const AttnDesc& a, hipStream_t s, int part);
 hipError_t attn_init_attributes();
 
 // ---------------------------------------------------------------- row-wise / elementwise

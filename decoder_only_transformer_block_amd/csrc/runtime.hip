@@ -105,8 +105,10 @@ int pick_tile(int64_t M, int64_t N) {
     return best;
 }
 
-// Weight gradient dW[M,N] = sum over K tokens: split K so that one round of
-// workgroups covers the CUs when the output alone has too few tiles.
+// Weight gradient dW[M,N] = sum over K tokens.  The output alone has few
+// tiles (e.g. 9 for 768 x 768) while K is the whole batch of tokens, so K is
+// split until one round of workgroups covers the CUs; large outputs use the
+// forward tile rule.
 WGrad pick_wgrad(Dt dt, int64_t M, int64_t N, int64_t K) {
     WGrad w;
     if (dt == Dt::F32) {
@@ -117,7 +119,12 @@ WGrad pick_wgrad(Dt dt, int64_t M, int64_t N, int64_t K) {
         w.splits = (int)std::max<int64_t>(1, s);
     } else {
         static const int bm[3] = {256, 256, 128}, bn[3] = {256, 128, 128};
-        w.tile = pick_tile(M, N);
+        const int64_t tiles0 = ((M + 255) / 256) * ((N + 255) / 256);
+        if (tiles0 < kCUs) {
+            w.tile = (M >= 256 && N >= 256) ? 0 : 2;
+        } else {
+            w.tile = pick_tile(M, N);
+        }
         int64_t tiles = ((M + bm[w.tile] - 1) / bm[w.tile]) * ((N + bn[w.tile] - 1) / bn[w.tile]);
         int64_t s = tiles >= kCUs ? 1 : kCUs / tiles;
         s = std::min<int64_t>(s, K / 512);
@@ -493,6 +500,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
         d.A = c->ws + p.xf; d.lda = C; d.B = weight(c, -1, 1); d.ldb = C;
         d.M = N; d.N = V; d.K = C;
         d.epi = Epi::StoreCd; d.out = c->ws + p.logits; d.ldo = V;
+        d.variant = 0;  // measured faster than the pipelined loop for this wide, short-K shape
         TRY(gemm(c, d));
     }
     c->state = 1;
@@ -598,8 +606,13 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             ad.qkv = qkv; ad.y = y; ad.lse = c->at<float>(c->lay(l, p.l_lse));
             ad.dy = c->ws + p.dy; ad.dqkv = c->ws + p.dqkv; ad.delta = c->at<float>(p.delta);
             const double pairs = (double)c->B * c->H * c->T * (c->T + 1) / 2.0;
-            TRY(launch(c, dt == Dt::BF16 ? "attn_bwd_bf16" : "attn_bwd_f32", 8.0 * c->D * pairs, 0.0,
-                       [&] { return launch_attn_bwd(ad, c->stream); }));
+            const bool bf = dt == Dt::BF16;
+            // algorithmic backward FLOPs: dV, dK and the dP product (6 D per pair) in the key-outer kernel,
+            // dQ (2 D per pair) in the query-outer one; the recomputed S and dP products are not counted
+            TRY(launch(c, bf ? "attn_bwd_dq_bf16" : "attn_bwd_dq_f32", 2.0 * c->D * pairs, 0.0,
+                       [&] { return launch_attn_bwd(ad, c->stream, 0); }));
+            TRY(launch(c, bf ? "attn_bwd_dkdv_bf16" : "attn_bwd_dkdv_f32", 6.0 * c->D * pairs, 0.0,
+                       [&] { return launch_attn_bwd(ad, c->stream, 1); }));
         }
         TRY(launch(c, "rope_qknorm_bwd", 0.0, (double)N * (c->H + c->Hkv) * c->D * 3 * e, [&] {
             return launch_rope_qknorm_bwd(dt, c->ws + p.dqkv, qkv, c->at<float>(c->lay(l, p.l_rstdq)),

@@ -160,9 +160,13 @@ def test_full_depth12_step_sampled():
         lo, acts = orc.forward(ocfg(wp), ids[b:b + 1, :P], tg[b:b + 1, :P], params)
         e = np.max(np.abs(lr[b, :P] - acts["loss_rows"])) / np.max(np.abs(acts["loss_rows"]))
         assert e <= 1e-2, (b, e)
-    # loss at initialisation: ln V + 0.02^2 C / 2 within the sampling band
+    # at initialisation every row's log-sum-exp is ln V + 0.02^2 C / 2 (unit-RMS final state, N(0, 0.02)
+    # head, averaged over the V logits of the row); the loss itself only within a wide band, because
+    # Zipf streams repeat (input, target) pairs and make the mean of z[target] far from independent
     expect = math.log(w.vocab_size) + 0.5 * 0.02 ** 2 * w.n_embd
-    assert abs(loss - expect) < 0.01 + 5 * math.sqrt(4e-4 * w.n_embd) / math.sqrt(w.n_tokens)
+    lse = s.probe("lse")
+    assert abs(lse.mean() - expect) < 1e-2, lse.mean()
+    assert abs(loss - expect) < 0.1
     g = s.grads_np()
     assert np.isfinite(g).all()
     # embedding gradient rows of ids absent from the batch are exactly zero, present ones are not
