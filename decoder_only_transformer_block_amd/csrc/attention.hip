@@ -100,15 +100,15 @@ struct TilePair {
 };
 
 // ======================================================================== bf16 forward
-// Workgroup: 256 queries of one head (4 waves x 64); K/V tiles of 64 keys,
-// double-buffered.  Each wave's 64 queries are two 32-row MFMA blocks sharing
-// every K and V fragment read.
-constexpr int kFwdLds = 2 * 2 * 64 * 128 * 2;  // 64 KB
-
-__global__ void __launch_bounds__(256, 1)
+// Workgroup: 4 waves x 32*QB queries of one head; K/V tiles of 64 keys,
+// double-buffered.  With QB = 1 a wave fits in 256 registers, so two
+// workgroups share a CU and one wave's softmax (VALU, exp) overlaps the other
+// wave's MFMAs.
+template <int QB>
+__global__ void __launch_bounds__(256, 2)
 attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restrict__ lse, int T, int H, int Hkv)
 {
-    constexpr int D = 128;
+    constexpr int D = 128, QW = 32 * QB, QBLK = 4 * QW;
     __shared__ __attribute__((aligned(16))) bf16 smK[2][64 * 128];
     __shared__ __attribute__((aligned(16))) bf16 smV[2][64 * 128];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
@@ -116,77 +116,83 @@ attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restr
     const int hq = blockIdx.y, b = blockIdx.z;
     const int g = hq / (H / Hkv);
     const int QKV = (H + 2 * Hkv) * D, HD = H * D, KD = Hkv * D;
-    const int q0 = qb * 256;
-    const int qw = q0 + 64 * w;                 // first query of this wave
+    const int q0 = qb * QBLK;
+    const int qw = q0 + QW * w;                 // first query of this wave
     const bool active = qw < T;
     const size_t rowbase = (size_t)b * T;
 
-    bf16x8 qf[2][8];
+    bf16x8 qf[QB][8];
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
+    for (int qq = 0; qq < QB; ++qq) {
         const int q = active ? qw + 32 * qq + l32 : 0;
         const bf16* qp = qkv + (rowbase + q) * QKV + hq * D + 8 * hh;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) qf[qq][kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
     }
-    f32x16 o[2][4];
+    f32x16 o[QB][4];
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq)
+    for (int qq = 0; qq < QB; ++qq)
 #pragma unroll
         for (int db = 0; db < 4; ++db) zero16(o[qq][db]);
-    float lsum[2] = {0.0f, 0.0f};
+    float lsum[QB];
+#pragma unroll
+    for (int qq = 0; qq < QB; ++qq) lsum[qq] = 0.0f;
     const float c1 = kLog2e * rsqrtf((float)D), c2 = sqrtf((float)D) * kLog2e;
 
     const bf16* kbase = qkv + rowbase * QKV + HD + g * D;
     TilePair st;
-    const int nkv = min(q0 + 256, T) / 64;
+    const int nkv = min(q0 + QBLK, T) / 64;
     st.load(kbase, kbase + KD, QKV, tid);
     st.store(smK[0], smV[0], tid);
     __syncthreads();
     for (int t = 0; t < nkv; ++t) {
         const int cur = t & 1, kv0 = t * 64;
         if (t + 1 < nkv) st.load(kbase + (size_t)(kv0 + 64) * QKV, kbase + (size_t)(kv0 + 64) * QKV + KD, QKV, tid);
-        if (active && kv0 <= qw + 63) {
+        if (active && kv0 <= qw + QW - 1) {
             const bf16* Ks = smK[cur];
             const bf16* Vs = smV[cur];
             const bool diag = kv0 + 63 > qw;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                f32x16 s[2];
-                zero16(s[0]);
-                zero16(s[1]);
+                f32x16 s[QB];
+#pragma unroll
+                for (int qq = 0; qq < QB; ++qq) zero16(s[qq]);
 #pragma unroll
                 for (int kk = 0; kk < 8; ++kk) {
                     const bf16x8 kf = rfrag(Ks, 32 * kb + l32, 2 * kk + hh);
-                    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0][kk], s[0], 0, 0, 0);
-                    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[1][kk], s[1], 0, 0, 0);
+#pragma unroll
+                    for (int qq = 0; qq < QB; ++qq)
+                        s[qq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qq][kk], s[qq], 0, 0, 0);
                 }
                 // lane holds S[q = qw + 32qq + l32][key = kv0 + 32kb + 8(r>>2) + 4hh + (r&3)] in s[qq][r]
 #pragma unroll
-                for (int qq = 0; qq < 2; ++qq) {
+                for (int qq = 0; qq < QB; ++qq) {
                     if (diag) {
                         const int q = qw + 32 * qq + l32;
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-                            const float p = exp2f(s[qq][r] * c1 - c2);
+                            const float p = __builtin_amdgcn_exp2f(s[qq][r] * c1 - c2);
                             s[qq][r] = key > q ? 0.0f : p;
                         }
                     } else {
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) s[qq][r] = exp2f(s[qq][r] * c1 - c2);
+                        for (int r = 0; r < 16; ++r) s[qq][r] = __builtin_amdgcn_exp2f(s[qq][r] * c1 - c2);
                     }
 #pragma unroll
                     for (int r = 0; r < 16; ++r) lsum[qq] += s[qq][r];
                 }
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const bf16x8 p0 = pack8(s[0], 8 * j), p1 = pack8(s[1], 8 * j);
+                    bf16x8 pf[QB];
+#pragma unroll
+                    for (int qq = 0; qq < QB; ++qq) pf[qq] = pack8(s[qq], 8 * j);
 #pragma unroll
                     for (int db = 0; db < 4; ++db) {
                         const bf16x8 vf = trfrag(Vs, 32 * db, 32 * kb + 16 * j, lane);
-                        o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p0, o[0][db], 0, 0, 0);
-                        o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p1, o[1][db], 0, 0, 0);
+#pragma unroll
+                        for (int qq = 0; qq < QB; ++qq)
+                            o[qq][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qq], o[qq][db], 0, 0, 0);
                     }
                 }
             }
@@ -196,7 +202,7 @@ attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restr
     }
     if (!active) return;
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
+    for (int qq = 0; qq < QB; ++qq) {
         const int q = qw + 32 * qq + l32;
         const float ltot = lsum[qq] + __shfl_xor(lsum[qq], 32, kWave);
         const float inv = 1.0f / ltot;
@@ -240,7 +246,7 @@ attn_delta(const T* __restrict__ dy, const T* __restrict__ y, float* __restrict_
 // kernel reads it afterwards), then for every tile recomputes S and dP, forms
 // dS = P (dP - delta) / sqrt(D) and accumulates dQ = dS K.
 template <int QB>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, 2)
 attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const bf16* __restrict__ dy,
                  const float* __restrict__ lse, float* __restrict__ delta, bf16* __restrict__ dqkv, int T, int H,
                  int Hkv)
@@ -321,7 +327,7 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
                     const int q = qw + 32 * qq + l32;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        float p = exp2f(s[qq][r] * c1 - l2[qq]);
+                        float p = __builtin_amdgcn_exp2f(s[qq][r] * c1 - l2[qq]);
                         if (diag) {
                             const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
                             p = key > q ? 0.0f : p;
@@ -455,7 +461,7 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int idx = 4 * gg + e;
-                        float p = exp2f(s[idx] * c1 - lv[e]);
+                        float p = __builtin_amdgcn_exp2f(s[idx] * c1 - lv[e]);
                         if (diag) p = q0 + ql + e < key ? 0.0f : p;
                         s[idx] = p;
                         dp[idx] = p * (dp[idx] - dv4[e]) * scale;
@@ -610,8 +616,8 @@ hipError_t attn_init_attributes() {
 hipError_t launch_attn_fwd(const AttnDesc& a, hipStream_t s) {
     if (a.dt == Dt::BF16) {
         if (a.D != 128 || a.T % 128) return hipErrorInvalidValue;
-        dim3 grid((a.T + 255) / 256, a.H, a.B);
-        hipLaunchKernelGGL(attn_fwd_bf16, grid, dim3(256), 0, s, (const bf16*)a.qkv, (bf16*)a.y, a.lse, a.T, a.H,
+        dim3 grid(a.T / 128, a.H, a.B);
+        hipLaunchKernelGGL(attn_fwd_bf16<1>, grid, dim3(256), 0, s, (const bf16*)a.qkv, (bf16*)a.y, a.lse, a.T, a.H,
                            a.Hkv);
         return hipGetLastError();
     }

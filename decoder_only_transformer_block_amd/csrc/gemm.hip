@@ -6,8 +6,8 @@
 // LDS (two stages, XOR-swizzled 16-byte chunks), 4 waves per workgroup in a
 // 2 x 2 grid.  Operands whose K index is not contiguous in memory (the
 // token-major activations of a weight gradient, the [out,in] weight of an
-// input gradient) are transposed 8x8 in registers with v_perm_b32 on their
-// way into LDS, so every MFMA fragment is one 16-byte LDS read.
+// input gradient) are copied to LDS in their natural layout and their MFMA
+// fragments are read with gfx950's transposing LDS load (ds_read_b64_tr_b16).
 //
 // The MFMA is issued with the two operands swapped (it computes C^T), which
 // leaves each lane holding 4 consecutive columns of one output row: the
@@ -149,33 +149,61 @@ template <int R> struct StageK {
     }
 };
 
-// MN-contiguous operand: element (r, k) at P[k*ld + r].  Each active thread
-// moves one 8 (k) x 8 (r) block: eight 16-byte row loads, a register
-// transpose (32 v_perm_b32), eight 16-byte LDS stores of 8 consecutive k.
+// MN-contiguous operand: element (r, k) at P[k*ld + r].  The tile is kept in
+// LDS in this natural layout, [64 k][R r] (16-byte chunks along r), and the
+// MFMA fragment (8 consecutive k of one r) is read with two
+// ds_read_b64_tr_b16.  A transposing read of one 16-lane group covers 4
+// consecutive k rows x 32 bytes; the chunk index is XOR-ed with
+// ((k & 3) << 2) so those 4 rows land in 4 different 64-byte bank groups.
+__device__ __forceinline__ int mn_chunk(int k, int c, int R) { return k * (R / 8) + (c ^ ((k & 3) << 2)); }
+
 template <int R> struct StageMN {
-    u32x4 v[8];
+    static constexpr int CPR = R / 8;            // 16-byte chunks per k row
+    static constexpr int NC = 64 * CPR / 256;    // chunks per thread
+    u32x4 v[NC];
     __device__ __forceinline__ void load(const bf16* __restrict__ P, int ld, int r0, int rmax, int k0, int tid) {
-        if (tid >= R) return;
-        int kb = tid & 7, rb = tid >> 3;
-        int gr = min(r0 + rb * 8, rmax - 8);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            v[i] = *reinterpret_cast<const u32x4*>(P + (size_t)(k0 + kb * 8 + i) * ld + gr);
+        for (int i = 0; i < NC; ++i) {
+            int u = tid + 256 * i;
+            int k = u / CPR, c = u % CPR;
+            int gr = min(r0 + c * 8, rmax - 8);
+            v[i] = *reinterpret_cast<const u32x4*>(P + (size_t)(k0 + k) * ld + gr);
+        }
     }
     __device__ __forceinline__ void store(bf16* S, int tid) const {
-        if (tid >= R) return;
-        int kb = tid & 7, rb = tid >> 3;
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-            const uint32_t sel = (rr & 1) ? 0x07060302u : 0x05040100u;
-            u32x4 o;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) o[p] = __builtin_amdgcn_perm(v[2 * p + 1][rr >> 1], v[2 * p][rr >> 1], sel);
-            int row = rb * 8 + rr;
-            *reinterpret_cast<u32x4*>(S + lds_chunk(row, kb) * 8) = o;
+        for (int i = 0; i < NC; ++i) {
+            int u = tid + 256 * i;
+            int k = u / CPR, c = u % CPR;
+            *reinterpret_cast<u32x4*>(S + mn_chunk(k, c, R) * 8) = v[i];
         }
     }
 };
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// MFMA fragment of lane `lane`: operand row r0 + (lane & 31), k = kk*16 + 8h .. +7.
+template <int R, bool KC>
+__device__ __forceinline__ bf16x8 frag(const bf16* S, int r0, int kk, int lane) {
+    const int h = lane >> 5;
+    if constexpr (KC) {
+        const int row = r0 + (lane & 31);
+        return *reinterpret_cast<const bf16x8*>(S + lds_chunk(row, kk * 2 + h) * 8);
+    } else {
+        // ds_read_b64_tr_b16: lane i of a 16-lane group receives element e of the
+        // 4-value row addressed by lane 4e + i/4, at position i % 4
+        const int sl = lane & 15;
+        const int r = r0 + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+        const int c = r >> 3, o = r & 7;
+        const int k = kk * 16 + 8 * h + (sl >> 2);
+        s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(S + mn_chunk(k, c, R) * 8 + o));
+        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(S + mn_chunk(k + 4, c, R) * 8 + o));
+        s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, v);
+    }
+}
 
 template <int R, bool KC> struct Stage;
 template <int R> struct Stage<R, true> : StageK<R> {};
@@ -235,17 +263,10 @@ gemm_bf16_mfma(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, in
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             bf16x8 af[FM], bfr[FN];
-            const int ch = kk * 2 + h;
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                int row = wm * WM + 32 * i + l32;
-                af[i] = *reinterpret_cast<const bf16x8*>(sA + lds_chunk(row, ch) * 8);
-            }
+            for (int i = 0; i < FM; ++i) af[i] = frag<BM, AK>(sA, wm * WM + 32 * i, kk, lane);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                int row = wn * WN + 32 * j + l32;
-                bfr[j] = *reinterpret_cast<const bf16x8*>(sB + lds_chunk(row, ch) * 8);
-            }
+            for (int j = 0; j < FN; ++j) bfr[j] = frag<BN, BK>(sB, wn * WN + 32 * j, kk, lane);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -315,17 +336,10 @@ gemm_bf16_mfma_pipe(const bf16* __restrict__ A, const bf16* __restrict__ B, int 
     auto lfrag = [&](int buf, int st, int kk) {
         const bf16* sA = base + st * (TA + TB);
         const bf16* sB = sA + TA;
-        const int ch = kk * 2 + h;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            int row = wm * WM + 32 * i + l32;
-            fa[buf][i] = *reinterpret_cast<const bf16x8*>(sA + lds_chunk(row, ch) * 8);
-        }
+        for (int i = 0; i < FM; ++i) fa[buf][i] = frag<BM, AK>(sA, wm * WM + 32 * i, kk, lane);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            int row = wn * WN + 32 * j + l32;
-            fb[buf][j] = *reinterpret_cast<const bf16x8*>(sB + lds_chunk(row, ch) * 8);
-        }
+        for (int j = 0; j < FN; ++j) fb[buf][j] = frag<BN, BK>(sB, wn * WN + 32 * j, kk, lane);
     };
 
     f32x16 acc[FM][FN];
@@ -431,17 +445,10 @@ gemm_bf16_mfma_db(const bf16* __restrict__ A, const bf16* __restrict__ B, int M,
     auto lfrag = [&](int buf, int st, int kk) {
         const bf16* sA = base + st * (TA + TB);
         const bf16* sB = sA + TA;
-        const int ch = kk * 2 + h;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            int row = wm * WM + 32 * i + l32;
-            fa[buf][i] = *reinterpret_cast<const bf16x8*>(sA + lds_chunk(row, ch) * 8);
-        }
+        for (int i = 0; i < FM; ++i) fa[buf][i] = frag<BM, AK>(sA, wm * WM + 32 * i, kk, lane);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            int row = wn * WN + 32 * j + l32;
-            fb[buf][j] = *reinterpret_cast<const bf16x8*>(sB + lds_chunk(row, ch) * 8);
-        }
+        for (int j = 0; j < FN; ++j) fb[buf][j] = frag<BN, BK>(sB, wn * WN + 32 * j, kk, lane);
     };
 
     f32x16 acc[FM][FN];
@@ -678,6 +685,7 @@ const char* gemm_kernel_name(const GemmDesc& d) {
         {"gemm_bf16_tn_256x256", "gemm_bf16_tn_256x128", "gemm_bf16_tn_128x128"}};
     int r = li == 3 ? 0 : (li == 2 ? 1 : 2);
     int t = d.tile < 0 ? 0 : (d.tile > 2 ? 2 : d.tile);
+    (void)lay;
     return names[r][t];
 }
 

@@ -45,7 +45,7 @@ struct GemmDesc {
     int splits = 1;         // split-K: K is cut into ceil(K / k_split) ranges of k_split (grid.y)
     int k_split = 0;        // multiple of 64; 0 = K / splits
     size_t split_stride = 0;
-    int tile = 0;     // MFMA tile: 0 = 256x256, 1 = 256x128, 2 = 128x128
+    int tile = -1;    // MFMA tile: 0 = 256x256, 1 = 256x128, 2 = 128x128; -1 = chosen from the shape
     int variant = -1; // MFMA main loop: 0 = plain two-stage, 1 = software-pipelined, 2 = two register stages;
                       // -1 = the default (gemm_set_variant)
 };

@@ -265,7 +265,7 @@ const char* intern(const std::string& s) {
 
 ncgpt_status gemm(ncgpt_ctx* c, GemmDesc d) {
     d.dt = c->dt;
-    if (c->dt == Dt::BF16 && d.epi != Epi::Grad && d.epi != Epi::SplitK) d.tile = pick_tile(d.M, d.N);
+    if (d.tile < 0) d.tile = pick_tile(d.M, d.N);
     const char* nm = intern(std::string(gemm_kernel_name(d)) + ":" + epi_name(d.epi));
     double fl = 2.0 * d.M * d.N * d.K;
     return launch(c, nm, fl, 0.0, [&] { return launch_gemm(d, c->stream); });
@@ -273,10 +273,12 @@ ncgpt_status gemm(ncgpt_ctx* c, GemmDesc d) {
 
 // weight gradient: out(f32 grads slice [M,N]) (+)= A^T-layout x B^T-layout over K tokens
 ncgpt_status wgrad(ncgpt_ctx* c, const void* dY, int ldy, const void* X, int ldx, int M, int N, float* g,
-                   int accumulate) {
+                   int accumulate, int tile = -1, int variant = -1) {
     const int K = (int)c->N;
     WGrad w = pick_wgrad(c->dt, M, N, K);
+    if (tile >= 0 && w.splits == 1) w.tile = tile;
     GemmDesc d;
+    d.variant = variant;
     d.A = dY; d.lda = ldy; d.a_kcontig = false;
     d.B = X; d.ldb = ldx; d.b_kcontig = false;
     d.M = M; d.N = N; d.K = K;
@@ -500,7 +502,9 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
         d.A = c->ws + p.xf; d.lda = C; d.B = weight(c, -1, 1); d.ldb = C;
         d.M = N; d.N = V; d.K = C;
         d.epi = Epi::StoreCd; d.out = c->ws + p.logits; d.ldo = V;
-        d.variant = 0;  // measured faster than the pipelined loop for this wide, short-K shape
+        // vocab-wide output, K = n_embd: 128 x 128 tiles with two register stages measured fastest
+        d.tile = 2;
+        d.variant = 2;
         TRY(gemm(c, d));
     }
     c->state = 1;
@@ -561,7 +565,8 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
         d.epi = Epi::StoreF32; d.out = dxn; d.ldo = C;
         TRY(gemm(c, d));
     }
-    TRY(wgrad(c, logits, V, c->ws + p.xf, C, V, C, gslice(-1, 1), acc));  // dWlm = dz^T xf
+    // dWlm = dz^T xf (vocab-wide output: 128 x 128 tiles with two register stages measured fastest)
+    TRY(wgrad(c, logits, V, c->ws + p.xf, C, V, C, gslice(-1, 1), acc, 2, 2));
     const double nb = (double)N * C * (e + 4 + 4 + (dt == Dt::BF16 ? 2 : 0)) + N * 4.0;
     TRY(launch(c, "rmsnorm_bwd", 0.0, nb, [&] {
         return launch_rmsnorm_bwd(dt, c->ws + p.xf, c->at<float>(p.rstdf), dxn, dx, dx_cd, N, C, 0, c->stream);
