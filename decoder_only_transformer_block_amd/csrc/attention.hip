@@ -366,18 +366,21 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
 }
 
 // ======================================================================== bf16 backward: dK, dV
-// Workgroup: 128 keys of one kv head (4 waves x 32 keys, K and V fragments
-// held in registers), looping over the r query heads of the group and over
-// the query tiles (64 rows) at or after the keys.  Q and dO tiles are
-// double-buffered in LDS with their log-sum-exp and delta rows.
+// Workgroup: 128 keys of one kv head (4 waves x 32 keys), looping over the r
+// query heads of the group and over the 64-row query tiles at or after the
+// keys.  K fragments stay in registers and the workgroup's V rows in LDS, so
+// a wave fits in 256 registers and two workgroups share a CU: the Q / dO tile
+// of each step is loaded straight into a single LDS buffer and the other
+// workgroup's MFMAs cover that load.
 struct DkvSmem {
-    bf16 Q[2][64 * 128];
-    bf16 dO[2][64 * 128];
-    float lse2[2][64];
-    float dlt[2][64];
+    bf16 Q[64 * 128];
+    bf16 dO[64 * 128];
+    bf16 V[128 * 128];
+    float lse2[64];
+    float dlt[64];
 };
 
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, 2)
 attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, const float* __restrict__ lse,
                    const float* __restrict__ delta, bf16* __restrict__ dqkv, int T, int H, int Hkv)
 {
@@ -395,93 +398,86 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
     const size_t rowbase = (size_t)b * T;
     const float scale = rsqrtf((float)D), c1 = kLog2e * scale;
 
-    bf16x8 kf[8], vf[8];
+    bf16x8 kf[8];
     {
         const bf16* kp = qkv + (rowbase + key) * QKV + HD + g * D + 8 * hh;
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            kf[kk] = *reinterpret_cast<const bf16x8*>(kp + 16 * kk);
-            vf[kk] = *reinterpret_cast<const bf16x8*>(kp + KD + 16 * kk);
-        }
+        for (int kk = 0; kk < 8; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(kp + 16 * kk);
+    }
+    // the workgroup's 128 V rows, once
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int u = tid + 256 * i, row = u >> 4, c = u & 15;
+        *reinterpret_cast<u32x4*>(sm.V + toff(row, c)) =
+            *reinterpret_cast<const u32x4*>(qkv + (rowbase + k0 + row) * QKV + HD + KD + g * D + c * 8);
     }
     f32x16 dk[4], dv[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) { zero16(dk[db]); zero16(dv[db]); }
 
-    TilePair st;
-    float srow = 0.0f;
-    // Q and dO rows have different strides: each half of the chunks uses its own
-    auto gload2 = [&](int hq, int q0) {
+    const int qt0 = k0 / 64, nqt = T / 64 - qt0;
+    const int total = r * nqt;
+    for (int it = 0; it < total; ++it) {
+        const int hq = g * r + it / nqt;
+        const int q0 = (qt0 + it % nqt) * 64;
+        __syncthreads();  // the previous tile has been consumed
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int u = tid + 256 * i, row = (u >> 4) & 63, c = u & 15;
             const bf16* src = i < 4 ? qkv + (rowbase + q0 + row) * QKV + hq * D + c * 8
                                     : dy + (rowbase + q0 + row) * HD + hq * D + c * 8;
-            st.v[i] = *reinterpret_cast<const u32x4*>(src);
+            *reinterpret_cast<u32x4*>((i < 4 ? sm.Q : sm.dO) + toff(row, c)) = *reinterpret_cast<const u32x4*>(src);
         }
-        if (tid < 64) srow = lse[((size_t)b * H + hq) * T + q0 + tid] * kLog2e;
-        else if (tid < 128) srow = delta[((size_t)b * H + hq) * T + q0 + tid - 64];
-    };
-    auto lstore = [&](int sidx) {
-        st.store(sm.Q[sidx], sm.dO[sidx], tid);
-        if (tid < 64) sm.lse2[sidx][tid] = srow;
-        else if (tid < 128) sm.dlt[sidx][tid - 64] = srow;
-    };
-
-    const int qt0 = k0 / 64, nqt = T / 64 - qt0;
-    const int total = r * nqt;
-    gload2(g * r, k0);
-    lstore(0);
-    __syncthreads();
-    for (int it = 0; it < total; ++it) {
-        const int cur = it & 1;
-        const int q0 = (qt0 + it % nqt) * 64;
-        if (it + 1 < total) gload2(g * r + (it + 1) / nqt, (qt0 + (it + 1) % nqt) * 64);
-        if (q0 + 63 >= kw) {  // wave-uniform: some query of the tile sees some key of the wave
-            const bf16* Qs = sm.Q[cur];
-            const bf16* Gs = sm.dO[cur];
-            const bool diag = q0 < kw + 31;
+        if (tid < 64) sm.lse2[tid] = lse[((size_t)b * H + hq) * T + q0 + tid] * kLog2e;
+        else if (tid < 128) sm.dlt[tid - 64] = delta[((size_t)b * H + hq) * T + q0 + tid - 64];
+        __syncthreads();
+        if (q0 + 63 < kw) continue;  // wave-uniform: every query of the tile precedes every key of the wave
+        const bool diag = q0 < kw + 31;
+        // Re-derive the lane index each step: the fragment addresses (swizzled,
+        // so not affine in the unrolled k-step) are then recomputed here rather
+        // than hoisted out of the loop into ~40 live registers.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int l32v = ln & 31, hhv = ln >> 5;
 #pragma unroll
-            for (int qb2 = 0; qb2 < 2; ++qb2) {
-                f32x16 s, dp;
-                zero16(s);
-                zero16(dp);
+        for (int qb2 = 0; qb2 < 2; ++qb2) {
+            f32x16 s, dp;
+            zero16(s);
+            zero16(dp);
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(Qs, 32 * qb2 + l32, 2 * kk + hh), kf[kk], s, 0, 0, 0);
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(Gs, 32 * qb2 + l32, 2 * kk + hh), vf[kk], dp, 0, 0, 0);
+            for (int kk = 0; kk < 8; ++kk) {
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(sm.Q, 32 * qb2 + l32v, 2 * kk + hhv), kf[kk], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(sm.dO, 32 * qb2 + l32v, 2 * kk + hhv),
+                                                             rfrag(sm.V, 32 * w + l32v, 2 * kk + hhv), dp, 0, 0, 0);
+            }
+            // lane holds S[q = q0 + 32qb2 + 8(e>>2) + 4hh + (e&3)][key] in s[e]
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                const int ql = 32 * qb2 + 8 * gg + 4 * hhv;
+                const float4 l4 = *reinterpret_cast<const float4*>(&sm.lse2[ql]);
+                const float4 d4 = *reinterpret_cast<const float4*>(&sm.dlt[ql]);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int idx = 4 * gg + e;
+                    float p = __builtin_amdgcn_exp2f(s[idx] * c1 - lv[e]);
+                    if (diag) p = q0 + ql + e < key ? 0.0f : p;
+                    s[idx] = p;
+                    dp[idx] = p * (dp[idx] - dv4[e]) * scale;
                 }
-                // lane holds S[q = q0 + 32qb2 + 8(e>>2) + 4hh + (e&3)][key] in s[e]
+            }
 #pragma unroll
-                for (int gg = 0; gg < 4; ++gg) {
-                    const int ql = 32 * qb2 + 8 * gg + 4 * hh;
-                    const float4 l4 = *reinterpret_cast<const float4*>(&sm.lse2[cur][ql]);
-                    const float4 d4 = *reinterpret_cast<const float4*>(&sm.dlt[cur][ql]);
-                    const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+            for (int j2 = 0; j2 < 2; ++j2) {
+                const bf16x8 pf = pack8(s, 8 * j2), dsf = pack8(dp, 8 * j2);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int idx = 4 * gg + e;
-                        float p = __builtin_amdgcn_exp2f(s[idx] * c1 - lv[e]);
-                        if (diag) p = q0 + ql + e < key ? 0.0f : p;
-                        s[idx] = p;
-                        dp[idx] = p * (dp[idx] - dv4[e]) * scale;
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const bf16x8 pf = pack8(s, 8 * j), dsf = pack8(dp, 8 * j);
-#pragma unroll
-                    for (int db = 0; db < 4; ++db) {
-                        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(Gs, 32 * db, 32 * qb2 + 16 * j, lane), pf,
-                                                                          dv[db], 0, 0, 0);
-                        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(Qs, 32 * db, 32 * qb2 + 16 * j, lane), dsf,
-                                                                          dk[db], 0, 0, 0);
-                    }
+                for (int db = 0; db < 4; ++db) {
+                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(sm.dO, 32 * db, 32 * qb2 + 16 * j2, ln), pf,
+                                                                      dv[db], 0, 0, 0);
+                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(sm.Q, 32 * db, 32 * qb2 + 16 * j2, ln), dsf,
+                                                                      dk[db], 0, 0, 0);
                 }
             }
         }
-        if (it + 1 < total) lstore(cur ^ 1);
-        __syncthreads();
     }
     bf16* kout = dqkv + (rowbase + key) * QKV + HD + g * D;
 #pragma unroll

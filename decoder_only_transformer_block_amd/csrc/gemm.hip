@@ -127,13 +127,13 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
 __device__ __forceinline__ int lds_chunk(int row, int ch) { return row * 8 + (ch ^ ((row & 7) ^ ((row >> 3) & 1))); }
 
 // K-contiguous operand: element (r, k) at P[r*ld + k].
-template <int R> struct StageK {
-    static constexpr int NC = R / 32;  // 16-byte chunks per thread
+template <int R, int NT = 256> struct StageK {
+    static constexpr int NC = R * 8 / NT;  // 16-byte chunks per thread
     u32x4 v[NC];
     __device__ __forceinline__ void load(const bf16* __restrict__ P, int ld, int r0, int rmax, int k0, int tid) {
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
-            int u = tid + 256 * i;
+            int u = tid + NT * i;
             int row = u >> 3, ch = u & 7;
             int gr = min(r0 + row, rmax - 1);
             v[i] = *reinterpret_cast<const u32x4*>(P + (size_t)gr * ld + k0 + ch * 8);
@@ -142,7 +142,7 @@ template <int R> struct StageK {
     __device__ __forceinline__ void store(bf16* S, int tid) const {
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
-            int u = tid + 256 * i;
+            int u = tid + NT * i;
             int row = u >> 3, ch = u & 7;
             *reinterpret_cast<u32x4*>(S + lds_chunk(row, ch) * 8) = v[i];
         }
@@ -157,14 +157,14 @@ template <int R> struct StageK {
 // ((k & 3) << 2) so those 4 rows land in 4 different 64-byte bank groups.
 __device__ __forceinline__ int mn_chunk(int k, int c, int R) { return k * (R / 8) + (c ^ ((k & 3) << 2)); }
 
-template <int R> struct StageMN {
+template <int R, int NT = 256> struct StageMN {
     static constexpr int CPR = R / 8;            // 16-byte chunks per k row
-    static constexpr int NC = 64 * CPR / 256;    // chunks per thread
+    static constexpr int NC = 64 * CPR / NT;     // chunks per thread
     u32x4 v[NC];
     __device__ __forceinline__ void load(const bf16* __restrict__ P, int ld, int r0, int rmax, int k0, int tid) {
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
-            int u = tid + 256 * i;
+            int u = tid + NT * i;
             int k = u / CPR, c = u % CPR;
             int gr = min(r0 + c * 8, rmax - 8);
             v[i] = *reinterpret_cast<const u32x4*>(P + (size_t)(k0 + k) * ld + gr);
@@ -173,7 +173,7 @@ template <int R> struct StageMN {
     __device__ __forceinline__ void store(bf16* S, int tid) const {
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
-            int u = tid + 256 * i;
+            int u = tid + NT * i;
             int k = u / CPR, c = u % CPR;
             *reinterpret_cast<u32x4*>(S + mn_chunk(k, c, R) * 8) = v[i];
         }
@@ -205,9 +205,9 @@ __device__ __forceinline__ bf16x8 frag(const bf16* S, int r0, int kk, int lane) 
     }
 }
 
-template <int R, bool KC> struct Stage;
-template <int R> struct Stage<R, true> : StageK<R> {};
-template <int R> struct Stage<R, false> : StageMN<R> {};
+template <int R, bool KC, int NT = 256> struct Stage;
+template <int R, int NT> struct Stage<R, true, NT> : StageK<R, NT> {};
+template <int R, int NT> struct Stage<R, false, NT> : StageMN<R, NT> {};
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
 template <int BM, int BN, bool AK, bool BK, class E>
@@ -388,6 +388,103 @@ gemm_bf16_mfma_pipe(const bf16* __restrict__ A, const bf16* __restrict__ B, int 
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
             }
+        }
+        lstore(cur ^ 1);
+        __syncthreads();
+        lfrag(0, cur ^ 1, 0);
+    }
+
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wm * WM + 32 * i + l32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * WN + 32 * j + 8 * g + 4 * h;
+                if (n < N) {
+                    float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    epi(m, n, split, v);
+                }
+            }
+    }
+}
+
+// ------------------------------------------------------------------ bf16 MFMA kernel, 8 waves
+// The pipelined loop above with 512 threads: 8 waves in a 2 x 4 grid, each
+// owning a (BM/2) x (BN/4) sub-tile, so a wave holds half the accumulators and
+// fits in 256 registers.  Two waves then share each SIMD, and one wave's LDS
+// reads, barrier and memory waits overlap the other's MFMAs; the LDS read
+// traffic per MFMA grows by half, which the 64-bank LDS absorbs.
+template <int BM, int BN, bool AK, bool BK, class E>
+__global__ void __launch_bounds__(512, 1)
+gemm_bf16_mfma_w8(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
+                  int k_split, E epi)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    constexpr int TA = BM * 64, TB = BN * 64;
+    constexpr int WM = BM / 2, WN = BN / 4, FM = WM / 32, FN = WN / 32;
+    bf16* base = reinterpret_cast<bf16*>(smem);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 2, wn = w & 3, h = lane >> 5, l32 = lane & 31;
+
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    int tm, tn;
+    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int split = blockIdx.y;
+    const int kbeg = split * k_split;
+    const int nk = min(k_split, K - kbeg) / 64;
+
+    Stage<BM, AK, 512> sa;
+    Stage<BN, BK, 512> sb;
+    auto gload = [&](int k0) {
+        sa.load(A, lda, m0, M, k0, tid);
+        sb.load(B, ldb, n0, N, k0, tid);
+    };
+    auto lstore = [&](int st) {
+        sa.store(base + st * (TA + TB), tid);
+        sb.store(base + st * (TA + TB) + TA, tid);
+    };
+    bf16x8 fa[2][FM], fb[2][FN];
+    auto lfrag = [&](int buf, int st, int kk) {
+        const bf16* sA = base + st * (TA + TB);
+        const bf16* sB = sA + TA;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[buf][i] = frag<BM, AK>(sA, wm * WM + 32 * i, kk, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[buf][j] = frag<BN, BK>(sB, wn * WN + 32 * j, kk, lane);
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    if (nk > 0) {
+        gload(kbeg);
+        lstore(0);
+    }
+    __syncthreads();
+    if (nk > 0) lfrag(0, 0, 0);
+    const int klast = kbeg + (nk - 1) * 64;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        gload(min(kbeg + (kt + 1) * 64, klast));  // past the end: a harmless reload of the last stage
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int fc = kk & 1;
+            if (kk < 3) lfrag(fc ^ 1, cur, kk + 1);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fc][j], fa[fc][i], acc[i][j], 0, 0, 0);
         }
         lstore(cur ^ 1);
         __syncthreads();
@@ -599,11 +696,13 @@ void gemm_set_variant(int v) { g_variant = v; }
 template <int BM, int BN, bool AK, bool BK, class E>
 static hipError_t run_mfma(const GemmDesc& d, E e, hipStream_t s) {
     constexpr size_t lds = 2 * (size_t)(BM + BN) * 64 * sizeof(bf16);
-    const int v = d.variant >= 0 && d.variant <= 2 ? d.variant : g_variant;
-    auto kern = v == 2   ? gemm_bf16_mfma_db<BM, BN, AK, BK, E>
+    const int v = d.variant >= 0 && d.variant <= 3 ? d.variant : g_variant;
+    auto kern = v == 3   ? gemm_bf16_mfma_w8<BM, BN, AK, BK, E>
+                : v == 2 ? gemm_bf16_mfma_db<BM, BN, AK, BK, E>
                 : v == 1 ? gemm_bf16_mfma_pipe<BM, BN, AK, BK, E>
                          : gemm_bf16_mfma<BM, BN, AK, BK, E>;
-    static bool attr_done[3] = {false, false, false};
+    const int nthreads = v == 3 ? 512 : 256;
+    static bool attr_done[4] = {false, false, false, false};
     if (!attr_done[v]) {
         hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -612,7 +711,7 @@ static hipError_t run_mfma(const GemmDesc& d, E e, hipStream_t s) {
     }
     int tiles = ((d.M + BM - 1) / BM) * ((d.N + BN - 1) / BN);
     dim3 grid(tiles, (d.K + d.k_split - 1) / d.k_split);
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, d.K, d.lda,
+    hipLaunchKernelGGL(kern, grid, dim3(nthreads), lds, s, (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, d.K, d.lda,
                        d.ldb, d.k_split, e);
     return hipGetLastError();
 }

@@ -46,7 +46,8 @@ struct GemmDesc {
     int k_split = 0;        // multiple of 64; 0 = K / splits
     size_t split_stride = 0;
     int tile = -1;    // MFMA tile: 0 = 256x256, 1 = 256x128, 2 = 128x128; -1 = chosen from the shape
-    int variant = -1; // MFMA main loop: 0 = plain two-stage, 1 = software-pipelined, 2 = two register stages;
+    int variant = -1; // MFMA main loop: 0 = plain two-stage, 1 = software-pipelined, 2 = two register stages,
+                      // 3 = software-pipelined with 8 waves;
                       // -1 = the default (gemm_set_variant)
 };
 
