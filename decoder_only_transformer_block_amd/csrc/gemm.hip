@@ -508,6 +508,180 @@ gemm_bf16_mfma_w8(const bf16* __restrict__ A, const bf16* __restrict__ B, int M,
     }
 }
 
+// ------------------------------------------------------------------ bf16 MFMA kernel, direct-to-LDS loads
+// Tiles travel from memory straight into LDS (buffer_load_dwordx4 ... lds):
+// no registers stage them and no LDS store instructions are issued.  One
+// wave-instruction fills 1 KB of consecutive LDS chunk slots; each lane
+// fetches the global 16-byte chunk whose swizzled slot it fills, so the LDS
+// layouts are exactly those of the register-staged kernels.  A lane's byte
+// offset differs between its instructions only by a wave-uniform stride,
+// which goes into the scalar offset, and the buffer base moves with k, so a
+// lane keeps one offset register per operand.  Rows past the matrix end lie
+// past the buffer's record count and read as zeros; columns past a ragged
+// edge read neighbouring elements of the same matrix and only reach outputs
+// that are never stored.  The loads of stage k+1 run under the MFMAs of stage
+// k; each wave waits for its own loads and a barrier publishes the stage.
+// The two stages are distinct LDS arrays, which lets the compiler see that
+// fragment reads of one never wait for the loads into the other.
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int R, bool KC>
+struct DmaTile {
+    static constexpr int NI = R / 32;                    // wave-instructions per wave and stage
+    static constexpr int CPR = R / 8;                    // 16-byte chunks per k-row (MN layout)
+    unsigned vo;                                         // lane's byte offset in its first instruction
+    int step;                                            // bytes between a lane's instructions
+    int w;                                               // wave index (uniform)
+
+    __device__ __forceinline__ void init(int ld, int tid) {
+        const int lane = tid & 63;
+        w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        if constexpr (KC) {
+            // chunk q = 64 w + 256 i + lane: row q / 8 (advances 32 per i), slot q % 8
+            const int row = 8 * w + (lane >> 3);
+            const int ch = (lane & 7) ^ ((lane >> 3) ^ (w & 1));
+            vo = (unsigned)(row * ld * 2 + ch * 16);
+            step = 32 * ld * 2;
+        } else {
+            // chunk q: k-row q / CPR (advances 256 / CPR per i), slot q % CPR
+            const int k = (64 * w + lane) / CPR;
+            const int c = (lane % CPR) ^ ((k & 3) << 2);
+            vo = (unsigned)(k * ld * 2 + c * 16);
+            step = (256 / CPR) * ld * 2;
+        }
+    }
+    // one 64-deep stage starting at k0 into S
+    __device__ __forceinline__ void load(const bf16* __restrict__ P, int ld, int r0, int rmax, int k0, bool valid,
+                                         bf16* S) const {
+        const bf16* base;
+        unsigned bytes;
+        if constexpr (KC) {
+            base = P + (size_t)r0 * ld + k0;
+            bytes = (unsigned)(((min(rmax - r0, R) - 1) * ld + 64) * 2);
+        } else {
+            base = P + (size_t)k0 * ld + r0;
+            bytes = (unsigned)((63 * ld + min(rmax - r0, R)) * 2);
+        }
+        if (!valid) bytes = 0;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(S + (64 * w + 256 * i) * 8), 16, vo, i * step,
+                                                     0, 0);
+    }
+};
+
+template <int BM, int BN, bool AK, bool BK, class E>
+__global__ void __launch_bounds__(256, 1)
+gemm_bf16_mfma_dma(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
+                   int k_split, E epi)
+{
+    __shared__ __attribute__((aligned(1024))) bf16 sA0[BM * 64];
+    __shared__ __attribute__((aligned(1024))) bf16 sB0[BN * 64];
+    __shared__ __attribute__((aligned(1024))) bf16 sA1[BM * 64];
+    __shared__ __attribute__((aligned(1024))) bf16 sB1[BN * 64];
+    constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+    constexpr int NL = DmaTile<BM, AK>::NI + DmaTile<BN, BK>::NI;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1, h = lane >> 5, l32 = lane & 31;
+
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    int tm, tn;
+    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int split = blockIdx.y;
+    const int kbeg = split * k_split;
+    const int nk = min(k_split, K - kbeg) / 64;
+
+    DmaTile<BM, AK> da;
+    DmaTile<BN, BK> db;
+    da.init(lda, tid);
+    db.init(ldb, tid);
+    auto dma = [&](int kt, bf16* sA, bf16* sB) {
+        da.load(A, lda, m0, M, kbeg + kt * 64, kt < nk, sA);
+        db.load(B, ldb, n0, N, kbeg + kt * 64, kt < nk, sB);
+    };
+    bf16x8 fa[2][FM], fb[2][FN];
+    auto lfrag = [&](int buf, const bf16* sA, const bf16* sB, int kk) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[buf][i] = frag<BM, AK>(sA, wm * WM + 32 * i, kk, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[buf][j] = frag<BN, BK>(sB, wn * WN + 32 * j, kk, lane);
+    };
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    // the MFMAs of one stage (its first fragments already in registers), with the
+    // next stage's loads spread over the first k-step
+    auto compute = [&](const bf16* sA, const bf16* sB) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int fc = kk & 1;
+            if (kk < 3) lfrag(fc ^ 1, sA, sB, kk + 1);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fc][j], fa[fc][i], acc[i][j], 0, 0, 0);
+            if (kk < 3) {
+#pragma unroll
+                for (int q = 0; q < FM + FN; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+                }
+            }
+            if (kk == 0) {
+#pragma unroll
+                for (int q = 0; q < NL && q < FM * FN - (FM + FN); ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 memory load
+                }
+            }
+        }
+    };
+    auto publish = [&]() {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+
+    // two stages per iteration; a stage past the end reads as zeros (its buffer
+    // holds no records), so an odd count costs one idle stage and no branch
+    dma(0, sA0, sB0);
+    publish();
+    lfrag(0, sA0, sB0, 0);
+    for (int kt = 0; kt < nk; kt += 2) {
+        dma(kt + 1, sA1, sB1);
+        compute(sA0, sB0);
+        publish();
+        lfrag(0, sA1, sB1, 0);
+        dma(kt + 2, sA0, sB0);
+        compute(sA1, sB1);
+        publish();
+        lfrag(0, sA0, sB0, 0);
+    }
+
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wm * WM + 32 * i + l32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * WN + 32 * j + 8 * g + 4 * h;
+                if (n < N) {
+                    float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    epi(m, n, split, v);
+                }
+            }
+    }
+}
+
 // ------------------------------------------------------------------ bf16 MFMA kernel, two register stages
 // The global loads of stage k+2 are issued while stage k is computed and
 // written to LDS only at the end of stage k+1, so every load has two stages of
@@ -690,20 +864,22 @@ gemm_f32_simt(const float* __restrict__ A, const float* __restrict__ B, int M, i
 }
 
 // ------------------------------------------------------------------ host side
-static int g_variant = 1;
+static int g_variant = 4;
 void gemm_set_variant(int v) { g_variant = v; }
 
 template <int BM, int BN, bool AK, bool BK, class E>
 static hipError_t run_mfma(const GemmDesc& d, E e, hipStream_t s) {
     constexpr size_t lds = 2 * (size_t)(BM + BN) * 64 * sizeof(bf16);
-    const int v = d.variant >= 0 && d.variant <= 3 ? d.variant : g_variant;
-    auto kern = v == 3   ? gemm_bf16_mfma_w8<BM, BN, AK, BK, E>
+    const int v = d.variant >= 0 && d.variant <= 4 ? d.variant : g_variant;
+    auto kern = v == 4   ? gemm_bf16_mfma_dma<BM, BN, AK, BK, E>
+                : v == 3 ? gemm_bf16_mfma_w8<BM, BN, AK, BK, E>
                 : v == 2 ? gemm_bf16_mfma_db<BM, BN, AK, BK, E>
                 : v == 1 ? gemm_bf16_mfma_pipe<BM, BN, AK, BK, E>
                          : gemm_bf16_mfma<BM, BN, AK, BK, E>;
     const int nthreads = v == 3 ? 512 : 256;
-    static bool attr_done[4] = {false, false, false, false};
-    if (!attr_done[v]) {
+    const size_t dyn = v == 4 ? 0 : lds;  // the direct-to-LDS kernel uses static LDS
+    static bool attr_done[5] = {false, false, false, false, false};
+    if (v != 4 && !attr_done[v]) {
         hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (st != hipSuccess) return st;
@@ -711,7 +887,7 @@ static hipError_t run_mfma(const GemmDesc& d, E e, hipStream_t s) {
     }
     int tiles = ((d.M + BM - 1) / BM) * ((d.N + BN - 1) / BN);
     dim3 grid(tiles, (d.K + d.k_split - 1) / d.k_split);
-    hipLaunchKernelGGL(kern, grid, dim3(nthreads), lds, s, (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, d.K, d.lda,
+    hipLaunchKernelGGL(kern, grid, dim3(nthreads), dyn, s, (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, d.K, d.lda,
                        d.ldb, d.k_split, e);
     return hipGetLastError();
 }

@@ -566,7 +566,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
         TRY(gemm(c, d));
     }
     // dWlm = dz^T xf (vocab-wide output: 128 x 128 tiles with two register stages measured fastest)
-    TRY(wgrad(c, logits, V, c->ws + p.xf, C, V, C, gslice(-1, 1), acc, 2, 2));
+    TRY(wgrad(c, logits, V, c->ws + p.xf, C, V, C, gslice(-1, 1), acc, 2));
     const double nb = (double)N * C * (e + 4 + 4 + (dt == Dt::BF16 ? 2 : 0)) + N * 4.0;
     TRY(launch(c, "rmsnorm_bwd", 0.0, nb, [&] {
         return launch_rmsnorm_bwd(dt, c->ws + p.xf, c->at<float>(p.rstdf), dxn, dx, dx_cd, N, C, 0, c->stream);
