@@ -9,8 +9,8 @@ throughput on a bounded sample of the same workload.
     python bench.py [--steps K] [--warmup W] [--workload d12] [--no-cpu-baseline]
 """
 import argparse
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -19,6 +19,8 @@ import numpy as np
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, 256 CUs at 2.4 GHz
 PEAK_HBM_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+COPY_MIB = 256              # size of the calibration copy (see copy_calibration)
 
 
 def flops_per_token(w):
@@ -30,15 +32,16 @@ def flops_per_token(w):
     return 6.0 * n_mm + 6.0 * w.n_layer * w.n_head * w.head_dim * (w.seq_len + 1)
 
 
-def cpu_baseline(w, seq_len=256):
-    """The CPU oracle (fp64, OpenMP) on one sequence of seq_len tokens of the
-    same model: forward + loss + backward, timed on this host."""
+def cpu_baseline(w):
+    """The CPU oracle (fp64, OpenMP) on one sequence of the workload's length
+    (same model, same sequence length, batch 1): forward + loss + backward,
+    timed on this host."""
     import oracle as orc
     from decoder_only_transformer_block_amd.inputs import init_params, split_stream, token_stream
-    ws = w.with_(batch=1, seq_len=seq_len)
+    ws = w.with_(batch=1)
     cfg = orc.OracleConfig(ws.n_layer, ws.n_embd, ws.n_head, ws.n_kv_head, ws.head_dim, ws.mlp_dim, ws.vocab_size,
                            ws.batch, ws.seq_len)
-    ids, tg = split_stream(token_stream(ws.vocab_size, 1, seq_len, ws.tokens, 1))
+    ids, tg = split_stream(token_stream(ws.vocab_size, 1, ws.seq_len, ws.tokens, 1))
     params = init_params(orc.num_params(cfg), seed=0)
     orc.lib()
     t0 = time.perf_counter()
@@ -46,9 +49,51 @@ def cpu_baseline(w, seq_len=256):
     dt = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     cores = min(cores, len(os.sched_getaffinity(0)))
-    return {"value": seq_len / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{w.name} model, 1 sequence x {seq_len} tokens, forward+loss+backward in fp64 "
-                      f"({dt:.1f} s); its attention share per token is below that of T={w.seq_len}"}
+    return {"value": round(ws.seq_len / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{w.name} model, 1 sequence x {ws.seq_len} tokens (1/{w.batch} of a step), "
+                      f"forward+loss+backward in fp64, {dt:.1f} s"}
+
+
+def copy_calibration(dev):
+    """One plain device-to-device copy of COPY_MIB MiB, outside every timed
+    region.  Under rocprofv3 --pmc its FETCH_SIZE and WRITE_SIZE readings
+    (known to be COPY_MIB MiB each) scale the same counters of the dominant
+    kernel into bytes."""
+    import torch
+    src = torch.ones(COPY_MIB << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def measured_traffic(kernel, workload):
+    """HBM-side bytes per launch of `kernel` from the committed rocprofv3
+    counter summary profiles/traffic_<kernel>_<workload>.txt, or None when
+    there is none or when the kernel's sources changed since it was taken
+    (their sha256 is recorded in the summary)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    try:
+        h = hashlib.sha256()
+        for src in kv["sources"].split():
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != kv["source_sha256"]:
+            return None
+        return {"bytes_per_launch": float(kv["traffic_bytes_per_launch"]),
+                "fetch_bytes": float(kv["fetch_bytes_per_launch"]), "write_bytes": float(kv["write_bytes_per_launch"]),
+                "fetch_factor": float(kv["fetch_factor"]), "write_factor": float(kv["write_factor"]),
+                "summary": os.path.relpath(path, ROOT)}
+    except (KeyError, ValueError, OSError):
+        return None
 
 
 def main():
@@ -81,6 +126,7 @@ def main():
     params = torch.from_numpy(init_params(m.n_params, seed=0)).to(dev)
     grads = torch.zeros(m.n_params, dtype=torch.float32, device=dev)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
+    copy_calibration(dev)
 
     def step():
         m.forward(ids_d, params)
@@ -125,7 +171,9 @@ def main():
         achieved = by / launches / (avg_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roof.update({"traffic": None, "avg_launch_ms": round(avg_ms, 4), "launches_per_step": launches // args.steps,
+    tr = measured_traffic(name, w.name)
+    roof.update({"traffic": tr["bytes_per_launch"] if tr else None, "traffic_detail": tr,
+                 "algorithmic_bytes_per_launch": by / launches if by else None, "avg_launch_ms": round(avg_ms, 4), "launches_per_step": launches // args.steps,
                  "share_of_step": round(tot_ms / sum(v[1] for v in table.values()), 4),
                  "region_ms_per_step": round((r1 - r0) * 1e3 / args.steps, 3)})
     if args.kernels:

@@ -466,8 +466,10 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             ad.dt = dt; ad.B = (int)c->B; ad.T = (int)c->T; ad.H = (int)c->H; ad.Hkv = (int)c->Hkv; ad.D = (int)c->D;
             ad.qkv = qkv; ad.y = y; ad.lse = c->at<float>(c->lay(l, p.l_lse));
             const double pairs = (double)c->B * c->H * c->T * (c->T + 1) / 2.0;
-            TRY(launch(c, dt == Dt::BF16 ? "attn_fwd_bf16" : "attn_fwd_f32", 4.0 * c->D * pairs, 0.0,
-                       [&] { return launch_attn_fwd(ad, c->stream); }));
+            // algorithmic bytes: read q, k, v; write y and the row log-sum-exp
+            const double qb = (double)N * c->H * c->D * e, kb = (double)N * c->Hkv * c->D * e;
+            TRY(launch(c, dt == Dt::BF16 ? "attn_fwd_bf16" : "attn_fwd_f32", 4.0 * c->D * pairs,
+                       2 * qb + 2 * kb + (double)N * c->H * 4, [&] { return launch_attn_fwd(ad, c->stream); }));
         }
         {
             GemmDesc d;
@@ -614,10 +616,14 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             const bool bf = dt == Dt::BF16;
             // algorithmic backward FLOPs: dV, dK and the dP product (6 D per pair) in the key-outer kernel,
             // dQ (2 D per pair) in the query-outer one; the recomputed S and dP products are not counted
-            TRY(launch(c, bf ? "attn_bwd_dq_bf16" : "attn_bwd_dq_f32", 2.0 * c->D * pairs, 0.0,
+            // algorithmic bytes: dQ reads q, k, v, y, dy and lse, writes dq and delta; dK/dV reads q, k, v,
+            // dy, lse and delta, writes dk and dv
+            const double qb = (double)N * c->H * c->D * e, kb = (double)N * c->Hkv * c->D * e;
+            const double rows = (double)N * c->H * 4;
+            TRY(launch(c, bf ? "attn_bwd_dq_bf16" : "attn_bwd_dq_f32", 2.0 * c->D * pairs, 4 * qb + 2 * kb + 2 * rows,
                        [&] { return launch_attn_bwd(ad, c->stream, 0); }));
-            TRY(launch(c, bf ? "attn_bwd_dkdv_bf16" : "attn_bwd_dkdv_f32", 6.0 * c->D * pairs, 0.0,
-                       [&] { return launch_attn_bwd(ad, c->stream, 1); }));
+            TRY(launch(c, bf ? "attn_bwd_dkdv_bf16" : "attn_bwd_dkdv_f32", 6.0 * c->D * pairs,
+                       2 * qb + 4 * kb + 2 * rows, [&] { return launch_attn_bwd(ad, c->stream, 1); }));
         }
         TRY(launch(c, "rope_qknorm_bwd", 0.0, (double)N * (c->H + c->Hkv) * c->D * 3 * e, [&] {
             return launch_rope_qknorm_bwd(dt, c->ws + p.dqkv, qkv, c->at<float>(c->lay(l, p.l_rstdq)),
