@@ -12,13 +12,17 @@
 // row (operand-swapped v_mfma_f32_32x32x16_bf16, as in the GEMMs), so the
 // row-wise softmax work stays in registers; the probabilities are fed back to
 // the next MFMA straight from the accumulator registers by contracting over
-// keys in the order the accumulator holds them.  K tiles sit in LDS row-major,
-// V (and, in the backward, Q, dO, K) also transposed.  The backward is two
-// kernels: dK/dV with the key block outer (sums over the r query heads of a
-// kv group in a fixed order) and dQ with the query block outer, so no
-// floating-point atomics are used and results are bitwise reproducible.
+// keys in the order the accumulator holds them.  Tiles travel from memory
+// straight into LDS, double-buffered, and are stored once in their natural
+// layout; products contracting over a tile's rows read it with the gfx950
+// transposing LDS read.  The backward is two kernels: dQ with the query block
+// outer (it also forms delta), then dK/dV with the key block outer (sums over
+// the r query heads of a kv group in a fixed order), so no floating-point
+// atomics are used and results are bitwise reproducible.
 //
 // fp32 path: plain SIMT kernels, one wave per row, for the fp32 compute mode.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -78,146 +82,6 @@ __device__ __forceinline__ void zero16(f32x16& a) {
     for (int r = 0; r < 16; ++r) a[r] = 0.0f;
 }
 
-// Copies two [64][128] tiles (e.g. K and V) from global to LDS through
-// registers: 8 16-byte chunks per thread.
-struct TilePair {
-    u32x4 v[8];
-    __device__ __forceinline__ void load(const bf16* __restrict__ p0, const bf16* __restrict__ p1, size_t ld, int tid) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int u = tid + 256 * i, row = (u >> 4) & 63, c = u & 15;
-            const bf16* src = (i < 4 ? p0 : p1) + row * ld + c * 8;
-            v[i] = *reinterpret_cast<const u32x4*>(src);
-        }
-    }
-    __device__ __forceinline__ void store(bf16* t0, bf16* t1, int tid) const {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int u = tid + 256 * i, row = (u >> 4) & 63, c = u & 15;
-            *reinterpret_cast<u32x4*>((i < 4 ? t0 : t1) + toff(row, c)) = v[i];
-        }
-    }
-};
-
-// ======================================================================== bf16 forward
-// Workgroup: 4 waves x 32*QB queries of one head; K/V tiles of 64 keys,
-// double-buffered.  With QB = 1 a wave fits in 256 registers, so two
-// workgroups share a CU and one wave's softmax (VALU, exp) overlaps the other
-// wave's MFMAs.
-template <int QB>
-__global__ void __launch_bounds__(256, 2)
-attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restrict__ lse, int T, int H, int Hkv)
-{
-    constexpr int D = 128, QW = 32 * QB, QBLK = 4 * QW;
-    __shared__ __attribute__((aligned(16))) bf16 smK[2][64 * 128];
-    __shared__ __attribute__((aligned(16))) bf16 smV[2][64 * 128];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
-    const int qb = gridDim.x - 1 - blockIdx.x;  // heavy (late) query blocks first
-    const int hq = blockIdx.y, b = blockIdx.z;
-    const int g = hq / (H / Hkv);
-    const int QKV = (H + 2 * Hkv) * D, HD = H * D, KD = Hkv * D;
-    const int q0 = qb * QBLK;
-    const int qw = q0 + QW * w;                 // first query of this wave
-    const bool active = qw < T;
-    const size_t rowbase = (size_t)b * T;
-
-    bf16x8 qf[QB][8];
-#pragma unroll
-    for (int qq = 0; qq < QB; ++qq) {
-        const int q = active ? qw + 32 * qq + l32 : 0;
-        const bf16* qp = qkv + (rowbase + q) * QKV + hq * D + 8 * hh;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) qf[qq][kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
-    }
-    f32x16 o[QB][4];
-#pragma unroll
-    for (int qq = 0; qq < QB; ++qq)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) zero16(o[qq][db]);
-    float lsum[QB];
-#pragma unroll
-    for (int qq = 0; qq < QB; ++qq) lsum[qq] = 0.0f;
-    const float c1 = kLog2e * rsqrtf((float)D), c2 = sqrtf((float)D) * kLog2e;
-
-    const bf16* kbase = qkv + rowbase * QKV + HD + g * D;
-    TilePair st;
-    const int nkv = min(q0 + QBLK, T) / 64;
-    st.load(kbase, kbase + KD, QKV, tid);
-    st.store(smK[0], smV[0], tid);
-    __syncthreads();
-    for (int t = 0; t < nkv; ++t) {
-        const int cur = t & 1, kv0 = t * 64;
-        if (t + 1 < nkv) st.load(kbase + (size_t)(kv0 + 64) * QKV, kbase + (size_t)(kv0 + 64) * QKV + KD, QKV, tid);
-        if (active && kv0 <= qw + QW - 1) {
-            const bf16* Ks = smK[cur];
-            const bf16* Vs = smV[cur];
-            const bool diag = kv0 + 63 > qw;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                f32x16 s[QB];
-#pragma unroll
-                for (int qq = 0; qq < QB; ++qq) zero16(s[qq]);
-#pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    const bf16x8 kf = rfrag(Ks, 32 * kb + l32, 2 * kk + hh);
-#pragma unroll
-                    for (int qq = 0; qq < QB; ++qq)
-                        s[qq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qq][kk], s[qq], 0, 0, 0);
-                }
-                // lane holds S[q = qw + 32qq + l32][key = kv0 + 32kb + 8(r>>2) + 4hh + (r&3)] in s[qq][r]
-#pragma unroll
-                for (int qq = 0; qq < QB; ++qq) {
-                    if (diag) {
-                        const int q = qw + 32 * qq + l32;
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-                            const float p = __builtin_amdgcn_exp2f(s[qq][r] * c1 - c2);
-                            s[qq][r] = key > q ? 0.0f : p;
-                        }
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) s[qq][r] = __builtin_amdgcn_exp2f(s[qq][r] * c1 - c2);
-                    }
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) lsum[qq] += s[qq][r];
-                }
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    bf16x8 pf[QB];
-#pragma unroll
-                    for (int qq = 0; qq < QB; ++qq) pf[qq] = pack8(s[qq], 8 * j);
-#pragma unroll
-                    for (int db = 0; db < 4; ++db) {
-                        const bf16x8 vf = trfrag(Vs, 32 * db, 32 * kb + 16 * j, lane);
-#pragma unroll
-                        for (int qq = 0; qq < QB; ++qq)
-                            o[qq][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qq], o[qq][db], 0, 0, 0);
-                    }
-                }
-            }
-        }
-        if (t + 1 < nkv) st.store(smK[cur ^ 1], smV[cur ^ 1], tid);
-        __syncthreads();
-    }
-    if (!active) return;
-#pragma unroll
-    for (int qq = 0; qq < QB; ++qq) {
-        const int q = qw + 32 * qq + l32;
-        const float ltot = lsum[qq] + __shfl_xor(lsum[qq], 32, kWave);
-        const float inv = 1.0f / ltot;
-        bf16* yp = y + (rowbase + q) * HD + hq * D;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                float v[4] = {o[qq][db][4 * gg] * inv, o[qq][db][4 * gg + 1] * inv, o[qq][db][4 * gg + 2] * inv,
-                              o[qq][db][4 * gg + 3] * inv};
-                Vec4<bf16>::store(yp + 32 * db + 8 * gg + 4 * hh, v);
-            }
-        if (hh == 0) lse[((size_t)b * H + hq) * T + q] = sqrtf((float)D) + logf(ltot);
-    }
-}
 
 // ======================================================================== delta = rowsum(dO * O) (fp32 path)
 template <typename T>
@@ -240,176 +104,338 @@ attn_delta(const T* __restrict__ dy, const T* __restrict__ y, float* __restrict_
     delta[((size_t)b * H + h) * T_ + t] = acc;
 }
 
-// ======================================================================== bf16 backward: dQ (and delta)
-// Workgroup: 4 waves x 32*QB queries of one head, K/V tiles of 64 keys.  Each
-// lane first forms delta = rowsum(dO * O) of its query rows (the key-outer
-// kernel reads it afterwards), then for every tile recomputes S and dP, forms
-// dS = P (dP - delta) / sqrt(D) and accumulates dQ = dS K.
-template <int QB>
+// ======================================================================== LDS-direct tile loads
+// LDS-direct loads: one wave-instruction fills 1 KB (64 consecutive 16-byte
+// chunk slots) of a [rows][128] tile; each lane fetches the global chunk whose
+// swizzled slot it fills.  Slot q = 64 (w + 4 i) + lane lies in row
+// 4 w + 16 i + lane / 16 at physical chunk lane % 16; that row's swizzle is
+// ((lane / 16) << 2) | w for every i, so a lane keeps one byte offset per
+// tensor and instruction i adds the uniform 16 rows x i.
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+// lane's byte offset of its chunk in a wave's first instruction (row stride ld elements)
+__device__ __forceinline__ unsigned dma_voff(int ld, int lane, int w) {
+    const int c = (lane & 15) ^ (((lane >> 4) << 2) | w);
+    return (unsigned)(((4 * w + (lane >> 4)) * ld + c * 8) * 2);
+}
+// wave w's share of a [ROWS][128] tile: ROWS / 16 instructions of 4 rows each
+template <int ROWS>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, unsigned vo, int ld, bf16* S, int w) {
+#pragma unroll
+    for (int i = 0; i < ROWS / 16; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(S + 64 * (w + 4 * i) * 8), 16, vo, i * 16 * ld * 2, 0,
+                                                 0);
+}
+
+// ======================================================================== bf16 forward
+// Workgroup: 128 queries of one head, 4 waves x 32 queries; K/V tiles of 64
+// keys travel straight from memory into LDS, double-buffered.  A wave fits in
+// 256 registers, so two workgroups share a CU and one wave's softmax (VALU,
+// exp) overlaps the other's MFMAs.
 __global__ void __launch_bounds__(256, 2)
-attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const bf16* __restrict__ dy,
-                 const float* __restrict__ lse, float* __restrict__ delta, bf16* __restrict__ dqkv, int T, int H,
-                 int Hkv)
+attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restrict__ lse, int T, int H, int Hkv,
+              int B)
 {
-    constexpr int D = 128, QW = 32 * QB, QBLK = 4 * QW;
-    __shared__ __attribute__((aligned(16))) bf16 smK[2][64 * 128];
-    __shared__ __attribute__((aligned(16))) bf16 smV[2][64 * 128];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
-    const int qb = gridDim.x - 1 - blockIdx.x;
-    const int hq = blockIdx.y, b = blockIdx.z;
+    constexpr int D = 128, QB = 128;
+    __shared__ __attribute__((aligned(1024))) bf16 sK0[64 * 128];
+    __shared__ __attribute__((aligned(1024))) bf16 sV0[64 * 128];
+    __shared__ __attribute__((aligned(1024))) bf16 sK1[64 * 128];
+    __shared__ __attribute__((aligned(1024))) bf16 sV1[64 * 128];
+    const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // late (heavy) query blocks first; (head, sequence) varies fastest
+    const int nqb = (T + QB - 1) / QB;
+    const int hb = blockIdx.x % (H * B), qblk = nqb - 1 - blockIdx.x / (H * B);
+    const int hq = hb / B, b = hb % B;
     const int g = hq / (H / Hkv);
     const int QKV = (H + 2 * Hkv) * D, HD = H * D, KD = Hkv * D;
-    const int q0 = qb * QBLK;
-    const int qw = q0 + QW * w;
-    const bool active = qw < T;
+    const int q0 = qblk * QB;
+    const int qw = q0 + 32 * w;                 // first query of this wave
+    const bool active = qw < T;                 // T is a multiple of 64
+    const int q = qw + l32;
+    const size_t rowbase = (size_t)b * T;
+
+    bf16x8 qf[8];
+    if (active) {
+        const bf16* qp = qkv + (rowbase + q) * QKV + hq * D + 8 * hh;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
+    }
+    f32x16 o[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) zero16(o[db]);
+    float lsum = 0.0f;
+    const float c1 = kLog2e * rsqrtf((float)D), c2 = sqrtf((float)D) * kLog2e;
+
+    const int nkt = min(q0 + QB, T) / 64;       // key tiles at or before the block's last query
+    const unsigned vo = dma_voff(QKV, lane, w);
+    const bf16* kbase = qkv + rowbase * QKV + HD + g * D;
+    auto issue = [&](int kt, bf16* Ks, bf16* Vs) {
+        const bf16* kp = kbase + (size_t)kt * 64 * QKV;
+        const unsigned bytes = (unsigned)((63 * QKV + 128) * 2);
+        dma_rows<64>(buf_rsrc(kp, bytes), vo, QKV, Ks, w);
+        dma_rows<64>(buf_rsrc(kp + KD, bytes), vo, QKV, Vs, w);
+    };
+    auto publish = [&]() {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+    auto compute = [&](int kt, const bf16* Ks, const bf16* Vs) {
+        const int kv0 = kt * 64;
+        if (!active || kv0 > qw + 31) return;  // wave-uniform: the whole tile lies after the wave's queries
+        const bool diag = kv0 + 63 > qw;
+        int ln = threadIdx.x & 63;             // opaque lane: keeps fragment addresses out of loop-invariant registers
+        asm volatile("" : "+v"(ln));
+        const int hv = ln >> 5, lv32 = ln & 31;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x16 sc;
+            zero16(sc);
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+                sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(Ks, 32 * kb + lv32, 2 * kk + hv), qf[kk], sc, 0, 0,
+                                                             0);
+            // lane holds S[q][key = kv0 + 32kb + 8(e>>2) + 4hh + (e&3)] in sc[e]
+            auto softmax = [&](auto masked) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float p = __builtin_amdgcn_exp2f(sc[e] * c1 - c2);
+                    if constexpr (decltype(masked)::value)
+                        p = kv0 + 32 * kb + 8 * (e >> 2) + 4 * hv + (e & 3) > qw + lv32 ? 0.0f : p;
+                    sc[e] = p;
+                    lsum += p;
+                }
+            };
+            if (diag)
+                softmax(std::true_type{});
+            else
+                softmax(std::false_type{});
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const bf16x8 pf = pack8(sc, 8 * j);
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(Vs, 32 * db, 32 * kb + 16 * j, ln), pf, o[db],
+                                                                    0, 0, 0);
+            }
+        }
+    };
+
+    issue(0, sK0, sV0);
+    publish();
+    for (int kt = 0; kt < nkt; kt += 2) {
+        if (kt + 1 < nkt) issue(kt + 1, sK1, sV1);
+        compute(kt, sK0, sV0);
+        publish();
+        if (kt + 2 < nkt) issue(kt + 2, sK0, sV0);
+        if (kt + 1 < nkt) compute(kt + 1, sK1, sV1);
+        publish();
+    }
+    if (!active) return;
+    const float ltot = lsum + __shfl_xor(lsum, 32, kWave);
+    const float inv = 1.0f / ltot;
+    bf16* yp = y + (rowbase + q) * HD + hq * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = o[db][4 * gg + e] * inv;
+            Vec4<bf16>::store(yp + 32 * db + 8 * gg + 4 * hh, v);
+        }
+    if (hh == 0) lse[((size_t)b * H + hq) * T + q] = sqrtf((float)D) + logf(ltot);
+}
+
+// ======================================================================== bf16 backward: dQ (and delta)
+// Workgroup: 128 queries of one head, 4 waves x 32 queries.  Each lane first
+// forms delta = rowsum(dO * O) of its query row and stores it with the LSE in
+// log2 units (both read by the key-outer kernel), keeps its Q and dO fragments
+// in registers, then for every 64-key tile recomputes S and dP, forms dS =
+// P (dP - delta) and accumulates dQ = dS K (scaled by 1/sqrt(D) at the end).
+// K and V tiles travel straight from memory into LDS, double-buffered.
+template <int OCC>
+__global__ void __launch_bounds__(256, OCC)
+attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const bf16* __restrict__ dy,
+                 const float* __restrict__ lse, float* __restrict__ delta, bf16* __restrict__ dqkv, int T, int H,
+                 int Hkv, int B)
+{
+    constexpr int D = 128, QB = 128;
+    __shared__ __attribute__((aligned(1024))) bf16 sK0[64 * 128];
+    __shared__ __attribute__((aligned(1024))) bf16 sV0[64 * 128];
+    __shared__ __attribute__((aligned(1024))) bf16 sK1[64 * 128];
+    __shared__ __attribute__((aligned(1024))) bf16 sV1[64 * 128];
+    const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // late (heavy) query blocks first; (head, sequence) varies fastest
+    const int nqb = (T + QB - 1) / QB;
+    const int hb = blockIdx.x % (H * B), qblk = nqb - 1 - blockIdx.x / (H * B);
+    const int hq = hb / B, b = hb % B;
+    const int g = hq / (H / Hkv);
+    const int QKV = (H + 2 * Hkv) * D, HD = H * D, KD = Hkv * D;
+    const int q0 = qblk * QB;
+    const int qw = q0 + 32 * w;                 // first query of this wave
+    const bool active = qw < T;                 // T is a multiple of 64
+    const int q = qw + l32;
     const size_t rowbase = (size_t)b * T;
     const float scale = rsqrtf((float)D), c1 = kLog2e * scale;
 
-    bf16x8 qf[QB][8], dof[QB][8];
-    float l2[QB], dl[QB];
-#pragma unroll
-    for (int qq = 0; qq < QB; ++qq) {
-        const int q = active ? qw + 32 * qq + l32 : 0;
+    bf16x8 qf[8], dof[8];
+    float l2 = 0.0f, dl = 0.0f;
+    if (active) {
         const bf16* qp = qkv + (rowbase + q) * QKV + hq * D + 8 * hh;
         const bf16* gp = dy + (rowbase + q) * HD + hq * D + 8 * hh;
         const bf16* yp = y + (rowbase + q) * HD + hq * D + 8 * hh;
         float part = 0.0f;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-            qf[qq][kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
-            dof[qq][kk] = *reinterpret_cast<const bf16x8*>(gp + 16 * kk);
+            qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
+            dof[kk] = *reinterpret_cast<const bf16x8*>(gp + 16 * kk);
             const bf16x8 yv = *reinterpret_cast<const bf16x8*>(yp + 16 * kk);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) part += (float)dof[qq][kk][e] * (float)yv[e];
+            for (int e = 0; e < 8; ++e) part += (float)dof[kk][e] * (float)yv[e];
         }
-        dl[qq] = part + __shfl_xor(part, 32, kWave);
+        dl = part + __shfl_xor(part, 32, kWave);
         const size_t li = ((size_t)b * H + hq) * T + q;
-        l2[qq] = lse[li] * kLog2e;
-        if (active && hh == 0) delta[li] = dl[qq];
+        l2 = lse[li] * kLog2e;
+        if (hh == 0) {
+            delta[li] = dl;
+            delta[(size_t)B * H * T + li] = l2;  // the LSE in log2 units, for the key-outer kernel
+        }
     }
-    f32x16 dq[QB][4];
+    f32x16 dq[4];
 #pragma unroll
-    for (int qq = 0; qq < QB; ++qq)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) zero16(dq[qq][db]);
+    for (int db = 0; db < 4; ++db) zero16(dq[db]);
 
+    const int nkt = min(q0 + QB, T) / 64;       // key tiles at or before the block's last query
+    const unsigned vo = dma_voff(QKV, lane, w);
     const bf16* kbase = qkv + rowbase * QKV + HD + g * D;
-    TilePair st;
-    const int nkv = min(q0 + QBLK, T) / 64;
-    st.load(kbase, kbase + KD, QKV, tid);
-    st.store(smK[0], smV[0], tid);
-    __syncthreads();
-    for (int t = 0; t < nkv; ++t) {
-        const int cur = t & 1, kv0 = t * 64;
-        if (t + 1 < nkv) st.load(kbase + (size_t)(kv0 + 64) * QKV, kbase + (size_t)(kv0 + 64) * QKV + KD, QKV, tid);
-        if (active && kv0 <= qw + QW - 1) {
-            const bf16* Ks = smK[cur];
-            const bf16* Vs = smV[cur];
-            const bool diag = kv0 + 63 > qw;
+    auto issue = [&](int kt, bf16* Ks, bf16* Vs) {
+        const bf16* kp = kbase + (size_t)kt * 64 * QKV;
+        const unsigned bytes = (unsigned)((63 * QKV + 128) * 2);
+        dma_rows<64>(buf_rsrc(kp, bytes), vo, QKV, Ks, w);
+        dma_rows<64>(buf_rsrc(kp + KD, bytes), vo, QKV, Vs, w);
+    };
+    auto publish = [&]() {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+    auto compute = [&](int kt, const bf16* Ks, const bf16* Vs) {
+        const int kv0 = kt * 64;
+        if (!active || kv0 > qw + 31) return;  // wave-uniform: the whole tile lies after the wave's queries
+        const bool diag = kv0 + 63 > qw;
+        int ln = threadIdx.x & 63;             // opaque lane: keeps fragment addresses out of loop-invariant registers
+        asm volatile("" : "+v"(ln));
+        const int hv = ln >> 5, lv32 = ln & 31;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                f32x16 s[QB], dp[QB];
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x16 s, dp;
+            zero16(s);
+            zero16(dp);
 #pragma unroll
-                for (int qq = 0; qq < QB; ++qq) { zero16(s[qq]); zero16(dp[qq]); }
+            for (int kk = 0; kk < 8; ++kk) {
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(Ks, 32 * kb + lv32, 2 * kk + hv), qf[kk], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(Vs, 32 * kb + lv32, 2 * kk + hv), dof[kk], dp, 0, 0,
+                                                             0);
+            }
+            // lane holds S[q][key = kv0 + 32kb + 8(e>>2) + 4hh + (e&3)] in s[e]
+            auto softmax = [&](auto masked) {
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    const bf16x8 kf = rfrag(Ks, 32 * kb + l32, 2 * kk + hh);
-                    const bf16x8 vf = rfrag(Vs, 32 * kb + l32, 2 * kk + hh);
-#pragma unroll
-                    for (int qq = 0; qq < QB; ++qq) {
-                        s[qq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qq][kk], s[qq], 0, 0, 0);
-                        dp[qq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[qq][kk], dp[qq], 0, 0, 0);
-                    }
+                for (int e = 0; e < 16; ++e) {
+                    float p = __builtin_amdgcn_exp2f(s[e] * c1 - l2);
+                    if constexpr (decltype(masked)::value)
+                        p = kv0 + 32 * kb + 8 * (e >> 2) + 4 * hv + (e & 3) > qw + lv32 ? 0.0f : p;
+                    dp[e] = p * (dp[e] - dl);
                 }
-                bf16x8 dsf[QB][2];
+            };
+            if (diag)
+                softmax(std::true_type{});
+            else
+                softmax(std::false_type{});
 #pragma unroll
-                for (int qq = 0; qq < QB; ++qq) {
-                    const int q = qw + 32 * qq + l32;
+            for (int j = 0; j < 2; ++j) {
+                const bf16x8 dsf = pack8(dp, 8 * j);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float p = __builtin_amdgcn_exp2f(s[qq][r] * c1 - l2[qq]);
-                        if (diag) {
-                            const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-                            p = key > q ? 0.0f : p;
-                        }
-                        dp[qq][r] = p * (dp[qq][r] - dl[qq]) * scale;
-                    }
-                    dsf[qq][0] = pack8(dp[qq], 0);
-                    dsf[qq][1] = pack8(dp[qq], 8);
-                }
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int db = 0; db < 4; ++db) {
-                        const bf16x8 kt = trfrag(Ks, 32 * db, 32 * kb + 16 * j, lane);
-#pragma unroll
-                        for (int qq = 0; qq < QB; ++qq)
-                            dq[qq][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsf[qq][j], dq[qq][db], 0, 0, 0);
-                    }
+                for (int db = 0; db < 4; ++db)
+                    dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(Ks, 32 * db, 32 * kb + 16 * j, ln), dsf,
+                                                                      dq[db], 0, 0, 0);
             }
         }
-        if (t + 1 < nkv) st.store(smK[cur ^ 1], smV[cur ^ 1], tid);
-        __syncthreads();
+    };
+
+    issue(0, sK0, sV0);
+    publish();
+    for (int kt = 0; kt < nkt; kt += 2) {
+        if (kt + 1 < nkt) issue(kt + 1, sK1, sV1);
+        compute(kt, sK0, sV0);
+        publish();
+        if (kt + 2 < nkt) issue(kt + 2, sK0, sV0);
+        if (kt + 1 < nkt) compute(kt + 1, sK1, sV1);
+        publish();
     }
     if (!active) return;
+    bf16* qout = dqkv + (rowbase + q) * QKV + hq * D;
 #pragma unroll
-    for (int qq = 0; qq < QB; ++qq) {
-        bf16* qout = dqkv + (rowbase + qw + 32 * qq + l32) * QKV + hq * D;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int gg = 0; gg < 4; ++gg) {
+            float a[4];
 #pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                float a[4] = {dq[qq][db][4 * gg], dq[qq][db][4 * gg + 1], dq[qq][db][4 * gg + 2], dq[qq][db][4 * gg + 3]};
-                Vec4<bf16>::store(qout + 32 * db + 8 * gg + 4 * hh, a);
-            }
-    }
+            for (int e = 0; e < 4; ++e) a[e] = dq[db][4 * gg + e] * scale;
+            Vec4<bf16>::store(qout + 32 * db + 8 * gg + 4 * hh, a);
+        }
 }
 
 // ======================================================================== bf16 backward: dK, dV
-// Workgroup: 128 keys of one kv head (4 waves x 32 keys), looping over the r
-// query heads of the group and over the 64-row query tiles at or after the
-// keys.  K fragments stay in registers and the workgroup's V rows in LDS, so
-// a wave fits in 256 registers and two workgroups share a CU: the Q / dO tile
-// of each step is loaded straight into a single LDS buffer and the other
-// workgroup's MFMAs cover that load.
-struct DkvSmem {
-    bf16 Q[64 * 128];
-    bf16 dO[64 * 128];
-    bf16 V[128 * 128];
-    float lse2[64];
-    float dlt[64];
-};
-
-__global__ void __launch_bounds__(256, 2)
-attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, const float* __restrict__ lse,
-                   const float* __restrict__ delta, bf16* __restrict__ dqkv, int T, int H, int Hkv)
+// Workgroup: 128 keys of one kv head, one wave per SIMD, each wave owning 32
+// keys.  A wave's dK and dV accumulators (32 keys x 128 dims each) and its K
+// fragments stay in registers, and nothing spills.  The workgroup loops over the r
+// query heads of the group and over the 64-query tiles at or after its first
+// key.  Q, dO, lse and delta tiles travel straight from memory into LDS
+// (buffer_load ... lds), double-buffered: the loads of tile i+1 run under the
+// MFMAs of tile i.  V (128 rows) is loaded the same way once.
+//
+__global__ void __launch_bounds__(256, 1)
+attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, const float* __restrict__ delta,
+                   bf16* __restrict__ dqkv, int T, int H, int Hkv, int B)
 {
-    constexpr int D = 128;
-    extern __shared__ __attribute__((aligned(16))) unsigned char smraw[];
-    DkvSmem& sm = *reinterpret_cast<DkvSmem*>(smraw);
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
-    const int kblk = blockIdx.x;  // keys early in the sequence see the most queries: schedule them first
-    const int g = blockIdx.y, b = blockIdx.z;
+    constexpr int D = 128, KB = 128;
+    __shared__ __attribute__((aligned(1024))) bf16 sV[KB * 128];
+    __shared__ __attribute__((aligned(1024))) bf16 sQ0[64 * 128];
+    __shared__ __attribute__((aligned(1024))) bf16 sO0[64 * 128];
+    __shared__ __attribute__((aligned(1024))) bf16 sQ1[64 * 128];
+    __shared__ __attribute__((aligned(1024))) bf16 sO1[64 * 128];
+    __shared__ __attribute__((aligned(16))) float sL0[64], sD0[64], sL1[64], sD1[64];
+
+    const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // key blocks early in the sequence see the most queries: they come first, and the
+    // (head, sequence) index varies fastest so one kv head's blocks share an XCD
+    const int gb = blockIdx.x % (Hkv * B), kblk = blockIdx.x / (Hkv * B);
+    const int g = gb / B, b = gb % B;
     const int r = H / Hkv;
     const int QKV = (H + 2 * Hkv) * D, HD = H * D, KD = Hkv * D;
-    const int k0 = kblk * 128;
-    const int kw = k0 + 32 * w;
+    const int k0 = kblk * KB;
+    const int kw = k0 + 32 * w;                   // first key of this wave
     const int key = kw + l32;
+    const bool active = kw < T;                   // T is a multiple of 64
     const size_t rowbase = (size_t)b * T;
     const float scale = rsqrtf((float)D), c1 = kLog2e * scale;
 
-    bf16x8 kf[8];
+    // V rows of the block (rows past T read as zeros)
     {
+        const int rows = min(KB, T - k0);
+        dma_rows<KB>(buf_rsrc(qkv + (rowbase + k0) * QKV + HD + KD + g * D, (unsigned)(((rows - 1) * QKV + 128) * 2)),
+                     dma_voff(QKV, lane, w), QKV, sV, w);
+    }
+    bf16x8 kf[8];
+    if (active) {
         const bf16* kp = qkv + (rowbase + key) * QKV + HD + g * D + 8 * hh;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(kp + 16 * kk);
-    }
-    // the workgroup's 128 V rows, once
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int u = tid + 256 * i, row = u >> 4, c = u & 15;
-        *reinterpret_cast<u32x4*>(sm.V + toff(row, c)) =
-            *reinterpret_cast<const u32x4*>(qkv + (rowbase + k0 + row) * QKV + HD + KD + g * D + c * 8);
     }
     f32x16 dk[4], dv[4];
 #pragma unroll
@@ -417,28 +443,34 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
 
     const int qt0 = k0 / 64, nqt = T / 64 - qt0;
     const int total = r * nqt;
-    for (int it = 0; it < total; ++it) {
-        const int hq = g * r + it / nqt;
-        const int q0 = (qt0 + it % nqt) * 64;
-        __syncthreads();  // the previous tile has been consumed
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int u = tid + 256 * i, row = (u >> 4) & 63, c = u & 15;
-            const bf16* src = i < 4 ? qkv + (rowbase + q0 + row) * QKV + hq * D + c * 8
-                                    : dy + (rowbase + q0 + row) * HD + hq * D + c * 8;
-            *reinterpret_cast<u32x4*>((i < 4 ? sm.Q : sm.dO) + toff(row, c)) = *reinterpret_cast<const u32x4*>(src);
-        }
-        if (tid < 64) sm.lse2[tid] = lse[((size_t)b * H + hq) * T + q0 + tid] * kLog2e;
-        else if (tid < 128) sm.dlt[tid - 64] = delta[((size_t)b * H + hq) * T + q0 + tid - 64];
+    const unsigned voq = dma_voff(QKV, lane, w), vod = dma_voff(HD, lane, w);
+    // loads of tile it (query head g r + it / nqt, queries from (qt0 + it % nqt) 64) into one stage
+    auto issue = [&](int it, bf16* Qs, bf16* Os, float* Ls, float* Ds) {
+        const int hq = g * r + it / nqt, q0 = (qt0 + it % nqt) * 64;
+        dma_rows<64>(buf_rsrc(qkv + (rowbase + q0) * QKV + hq * D, (unsigned)((63 * QKV + 128) * 2)), voq, QKV, Qs, w);
+        dma_rows<64>(buf_rsrc(dy + (rowbase + q0) * HD + hq * D, (unsigned)((63 * HD + 128) * 2)), vod, HD, Os, w);
+        const size_t li = ((size_t)b * H + hq) * T + q0;
+        if (w == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(buf_rsrc(delta + (size_t)B * H * T + li, 256), (lds_void*)Ls, 4,
+                                                     lane * 4, 0, 0, 0);
+        else if (w == 1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(buf_rsrc(delta + li, 256), (lds_void*)Ds, 4, lane * 4, 0, 0, 0);
+    };
+    auto publish = [&]() {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (q0 + 63 < kw) continue;  // wave-uniform: every query of the tile precedes every key of the wave
+    };
+    // one tile: S and dP for the wave's 32 keys x 64 queries, then dV += P^T dO, dK += dS^T Q
+    auto compute = [&](int it, const bf16* Qs, const bf16* Os, const float* Ls, const float* Ds) {
+        const int q0 = (qt0 + it % nqt) * 64;
+        if (!active || q0 + 63 < kw) return;  // wave-uniform: every query of the tile precedes every key
         const bool diag = q0 < kw + 31;
-        // Re-derive the lane index each step: the fragment addresses (swizzled,
-        // so not affine in the unrolled k-step) are then recomputed here rather
-        // than hoisted out of the loop into ~40 live registers.
-        int ln = lane;
+        // Re-derive the lane index per tile: the swizzled fragment addresses are then
+        // formed here (constant parts folded into the LDS offsets) instead of being
+        // hoisted out of the loop into many live registers.
+        int ln = threadIdx.x & 63;
         asm volatile("" : "+v"(ln));
-        const int l32v = ln & 31, hhv = ln >> 5;
+        const int hv = ln >> 5, lv32 = ln & 31;
 #pragma unroll
         for (int qb2 = 0; qb2 < 2; ++qb2) {
             f32x16 s, dp;
@@ -446,46 +478,71 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
             zero16(dp);
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(sm.Q, 32 * qb2 + l32v, 2 * kk + hhv), kf[kk], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(sm.dO, 32 * qb2 + l32v, 2 * kk + hhv),
-                                                             rfrag(sm.V, 32 * w + l32v, 2 * kk + hhv), dp, 0, 0, 0);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(Qs, 32 * qb2 + lv32, 2 * kk + hv), kf[kk], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(Os, 32 * qb2 + lv32, 2 * kk + hv),
+                                                             rfrag(sV, 32 * w + lv32, 2 * kk + hv), dp, 0, 0, 0);
             }
-            // lane holds S[q = q0 + 32qb2 + 8(e>>2) + 4hh + (e&3)][key] in s[e]
+            // lane holds S[q = q0 + 32qb2 + 8(e>>2) + 4hh + (e&3)][key] in s[e]; P = exp2(S c1 - lse2),
+            // dS / scale = P (dP - delta) (dK is scaled at the end); the mask only on diagonal tiles
+            auto softmax = [&](auto masked) {
 #pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                const int ql = 32 * qb2 + 8 * gg + 4 * hhv;
-                const float4 l4 = *reinterpret_cast<const float4*>(&sm.lse2[ql]);
-                const float4 d4 = *reinterpret_cast<const float4*>(&sm.dlt[ql]);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+                for (int gg = 0; gg < 4; ++gg) {
+                    const int ql = 32 * qb2 + 8 * gg + 4 * hv;
+                    const float4 l4 = *reinterpret_cast<const float4*>(Ls + ql);
+                    const float4 d4 = *reinterpret_cast<const float4*>(Ds + ql);
+                    const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int idx = 4 * gg + e;
-                    float p = __builtin_amdgcn_exp2f(s[idx] * c1 - lv[e]);
-                    if (diag) p = q0 + ql + e < key ? 0.0f : p;
-                    s[idx] = p;
-                    dp[idx] = p * (dp[idx] - dv4[e]) * scale;
+                    for (int e = 0; e < 4; ++e) {
+                        const int idx = 4 * gg + e;
+                        float p = __builtin_amdgcn_exp2f(s[idx] * c1 - lv[e]);
+                        if constexpr (decltype(masked)::value) p = q0 + ql + e < kw + lv32 ? 0.0f : p;
+                        s[idx] = p;
+                        dp[idx] = p * (dp[idx] - dv4[e]);
+                    }
                 }
-            }
+            };
+            if (diag)
+                softmax(std::true_type{});
+            else
+                softmax(std::false_type{});
 #pragma unroll
             for (int j2 = 0; j2 < 2; ++j2) {
                 const bf16x8 pf = pack8(s, 8 * j2), dsf = pack8(dp, 8 * j2);
 #pragma unroll
                 for (int db = 0; db < 4; ++db) {
-                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(sm.dO, 32 * db, 32 * qb2 + 16 * j2, ln), pf,
+                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(Os, 32 * db, 32 * qb2 + 16 * j2, ln), pf,
                                                                       dv[db], 0, 0, 0);
-                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(sm.Q, 32 * db, 32 * qb2 + 16 * j2, ln), dsf,
+                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(Qs, 32 * db, 32 * qb2 + 16 * j2, ln), dsf,
                                                                       dk[db], 0, 0, 0);
                 }
             }
         }
+    };
+
+    // two tiles per iteration on the two static stages (so the compiler sees that
+    // reads of one stage never wait on loads into the other)
+    issue(0, sQ0, sO0, sL0, sD0);
+    publish();
+    for (int it = 0; it < total; it += 2) {
+        if (it + 1 < total) issue(it + 1, sQ1, sO1, sL1, sD1);
+        compute(it, sQ0, sO0, sL0, sD0);
+        publish();
+        if (it + 2 < total) issue(it + 2, sQ0, sO0, sL0, sD0);
+        if (it + 1 < total) compute(it + 1, sQ1, sO1, sL1, sD1);
+        publish();
     }
+    if (!active) return;
     bf16* kout = dqkv + (rowbase + key) * QKV + HD + g * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
-            float a[4] = {dk[db][4 * gg], dk[db][4 * gg + 1], dk[db][4 * gg + 2], dk[db][4 * gg + 3]};
-            float c[4] = {dv[db][4 * gg], dv[db][4 * gg + 1], dv[db][4 * gg + 2], dv[db][4 * gg + 3]};
+            float a[4], c[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a[e] = dk[db][4 * gg + e] * scale;
+                c[e] = dv[db][4 * gg + e];
+            }
             Vec4<bf16>::store(kout + 32 * db + 8 * gg + 4 * hh, a);
             Vec4<bf16>::store(kout + KD + 32 * db + 8 * gg + 4 * hh, c);
         }
@@ -604,17 +661,13 @@ attn_bwd_dkdv_f32(const float* __restrict__ qkv, const float* __restrict__ dy, c
 }
 
 // ======================================================================== host
-hipError_t attn_init_attributes() {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(attn_bwd_dkdv_bf16),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(DkvSmem));
-}
+hipError_t attn_init_attributes() { return hipSuccess; }
 
 hipError_t launch_attn_fwd(const AttnDesc& a, hipStream_t s) {
     if (a.dt == Dt::BF16) {
-        if (a.D != 128 || a.T % 128) return hipErrorInvalidValue;
-        dim3 grid(a.T / 128, a.H, a.B);
-        hipLaunchKernelGGL(attn_fwd_bf16<1>, grid, dim3(256), 0, s, (const bf16*)a.qkv, (bf16*)a.y, a.lse, a.T, a.H,
-                           a.Hkv);
+        if (a.D != 128 || a.T % 64) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(attn_fwd_bf16, dim3(((a.T + 127) / 128) * a.H * a.B), dim3(256), 0, s, (const bf16*)a.qkv,
+                           (bf16*)a.y, a.lse, a.T, a.H, a.Hkv, a.B);
         return hipGetLastError();
     }
     dim3 grid((unsigned)(((size_t)a.B * a.T * a.H + 3) / 4));
@@ -632,16 +685,16 @@ hipError_t launch_attn_fwd(const AttnDesc& a, hipStream_t s) {
 hipError_t launch_attn_bwd(const AttnDesc& a, hipStream_t s, int part) {
     const int N = a.B * a.T;
     const bool bf = a.dt == Dt::BF16;
-    if (bf ? (a.D != 128 || a.T % 128) : (a.D != 128 && a.D != 64)) return hipErrorInvalidValue;
+    if (bf ? (a.D != 128 || a.T % 64) : (a.D != 128 && a.D != 64)) return hipErrorInvalidValue;
     if (bf) {
         if (part == 0)
-            hipLaunchKernelGGL(attn_bwd_dq_bf16<1>, dim3(a.T / 128, a.H, a.B), dim3(256), 0, s, (const bf16*)a.qkv,
-                               (const bf16*)a.y, (const bf16*)a.dy, (const float*)a.lse, a.delta, (bf16*)a.dqkv, a.T,
-                               a.H, a.Hkv);
+            hipLaunchKernelGGL(attn_bwd_dq_bf16<2>, dim3(((a.T + 127) / 128) * a.H * a.B), dim3(256), 0, s,
+                               (const bf16*)a.qkv, (const bf16*)a.y, (const bf16*)a.dy, (const float*)a.lse, a.delta,
+                               (bf16*)a.dqkv, a.T, a.H, a.Hkv, a.B);
         else
-            hipLaunchKernelGGL(attn_bwd_dkdv_bf16, dim3(a.T / 128, a.Hkv, a.B), dim3(256), sizeof(DkvSmem), s,
-                               (const bf16*)a.qkv, (const bf16*)a.dy, (const float*)a.lse, (const float*)a.delta,
-                               (bf16*)a.dqkv, a.T, a.H, a.Hkv);
+            hipLaunchKernelGGL(attn_bwd_dkdv_bf16, dim3(((a.T + 127) / 128) * a.Hkv * a.B), dim3(256), 0, s,
+                               (const bf16*)a.qkv, (const bf16*)a.dy, (const float*)a.delta, (bf16*)a.dqkv, a.T, a.H,
+                               a.Hkv, a.B);
         return hipGetLastError();
     }
     dim3 gq((unsigned)(((size_t)N * a.H + 3) / 4)), gk((unsigned)(((size_t)N * a.Hkv + 3) / 4));

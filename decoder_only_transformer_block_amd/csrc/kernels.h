@@ -70,7 +70,7 @@ struct AttnDesc {
     float* lse = nullptr;       // [B, H, T] natural-log LSE of the scaled scores
     const void* dy = nullptr;   // [B*T, H*D] cd (backward)
     void* dqkv = nullptr;       // [B*T, (H+2Hkv)*D] cd (backward)
-    float* delta = nullptr;     // [B, H, T] scratch (backward)
+    float* delta = nullptr;     // [2, B, H, T] scratch (backward): delta, then (bf16) the LSE in log2 units
 };
 hipError_t launch_attn_fwd(const AttnDesc& a, hipStream_t s);
 // part 0: dQ (and delta = rowsum(dy * y), which part 1 reads); part 1: dK, dV -- in this order

@@ -175,7 +175,7 @@ void make_plan(ncgpt_ctx* c) {
     p.dh = A(N * c->F * e);
     p.dy = A(N * c->HD * e);
     p.dqkv = A(N * c->QKV * e);
-    p.delta = A((size_t)c->B * c->H * c->T * 4);
+    p.delta = A((size_t)2 * c->B * c->H * c->T * 4);
     // split-K partials: the largest splits * M * N over the weight gradients
     size_t sk = 0;
     const int64_t shapes[5][2] = {{c->QKV, c->C}, {c->C, c->HD}, {c->F, c->C}, {c->C, c->F}, {c->V, c->C}};
