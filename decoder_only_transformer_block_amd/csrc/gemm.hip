@@ -525,10 +525,11 @@ gemm_bf16_mfma_w8(const bf16* __restrict__ A, const bf16* __restrict__ B, int M,
 // fragment reads of one never wait for the loads into the other.
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int R, bool KC>
+template <int R, bool KC, int NW>
 struct DmaTile {
-    static constexpr int NI = R / 32;                    // wave-instructions per wave and stage
+    static constexpr int NI = R / (8 * NW);              // wave-instructions per wave and stage
     static constexpr int CPR = R / 8;                    // 16-byte chunks per k-row (MN layout)
+    static_assert(NI >= 1 && (64 * NW / CPR) % 4 == 0, "tile too small for the wave count");
     unsigned vo;                                         // lane's byte offset in its first instruction
     int step;                                            // bytes between a lane's instructions
     int w;                                               // wave index (uniform)
@@ -537,17 +538,17 @@ struct DmaTile {
         const int lane = tid & 63;
         w = __builtin_amdgcn_readfirstlane(tid >> 6);
         if constexpr (KC) {
-            // chunk q = 64 w + 256 i + lane: row q / 8 (advances 32 per i), slot q % 8
+            // chunk q = 64 (w + NW i) + lane: row q / 8 (advances 8 NW per i), slot q % 8
             const int row = 8 * w + (lane >> 3);
             const int ch = (lane & 7) ^ ((lane >> 3) ^ (w & 1));
             vo = (unsigned)(row * ld * 2 + ch * 16);
-            step = 32 * ld * 2;
+            step = 8 * NW * ld * 2;
         } else {
-            // chunk q: k-row q / CPR (advances 256 / CPR per i), slot q % CPR
+            // chunk q: k-row q / CPR (advances 64 NW / CPR per i), slot q % CPR
             const int k = (64 * w + lane) / CPR;
             const int c = (lane % CPR) ^ ((k & 3) << 2);
             vo = (unsigned)(k * ld * 2 + c * 16);
-            step = (256 / CPR) * ld * 2;
+            step = (64 * NW / CPR) * ld * 2;
         }
     }
     // one 64-deep stage starting at k0 into S
@@ -566,13 +567,15 @@ struct DmaTile {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
 #pragma unroll
         for (int i = 0; i < NI; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(S + (64 * w + 256 * i) * 8), 16, vo, i * step,
-                                                     0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(S + 64 * (w + NW * i) * 8), 16, vo, i * step, 0,
+                                                     0);
     }
 };
 
-template <int BM, int BN, bool AK, bool BK, class E>
-__global__ void __launch_bounds__(256, 1)
+// WGM x WGN waves (4 or 8); with 8, two waves share each SIMD and one wave's
+// memory-instruction stalls are covered by the other's MFMAs.
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BK, class E>
+__global__ void __launch_bounds__(64 * WGM * WGN, 1)
 gemm_bf16_mfma_dma(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
                    int k_split, E epi)
 {
@@ -580,11 +583,12 @@ gemm_bf16_mfma_dma(const bf16* __restrict__ A, const bf16* __restrict__ B, int M
     __shared__ __attribute__((aligned(1024))) bf16 sB0[BN * 64];
     __shared__ __attribute__((aligned(1024))) bf16 sA1[BM * 64];
     __shared__ __attribute__((aligned(1024))) bf16 sB1[BN * 64];
-    constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-    constexpr int NL = DmaTile<BM, AK>::NI + DmaTile<BN, BK>::NI;
+    constexpr int NW = WGM * WGN;
+    constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
+    constexpr int NL = DmaTile<BM, AK, NW>::NI + DmaTile<BN, BK, NW>::NI;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1, h = lane >> 5, l32 = lane & 31;
+    const int wm = w / WGN, wn = w % WGN, h = lane >> 5, l32 = lane & 31;
 
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     int tm, tn;
@@ -594,8 +598,8 @@ gemm_bf16_mfma_dma(const bf16* __restrict__ A, const bf16* __restrict__ B, int M
     const int kbeg = split * k_split;
     const int nk = min(k_split, K - kbeg) / 64;
 
-    DmaTile<BM, AK> da;
-    DmaTile<BN, BK> db;
+    DmaTile<BM, AK, NW> da;
+    DmaTile<BN, BK, NW> db;
     da.init(lda, tid);
     db.init(ldb, tid);
     auto dma = [&](int kt, bf16* sA, bf16* sB) {
@@ -680,6 +684,312 @@ gemm_bf16_mfma_dma(const bf16* __restrict__ A, const bf16* __restrict__ B, int M
                 }
             }
     }
+}
+
+// ------------------------------------------------------------------ bf16 MFMA kernel, four-stage ring
+// Stages of 32 k in a ring of four LDS buffers, filled straight from memory
+// three stages ahead.  The barrier that publishes stage s+1 sits between the
+// two k-steps of stage s: after it, the first fragments of stage s+1 are read
+// while the last MFMAs of stage s run, so no MFMA waits on a cold LDS read.
+// The barrier is a bare s_barrier after explicit waits: each wave's own loads
+// of stage s+1 (the two later stages stay in flight) and its own LDS reads
+// (stage s-1's buffer is refilled right after the barrier).
+//
+// 32-deep tiles: K-contiguous [R][32] (4 chunks of 16 bytes per row, chunk
+// XOR-ed with (row >> 2) & 3, so 16 consecutive rows hit 16 distinct bank
+// groups); K-strided [32 k][R] in the mn_chunk layout.
+__device__ __forceinline__ int lds_chunk32(int row, int ch) { return row * 4 + (ch ^ ((row >> 2) & 3)); }
+
+template <int R, bool KC, int NW>
+struct DmaTile32 {
+    static constexpr int CPR = R / 8;                    // 16-byte chunks per k-row (MN layout)
+    static constexpr int NI = R * 4 / (64 * NW);         // wave-instructions per wave and stage
+    static_assert(NI >= 1 && (64 * NW / CPR) % 4 == 0, "tile too small for the wave count");
+    unsigned vo;
+    int step;
+    int w;
+
+    __device__ __forceinline__ void init(int ld, int tid) {
+        const int lane = tid & 63;
+        w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        if constexpr (KC) {
+            // chunk q = 64 (w + NW i) + lane: row q / 4 (advances 16 NW per i), slot q % 4;
+            // (row >> 2) & 3 = (lane >> 4) & 3 for every i
+            const int row = 16 * w + (lane >> 2);
+            const int ch = (lane & 3) ^ ((lane >> 4) & 3);
+            vo = (unsigned)(row * ld * 2 + ch * 16);
+            step = 16 * NW * ld * 2;
+        } else {
+            const int k = (64 * w + lane) / CPR;
+            const int c = (lane % CPR) ^ ((k & 3) << 2);
+            vo = (unsigned)(k * ld * 2 + c * 16);
+            step = (64 * NW / CPR) * ld * 2;
+        }
+    }
+    __device__ __forceinline__ void load(const bf16* __restrict__ P, int ld, int r0, int rmax, int k0, bool valid,
+                                         bf16* S) const {
+        const bf16* base;
+        unsigned bytes;
+        if constexpr (KC) {
+            base = P + (size_t)r0 * ld + k0;
+            bytes = (unsigned)(((min(rmax - r0, R) - 1) * ld + 32) * 2);
+        } else {
+            base = P + (size_t)k0 * ld + r0;
+            bytes = (unsigned)((31 * ld + min(rmax - r0, R)) * 2);
+        }
+        if (!valid) bytes = 0;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(S + 64 * (w + NW * i) * 8), 16, vo, i * step, 0,
+                                                     0);
+    }
+};
+
+template <int R, bool KC>
+__device__ __forceinline__ bf16x8 frag32(const bf16* S, int r0, int kk, int lane) {
+    if constexpr (KC) {
+        const int row = r0 + (lane & 31);
+        return *reinterpret_cast<const bf16x8*>(S + lds_chunk32(row, kk * 2 + (lane >> 5)) * 8);
+    } else {
+        return frag<R, false>(S, r0, kk, lane);
+    }
+}
+
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BK, class E>
+__global__ void __launch_bounds__(64 * WGM * WGN, 1)
+gemm_bf16_mfma_ring(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
+                    int k_split, E epi)
+{
+    __shared__ __attribute__((aligned(1024))) bf16 sA0[BM * 32];
+    __shared__ __attribute__((aligned(1024))) bf16 sB0[BN * 32];
+    __shared__ __attribute__((aligned(1024))) bf16 sA1[BM * 32];
+    __shared__ __attribute__((aligned(1024))) bf16 sB1[BN * 32];
+    __shared__ __attribute__((aligned(1024))) bf16 sA2[BM * 32];
+    __shared__ __attribute__((aligned(1024))) bf16 sB2[BN * 32];
+    __shared__ __attribute__((aligned(1024))) bf16 sA3[BM * 32];
+    __shared__ __attribute__((aligned(1024))) bf16 sB3[BN * 32];
+    constexpr int NW = WGM * WGN;
+    constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
+    constexpr int NL = DmaTile32<BM, AK, NW>::NI + DmaTile32<BN, BK, NW>::NI;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w / WGN, wn = w % WGN, h = lane >> 5, l32 = lane & 31;
+
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    int tm, tn;
+    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int split = blockIdx.y;
+    const int kbeg = split * k_split;
+    const int nk = min(k_split, K - kbeg) / 32;
+
+    DmaTile32<BM, AK, NW> da;
+    DmaTile32<BN, BK, NW> db;
+    da.init(lda, tid);
+    db.init(ldb, tid);
+    auto dma = [&](int kt, bf16* sA, bf16* sB) {
+        da.load(A, lda, m0, M, kbeg + kt * 32, kt < nk, sA);
+        db.load(B, ldb, n0, N, kbeg + kt * 32, kt < nk, sB);
+    };
+    bf16x8 fa[2][FM], fb[2][FN];
+    auto lfrag = [&](int buf, const bf16* sA, const bf16* sB, int kk) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[buf][i] = frag32<BM, AK>(sA, wm * WM + 32 * i, kk, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[buf][j] = frag32<BN, BK>(sB, wn * WN + 32 * j, kk, lane);
+    };
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    auto mma = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+    };
+    // own loads of the next stage done (the two later stages may still fly), own LDS reads done, then the barrier
+    auto sync_next = [&]() {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL) : "memory");
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    // one stage: its loads three stages ahead, k-step 0, publish the next stage, k-step 1
+    auto stage = [&](int kt, const bf16* cA, const bf16* cB, const bf16* nA, const bf16* nB, bf16* xA, bf16* xB) {
+        dma(kt + 3, xA, xB);
+        lfrag(1, cA, cB, 1);
+        mma(0);
+        sync_next();
+        lfrag(0, nA, nB, 0);
+        mma(1);
+    };
+
+    dma(0, sA0, sB0);
+    dma(1, sA1, sB1);
+    dma(2, sA2, sB2);
+    sync_next();
+    lfrag(0, sA0, sB0, 0);
+    for (int kt = 0; kt < nk; kt += 4) {
+        stage(kt, sA0, sB0, sA1, sB1, sA3, sB3);
+        stage(kt + 1, sA1, sB1, sA2, sB2, sA0, sB0);
+        stage(kt + 2, sA2, sB2, sA3, sB3, sA1, sB1);
+        stage(kt + 3, sA3, sB3, sA0, sB0, sA2, sB2);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the loads past the end before the stores
+
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wm * WM + 32 * i + l32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * WN + 32 * j + 8 * g + 4 * h;
+                if (n < N) {
+                    float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    epi(m, n, split, v);
+                }
+            }
+    }
+}
+
+// ------------------------------------------------------------------ persistent four-stage ring
+// The ring kernel made persistent: a workgroup walks work items (k split,
+// tile) number r G + slot for rounds r = 0, 1, ..., where G is the grid size
+// and slot the workgroup's XCD-contiguous position, and its loads stream three
+// stages ahead across item boundaries, so the first stages of the next item
+// are in flight while the current item's epilogue stores run.  Each item runs
+// a multiple of four stages (stages past its k range read zeros).  Loads and
+// stores share the vector-memory counter and may complete out of order, so the
+// first wait after an epilogue waits for everything.
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BK, class E>
+__global__ void __launch_bounds__(64 * WGM * WGN, 1)
+gemm_bf16_mfma_pring(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
+                     int k_split, int splits, E epi)
+{
+    __shared__ __attribute__((aligned(1024))) bf16 sA0[BM * 32];
+    __shared__ __attribute__((aligned(1024))) bf16 sB0[BN * 32];
+    __shared__ __attribute__((aligned(1024))) bf16 sA1[BM * 32];
+    __shared__ __attribute__((aligned(1024))) bf16 sB1[BN * 32];
+    __shared__ __attribute__((aligned(1024))) bf16 sA2[BM * 32];
+    __shared__ __attribute__((aligned(1024))) bf16 sB2[BN * 32];
+    __shared__ __attribute__((aligned(1024))) bf16 sA3[BM * 32];
+    __shared__ __attribute__((aligned(1024))) bf16 sB3[BN * 32];
+    constexpr int NW = WGM * WGN;
+    constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
+    constexpr int NL = DmaTile32<BM, AK, NW>::NI + DmaTile32<BN, BK, NW>::NI;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w / WGN, wn = w % WGN, h = lane >> 5, l32 = lane & 31;
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN, tiles = tiles_m * tiles_n;
+    const int items = tiles * splits;
+    const int G = gridDim.x, slot = xcd_remap(blockIdx.x, G);
+
+    struct Item {
+        int m0, n0, split, kbeg, nk4;
+        int nk;
+        bool valid;
+    };
+    auto item = [&](int r) {
+        Item it;
+        const int L = r * G + slot;
+        it.valid = L < items;
+        const int Lc = it.valid ? L : 0;
+        it.split = Lc / tiles;
+        int tm, tn;
+        tile_coords(Lc % tiles, tiles_m, tiles_n, tm, tn);
+        it.m0 = tm * BM;
+        it.n0 = tn * BN;
+        it.kbeg = it.split * k_split;
+        it.nk = min(k_split, K - it.kbeg) / 32;
+        it.nk4 = (it.nk + 3) & ~3;
+        return it;
+    };
+
+    DmaTile32<BM, AK, NW> da;
+    DmaTile32<BN, BK, NW> db;
+    da.init(lda, tid);
+    db.init(ldb, tid);
+    auto dma_at = [&](const Item& it, int kt, bf16* sA, bf16* sB) {
+        const bool v = it.valid && kt < it.nk;
+        da.load(A, lda, it.m0, M, it.kbeg + kt * 32, v, sA);
+        db.load(B, ldb, it.n0, N, it.kbeg + kt * 32, v, sB);
+    };
+    bf16x8 fa[2][FM], fb[2][FN];
+    auto lfrag = [&](int buf, const bf16* sA, const bf16* sB, int kk) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[buf][i] = frag32<BM, AK>(sA, wm * WM + 32 * i, kk, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[buf][j] = frag32<BN, BK>(sB, wn * WN + 32 * j, kk, lane);
+    };
+    f32x16 acc[FM][FN];
+    auto mma = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+    };
+    auto sync_next = [&](bool drain) {
+        if (drain) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL) : "memory");
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+
+    Item cur = item(0), nxt = item(1);
+    auto stage = [&](int kt, const bf16* cA, const bf16* cB, const bf16* nA, const bf16* nB, bf16* xA, bf16* xB) {
+        if (kt + 3 < cur.nk4) dma_at(cur, kt + 3, xA, xB);
+        else dma_at(nxt, kt + 3 - cur.nk4, xA, xB);
+        lfrag(1, cA, cB, 1);
+        mma(0);
+        sync_next(kt == 0);
+        lfrag(0, nA, nB, 0);
+        mma(1);
+    };
+
+    dma_at(cur, 0, sA0, sB0);
+    dma_at(cur, 1, sA1, sB1);
+    dma_at(cur, 2, sA2, sB2);
+    sync_next(true);
+    lfrag(0, sA0, sB0, 0);
+    for (int r = 0; cur.valid; ++r) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+        for (int kt = 0; kt < cur.nk4; kt += 4) {
+            stage(kt, sA0, sB0, sA1, sB1, sA3, sB3);
+            stage(kt + 1, sA1, sB1, sA2, sB2, sA0, sB0);
+            stage(kt + 2, sA2, sB2, sA3, sB3, sA1, sB1);
+            stage(kt + 3, sA3, sB3, sA0, sB0, sA2, sB2);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = cur.m0 + wm * WM + 32 * i + l32;
+            if (m >= M) continue;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = cur.n0 + wn * WN + 32 * j + 8 * g + 4 * h;
+                    if (n < N) {
+                        float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                      acc[i][j][4 * g + 3]};
+                        epi(m, n, cur.split, v);
+                    }
+                }
+        }
+        cur = nxt;
+        nxt = item(r + 2);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel, two register stages
@@ -864,22 +1174,54 @@ gemm_f32_simt(const float* __restrict__ A, const float* __restrict__ B, int M, i
 }
 
 // ------------------------------------------------------------------ host side
-static int g_variant = 4;
+static int g_variant = 9;
 void gemm_set_variant(int v) { g_variant = v; }
+
+// compute units of the current device (queried once per process)
+static int num_cus() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+            n = 256;
+    }
+    return n;
+}
 
 template <int BM, int BN, bool AK, bool BK, class E>
 static hipError_t run_mfma(const GemmDesc& d, E e, hipStream_t s) {
     constexpr size_t lds = 2 * (size_t)(BM + BN) * 64 * sizeof(bf16);
-    const int v = d.variant >= 0 && d.variant <= 4 ? d.variant : g_variant;
-    auto kern = v == 4   ? gemm_bf16_mfma_dma<BM, BN, AK, BK, E>
+    const int v = d.variant >= 0 && d.variant <= 9 ? d.variant : g_variant;
+    if (v >= 8) {
+        auto pk = v == 9 ? gemm_bf16_mfma_pring<BM, BN, 2, 4, AK, BK, E> : gemm_bf16_mfma_pring<BM, BN, 2, 2, AK, BK, E>;
+        const int nt = v == 9 ? 512 : 256;
+        static int resident[2] = {0, 0};  // workgroups per CU, from the occupancy query
+        int& occ = resident[v - 8];
+        if (occ == 0) {
+            hipError_t st = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(pk), nt, 0);
+            if (st != hipSuccess) return st;
+            if (occ < 1) occ = 1;
+        }
+        const int splits = (d.K + d.k_split - 1) / d.k_split;
+        const int items = ((d.M + BM - 1) / BM) * ((d.N + BN - 1) / BN) * splits;
+        const int grid = std::min(items, occ * num_cus());
+        hipLaunchKernelGGL(pk, dim3(grid), dim3(nt), 0, s, (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, d.K, d.lda,
+                           d.ldb, d.k_split, splits, e);
+        return hipGetLastError();
+    }
+    auto kern = v == 7   ? gemm_bf16_mfma_ring<BM, BN, 2, 4, AK, BK, E>
+                : v == 6 ? gemm_bf16_mfma_ring<BM, BN, 2, 2, AK, BK, E>
+                : v == 5 ? gemm_bf16_mfma_dma<BM, BN, 2, 4, AK, BK, E>
+                : v == 4 ? gemm_bf16_mfma_dma<BM, BN, 2, 2, AK, BK, E>
                 : v == 3 ? gemm_bf16_mfma_w8<BM, BN, AK, BK, E>
                 : v == 2 ? gemm_bf16_mfma_db<BM, BN, AK, BK, E>
                 : v == 1 ? gemm_bf16_mfma_pipe<BM, BN, AK, BK, E>
                          : gemm_bf16_mfma<BM, BN, AK, BK, E>;
-    const int nthreads = v == 3 ? 512 : 256;
-    const size_t dyn = v == 4 ? 0 : lds;  // the direct-to-LDS kernel uses static LDS
-    static bool attr_done[5] = {false, false, false, false, false};
-    if (v != 4 && !attr_done[v]) {
+    const int nthreads = v == 3 || v == 5 || v == 7 ? 512 : 256;
+    const size_t dyn = v >= 4 ? 0 : lds;  // the direct-to-LDS kernels use static LDS
+    static bool attr_done[4] = {false, false, false, false};
+    if (v < 4 && !attr_done[v]) {
         hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (st != hipSuccess) return st;

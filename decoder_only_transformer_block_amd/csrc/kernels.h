@@ -47,7 +47,9 @@ struct GemmDesc {
     size_t split_stride = 0;
     int tile = -1;    // MFMA tile: 0 = 256x256, 1 = 256x128, 2 = 128x128; -1 = chosen from the shape
     int variant = -1; // MFMA main loop: 0 = plain two-stage, 1 = software-pipelined, 2 = two register stages,
-                      // 3 = software-pipelined with 8 waves, 4 = direct-to-LDS loads;
+                      // 3 = software-pipelined with 8 waves, 4 = direct-to-LDS loads, 5 = the same with 8 waves,
+                      // 6 = four-stage ring of 32-deep direct-to-LDS stages, 7 = the same with 8 waves,
+                      // 8 = persistent four-stage ring, 9 = the same with 8 waves;
                       // -1 = the default (gemm_set_variant)
 };
 
@@ -58,7 +60,7 @@ hipError_t launch_splitk_reduce(const float* part, int splits, size_t stride, fl
                                 int accumulate, hipStream_t s);
 // MFMA kernels need more than the default 64 KB of dynamic LDS; call once per device.
 hipError_t gemm_init_attributes();
-// kernel variant of the bf16 GEMM (numbering as GemmDesc::variant; 4, direct-to-LDS loads, is the default)
+// kernel variant of the bf16 GEMM (numbering as GemmDesc::variant; 9, the persistent 8-wave ring, is the default)
 void gemm_set_variant(int v);
 
 // ---------------------------------------------------------------- attention

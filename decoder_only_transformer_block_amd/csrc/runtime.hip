@@ -486,6 +486,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.A = xn2; d.lda = C; d.B = weight(c, l, 4); d.ldb = C;
             d.M = N; d.N = F; d.K = C;
             d.epi = Epi::ReluSq; d.out = a; d.out2 = act; d.ldo = F;
+            d.variant = 6;  // two stores per element: the non-persistent ring measured fastest
             TRY(gemm(c, d));
         }
         {
@@ -504,9 +505,6 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
         d.A = c->ws + p.xf; d.lda = C; d.B = weight(c, -1, 1); d.ldb = C;
         d.M = N; d.N = V; d.K = C;
         d.epi = Epi::StoreCd; d.out = c->ws + p.logits; d.ldo = V;
-        // vocab-wide output, K = n_embd: 128 x 128 tiles with two register stages measured fastest
-        d.tile = 2;
-        d.variant = 2;
         TRY(gemm(c, d));
     }
     c->state = 1;
@@ -568,7 +566,8 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
         TRY(gemm(c, d));
     }
     // dWlm = dz^T xf (vocab-wide output: 128 x 128 tiles with two register stages measured fastest)
-    TRY(wgrad(c, logits, V, c->ws + p.xf, C, V, C, gslice(-1, 1), acc, 2));
+    // vocab x n_embd output over all tokens: 256 x 128 tiles, the four-wave persistent ring measured fastest
+    TRY(wgrad(c, logits, V, c->ws + p.xf, C, V, C, gslice(-1, 1), acc, 1, 8));
     const double nb = (double)N * C * (e + 4 + 4 + (dt == Dt::BF16 ? 2 : 0)) + N * 4.0;
     TRY(launch(c, "rmsnorm_bwd", 0.0, nb, [&] {
         return launch_rmsnorm_bwd(dt, c->ws + p.xf, c->at<float>(p.rstdf), dxn, dx, dx_cd, N, C, 0, c->stream);
