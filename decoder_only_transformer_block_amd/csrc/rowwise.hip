@@ -142,12 +142,36 @@ hipError_t launch_rmsnorm_bwd(Dt dt, const void* y, const float* rstd, const flo
 // For each token n (position t = n mod T) and each q and k head: rotate pair
 // (i, i + D/2) as y_i = x_i cos + x_{i+D/2} sin, y_{i+D/2} = -x_i sin +
 // x_{i+D/2} cos ("nanochat 项目深度分析" §2.1 item 1, §5.3), then RMS-normalise
-// the head (item 2).  One group of D/2 lanes per head, lane i owning pair i.
+// the head (item 2).
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
     for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
     return v;
+}
+
+// Each head is handled by L = D / 16 lanes; lane j of a head holds the 8
+// consecutive elements 8j..8j+7 of the first half and their rotation partners
+// D/2 + 8j.. of the second half, so every access is 16 bytes (bf16) wide.
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void load8(const bf16* p, float (&v)[8]) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)a[e];
+}
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ void store8(bf16* p, const float (&v)[8]) {
+    bf16x8 a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = (bf16)v[e];
+    *reinterpret_cast<bf16x8*>(p) = a;
 }
 
 template <typename T, int D>
@@ -156,23 +180,34 @@ rope_qknorm_fwd_kernel(T* __restrict__ qkv, float* __restrict__ rstdq, float* __
                        const float* __restrict__ cosv, const float* __restrict__ sinv, int N, int T_, int H, int Hkv,
                        float eps)
 {
-    constexpr int G = D / 2;               // lanes per head
-    const int gid = blockIdx.x * (256 / G) + threadIdx.x / G;  // (n, head) with head in [0, H+Hkv)
-    const int i = threadIdx.x % G;
+    constexpr int G = D / 2, L = D / 16;      // half width, lanes per head
+    const int gid = blockIdx.x * (256 / L) + threadIdx.x / L;  // (n, head) with head in [0, H+Hkv)
+    const int j = threadIdx.x % L;
     const int nh = H + Hkv;
-    if (gid >= N * nh) return;
+    if (gid >= N * nh) return;                // whole heads leave together (L divides 64)
     const int n = gid / nh, hd = gid % nh;
     const int t = n % T_;
     const int QKV = (H + 2 * Hkv) * D;
-    T* v = qkv + (size_t)n * QKV + hd * D;   // k heads follow the q heads
-    const float x1 = to_f32(v[i]), x2 = to_f32(v[i + G]);
-    const float c = cosv[t * G + i], s = sinv[t * G + i];
-    const float y1 = x1 * c + x2 * s, y2 = -x1 * s + x2 * c;
-    const float ss = group_sum<G>(y1 * y1 + y2 * y2);
+    T* v = qkv + (size_t)n * QKV + hd * D + 8 * j;   // k heads follow the q heads
+    float x1[8], x2[8], c[8], sn[8];
+    load8(v, x1);
+    load8(v + G, x2);
+    load8(cosv + t * G + 8 * j, c);
+    load8(sinv + t * G + 8 * j, sn);
+    float y1[8], y2[8], ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        y1[e] = x1[e] * c[e] + x2[e] * sn[e];
+        y2[e] = -x1[e] * sn[e] + x2[e] * c[e];
+        ss += y1[e] * y1[e] + y2[e] * y2[e];
+    }
+    ss = group_sum<L>(ss);
     const float rs = 1.0f / sqrtf(ss / (float)D + eps);
-    v[i] = from_f32<T>(y1 * rs);
-    v[i + G] = from_f32<T>(y2 * rs);
-    if (i == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { y1[e] *= rs; y2[e] *= rs; }
+    store8(v, y1);
+    store8(v + G, y2);
+    if (j == 0) {
         if (hd < H) rstdq[(size_t)n * H + hd] = rs;
         else rstdk[(size_t)n * Hkv + hd - H] = rs;
     }
@@ -186,23 +221,36 @@ rope_qknorm_bwd_kernel(T* __restrict__ dqkv, const T* __restrict__ qkv, const fl
                        const float* __restrict__ rstdk, const float* __restrict__ cosv, const float* __restrict__ sinv,
                        int N, int T_, int H, int Hkv)
 {
-    constexpr int G = D / 2;
-    const int gid = blockIdx.x * (256 / G) + threadIdx.x / G;
-    const int i = threadIdx.x % G;
+    constexpr int G = D / 2, L = D / 16;
+    const int gid = blockIdx.x * (256 / L) + threadIdx.x / L;
+    const int j = threadIdx.x % L;
     const int nh = H + Hkv;
     if (gid >= N * nh) return;
     const int n = gid / nh, hd = gid % nh;
     const int t = n % T_;
     const int QKV = (H + 2 * Hkv) * D;
-    const size_t o = (size_t)n * QKV + hd * D;
-    const float y1 = to_f32(qkv[o + i]), y2 = to_f32(qkv[o + i + G]);
-    const float g1 = to_f32(dqkv[o + i]), g2 = to_f32(dqkv[o + i + G]);
+    const size_t o = (size_t)n * QKV + hd * D + 8 * j;
+    float y1[8], y2[8], g1[8], g2[8], c[8], sn[8];
+    load8(qkv + o, y1);
+    load8(qkv + o + G, y2);
+    load8(dqkv + o, g1);
+    load8(dqkv + o + G, g2);
+    load8(cosv + t * G + 8 * j, c);
+    load8(sinv + t * G + 8 * j, sn);
     const float rs = hd < H ? rstdq[(size_t)n * H + hd] : rstdk[(size_t)n * Hkv + hd - H];
-    const float dot = group_sum<G>(g1 * y1 + g2 * y2) / (float)D;
-    const float r1 = rs * (g1 - y1 * dot), r2 = rs * (g2 - y2 * dot);
-    const float c = cosv[t * G + i], s = sinv[t * G + i];
-    dqkv[o + i] = from_f32<T>(r1 * c - r2 * s);
-    dqkv[o + i + G] = from_f32<T>(r1 * s + r2 * c);
+    float dot = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dot += g1[e] * y1[e] + g2[e] * y2[e];
+    dot = group_sum<L>(dot) / (float)D;
+    float o1[8], o2[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float r1 = rs * (g1[e] - y1[e] * dot), r2 = rs * (g2[e] - y2[e] * dot);
+        o1[e] = r1 * c[e] - r2 * sn[e];
+        o2[e] = r1 * sn[e] + r2 * c[e];
+    }
+    store8(dqkv + o, o1);
+    store8(dqkv + o + G, o2);
 }
 
 template <typename T>
@@ -210,11 +258,11 @@ static hipError_t rope_fwd_t(T* qkv, float* rq, float* rk, const float* c, const
                              int Hkv, int D, float eps, hipStream_t s) {
     const size_t heads = (size_t)N * (H + Hkv);
     if (D == 128) {
-        hipLaunchKernelGGL((rope_qknorm_fwd_kernel<T, 128>), dim3((unsigned)((heads + 3) / 4)), dim3(256), 0, s, qkv, rq,
-                           rk, c, sn, N, T_, H, Hkv, eps);
+        hipLaunchKernelGGL((rope_qknorm_fwd_kernel<T, 128>), dim3((unsigned)((heads + 31) / 32)), dim3(256), 0, s, qkv,
+                           rq, rk, c, sn, N, T_, H, Hkv, eps);
     } else if (D == 64) {
-        hipLaunchKernelGGL((rope_qknorm_fwd_kernel<T, 64>), dim3((unsigned)((heads + 7) / 8)), dim3(256), 0, s, qkv, rq,
-                           rk, c, sn, N, T_, H, Hkv, eps);
+        hipLaunchKernelGGL((rope_qknorm_fwd_kernel<T, 64>), dim3((unsigned)((heads + 63) / 64)), dim3(256), 0, s, qkv,
+                           rq, rk, c, sn, N, T_, H, Hkv, eps);
     } else {
         return hipErrorInvalidValue;
     }
@@ -226,10 +274,10 @@ static hipError_t rope_bwd_t(T* dqkv, const T* qkv, const float* rq, const float
                              int N, int T_, int H, int Hkv, int D, hipStream_t s) {
     const size_t heads = (size_t)N * (H + Hkv);
     if (D == 128) {
-        hipLaunchKernelGGL((rope_qknorm_bwd_kernel<T, 128>), dim3((unsigned)((heads + 3) / 4)), dim3(256), 0, s, dqkv,
+        hipLaunchKernelGGL((rope_qknorm_bwd_kernel<T, 128>), dim3((unsigned)((heads + 31) / 32)), dim3(256), 0, s, dqkv,
                            qkv, rq, rk, c, sn, N, T_, H, Hkv);
     } else if (D == 64) {
-        hipLaunchKernelGGL((rope_qknorm_bwd_kernel<T, 64>), dim3((unsigned)((heads + 7) / 8)), dim3(256), 0, s, dqkv,
+        hipLaunchKernelGGL((rope_qknorm_bwd_kernel<T, 64>), dim3((unsigned)((heads + 63) / 64)), dim3(256), 0, s, dqkv,
                            qkv, rq, rk, c, sn, N, T_, H, Hkv);
     } else {
         return hipErrorInvalidValue;
@@ -253,30 +301,39 @@ hipError_t launch_rope_qknorm_bwd(Dt dt, void* dqkv, const void* qkv, const floa
 
 // ------------------------------------------------------------------ cross-entropy
 // Per row of logits z: lse = log sum exp z, loss_row = lse - z[target] (0
-// when target < 0, i.e. ignored).  One workgroup per row.
+// when target < 0, i.e. ignored).  One workgroup per row; each thread reads 8
+// consecutive logits per step (16 bytes in bf16) and keeps a running (max,
+// sum of exp) pair in the base-2 domain.
 template <typename T>
 __global__ void __launch_bounds__(256)
 ce_fwd_rows_kernel(const T* __restrict__ z, const int32_t* __restrict__ targets, float* __restrict__ lse,
                    float* __restrict__ loss_rows, int V, uint32_t* err)
 {
+    constexpr float kL2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
     __shared__ float red_m[4], red_s[4];
     const int n = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const T* zr = z + (size_t)n * V;
-    float m = -INFINITY, s = 0.0f;
-    for (int c = tid * 4; c < V; c += 1024) {
-        float v[4];
-        Vec4<T>::load(zr + c, v);
-        float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-        float mn = fmaxf(m, mx);
-        s = s * expf(m - mn) + expf(v[0] - mn) + expf(v[1] - mn) + expf(v[2] - mn) + expf(v[3] - mn);
-        m = mn;
+    float m = -INFINITY, s = 0.0f;               // max of z log2(e), sum of 2^(z log2 e - m)
+    for (int c = tid * 8; c < V; c += 2048) {
+        float v[8];
+        load8(zr + c, v);
+        float mx = v[0] * kL2e;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { v[e] *= kL2e; mx = fmaxf(mx, v[e]); }
+        if (mx > m) {
+            s *= __builtin_amdgcn_exp2f(m - mx);
+            m = mx;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f(v[e] - m);
     }
     // combine (m, s) across the wave, then across the 4 waves
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         float mo = __shfl_xor(m, o, kWave), so = __shfl_xor(s, o, kWave);
         float mn = fmaxf(m, mo);
-        s = (m == -INFINITY ? 0.0f : s * expf(m - mn)) + (mo == -INFINITY ? 0.0f : so * expf(mo - mn));
+        s = (m == -INFINITY ? 0.0f : s * __builtin_amdgcn_exp2f(m - mn)) +
+            (mo == -INFINITY ? 0.0f : so * __builtin_amdgcn_exp2f(mo - mn));
         m = mn;
     }
     if (lane == 0) { red_m[w] = m; red_s[w] = s; }
@@ -285,8 +342,8 @@ ce_fwd_rows_kernel(const T* __restrict__ z, const int32_t* __restrict__ targets,
         float M = red_m[0];
         for (int i = 1; i < 4; ++i) M = fmaxf(M, red_m[i]);
         float S = 0.0f;
-        for (int i = 0; i < 4; ++i) S += red_s[i] * expf(red_m[i] - M);
-        const float l = M + logf(S);
+        for (int i = 0; i < 4; ++i) S += red_s[i] * __builtin_amdgcn_exp2f(red_m[i] - M);
+        const float l = (M + __builtin_amdgcn_logf(S)) * kLn2;
         lse[n] = l;
         const int t = targets[n];
         float lr = 0.0f;
@@ -349,41 +406,43 @@ hipError_t launch_loss_reduce(const float* loss_rows, const int32_t* targets, in
 }
 
 // dz = grad_scale * inv_valid * (exp(z - lse) - onehot(target)) on valid rows,
-// 0 on ignored rows; written over the logits.
+// 0 on ignored rows; written over the logits.  One workgroup per row, 8
+// consecutive logits per thread and step.
 template <typename T>
 __global__ void __launch_bounds__(256)
 ce_bwd_kernel(T* __restrict__ z, const float* __restrict__ lse, const int32_t* __restrict__ targets,
-              const float* __restrict__ inv_valid, float grad_scale, size_t total4, int V4)
+              const float* __restrict__ inv_valid, float grad_scale, int V)
 {
-    const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;  // one group of 4 logits
-    if (q >= total4) return;
-    const int n = (int)(q / V4);
-    const int c = (int)(q % V4) * 4;
-    const int V = V4 * 4;
+    constexpr float kL2e = 1.4426950408889634f;
+    const int n = blockIdx.x;
     const int t = targets[n];
-    T* zr = z + (size_t)n * V + c;
-    float v[4];
-    if (t < 0 || t >= V) {
-        v[0] = v[1] = v[2] = v[3] = 0.0f;
-    } else {
-        const float k = grad_scale * (*inv_valid), l = lse[n];
-        Vec4<T>::load(zr, v);
+    T* zr = z + (size_t)n * V;
+    const bool valid = t >= 0 && t < V;
+    const float k = valid ? grad_scale * (*inv_valid) : 0.0f, l2 = valid ? lse[n] * kL2e : 0.0f;
+    for (int c = threadIdx.x * 8; c < V; c += 2048) {
+        float v[8];
+        if (valid) {
+            load8(zr + c, v);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = k * (expf(v[i] - l) - (c + i == t ? 1.0f : 0.0f));
+            for (int e = 0; e < 8; ++e)
+                v[e] = k * (__builtin_amdgcn_exp2f(v[e] * kL2e - l2) - (c + e == t ? 1.0f : 0.0f));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+        }
+        store8(zr + c, v);
     }
-    Vec4<T>::store(zr, v);
 }
 
 hipError_t launch_ce_bwd(Dt dt, void* logits, const float* lse, const int32_t* targets, const float* inv_valid,
                          float grad_scale, int N, int V, hipStream_t s) {
-    const size_t total4 = (size_t)N * (V / 4);
-    dim3 grid((unsigned)((total4 + 255) / 256));
+    if (V % 8) return hipErrorInvalidValue;
     if (dt == Dt::BF16)
-        hipLaunchKernelGGL(ce_bwd_kernel<bf16>, grid, dim3(256), 0, s, (bf16*)logits, lse, targets, inv_valid,
-                           grad_scale, total4, V / 4);
+        hipLaunchKernelGGL(ce_bwd_kernel<bf16>, dim3(N), dim3(256), 0, s, (bf16*)logits, lse, targets, inv_valid,
+                           grad_scale, V);
     else
-        hipLaunchKernelGGL(ce_bwd_kernel<float>, grid, dim3(256), 0, s, (float*)logits, lse, targets, inv_valid,
-                           grad_scale, total4, V / 4);
+        hipLaunchKernelGGL(ce_bwd_kernel<float>, dim3(N), dim3(256), 0, s, (float*)logits, lse, targets, inv_valid,
+                           grad_scale, V);
     return hipGetLastError();
 }
 
