@@ -15,25 +15,48 @@
 //
 // fp32 path: a plain LDS-tiled SIMT kernel with the same epilogues (the fp32
 // compute mode of the precision scheme is a correctness path).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace ncgpt {
 
 // ------------------------------------------------------------------ epilogues
+// Each epilogue takes (row m, first column n, k split, 4 consecutive values).
+// The bf16 ones also take 8 consecutive values (put8): the MFMA kernels
+// exchange half-tiles between lanes l and l+32 so that a lane owns 8
+// consecutive columns and stores 16 bytes at once.
+__device__ __forceinline__ void ld8(const bf16* p, float (&v)[8]) {
+    const bf16x8 t = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)t[e];
+}
+__device__ __forceinline__ void st8(bf16* p, const float (&v)[8]) {
+    bf16x8 t;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = (bf16)v[e];
+    *reinterpret_cast<bf16x8*>(p) = t;
+}
+
 template <typename T> struct EStoreCd {
+    static constexpr bool kWide = std::is_same<T, bf16>::value;
     T* out; int ldo;
     __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
         Vec4<T>::store(out + (size_t)m * ldo + n, v);
     }
+    __device__ void put8(int m, int n, int, const float (&v)[8]) const { st8(out + (size_t)m * ldo + n, v); }
 };
 struct EStoreF32 {
+    static constexpr bool kWide = false;
     float* out; int ldo;
     __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
         Vec4<float>::store(out + (size_t)m * ldo + n, v);
     }
+    __device__ void put8(int, int, int, const float (&)[8]) const {}
 };
 template <typename T> struct EResidual {
+    static constexpr bool kWide = std::is_same<T, bf16>::value;
     T* out; const T* in; int ldo;
     __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
         size_t o = (size_t)m * ldo + n;
@@ -43,9 +66,18 @@ template <typename T> struct EResidual {
         for (int i = 0; i < 4; ++i) x[i] += v[i];
         Vec4<T>::store(out + o, x);
     }
+    __device__ void put8(int m, int n, int, const float (&v)[8]) const {
+        const size_t o = (size_t)m * ldo + n;
+        float x[8];
+        ld8(in + o, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] += v[i];
+        st8(out + o, x);
+    }
 };
 // a = relu(v) is stored for the backward; act = a^2 (of the stored, rounded a) feeds the next GEMM
 template <typename T> struct EReluSq {
+    static constexpr bool kWide = std::is_same<T, bf16>::value;
     T* a; T* act; int ldo;
     __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
         size_t o = (size_t)m * ldo + n;
@@ -58,9 +90,21 @@ template <typename T> struct EReluSq {
         Vec4<T>::store(a + o, r);
         Vec4<T>::store(act + o, s);
     }
+    __device__ void put8(int m, int n, int, const float (&v)[8]) const {
+        const size_t o = (size_t)m * ldo + n;
+        float r[8], s[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            r[i] = (float)(bf16)fmaxf(v[i], 0.0f);
+            s[i] = r[i] * r[i];
+        }
+        st8(a + o, r);
+        st8(act + o, s);
+    }
 };
 // dh = dact * d(relu(h)^2)/dh = dact * 2 * relu(h)
 template <typename T> struct EReluSqBwd {
+    static constexpr bool kWide = std::is_same<T, bf16>::value;
     T* out; const T* a; int ldo;
     __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
         size_t o = (size_t)m * ldo + n;
@@ -70,8 +114,17 @@ template <typename T> struct EReluSqBwd {
         for (int i = 0; i < 4; ++i) x[i] = v[i] * 2.0f * x[i];
         Vec4<T>::store(out + o, x);
     }
+    __device__ void put8(int m, int n, int, const float (&v)[8]) const {
+        const size_t o = (size_t)m * ldo + n;
+        float x[8];
+        ld8(a + o, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = v[i] * 2.0f * x[i];
+        st8(out + o, x);
+    }
 };
 struct EGrad {
+    static constexpr bool kWide = false;
     float* out; int ldo; int acc;
     __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
         float* p = out + (size_t)m * ldo + n;
@@ -84,13 +137,60 @@ struct EGrad {
         }
         Vec4<float>::store(p, x);
     }
+    __device__ void put8(int, int, int, const float (&)[8]) const {}
 };
 struct ESplitK {
+    static constexpr bool kWide = false;
     float* out; int ldo; size_t stride;
     __device__ void operator()(int m, int n, int split, const float (&v)[4]) const {
         Vec4<float>::store(out + (size_t)split * stride + (size_t)m * ldo + n, v);
     }
+    __device__ void put8(int, int, int, const float (&)[8]) const {}
 };
+
+// Epilogue of an MFMA wave tile: FM x FN accumulators of 32 x 32 (operand-swapped
+// layout: lane l holds row l % 32 and, in registers 4g..4g+3, columns
+// 8g + 4(l / 32) + 0..3).  m0, n0: the wave tile's first row and column.
+template <int FM, int FN, class E>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], int m0, int n0, int split, int M, int N,
+                                           int lane, const E& epi) {
+    const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = m0 + 32 * i + l32;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            if constexpr (E::kWide) {
+                // registers of column groups 2p and 2p+1 trade halves: lanes 0..31 end up with
+                // columns 16p + 0..7, lanes 32..63 with columns 16p + 8..15
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][j][8 * p + e]),
+                                                                        __float_as_uint(acc[i][j][8 * p + 4 + e]),
+                                                                        false, false);
+                        v[e] = __uint_as_float(r[0]);
+                        v[4 + e] = __uint_as_float(r[1]);
+                    }
+                    const int n = n0 + 32 * j + 16 * p + 8 * h;
+                    if (m < M && n < N) epi.put8(m, n, split, v);
+                }
+            } else {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + 32 * j + 8 * g + 4 * h;
+                    if (m < M && n < N) {
+                        float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                      acc[i][j][4 * g + 3]};
+                        epi(m, n, split, v);
+                    }
+                }
+            }
+        }
+    }
+}
 
 // ------------------------------------------------------------------ tile order
 // Workgroups are dealt round-robin to the 8 XCDs; renumber them so each XCD
@@ -669,21 +769,7 @@ gemm_bf16_mfma_dma(const bf16* __restrict__ A, const bf16* __restrict__ B, int M
         lfrag(0, sA0, sB0, 0);
     }
 
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wm * WM + 32 * i + l32;
-        if (m >= M) continue;
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * WN + 32 * j + 8 * g + 4 * h;
-                if (n < N) {
-                    float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                    epi(m, n, split, v);
-                }
-            }
-    }
+    store_tile<FM, FN>(acc, m0 + wm * WM, n0 + wn * WN, split, M, N, lane, epi);
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel, four-stage ring
@@ -813,6 +899,23 @@ gemm_bf16_mfma_ring(const bf16* __restrict__ A, const bf16* __restrict__ B, int 
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
     };
+    // Instruction order inside one k-step's region: each MFMA is followed by at most one
+    // load and one fragment read, so neither memory queue receives a burst.  None of the
+    // region's MFMAs depends on its reads (they fill the other fragment buffer).
+    auto interleave = [&](auto with_loads) {
+        constexpr int NDS = (AK ? FM : 2 * FM) + (BK ? FN : 2 * FN);  // LDS read instructions of one k-step
+        constexpr int NMF = FM * FN;
+        constexpr int NV = decltype(with_loads)::value ? NL : 0;
+#pragma unroll
+        for (int q = 0; q < NMF; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // one MFMA
+            if constexpr (NV > 0) if (q < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one load
+            if (q < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // one fragment read
+        }
+        if constexpr (NDS > NMF) __builtin_amdgcn_sched_group_barrier(0x100, NDS - NMF, 0);
+        if constexpr (NV > NMF) __builtin_amdgcn_sched_group_barrier(0x020, NV - NMF, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
     // own loads of the next stage done (the two later stages may still fly), own LDS reads done, then the barrier
     auto sync_next = [&]() {
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL) : "memory");
@@ -823,9 +926,11 @@ gemm_bf16_mfma_ring(const bf16* __restrict__ A, const bf16* __restrict__ B, int 
         dma(kt + 3, xA, xB);
         lfrag(1, cA, cB, 1);
         mma(0);
+        interleave(std::true_type{});
         sync_next();
         lfrag(0, nA, nB, 0);
         mma(1);
+        interleave(std::false_type{});
     };
 
     dma(0, sA0, sB0);
@@ -841,21 +946,7 @@ gemm_bf16_mfma_ring(const bf16* __restrict__ A, const bf16* __restrict__ B, int 
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the loads past the end before the stores
 
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wm * WM + 32 * i + l32;
-        if (m >= M) continue;
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * WN + 32 * j + 8 * g + 4 * h;
-                if (n < N) {
-                    float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                    epi(m, n, split, v);
-                }
-            }
-    }
+    store_tile<FM, FN>(acc, m0 + wm * WM, n0 + wn * WN, split, M, N, lane, epi);
 }
 
 // ------------------------------------------------------------------ persistent four-stage ring
@@ -935,6 +1026,23 @@ gemm_bf16_mfma_pring(const bf16* __restrict__ A, const bf16* __restrict__ B, int
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
     };
+    // Instruction order inside one k-step's region: each MFMA is followed by at most one
+    // load and one fragment read, so neither memory queue receives a burst.  None of the
+    // region's MFMAs depends on its reads (they fill the other fragment buffer).
+    auto interleave = [&](auto with_loads) {
+        constexpr int NDS = (AK ? FM : 2 * FM) + (BK ? FN : 2 * FN);  // LDS read instructions of one k-step
+        constexpr int NMF = FM * FN;
+        constexpr int NV = decltype(with_loads)::value ? NL : 0;
+#pragma unroll
+        for (int q = 0; q < NMF; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // one MFMA
+            if constexpr (NV > 0) if (q < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one load
+            if (q < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // one fragment read
+        }
+        if constexpr (NDS > NMF) __builtin_amdgcn_sched_group_barrier(0x100, NDS - NMF, 0);
+        if constexpr (NV > NMF) __builtin_amdgcn_sched_group_barrier(0x020, NV - NMF, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
     auto sync_next = [&](bool drain) {
         if (drain) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL) : "memory");
@@ -947,9 +1055,11 @@ gemm_bf16_mfma_pring(const bf16* __restrict__ A, const bf16* __restrict__ B, int
         else dma_at(nxt, kt + 3 - cur.nk4, xA, xB);
         lfrag(1, cA, cB, 1);
         mma(0);
+        interleave(std::true_type{});
         sync_next(kt == 0);
         lfrag(0, nA, nB, 0);
         mma(1);
+        interleave(std::false_type{});
     };
 
     dma_at(cur, 0, sA0, sB0);
@@ -970,22 +1080,7 @@ gemm_bf16_mfma_pring(const bf16* __restrict__ A, const bf16* __restrict__ B, int
             stage(kt + 2, sA2, sB2, sA3, sB3, sA1, sB1);
             stage(kt + 3, sA3, sB3, sA0, sB0, sA2, sB2);
         }
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int m = cur.m0 + wm * WM + 32 * i + l32;
-            if (m >= M) continue;
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = cur.n0 + wn * WN + 32 * j + 8 * g + 4 * h;
-                    if (n < N) {
-                        float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                      acc[i][j][4 * g + 3]};
-                        epi(m, n, cur.split, v);
-                    }
-                }
-        }
+        store_tile<FM, FN>(acc, cur.m0 + wm * WM, cur.n0 + wn * WN, cur.split, M, N, lane, epi);
         cur = nxt;
         nxt = item(r + 2);
     }

@@ -454,6 +454,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.A = xn1; d.lda = C; d.B = weight(c, l, 0); d.ldb = C;
             d.M = N; d.N = QKV; d.K = C;
             d.epi = Epi::StoreCd; d.out = qkv; d.ldo = QKV;
+            d.variant = 7;  // few tiles per CU: the non-persistent eight-wave ring measured fastest
             TRY(gemm(c, d));
         }
         TRY(launch(c, "rope_qknorm_fwd", 0.0, (double)N * (c->H + c->Hkv) * c->D * 2 * e, [&] {
