@@ -107,10 +107,10 @@ attn_delta(const T* __restrict__ dy, const T* __restrict__ y, float* __restrict_
 // ======================================================================== LDS-direct tile loads
 // LDS-direct loads: one wave-instruction fills 1 KB (64 consecutive 16-byte
 // chunk slots) of a [rows][128] tile; each lane fetches the global chunk whose
-// swizzled slot it fills.  Slot q = 64 (w + 4 i) + lane lies in row
-// 4 w + 16 i + lane / 16 at physical chunk lane % 16; that row's swizzle is
-// ((lane / 16) << 2) | w for every i, so a lane keeps one byte offset per
-// tensor and instruction i adds the uniform 16 rows x i.
+// swizzled slot it fills.  With NW waves, slot q = 64 (w + NW i) + lane lies in
+// row 4 w + 4 NW i + lane / 16 at physical chunk lane % 16; that row's swizzle
+// is ((lane / 16) << 2) | (w & 3) for every i (NW is a multiple of 4), so a lane
+// keeps one byte offset per tensor and instruction i adds 4 NW rows x i.
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, unsigned bytes) {
@@ -118,16 +118,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uns
 }
 // lane's byte offset of its chunk in a wave's first instruction (row stride ld elements)
 __device__ __forceinline__ unsigned dma_voff(int ld, int lane, int w) {
-    const int c = (lane & 15) ^ (((lane >> 4) << 2) | w);
+    const int c = (lane & 15) ^ (((lane >> 4) << 2) | (w & 3));
     return (unsigned)(((4 * w + (lane >> 4)) * ld + c * 8) * 2);
 }
-// wave w's share of a [ROWS][128] tile: ROWS / 16 instructions of 4 rows each
-template <int ROWS>
+// wave w's share of a [ROWS][128] tile among NW waves: ROWS / (4 NW) instructions of 4 rows each
+template <int ROWS, int NW = 4>
 __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, unsigned vo, int ld, bf16* S, int w) {
+    static_assert(NW % 4 == 0 && ROWS % (4 * NW) == 0, "row count must split evenly over the waves");
 #pragma unroll
-    for (int i = 0; i < ROWS / 16; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(S + 64 * (w + 4 * i) * 8), 16, vo, i * 16 * ld * 2, 0,
-                                                 0);
+    for (int i = 0; i < ROWS / (4 * NW); ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(S + 64 * (w + NW * i) * 8), 16, vo,
+                                                 i * 4 * NW * ld * 2, 0, 0);
 }
 
 // ======================================================================== bf16 forward
@@ -390,19 +391,22 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
 }
 
 // ======================================================================== bf16 backward: dK, dV
-// Workgroup: 128 keys of one kv head, one wave per SIMD, each wave owning 32
-// keys.  A wave's dK and dV accumulators (32 keys x 128 dims each) and its K
-// fragments stay in registers, and nothing spills.  The workgroup loops over the r
-// query heads of the group and over the 64-query tiles at or after its first
-// key.  Q, dO, lse and delta tiles travel straight from memory into LDS
+// Workgroup: 128 keys of one kv head and 8 waves, two per SIMD so that one
+// wave's softmax runs under the other's MFMAs.  Waves w and w + 4 own the same
+// 32 keys (block w % 4) and take the two 32-query halves of every 64-query
+// tile; each accumulates its half's share of dK and dV (32 keys x 128 dims
+// each) in registers, and the two shares are added in a fixed order at the end
+// (deterministic).  K and V rows of the block sit in LDS; the workgroup loops
+// over the r query heads of the group and over the query tiles at or after its
+// first key.  Q, dO, lse and delta tiles travel straight from memory into LDS
 // (buffer_load ... lds), double-buffered: the loads of tile i+1 run under the
-// MFMAs of tile i.  V (128 rows) is loaded the same way once.
-//
-__global__ void __launch_bounds__(256, 1)
+// MFMAs of tile i.
+__global__ void __launch_bounds__(512, 1)
 attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, const float* __restrict__ delta,
                    bf16* __restrict__ dqkv, int T, int H, int Hkv, int B)
 {
-    constexpr int D = 128, KB = 128;
+    constexpr int D = 128, KB = 128, NW = 8;
+    __shared__ __attribute__((aligned(1024))) bf16 sK[KB * 128];
     __shared__ __attribute__((aligned(1024))) bf16 sV[KB * 128];
     __shared__ __attribute__((aligned(1024))) bf16 sQ0[64 * 128];
     __shared__ __attribute__((aligned(1024))) bf16 sO0[64 * 128];
@@ -412,6 +416,7 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
 
     const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kq = w & 3, qh = w >> 2;            // key block of the wave, query half of each tile
     // key blocks early in the sequence see the most queries: they come first, and the
     // (head, sequence) index varies fastest so one kv head's blocks share an XCD
     const int gb = blockIdx.x % (Hkv * B), kblk = blockIdx.x / (Hkv * B);
@@ -419,23 +424,19 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
     const int r = H / Hkv;
     const int QKV = (H + 2 * Hkv) * D, HD = H * D, KD = Hkv * D;
     const int k0 = kblk * KB;
-    const int kw = k0 + 32 * w;                   // first key of this wave
-    const int key = kw + l32;
+    const int kw = k0 + 32 * kq;                  // first key of this wave
     const bool active = kw < T;                   // T is a multiple of 64
     const size_t rowbase = (size_t)b * T;
     const float scale = rsqrtf((float)D), c1 = kLog2e * scale;
 
-    // V rows of the block (rows past T read as zeros)
+    // K and V rows of the block (rows past T read as zeros)
     {
         const int rows = min(KB, T - k0);
-        dma_rows<KB>(buf_rsrc(qkv + (rowbase + k0) * QKV + HD + KD + g * D, (unsigned)(((rows - 1) * QKV + 128) * 2)),
-                     dma_voff(QKV, lane, w), QKV, sV, w);
-    }
-    bf16x8 kf[8];
-    if (active) {
-        const bf16* kp = qkv + (rowbase + key) * QKV + HD + g * D + 8 * hh;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(kp + 16 * kk);
+        const unsigned bytes = (unsigned)(((rows - 1) * QKV + 128) * 2);
+        const bf16* kp = qkv + (rowbase + k0) * QKV + HD + g * D;
+        const unsigned vo = dma_voff(QKV, lane, w);
+        dma_rows<KB, NW>(buf_rsrc(kp, bytes), vo, QKV, sK, w);
+        dma_rows<KB, NW>(buf_rsrc(kp + KD, bytes), vo, QKV, sV, w);
     }
     f32x16 dk[4], dv[4];
 #pragma unroll
@@ -447,8 +448,9 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
     // loads of tile it (query head g r + it / nqt, queries from (qt0 + it % nqt) 64) into one stage
     auto issue = [&](int it, bf16* Qs, bf16* Os, float* Ls, float* Ds) {
         const int hq = g * r + it / nqt, q0 = (qt0 + it % nqt) * 64;
-        dma_rows<64>(buf_rsrc(qkv + (rowbase + q0) * QKV + hq * D, (unsigned)((63 * QKV + 128) * 2)), voq, QKV, Qs, w);
-        dma_rows<64>(buf_rsrc(dy + (rowbase + q0) * HD + hq * D, (unsigned)((63 * HD + 128) * 2)), vod, HD, Os, w);
+        dma_rows<64, NW>(buf_rsrc(qkv + (rowbase + q0) * QKV + hq * D, (unsigned)((63 * QKV + 128) * 2)), voq, QKV,
+                         Qs, w);
+        dma_rows<64, NW>(buf_rsrc(dy + (rowbase + q0) * HD + hq * D, (unsigned)((63 * HD + 128) * 2)), vod, HD, Os, w);
         const size_t li = ((size_t)b * H + hq) * T + q0;
         if (w == 0)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(buf_rsrc(delta + (size_t)B * H * T + li, 256), (lds_void*)Ls, 4,
@@ -460,10 +462,10 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     };
-    // one tile: S and dP for the wave's 32 keys x 64 queries, then dV += P^T dO, dK += dS^T Q
+    // one tile: S and dP for the wave's 32 keys x 32 queries, then dV += P^T dO, dK += dS^T Q
     auto compute = [&](int it, const bf16* Qs, const bf16* Os, const float* Ls, const float* Ds) {
-        const int q0 = (qt0 + it % nqt) * 64;
-        if (!active || q0 + 63 < kw) return;  // wave-uniform: every query of the tile precedes every key
+        const int q0 = (qt0 + it % nqt) * 64 + 32 * qh;  // the wave's 32 queries
+        if (!active || q0 + 31 < kw) return;  // wave-uniform: every query precedes every key of the wave
         const bool diag = q0 < kw + 31;
         // Re-derive the lane index per tile: the swizzled fragment addresses are then
         // formed here (constant parts folded into the LDS offsets) instead of being
@@ -471,50 +473,48 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
         int ln = threadIdx.x & 63;
         asm volatile("" : "+v"(ln));
         const int hv = ln >> 5, lv32 = ln & 31;
+        f32x16 s, dp;
+        zero16(s);
+        zero16(dp);
 #pragma unroll
-        for (int qb2 = 0; qb2 < 2; ++qb2) {
-            f32x16 s, dp;
-            zero16(s);
-            zero16(dp);
+        for (int kk = 0; kk < 8; ++kk) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(Qs, 32 * qh + lv32, 2 * kk + hv),
+                                                        rfrag(sK, 32 * kq + lv32, 2 * kk + hv), s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(Os, 32 * qh + lv32, 2 * kk + hv),
+                                                         rfrag(sV, 32 * kq + lv32, 2 * kk + hv), dp, 0, 0, 0);
+        }
+        // lane holds S[q = q0 + 8(e>>2) + 4hh + (e&3)][key = kw + l32] in s[e]; P = exp2(S c1 - lse2),
+        // dS / scale = P (dP - delta) (dK is scaled at the end); the mask only on diagonal tiles
+        auto softmax = [&](auto masked) {
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(Qs, 32 * qb2 + lv32, 2 * kk + hv), kf[kk], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(Os, 32 * qb2 + lv32, 2 * kk + hv),
-                                                             rfrag(sV, 32 * w + lv32, 2 * kk + hv), dp, 0, 0, 0);
+            for (int gg = 0; gg < 4; ++gg) {
+                const int ql = 32 * qh + 8 * gg + 4 * hv;
+                const float4 l4 = *reinterpret_cast<const float4*>(Ls + ql);
+                const float4 d4 = *reinterpret_cast<const float4*>(Ds + ql);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int idx = 4 * gg + e;
+                    float p = __builtin_amdgcn_exp2f(s[idx] * c1 - lv[e]);
+                    if constexpr (decltype(masked)::value) p = q0 + 8 * gg + 4 * hv + e < kw + lv32 ? 0.0f : p;
+                    s[idx] = p;
+                    dp[idx] = p * (dp[idx] - dv4[e]);
+                }
             }
-            // lane holds S[q = q0 + 32qb2 + 8(e>>2) + 4hh + (e&3)][key] in s[e]; P = exp2(S c1 - lse2),
-            // dS / scale = P (dP - delta) (dK is scaled at the end); the mask only on diagonal tiles
-            auto softmax = [&](auto masked) {
+        };
+        if (diag)
+            softmax(std::true_type{});
+        else
+            softmax(std::false_type{});
 #pragma unroll
-                for (int gg = 0; gg < 4; ++gg) {
-                    const int ql = 32 * qb2 + 8 * gg + 4 * hv;
-                    const float4 l4 = *reinterpret_cast<const float4*>(Ls + ql);
-                    const float4 d4 = *reinterpret_cast<const float4*>(Ds + ql);
-                    const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        for (int j2 = 0; j2 < 2; ++j2) {
+            const bf16x8 pf = pack8(s, 8 * j2), dsf = pack8(dp, 8 * j2);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int idx = 4 * gg + e;
-                        float p = __builtin_amdgcn_exp2f(s[idx] * c1 - lv[e]);
-                        if constexpr (decltype(masked)::value) p = q0 + ql + e < kw + lv32 ? 0.0f : p;
-                        s[idx] = p;
-                        dp[idx] = p * (dp[idx] - dv4[e]);
-                    }
-                }
-            };
-            if (diag)
-                softmax(std::true_type{});
-            else
-                softmax(std::false_type{});
-#pragma unroll
-            for (int j2 = 0; j2 < 2; ++j2) {
-                const bf16x8 pf = pack8(s, 8 * j2), dsf = pack8(dp, 8 * j2);
-#pragma unroll
-                for (int db = 0; db < 4; ++db) {
-                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(Os, 32 * db, 32 * qb2 + 16 * j2, ln), pf,
-                                                                      dv[db], 0, 0, 0);
-                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(Qs, 32 * db, 32 * qb2 + 16 * j2, ln), dsf,
-                                                                      dk[db], 0, 0, 0);
-                }
+            for (int db = 0; db < 4; ++db) {
+                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(Os, 32 * db, 32 * qh + 16 * j2, ln), pf,
+                                                                  dv[db], 0, 0, 0);
+                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(Qs, 32 * db, 32 * qh + 16 * j2, ln), dsf,
+                                                                  dk[db], 0, 0, 0);
             }
         }
     };
@@ -531,17 +531,44 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
         if (it + 1 < total) compute(it + 1, sQ1, sO1, sL1, sD1);
         publish();
     }
-    if (!active) return;
+
+    // the second query half's shares go through LDS (all tiles consumed: the last publish
+    // was a barrier), 32 KB per key block: dK then dV, 16 KB each, lane-major float4s
+    float* red = kq == 0 ? reinterpret_cast<float*>(sK)
+               : kq == 1 ? reinterpret_cast<float*>(sV)
+               : kq == 2 ? reinterpret_cast<float*>(sQ0) : reinterpret_cast<float*>(sQ1);
+    float* red2 = kq == 0 ? reinterpret_cast<float*>(sK) + 4096
+                : kq == 1 ? reinterpret_cast<float*>(sV) + 4096
+                : kq == 2 ? reinterpret_cast<float*>(sO0) : reinterpret_cast<float*>(sO1);
+    if (qh == 1) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int o = ((db * 4 + q4) * 64 + lane) * 4;
+                *reinterpret_cast<float4*>(red + o) =
+                    make_float4(dk[db][4 * q4], dk[db][4 * q4 + 1], dk[db][4 * q4 + 2], dk[db][4 * q4 + 3]);
+                *reinterpret_cast<float4*>(red2 + o) =
+                    make_float4(dv[db][4 * q4], dv[db][4 * q4 + 1], dv[db][4 * q4 + 2], dv[db][4 * q4 + 3]);
+            }
+    }
+    __syncthreads();
+    if (qh == 1 || !active) return;
+    const int key = kw + l32;
     bf16* kout = dqkv + (rowbase + key) * QKV + HD + g * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
+            const int o = ((db * 4 + gg) * 64 + lane) * 4;
+            const float4 pk = *reinterpret_cast<const float4*>(red + o);
+            const float4 pv = *reinterpret_cast<const float4*>(red2 + o);
+            const float ok[4] = {pk.x, pk.y, pk.z, pk.w}, ov[4] = {pv.x, pv.y, pv.z, pv.w};
             float a[4], c[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                a[e] = dk[db][4 * gg + e] * scale;
-                c[e] = dv[db][4 * gg + e];
+                a[e] = (dk[db][4 * gg + e] + ok[e]) * scale;
+                c[e] = dv[db][4 * gg + e] + ov[e];
             }
             Vec4<bf16>::store(kout + 32 * db + 8 * gg + 4 * hh, a);
             Vec4<bf16>::store(kout + KD + 32 * db + 8 * gg + 4 * hh, c);
@@ -692,7 +719,7 @@ hipError_t launch_attn_bwd(const AttnDesc& a, hipStream_t s, int part) {
                                (const bf16*)a.qkv, (const bf16*)a.y, (const bf16*)a.dy, (const float*)a.lse, a.delta,
                                (bf16*)a.dqkv, a.T, a.H, a.Hkv, a.B);
         else
-            hipLaunchKernelGGL(attn_bwd_dkdv_bf16, dim3(((a.T + 127) / 128) * a.Hkv * a.B), dim3(256), 0, s,
+            hipLaunchKernelGGL(attn_bwd_dkdv_bf16, dim3(((a.T + 127) / 128) * a.Hkv * a.B), dim3(512), 0, s,
                                (const bf16*)a.qkv, (const bf16*)a.dy, (const float*)a.delta, (bf16*)a.dqkv, a.T, a.H,
                                a.Hkv, a.B);
         return hipGetLastError();
