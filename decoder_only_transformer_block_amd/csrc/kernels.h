@@ -86,7 +86,7 @@ hipError_t launch_embed_fwd(Dt dt, const int32_t* ids, const float* wte, void* x
 hipError_t launch_rmsnorm_fwd(Dt dt, const void* x, void* y, float* rstd, int rows, int C, float eps,
                               hipStream_t s);
 // dx(f32) = (accumulate ? dx : 0) + rstd*(dy - y*mean(dy*y)); dx_cd = cd(dx) when non-null
-hipError_t launch_rmsnorm_bwd(Dt dt, const void* y, const float* rstd, const float* dy, float* dx, void* dx_cd,
+hipError_t launch_rmsnorm_bwd(Dt dt, const void* y, const float* rstd, const void* dy, float* dx, void* dx_cd,
                               int rows, int C, int accumulate, hipStream_t s);
 hipError_t launch_rope_qknorm_fwd(Dt dt, void* qkv, float* rstdq, float* rstdk, const float* cosv,
                                   const float* sinv, int N, int T, int H, int Hkv, int D, float eps, hipStream_t s);

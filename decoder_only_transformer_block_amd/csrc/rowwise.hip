@@ -97,9 +97,10 @@ hipError_t launch_rmsnorm_fwd(Dt dt, const void* x, void* y, float* rstd, int ro
 
 // Derivative of the map above, from its saved output y and scale rstd:
 // dx = rstd * (dy - y * mean(dy * y)).
+// dy arrives in the compute dtype; dx (the residual-stream gradient) stays fp32.
 template <typename T>
 __global__ void __launch_bounds__(256)
-rmsnorm_bwd_kernel(const T* __restrict__ y, const float* __restrict__ rstd, const float* __restrict__ dy,
+rmsnorm_bwd_kernel(const T* __restrict__ y, const float* __restrict__ rstd, const T* __restrict__ dy,
                    float* __restrict__ dx, T* __restrict__ dx_cd, int rows, int C, int accumulate)
 {
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -109,7 +110,7 @@ rmsnorm_bwd_kernel(const T* __restrict__ y, const float* __restrict__ rstd, cons
     for (int c = lane * 4; c < C; c += 256) {
         float a[4], b[4];
         Vec4<T>::load(y + base + c, a);
-        Vec4<float>::load(dy + base + c, b);
+        Vec4<T>::load(dy + base + c, b);
         dot += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
     }
     dot = wave_sum(dot) / (float)C;
@@ -117,7 +118,7 @@ rmsnorm_bwd_kernel(const T* __restrict__ y, const float* __restrict__ rstd, cons
     for (int c = lane * 4; c < C; c += 256) {
         float a[4], b[4], o[4] = {0.f, 0.f, 0.f, 0.f};
         Vec4<T>::load(y + base + c, a);
-        Vec4<float>::load(dy + base + c, b);
+        Vec4<T>::load(dy + base + c, b);
         if (accumulate) Vec4<float>::load(dx + base + c, o);
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] += rs * (b[i] - a[i] * dot);
@@ -126,15 +127,15 @@ rmsnorm_bwd_kernel(const T* __restrict__ y, const float* __restrict__ rstd, cons
     }
 }
 
-hipError_t launch_rmsnorm_bwd(Dt dt, const void* y, const float* rstd, const float* dy, float* dx, void* dx_cd,
+hipError_t launch_rmsnorm_bwd(Dt dt, const void* y, const float* rstd, const void* dy, float* dx, void* dx_cd,
                               int rows, int C, int accumulate, hipStream_t s) {
     dim3 grid((rows + 3) / 4);
     if (dt == Dt::BF16)
-        hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)y, rstd, dy, dx, (bf16*)dx_cd,
-                           rows, C, accumulate);
+        hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)y, rstd, (const bf16*)dy, dx,
+                           (bf16*)dx_cd, rows, C, accumulate);
     else
-        hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, grid, dim3(256), 0, s, (const float*)y, rstd, dy, dx,
-                           (float*)dx_cd, rows, C, accumulate);
+        hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, grid, dim3(256), 0, s, (const float*)y, rstd, (const float*)dy,
+                           dx, (float*)dx_cd, rows, C, accumulate);
     return hipGetLastError();
 }
 

@@ -563,13 +563,13 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
         GemmDesc d;
         d.A = logits; d.lda = V; d.B = weight(c, -1, 1); d.ldb = C; d.b_kcontig = false;
         d.M = N; d.N = C; d.K = V;
-        d.epi = Epi::StoreF32; d.out = dxn; d.ldo = C;
+        d.epi = Epi::StoreCd; d.out = dxn; d.ldo = C;  // compute dtype
         TRY(gemm(c, d));
     }
     // dWlm = dz^T xf (vocab-wide output: 128 x 128 tiles with two register stages measured fastest)
     // vocab x n_embd output over all tokens: 256 x 128 tiles, the four-wave persistent ring measured fastest
     TRY(wgrad(c, logits, V, c->ws + p.xf, C, V, C, gslice(-1, 1), acc, 1, 8));
-    const double nb = (double)N * C * (e + 4 + 4 + (dt == Dt::BF16 ? 2 : 0)) + N * 4.0;
+    const double nb = (double)N * C * (e + e + 4 + (dt == Dt::BF16 ? 2 : 0)) + N * 4.0;
     TRY(launch(c, "rmsnorm_bwd", 0.0, nb, [&] {
         return launch_rmsnorm_bwd(dt, c->ws + p.xf, c->at<float>(p.rstdf), dxn, dx, dx_cd, N, C, 0, c->stream);
     }));
@@ -592,7 +592,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             GemmDesc d;
             d.A = c->ws + p.dh; d.lda = F; d.B = weight(c, l, 4); d.ldb = C; d.b_kcontig = false;
             d.M = N; d.N = C; d.K = F;
-            d.epi = Epi::StoreF32; d.out = dxn; d.ldo = C;
+            d.epi = Epi::StoreCd; d.out = dxn; d.ldo = C;  // compute dtype
             TRY(gemm(c, d));
         }
         TRY(wgrad(c, c->ws + p.dh, F, xn2, C, F, C, gslice(l, 4), acc));  // dWfc = dh^T xn2
@@ -635,7 +635,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             GemmDesc d;
             d.A = c->ws + p.dqkv; d.lda = QKV; d.B = weight(c, l, 0); d.ldb = C; d.b_kcontig = false;
             d.M = N; d.N = C; d.K = QKV;
-            d.epi = Epi::StoreF32; d.out = dxn; d.ldo = C;
+            d.epi = Epi::StoreCd; d.out = dxn; d.ldo = C;  // compute dtype
             TRY(gemm(c, d));
         }
         TRY(wgrad(c, c->ws + p.dqkv, QKV, xn1, C, QKV, C, gslice(l, 0), acc));  // dWqkv = dqkv^T xn1
