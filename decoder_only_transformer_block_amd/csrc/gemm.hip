@@ -75,51 +75,48 @@ template <typename T> struct EResidual {
         st8(out + o, x);
     }
 };
-// a = relu(v) is stored for the backward; act = a^2 (of the stored, rounded a) feeds the next GEMM
+// act = a^2 with a = relu(v) rounded to the compute dtype: the only stored output of
+// the MLP's first linear; the backward recovers a as sqrt(act)
 template <typename T> struct EReluSq {
     static constexpr bool kWide = std::is_same<T, bf16>::value;
-    T* a; T* act; int ldo;
+    T* act; int ldo;
     __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
-        size_t o = (size_t)m * ldo + n;
-        float r[4], s[4];
+        float s[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            r[i] = to_f32(from_f32<T>(fmaxf(v[i], 0.0f)));
-            s[i] = r[i] * r[i];
+            const float r = to_f32(from_f32<T>(fmaxf(v[i], 0.0f)));
+            s[i] = r * r;
         }
-        Vec4<T>::store(a + o, r);
-        Vec4<T>::store(act + o, s);
+        Vec4<T>::store(act + (size_t)m * ldo + n, s);
     }
     __device__ void put8(int m, int n, int, const float (&v)[8]) const {
-        const size_t o = (size_t)m * ldo + n;
-        float r[8], s[8];
+        float s[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            r[i] = (float)(bf16)fmaxf(v[i], 0.0f);
-            s[i] = r[i] * r[i];
+            const float r = (float)(bf16)fmaxf(v[i], 0.0f);
+            s[i] = r * r;
         }
-        st8(a + o, r);
-        st8(act + o, s);
+        st8(act + (size_t)m * ldo + n, s);
     }
 };
-// dh = dact * d(relu(h)^2)/dh = dact * 2 * relu(h)
+// dh = dact * d(relu(h)^2)/dh = dact * 2 relu(h), with relu(h) = sqrt(act)
 template <typename T> struct EReluSqBwd {
     static constexpr bool kWide = std::is_same<T, bf16>::value;
-    T* out; const T* a; int ldo;
+    T* out; const T* act; int ldo;
     __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
         size_t o = (size_t)m * ldo + n;
         float x[4];
-        Vec4<T>::load(a + o, x);
+        Vec4<T>::load(act + o, x);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = v[i] * 2.0f * x[i];
+        for (int i = 0; i < 4; ++i) x[i] = v[i] * 2.0f * __builtin_amdgcn_sqrtf(x[i]);
         Vec4<T>::store(out + o, x);
     }
     __device__ void put8(int m, int n, int, const float (&v)[8]) const {
         const size_t o = (size_t)m * ldo + n;
         float x[8];
-        ld8(a + o, x);
+        ld8(act + o, x);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = v[i] * 2.0f * x[i];
+        for (int i = 0; i < 8; ++i) x[i] = v[i] * 2.0f * __builtin_amdgcn_sqrtf(x[i]);
         st8(out + o, x);
     }
 };
@@ -1357,7 +1354,7 @@ static hipError_t dispatch_epi(const GemmDesc& d, hipStream_t s) {
     case Epi::StoreCd: return run(EStoreCd<T>{(T*)d.out, d.ldo});
     case Epi::StoreF32: return run(EStoreF32{(float*)d.out, d.ldo});
     case Epi::ResidualCd: return run(EResidual<T>{(T*)d.out, (const T*)d.in, d.ldo});
-    case Epi::ReluSq: return run(EReluSq<T>{(T*)d.out, (T*)d.out2, d.ldo});
+    case Epi::ReluSq: return run(EReluSq<T>{(T*)d.out, d.ldo});
     case Epi::ReluSqBwd: return run(EReluSqBwd<T>{(T*)d.out, (const T*)d.in, d.ldo});
     case Epi::Grad: return run(EGrad{(float*)d.out, d.ldo, d.accumulate});
     case Epi::SplitK: return run(ESplitK{(float*)d.out, d.ldo, d.split_stride});

@@ -21,7 +21,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
     size_t flag, cosv, sinv, wcast, x0, x, layer0, layer_stride;
-    size_t l_xn1, l_rstd1, l_qkv, l_rstdq, l_rstdk, l_y, l_lse, l_xn2, l_rstd2, l_a, l_act;
+    size_t l_xn1, l_rstd1, l_qkv, l_rstdq, l_rstdk, l_y, l_lse, l_xn2, l_rstd2, l_act;
     size_t xf, rstdf, logits, lse, loss_rows, dxn, dx, dx_cd, dh, dy, dqkv, delta, splitk, iscr, total;
 };
 
@@ -160,7 +160,6 @@ void make_plan(ncgpt_ctx* c) {
     p.l_lse = LA((size_t)c->B * c->H * c->T * 4);
     p.l_xn2 = LA(N * c->C * e);
     p.l_rstd2 = LA(N * 4);
-    p.l_a = LA(N * c->F * e);
     p.l_act = LA(N * c->F * e);
     p.layer_stride = lo;
     p.layer0 = A(lo * c->L);
@@ -444,7 +443,6 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
         uint8_t* qkv = c->ws + c->lay(l, p.l_qkv);
         uint8_t* y = c->ws + c->lay(l, p.l_y);
         uint8_t* xn2 = c->ws + c->lay(l, p.l_xn2);
-        uint8_t* a = c->ws + c->lay(l, p.l_a);
         uint8_t* act = c->ws + c->lay(l, p.l_act);
         TRY(launch(c, "rmsnorm_fwd", 0.0, norm_bytes, [&] {
             return launch_rmsnorm_fwd(dt, xin, xn1, c->at<float>(c->lay(l, p.l_rstd1)), N, C, eps, c->stream);
@@ -486,7 +484,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             GemmDesc d;
             d.A = xn2; d.lda = C; d.B = weight(c, l, 4); d.ldb = C;
             d.M = N; d.N = F; d.K = C;
-            d.epi = Epi::ReluSq; d.out = a; d.out2 = act; d.ldo = F;
+            d.epi = Epi::ReluSq; d.out = act; d.ldo = F;
             d.variant = 6;  // two stores per element: the non-persistent ring measured fastest
             TRY(gemm(c, d));
         }
@@ -578,13 +576,12 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
         uint8_t* qkv = c->ws + c->lay(l, p.l_qkv);
         uint8_t* y = c->ws + c->lay(l, p.l_y);
         uint8_t* xn2 = c->ws + c->lay(l, p.l_xn2);
-        uint8_t* a = c->ws + c->lay(l, p.l_a);
         uint8_t* act = c->ws + c->lay(l, p.l_act);
-        {   // dh = (dx Wproj) * 2a
+        {   // dh = (dx Wproj) * 2 relu(h), relu(h) = sqrt(act)
             GemmDesc d;
             d.A = dxg; d.lda = C; d.B = weight(c, l, 5); d.ldb = F; d.b_kcontig = false;
             d.M = N; d.N = F; d.K = C;
-            d.epi = Epi::ReluSqBwd; d.out = c->ws + p.dh; d.in = a; d.ldo = F;
+            d.epi = Epi::ReluSqBwd; d.out = c->ws + p.dh; d.in = act; d.ldo = F;
             TRY(gemm(c, d));
         }
         TRY(wgrad(c, dxg, C, act, F, C, F, gslice(l, 5), acc));  // dWproj = dx^T act
@@ -701,7 +698,7 @@ ncgpt_status ncgpt_probe(ncgpt_ctx* c, int what, int layer, float* dst) {
     case 3: src = c->ws + c->lay(layer, p.l_y); break;
     case 4: src = c->ws + c->lay(layer, p.l_lse); dt = Dt::F32; break;
     case 5: src = c->ws + c->lay(layer, p.l_xn2); break;
-    case 6: src = c->ws + c->lay(layer, p.l_a); break;
+    case 6: src = c->ws + c->lay(layer, p.l_act); break;
     case 7: src = c->ws + p.xf; break;
     case 8: src = c->ws + p.lse; dt = Dt::F32; break;
     case 9: src = c->ws + p.loss_rows; dt = Dt::F32; break;

@@ -19,7 +19,7 @@ F32, BF16 = 0, 1
 _STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "ENOMEM", -4: "EHIP", -5: "ESTATE", -6: "EDEVICE"}
 
 # probe ids (ncgpt_probe)
-PROBE = {"x0": 0, "xn1": 1, "qkv": 2, "y": 3, "lse_att": 4, "xn2": 5, "a": 6, "xf": 7, "lse": 8, "loss_rows": 9,
+PROBE = {"x0": 0, "xn1": 1, "qkv": 2, "y": 3, "lse_att": 4, "xn2": 5, "act": 6, "xf": 7, "lse": 8, "loss_rows": 9,
          "dx0": 10}
 WQ, WK, WV, WO, WFC, WPROJ = range(6)
 

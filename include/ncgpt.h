@@ -113,7 +113,7 @@ ncgpt_status ncgpt_check(ncgpt_ctx* ctx);
  *   0 x0 [N,C] embedding output          1 xn1 [N,C] pre-attention norm (layer)
  *   2 qkv [N,(H+2Hkv)D] after RoPE/QK-norm (layer)   3 y [N,H*D] attention output (layer)
  *   4 lse_att [B,H,T] attention log-sum-exp (layer)  5 xn2 [N,C] pre-MLP norm (layer)
- *   6 a [N,F] relu(xn2 Wfc^T) (layer)    7 xf [N,C] final norm      8 lse [N] logits log-sum-exp
+ *   6 act [N,F] relu(xn2 Wfc^T)^2 (layer)  7 xf [N,C] final norm    8 lse [N] logits log-sum-exp
  *   9 loss_rows [N] per-token loss (0 when ignored)  10 dx0 [N,C] gradient w.r.t. x0 (after backward)
  * EINVAL for an unknown what or layer, ESTATE before the forward that produces it. */
 ncgpt_status ncgpt_probe_numel(const ncgpt_ctx* ctx, int what, size_t* numel);
