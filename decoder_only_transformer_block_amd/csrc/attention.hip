@@ -132,15 +132,17 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, unsigned vo,
 }
 
 // ======================================================================== bf16 forward
-// Workgroup: 128 queries of one head, 4 waves x 32 queries; K/V tiles of 64
-// keys travel straight from memory into LDS, double-buffered.  A wave fits in
-// 256 registers, so two workgroups share a CU and one wave's softmax (VALU,
-// exp) overlaps the other's MFMAs.
-__global__ void __launch_bounds__(256, 2)
+// Workgroup: 4 waves x 32 QB queries of one head; K/V tiles of 64 keys travel
+// straight from memory into LDS, double-buffered.  QB = 2 reuses every K and V
+// fragment read from LDS for two 32-query blocks at one wave per SIMD; QB = 1
+// fits two workgroups per CU, so one wave's softmax runs under the other's
+// MFMAs.
+template <int QB>
+__global__ void __launch_bounds__(256, QB == 1 ? 2 : 1)
 attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restrict__ lse, int T, int H, int Hkv,
               int B)
 {
-    constexpr int D = 128, QB = 128;
+    constexpr int D = 128, QW = 32 * QB, QBLK = 4 * QW;
     __shared__ __attribute__((aligned(1024))) bf16 sK0[64 * 128];
     __shared__ __attribute__((aligned(1024))) bf16 sV0[64 * 128];
     __shared__ __attribute__((aligned(1024))) bf16 sK1[64 * 128];
@@ -148,30 +150,37 @@ attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restr
     const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     // late (heavy) query blocks first; (head, sequence) varies fastest
-    const int nqb = (T + QB - 1) / QB;
+    const int nqb = (T + QBLK - 1) / QBLK;
     const int hb = blockIdx.x % (H * B), qblk = nqb - 1 - blockIdx.x / (H * B);
     const int hq = hb / B, b = hb % B;
     const int g = hq / (H / Hkv);
     const int QKV = (H + 2 * Hkv) * D, HD = H * D, KD = Hkv * D;
-    const int q0 = qblk * QB;
-    const int qw = q0 + 32 * w;                 // first query of this wave
+    const int q0 = qblk * QBLK;
+    const int qw = q0 + QW * w;                 // first query of this wave
     const bool active = qw < T;                 // T is a multiple of 64
-    const int q = qw + l32;
     const size_t rowbase = (size_t)b * T;
 
-    bf16x8 qf[8];
+    bf16x8 qf[QB][8];
     if (active) {
-        const bf16* qp = qkv + (rowbase + q) * QKV + hq * D + 8 * hh;
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
+        for (int qq = 0; qq < QB; ++qq) {
+            const int q = min(qw + 32 * qq + l32, T - 1);
+            const bf16* qp = qkv + (rowbase + q) * QKV + hq * D + 8 * hh;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) qf[qq][kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
+        }
     }
-    f32x16 o[4];
+    f32x16 o[QB][4];
+    float lsum[QB];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) zero16(o[db]);
-    float lsum = 0.0f;
+    for (int qq = 0; qq < QB; ++qq) {
+        lsum[qq] = 0.0f;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) zero16(o[qq][db]);
+    }
     const float c1 = kLog2e * rsqrtf((float)D), c2 = sqrtf((float)D) * kLog2e;
 
-    const int nkt = min(q0 + QB, T) / 64;       // key tiles at or before the block's last query
+    const int nkt = min(q0 + QBLK, T) / 64;     // key tiles at or before the block's last query
     const unsigned vo = dma_voff(QKV, lane, w);
     const bf16* kbase = qkv + rowbase * QKV + HD + g * D;
     auto issue = [&](int kt, bf16* Ks, bf16* Vs) {
@@ -186,29 +195,35 @@ attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restr
     };
     auto compute = [&](int kt, const bf16* Ks, const bf16* Vs) {
         const int kv0 = kt * 64;
-        if (!active || kv0 > qw + 31) return;  // wave-uniform: the whole tile lies after the wave's queries
+        if (!active || kv0 > qw + QW - 1) return;  // wave-uniform: the whole tile lies after the wave's queries
         const bool diag = kv0 + 63 > qw;
         int ln = threadIdx.x & 63;             // opaque lane: keeps fragment addresses out of loop-invariant registers
         asm volatile("" : "+v"(ln));
         const int hv = ln >> 5, lv32 = ln & 31;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            f32x16 sc;
-            zero16(sc);
+            f32x16 sc[QB];
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk)
-                sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(Ks, 32 * kb + lv32, 2 * kk + hv), qf[kk], sc, 0, 0,
-                                                             0);
-            // lane holds S[q][key = kv0 + 32kb + 8(e>>2) + 4hh + (e&3)] in sc[e]
+            for (int qq = 0; qq < QB; ++qq) zero16(sc[qq]);
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                const bf16x8 kf = rfrag(Ks, 32 * kb + lv32, 2 * kk + hv);
+#pragma unroll
+                for (int qq = 0; qq < QB; ++qq)
+                    sc[qq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qq][kk], sc[qq], 0, 0, 0);
+            }
+            // lane holds S[q = qw + 32qq + l32][key = kv0 + 32kb + 8(e>>2) + 4hh + (e&3)] in sc[qq][e]
             auto softmax = [&](auto masked) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    float p = __builtin_amdgcn_exp2f(sc[e] * c1 - c2);
-                    if constexpr (decltype(masked)::value)
-                        p = kv0 + 32 * kb + 8 * (e >> 2) + 4 * hv + (e & 3) > qw + lv32 ? 0.0f : p;
-                    sc[e] = p;
-                    lsum += p;
-                }
+                for (int qq = 0; qq < QB; ++qq)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        float p = __builtin_amdgcn_exp2f(sc[qq][e] * c1 - c2);
+                        if constexpr (decltype(masked)::value)
+                            p = kv0 + 32 * kb + 8 * (e >> 2) + 4 * hv + (e & 3) > qw + 32 * qq + lv32 ? 0.0f : p;
+                        sc[qq][e] = p;
+                        lsum[qq] += p;
+                    }
             };
             if (diag)
                 softmax(std::true_type{});
@@ -216,11 +231,16 @@ attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restr
                 softmax(std::false_type{});
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const bf16x8 pf = pack8(sc, 8 * j);
+                bf16x8 pf[QB];
 #pragma unroll
-                for (int db = 0; db < 4; ++db)
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(Vs, 32 * db, 32 * kb + 16 * j, ln), pf, o[db],
-                                                                    0, 0, 0);
+                for (int qq = 0; qq < QB; ++qq) pf[qq] = pack8(sc[qq], 8 * j);
+#pragma unroll
+                for (int db = 0; db < 4; ++db) {
+                    const bf16x8 vf = trfrag(Vs, 32 * db, 32 * kb + 16 * j, ln);
+#pragma unroll
+                    for (int qq = 0; qq < QB; ++qq)
+                        o[qq][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qq], o[qq][db], 0, 0, 0);
+                }
             }
         }
     };
@@ -236,19 +256,24 @@ attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restr
         publish();
     }
     if (!active) return;
-    const float ltot = lsum + __shfl_xor(lsum, 32, kWave);
-    const float inv = 1.0f / ltot;
-    bf16* yp = y + (rowbase + q) * HD + hq * D;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int qq = 0; qq < QB; ++qq) {
+        const int q = qw + 32 * qq + l32;
+        const float ltot = lsum[qq] + __shfl_xor(lsum[qq], 32, kWave);
+        const float inv = 1.0f / ltot;
+        if (q >= T) continue;
+        bf16* yp = y + (rowbase + q) * HD + hq * D;
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-            float v[4];
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = o[db][4 * gg + e] * inv;
-            Vec4<bf16>::store(yp + 32 * db + 8 * gg + 4 * hh, v);
-        }
-    if (hh == 0) lse[((size_t)b * H + hq) * T + q] = sqrtf((float)D) + logf(ltot);
+            for (int gg = 0; gg < 4; ++gg) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = o[qq][db][4 * gg + e] * inv;
+                Vec4<bf16>::store(yp + 32 * db + 8 * gg + 4 * hh, v);
+            }
+        if (hh == 0) lse[((size_t)b * H + hq) * T + q] = sqrtf((float)D) + logf(ltot);
+    }
 }
 
 // ======================================================================== bf16 backward: dQ (and delta)
@@ -693,8 +718,10 @@ hipError_t attn_init_attributes() { return hipSuccess; }
 hipError_t launch_attn_fwd(const AttnDesc& a, hipStream_t s) {
     if (a.dt == Dt::BF16) {
         if (a.D != 128 || a.T % 64) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(attn_fwd_bf16, dim3(((a.T + 127) / 128) * a.H * a.B), dim3(256), 0, s, (const bf16*)a.qkv,
-                           (bf16*)a.y, a.lse, a.T, a.H, a.Hkv, a.B);
+        // one 32-query block per wave: two workgroups per CU (softmax under the other's MFMAs)
+        // measured faster than two blocks per wave at one workgroup per CU
+        hipLaunchKernelGGL(attn_fwd_bf16<1>, dim3(((a.T + 127) / 128) * a.H * a.B), dim3(256), 0, s,
+                           (const bf16*)a.qkv, (bf16*)a.y, a.lse, a.T, a.H, a.Hkv, a.B);
         return hipGetLastError();
     }
     dim3 grid((unsigned)(((size_t)a.B * a.T * a.H + 3) / 4));
