@@ -131,6 +131,51 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, unsigned vo,
                                                  i * 4 * NW * ld * 2, 0, 0);
 }
 
+// ======================================================================== fused RoPE + QK-norm backward
+// A head row's gradient g (w.r.t. the normalised, rotated q or k) held by a lane
+// pair in the MFMA accumulator layout: lane half hh holds dims
+// d = 32 db + 8 gg + 4 hh + e in v[db][4 gg + e].  The QK-norm derivative needs
+// the saved normalised row y and 1/rms rs: r = rs (g - y mean(g y)); the
+// rotation's transpose then maps the pair (i, i + D/2):
+// out_i = r_i cos - r_{i+D/2} sin, out_{i+D/2} = r_i sin + r_{i+D/2} cos.
+// Dims d and d + 64 sit in the same lane (db and db + 2).
+__device__ __forceinline__ void rope_qknorm_bwd_row(float (&v)[4][16], const bf16* __restrict__ yrow, float rs,
+                                                    const float* __restrict__ cs, const float* __restrict__ sn,
+                                                    int hh) {
+    float yv[4][16];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            float t[4];
+            Vec4<bf16>::load(yrow + 32 * db + 8 * gg + 4 * hh, t);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) yv[db][4 * gg + e] = t[e];
+        }
+    float dot = 0.0f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dot += v[db][i] * yv[db][i];
+    dot = (dot + __shfl_xor(dot, 32, kWave)) * (1.0f / 128.0f);
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            float c[4], s[4];
+            const int i0 = 32 * db + 8 * gg + 4 * hh;
+            Vec4<float>::load(cs + i0, c);
+            Vec4<float>::load(sn + i0, s);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int k = 4 * gg + e;
+                const float r1 = rs * (v[db][k] - yv[db][k] * dot), r2 = rs * (v[db + 2][k] - yv[db + 2][k] * dot);
+                v[db][k] = r1 * c[e] - r2 * s[e];
+                v[db + 2][k] = r1 * s[e] + r2 * c[e];
+            }
+        }
+}
+
 // ======================================================================== bf16 forward
 // Workgroup: 4 waves x 32 QB queries of one head; K/V tiles of 64 keys travel
 // straight from memory into LDS, double-buffered.  QB = 2 reuses every K and V
@@ -286,8 +331,9 @@ attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restr
 template <int OCC>
 __global__ void __launch_bounds__(256, OCC)
 attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const bf16* __restrict__ dy,
-                 const float* __restrict__ lse, float* __restrict__ delta, bf16* __restrict__ dqkv, int T, int H,
-                 int Hkv, int B)
+                 const float* __restrict__ lse, float* __restrict__ delta, bf16* __restrict__ dqkv,
+                 const float* __restrict__ rstdq, const float* __restrict__ cosv, const float* __restrict__ sinv,
+                 int T, int H, int Hkv, int B)
 {
     constexpr int D = 128, QB = 128;
     __shared__ __attribute__((aligned(1024))) bf16 sK0[64 * 128];
@@ -403,14 +449,19 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
         publish();
     }
     if (!active) return;
+    float gq[4][16];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) gq[db][i] = dq[db][i] * scale;
+    rope_qknorm_bwd_row(gq, qkv + (rowbase + q) * QKV + hq * D, rstdq[(rowbase + q) * H + hq], cosv + q * (D / 2),
+                        sinv + q * (D / 2), hh);
     bf16* qout = dqkv + (rowbase + q) * QKV + hq * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
-            float a[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) a[e] = dq[db][4 * gg + e] * scale;
+            const float a[4] = {gq[db][4 * gg], gq[db][4 * gg + 1], gq[db][4 * gg + 2], gq[db][4 * gg + 3]};
             Vec4<bf16>::store(qout + 32 * db + 8 * gg + 4 * hh, a);
         }
 }
@@ -428,7 +479,8 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
 // MFMAs of tile i.
 __global__ void __launch_bounds__(512, 1)
 attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, const float* __restrict__ delta,
-                   bf16* __restrict__ dqkv, int T, int H, int Hkv, int B)
+                   bf16* __restrict__ dqkv, const float* __restrict__ rstdk, const float* __restrict__ cosv,
+                   const float* __restrict__ sinv, int T, int H, int Hkv, int B)
 {
     constexpr int D = 128, KB = 128, NW = 8;
     __shared__ __attribute__((aligned(1024))) bf16 sK[KB * 128];
@@ -581,6 +633,7 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
     if (qh == 1 || !active) return;
     const int key = kw + l32;
     bf16* kout = dqkv + (rowbase + key) * QKV + HD + g * D;
+    float gk[4][16];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -589,14 +642,22 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
             const float4 pk = *reinterpret_cast<const float4*>(red + o);
             const float4 pv = *reinterpret_cast<const float4*>(red2 + o);
             const float ok[4] = {pk.x, pk.y, pk.z, pk.w}, ov[4] = {pv.x, pv.y, pv.z, pv.w};
-            float a[4], c[4];
+            float c[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                a[e] = (dk[db][4 * gg + e] + ok[e]) * scale;
+                gk[db][4 * gg + e] = (dk[db][4 * gg + e] + ok[e]) * scale;
                 c[e] = dv[db][4 * gg + e] + ov[e];
             }
-            Vec4<bf16>::store(kout + 32 * db + 8 * gg + 4 * hh, a);
             Vec4<bf16>::store(kout + KD + 32 * db + 8 * gg + 4 * hh, c);
+        }
+    rope_qknorm_bwd_row(gk, qkv + (rowbase + key) * QKV + HD + g * D, rstdk[(rowbase + key) * Hkv + g],
+                        cosv + key * (D / 2), sinv + key * (D / 2), hh);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            const float a[4] = {gk[db][4 * gg], gk[db][4 * gg + 1], gk[db][4 * gg + 2], gk[db][4 * gg + 3]};
+            Vec4<bf16>::store(kout + 32 * db + 8 * gg + 4 * hh, a);
         }
 }
 
@@ -739,16 +800,17 @@ hipError_t launch_attn_fwd(const AttnDesc& a, hipStream_t s) {
 hipError_t launch_attn_bwd(const AttnDesc& a, hipStream_t s, int part) {
     const int N = a.B * a.T;
     const bool bf = a.dt == Dt::BF16;
-    if (bf ? (a.D != 128 || a.T % 64) : (a.D != 128 && a.D != 64)) return hipErrorInvalidValue;
+    if (bf ? (a.D != 128 || a.T % 64 || !a.rstdq || !a.rstdk || !a.cosv || !a.sinv) : (a.D != 128 && a.D != 64))
+        return hipErrorInvalidValue;
     if (bf) {
         if (part == 0)
             hipLaunchKernelGGL(attn_bwd_dq_bf16<2>, dim3(((a.T + 127) / 128) * a.H * a.B), dim3(256), 0, s,
                                (const bf16*)a.qkv, (const bf16*)a.y, (const bf16*)a.dy, (const float*)a.lse, a.delta,
-                               (bf16*)a.dqkv, a.T, a.H, a.Hkv, a.B);
+                               (bf16*)a.dqkv, a.rstdq, a.cosv, a.sinv, a.T, a.H, a.Hkv, a.B);
         else
             hipLaunchKernelGGL(attn_bwd_dkdv_bf16, dim3(((a.T + 127) / 128) * a.Hkv * a.B), dim3(512), 0, s,
-                               (const bf16*)a.qkv, (const bf16*)a.dy, (const float*)a.delta, (bf16*)a.dqkv, a.T, a.H,
-                               a.Hkv, a.B);
+                               (const bf16*)a.qkv, (const bf16*)a.dy, (const float*)a.delta, (bf16*)a.dqkv, a.rstdk,
+                               a.cosv, a.sinv, a.T, a.H, a.Hkv, a.B);
         return hipGetLastError();
     }
     dim3 gq((unsigned)(((size_t)N * a.H + 3) / 4)), gk((unsigned)(((size_t)N * a.Hkv + 3) / 4));

@@ -73,9 +73,15 @@ struct AttnDesc {
     const void* dy = nullptr;   // [B*T, H*D] cd (backward)
     void* dqkv = nullptr;       // [B*T, (H+2Hkv)*D] cd (backward)
     float* delta = nullptr;     // [2, B, H, T] scratch (backward): delta, then (bf16) the LSE in log2 units
+    // bf16 backward only: the RoPE + QK-norm backward is applied to dq and dk before they are stored
+    const float* rstdq = nullptr;  // [B*T, H] saved 1/rms of the rotated q heads
+    const float* rstdk = nullptr;  // [B*T, Hkv]
+    const float* cosv = nullptr;   // [T, D/2] rotation tables
+    const float* sinv = nullptr;
 };
 hipError_t launch_attn_fwd(const AttnDesc& a, hipStream_t s);
-// part 0: dQ (and delta = rowsum(dy * y), which part 1 reads); part 1: dK, dV -- in this order
+// part 0: dQ (and delta = rowsum(dy * y), which part 1 reads); part 1: dK, dV -- in this order.  In bf16
+// the q and k gradients leave already taken back through QK-norm and RoPE (rstdq/rstdk/cosv/sinv).
 hipError_t launch_attn_bwd(const AttnDesc& a, hipStream_t s, int part);
 hipError_t attn_init_attributes();
 

@@ -609,6 +609,8 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             ad.dt = dt; ad.B = (int)c->B; ad.T = (int)c->T; ad.H = (int)c->H; ad.Hkv = (int)c->Hkv; ad.D = (int)c->D;
             ad.qkv = qkv; ad.y = y; ad.lse = c->at<float>(c->lay(l, p.l_lse));
             ad.dy = c->ws + p.dy; ad.dqkv = c->ws + p.dqkv; ad.delta = c->at<float>(p.delta);
+            ad.rstdq = c->at<float>(c->lay(l, p.l_rstdq)); ad.rstdk = c->at<float>(c->lay(l, p.l_rstdk));
+            ad.cosv = c->at<float>(p.cosv); ad.sinv = c->at<float>(p.sinv);
             const double pairs = (double)c->B * c->H * c->T * (c->T + 1) / 2.0;
             const bool bf = dt == Dt::BF16;
             // algorithmic backward FLOPs: dV, dK and the dP product (6 D per pair) in the key-outer kernel,
@@ -622,12 +624,14 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             TRY(launch(c, bf ? "attn_bwd_dkdv_bf16" : "attn_bwd_dkdv_f32", 6.0 * c->D * pairs,
                        2 * qb + 4 * kb + 2 * rows, [&] { return launch_attn_bwd(ad, c->stream, 1); }));
         }
-        TRY(launch(c, "rope_qknorm_bwd", 0.0, (double)N * (c->H + c->Hkv) * c->D * 3 * e, [&] {
-            return launch_rope_qknorm_bwd(dt, c->ws + p.dqkv, qkv, c->at<float>(c->lay(l, p.l_rstdq)),
-                                          c->at<float>(c->lay(l, p.l_rstdk)), c->at<float>(p.cosv),
-                                          c->at<float>(p.sinv), N, (int)c->T, (int)c->H, (int)c->Hkv, (int)c->D,
-                                          c->stream);
-        }));
+        if (dt != Dt::BF16) {  // the bf16 attention backward applies it in its epilogues
+            TRY(launch(c, "rope_qknorm_bwd", 0.0, (double)N * (c->H + c->Hkv) * c->D * 3 * e, [&] {
+                return launch_rope_qknorm_bwd(dt, c->ws + p.dqkv, qkv, c->at<float>(c->lay(l, p.l_rstdq)),
+                                              c->at<float>(c->lay(l, p.l_rstdk)), c->at<float>(p.cosv),
+                                              c->at<float>(p.sinv), N, (int)c->T, (int)c->H, (int)c->Hkv, (int)c->D,
+                                              c->stream);
+            }));
+        }
         {   // dxn1 = dqkv Wqkv
             GemmDesc d;
             d.A = c->ws + p.dqkv; d.lda = QKV; d.B = weight(c, l, 0); d.ldb = C; d.b_kcontig = false;
