@@ -107,6 +107,8 @@ hipError_t launch_ce_bwd(Dt dt, void* logits, const float* lse, const int32_t* t
                          float grad_scale, int N, int V, hipStream_t s);
 // dwte = (accumulate ? dwte : 0) + segment sums of dx rows by token id; deterministic.
 // scratch: 4*N int32 + N*C f32 (the latter may alias any free [N,C] f32 buffer)
+// iscratch: embed_bwd_scratch_ints(N, V) ints; partial: N x C floats; V <= 65536
+size_t embed_bwd_scratch_ints(int N, int V);
 hipError_t launch_embed_bwd(const int32_t* ids, const float* dx, float* dwte, int N, int C, int V, int accumulate,
                             int32_t* iscratch, float* partial, hipStream_t s);
 hipError_t launch_to_f32(Dt dt, const void* src, float* dst, size_t n, hipStream_t s);

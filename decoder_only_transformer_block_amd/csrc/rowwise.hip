@@ -450,62 +450,94 @@ hipError_t launch_ce_bwd(Dt dt, void* logits, const float* lse, const int32_t* t
 // ------------------------------------------------------------------ embedding backward
 // dwte[v] = sum of dx rows of the tokens with id v, summed in a fixed order so
 // the result is bitwise reproducible (no float atomics):
-//   1. stable LSD radix sort of (id, position) pairs by id (one workgroup);
+//   1. a stable counting sort of (id, position) pairs by id: per block of 1024
+//      tokens an id histogram, an exclusive prefix over blocks per id and over
+//      ids, and a scatter at base[id] + (earlier blocks' count of id) + (earlier
+//      tokens of id in the block);
 //   2. the sorted array is cut into fixed chunks of 64; each chunk sums the
 //      rows of every run of equal ids inside it and writes the partial sum at
 //      the run's first sorted index;
 //   3. each vocab row sums its runs' partials (its sorted range [a, b) has
 //      partials at a and at every chunk start inside it), in order.
-constexpr int kSortThreads = 512;
+constexpr int kSortBlock = 1024;   // tokens per counting block
+constexpr int kMaxSortVocab = 65536;
 constexpr int kChunk = 64;
 
-__global__ void __launch_bounds__(kSortThreads)
-radix_sort_ids_kernel(const int32_t* __restrict__ ids, int N, int V, int32_t* __restrict__ keys_a,
-                      int32_t* __restrict__ vals_a, int32_t* __restrict__ keys_b, int32_t* __restrict__ vals_b)
+__device__ __forceinline__ int clamp_id(int id, int V) { return (id >= 0 && id < V) ? id : 0; }  // bad ids: reported by the forward
+
+// cnt[b][v] = number of tokens of block b with id v (two 16-bit counters per LDS word)
+__global__ void __launch_bounds__(1024)
+embed_hist_kernel(const int32_t* __restrict__ ids, int N, int V, uint32_t* __restrict__ cnt)
 {
-    __shared__ uint32_t cnt[16][kSortThreads];
-    __shared__ uint32_t tot[16];
-    const int tid = threadIdx.x;
-    const int per = (N + kSortThreads - 1) / kSortThreads;
-    const int beg = min(N, tid * per), end = min(N, beg + per);
-    for (int i = beg; i < end; ++i) {
-        int id = ids[i];
-        keys_a[i] = (id >= 0 && id < V) ? id : 0;  // bad ids were reported by the forward
-        vals_a[i] = i;
-    }
-    int bits = 1;
-    while ((1 << bits) < V) ++bits;
+    __shared__ uint32_t h[kMaxSortVocab / 2];
+    const int b = blockIdx.x, t = threadIdx.x;
+    for (int i = t; i < (V + 1) / 2; i += 1024) h[i] = 0;
     __syncthreads();
-    int32_t *ks = keys_a, *vs = vals_a, *kd = keys_b, *vd = vals_b;
-    for (int shift = 0; shift < bits; shift += 4) {
-        for (int d = 0; d < 16; ++d) cnt[d][tid] = 0;
-        for (int i = beg; i < end; ++i) cnt[(ks[i] >> shift) & 15][tid]++;
-        __syncthreads();
-        if (tid < 16) {  // exclusive scan along threads for digit tid
-            uint32_t run = 0;
-            for (int t = 0; t < kSortThreads; ++t) { uint32_t c = cnt[tid][t]; cnt[tid][t] = run; run += c; }
-            tot[tid] = run;
-        }
-        __syncthreads();
-        if (tid == 0) {  // digit offsets
-            uint32_t run = 0;
-            for (int d = 0; d < 16; ++d) { uint32_t c = tot[d]; tot[d] = run; run += c; }
-        }
-        __syncthreads();
-        for (int i = beg; i < end; ++i) {
-            int k = ks[i], d = (k >> shift) & 15;
-            uint32_t pos = tot[d] + cnt[d][tid]++;
-            kd[pos] = k;
-            vd[pos] = vs[i];
-        }
-        __syncthreads();
-        int32_t* t0 = ks; ks = kd; kd = t0;
-        int32_t* t1 = vs; vs = vd; vd = t1;
+    const int n = b * kSortBlock + t;
+    if (n < N) {
+        const int id = clamp_id(ids[n], V);
+        atomicAdd(&h[id >> 1], 1u << (16 * (id & 1)));
     }
-    // result must end in (keys_a, vals_a)
-    if (ks != keys_a) {
-        for (int i = beg; i < end; ++i) { keys_a[i] = ks[i]; vals_a[i] = vs[i]; }
+    __syncthreads();
+    uint32_t* row = cnt + (size_t)b * V;
+    for (int v = t; v < V; v += 1024) row[v] = (h[v >> 1] >> (16 * (v & 1))) & 0xffffu;
+}
+
+// per id: cnt[b][v] <- tokens of id v in blocks before b; total[v] <- all tokens of id v
+__global__ void __launch_bounds__(256)
+embed_colscan_kernel(uint32_t* __restrict__ cnt, int G, int V, uint32_t* __restrict__ total)
+{
+    const int v = blockIdx.x * 256 + threadIdx.x;
+    if (v >= V) return;
+    uint32_t run = 0;
+    for (int b = 0; b < G; ++b) {
+        const uint32_t c = cnt[(size_t)b * V + v];
+        cnt[(size_t)b * V + v] = run;
+        run += c;
     }
+    total[v] = run;
+}
+
+// total[v] <- exclusive prefix sum over ids (one workgroup)
+__global__ void __launch_bounds__(1024)
+embed_idscan_kernel(uint32_t* __restrict__ total, int V)
+{
+    __shared__ uint32_t part[1024];
+    const int t = threadIdx.x;
+    const int per = (V + 1023) / 1024, beg = min(V, t * per), end = min(V, beg + per);
+    uint32_t sum = 0;
+    for (int v = beg; v < end; ++v) sum += total[v];
+    part[t] = sum;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan of the per-thread sums
+        const uint32_t x = t >= o ? part[t - o] : 0u;
+        __syncthreads();
+        part[t] += x;
+        __syncthreads();
+    }
+    uint32_t run = t > 0 ? part[t - 1] : 0u;
+    for (int v = beg; v < end; ++v) {
+        const uint32_t c = total[v];
+        total[v] = run;
+        run += c;
+    }
+}
+
+__global__ void __launch_bounds__(1024)
+embed_scatter_kernel(const int32_t* __restrict__ ids, int N, int V, const uint32_t* __restrict__ cnt,
+                     const uint32_t* __restrict__ base, int32_t* __restrict__ skeys, int32_t* __restrict__ spos)
+{
+    __shared__ int32_t bid[kSortBlock];
+    const int b = blockIdx.x, t = threadIdx.x, n = b * kSortBlock + t;
+    const int id = n < N ? clamp_id(ids[n], V) : -1;
+    bid[t] = id;
+    __syncthreads();
+    if (n >= N) return;
+    int rank = 0;  // earlier tokens of the block with the same id (all lanes read the same word: a broadcast)
+    for (int j = 0; j < t; ++j) rank += bid[j] == id;
+    const uint32_t pos = base[id] + cnt[(size_t)b * V + id] + (uint32_t)rank;
+    skeys[pos] = id;
+    spos[pos] = n;
 }
 
 __global__ void __launch_bounds__(256)
@@ -561,16 +593,26 @@ embed_bwd_combine_kernel(const int32_t* __restrict__ skeys, const float* __restr
     }
 }
 
+size_t embed_bwd_scratch_ints(int N, int V) {
+    const size_t G = ((size_t)N + kSortBlock - 1) / kSortBlock;
+    return 2 * (size_t)N + G * (size_t)V + (size_t)V;
+}
+
 hipError_t launch_embed_bwd(const int32_t* ids, const float* dx, float* dwte, int N, int C, int V, int accumulate,
                             int32_t* iscratch, float* partial, hipStream_t s) {
-    int32_t* ka = iscratch;
-    int32_t* va = iscratch + N;
-    int32_t* kb = iscratch + 2 * (size_t)N;
-    int32_t* vb = iscratch + 3 * (size_t)N;
-    hipLaunchKernelGGL(radix_sort_ids_kernel, dim3(1), dim3(kSortThreads), 0, s, ids, N, V, ka, va, kb, vb);
-    hipLaunchKernelGGL(embed_bwd_chunks_kernel, dim3((N + kChunk - 1) / kChunk), dim3(256), 0, s, ka, va, dx, partial,
-                       N, C);
-    hipLaunchKernelGGL(embed_bwd_combine_kernel, dim3(V), dim3(256), 0, s, ka, partial, dwte, N, C, accumulate);
+    if (V > kMaxSortVocab || N <= 0) return hipErrorInvalidValue;
+    const int G = (N + kSortBlock - 1) / kSortBlock;
+    int32_t* skeys = iscratch;
+    int32_t* spos = iscratch + N;
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(iscratch + 2 * (size_t)N);
+    uint32_t* base = cnt + (size_t)G * V;
+    hipLaunchKernelGGL(embed_hist_kernel, dim3(G), dim3(1024), 0, s, ids, N, V, cnt);
+    hipLaunchKernelGGL(embed_colscan_kernel, dim3((V + 255) / 256), dim3(256), 0, s, cnt, G, V, base);
+    hipLaunchKernelGGL(embed_idscan_kernel, dim3(1), dim3(1024), 0, s, base, V);
+    hipLaunchKernelGGL(embed_scatter_kernel, dim3(G), dim3(1024), 0, s, ids, N, V, cnt, base, skeys, spos);
+    hipLaunchKernelGGL(embed_bwd_chunks_kernel, dim3((N + kChunk - 1) / kChunk), dim3(256), 0, s, skeys, spos, dx,
+                       partial, N, C);
+    hipLaunchKernelGGL(embed_bwd_combine_kernel, dim3(V), dim3(256), 0, s, skeys, partial, dwte, N, C, accumulate);
     return hipGetLastError();
 }
 

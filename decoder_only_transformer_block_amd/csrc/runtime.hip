@@ -183,7 +183,7 @@ void make_plan(ncgpt_ctx* c) {
         if (w.splits > 1) sk = std::max(sk, (size_t)w.splits * s[0] * s[1] * 4);
     }
     p.splitk = A(sk);
-    p.iscr = A(4 * N * 4);
+    p.iscr = A(embed_bwd_scratch_ints((int)N, (int)c->V) * 4);
     p.total = off;
 }
 
@@ -352,6 +352,7 @@ ncgpt_status ncgpt_create(const ncgpt_config* g, ncgpt_dtype dtype, ncgpt_ctx** 
     if (g->n_head % g->n_kv_head) return NCGPT_EUNSUPPORTED;
     if (bf ? g->head_dim != 128 : (g->head_dim != 64 && g->head_dim != 128)) return NCGPT_EUNSUPPORTED;
     if (g->n_embd % 64 || g->mlp_dim % 64 || g->vocab_size % 64) return NCGPT_EUNSUPPORTED;
+    if (g->vocab_size > 65536) return NCGPT_EUNSUPPORTED;  // the embedding-gradient counting sort
     if (bf ? g->seq_len % 128 : g->seq_len % 64) return NCGPT_EUNSUPPORTED;
     if ((double)g->batch * g->seq_len * g->vocab_size > 4.0e12) return NCGPT_EUNSUPPORTED;
     if (!(g->norm_eps >= 0.0f) || !(g->rope_base > 0.0f)) return NCGPT_EINVAL;
@@ -564,8 +565,8 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
         d.epi = Epi::StoreCd; d.out = dxn; d.ldo = C;  // compute dtype
         TRY(gemm(c, d));
     }
-    // dWlm = dz^T xf (vocab-wide output: 128 x 128 tiles with two register stages measured fastest)
-    // vocab x n_embd output over all tokens: 256 x 128 tiles, the four-wave persistent ring measured fastest
+    // dWlm = dz^T xf: vocab x n_embd output over all tokens; 256 x 128 tiles, the four-wave persistent ring
+    // measured fastest
     TRY(wgrad(c, logits, V, c->ws + p.xf, C, V, C, gslice(-1, 1), acc, 1, 8));
     const double nb = (double)N * C * (e + e + 4 + (dt == Dt::BF16 ? 2 : 0)) + N * 4.0;
     TRY(launch(c, "rmsnorm_bwd", 0.0, nb, [&] {

@@ -77,8 +77,8 @@ ncgpt_status ncgpt_param_slice(const ncgpt_config* cfg, int layer, int which, si
 
 /* Create a context (host memory only; no device work).  EUNSUPPORTED unless head_dim is 64 or 128
  * (128 for NCGPT_BF16), n_head % n_kv_head == 0, n_embd, mlp_dim and vocab_size are multiples of 64,
- * seq_len is a multiple of 128 for NCGPT_BF16 (of 64 for NCGPT_F32), and batch*seq_len*vocab fits the
- * workspace plan.  *out receives the context; free it with ncgpt_destroy. */
+ * vocab_size <= 65536, seq_len is a multiple of 128 for NCGPT_BF16 (of 64 for NCGPT_F32), and
+ * batch*seq_len*vocab fits the workspace plan.  *out receives the context; free it with ncgpt_destroy. */
 ncgpt_status ncgpt_create(const ncgpt_config* cfg, ncgpt_dtype dtype, ncgpt_ctx** out);
 
 /* Bytes of device workspace the context needs (saved activations, cast weights, logits, scratch). */

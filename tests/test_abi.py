@@ -81,6 +81,7 @@ def test_create_validates_shapes_and_plans_workspace():
         (dict(n_kv_head=3, n_head=2), ncgpt.BF16, ncgpt.EUNSUPPORTED),
         (dict(n_embd=200), ncgpt.BF16, ncgpt.EUNSUPPORTED),
         (dict(vocab_size=8200), ncgpt.BF16, ncgpt.EUNSUPPORTED),
+        (dict(vocab_size=65536 + 64), ncgpt.F32, ncgpt.EUNSUPPORTED),  # the embedding-gradient sort's limit
         (dict(seq_len=192), ncgpt.BF16, ncgpt.EUNSUPPORTED),
         (dict(batch=0), ncgpt.BF16, ncgpt.EINVAL),
     ]
