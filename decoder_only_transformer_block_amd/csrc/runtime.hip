@@ -277,7 +277,9 @@ ncgpt_status wgrad(ncgpt_ctx* c, const void* dY, int ldy, const void* X, int ldx
     WGrad w = pick_wgrad(c->dt, M, N, K);
     if (tile >= 0 && w.splits == 1) w.tile = tile;
     GemmDesc d;
-    d.variant = variant;
+    // both operands are read through transposing LDS reads (half rate): the four-wave persistent
+    // ring, which reads fewer fragments per MFMA, measured fastest
+    d.variant = variant >= 0 ? variant : 8;
     d.A = dY; d.lda = ldy; d.a_kcontig = false;
     d.B = X; d.ldb = ldx; d.b_kcontig = false;
     d.M = M; d.N = N; d.K = K;
@@ -486,7 +488,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.A = xn2; d.lda = C; d.B = weight(c, l, 4); d.ldb = C;
             d.M = N; d.N = F; d.K = C;
             d.epi = Epi::ReluSq; d.out = act; d.ldo = F;
-            d.variant = 6;  // two stores per element: the non-persistent ring measured fastest
+            d.variant = 7;  // the non-persistent eight-wave ring measured fastest for this shape
             TRY(gemm(c, d));
         }
         {
@@ -563,6 +565,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
         d.A = logits; d.lda = V; d.B = weight(c, -1, 1); d.ldb = C; d.b_kcontig = false;
         d.M = N; d.N = C; d.K = V;
         d.epi = Epi::StoreCd; d.out = dxn; d.ldo = C;  // compute dtype
+        d.variant = 7;  // input gradients (NN): the non-persistent eight-wave ring measured fastest
         TRY(gemm(c, d));
     }
     // dWlm = dz^T xf: vocab x n_embd output over all tokens; 256 x 128 tiles, the four-wave persistent ring
@@ -591,6 +594,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             d.A = c->ws + p.dh; d.lda = F; d.B = weight(c, l, 4); d.ldb = C; d.b_kcontig = false;
             d.M = N; d.N = C; d.K = F;
             d.epi = Epi::StoreCd; d.out = dxn; d.ldo = C;  // compute dtype
+            d.variant = 7;  // input gradients (NN): the non-persistent eight-wave ring measured fastest
             TRY(gemm(c, d));
         }
         TRY(wgrad(c, c->ws + p.dh, F, xn2, C, F, C, gslice(l, 4), acc));  // dWfc = dh^T xn2
@@ -638,6 +642,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             d.A = c->ws + p.dqkv; d.lda = QKV; d.B = weight(c, l, 0); d.ldb = C; d.b_kcontig = false;
             d.M = N; d.N = C; d.K = QKV;
             d.epi = Epi::StoreCd; d.out = dxn; d.ldo = C;  // compute dtype
+            d.variant = 7;  // input gradients (NN): the non-persistent eight-wave ring measured fastest
             TRY(gemm(c, d));
         }
         TRY(wgrad(c, c->ws + p.dqkv, QKV, xn1, C, QKV, C, gslice(l, 0), acc));  // dWqkv = dqkv^T xn1
