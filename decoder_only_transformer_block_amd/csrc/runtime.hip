@@ -262,17 +262,29 @@ const char* intern(const std::string& s) {
     return names.back()->c_str();
 }
 
-ncgpt_status gemm(ncgpt_ctx* c, GemmDesc d) {
+// tag: the call site (qkv, lm_head, dWfc, ...), so every timing row is one shape
+ncgpt_status gemm(ncgpt_ctx* c, GemmDesc d, const char* tag) {
     d.dt = c->dt;
     if (d.tile < 0) d.tile = pick_tile(d.M, d.N);
-    const char* nm = intern(std::string(gemm_kernel_name(d)) + ":" + epi_name(d.epi));
-    double fl = 2.0 * d.M * d.N * d.K;
-    return launch(c, nm, fl, 0.0, [&] { return launch_gemm(d, c->stream); });
+    const char* nm = intern(std::string(gemm_kernel_name(d)) + ":" + epi_name(d.epi) + ":" + tag);
+    const double fl = 2.0 * d.M * d.N * d.K;
+    // algorithmic bytes: both operands once, the output (and what the epilogue reads) once
+    const double e = d.dt == Dt::BF16 ? 2.0 : 4.0, mn = (double)d.M * d.N;
+    double out = e;
+    switch (d.epi) {
+    case Epi::StoreF32: out = 4.0; break;
+    case Epi::ResidualCd: case Epi::ReluSqBwd: out = 2.0 * e; break;
+    case Epi::Grad: out = d.accumulate ? 8.0 : 4.0; break;
+    case Epi::SplitK: out = 4.0 * std::max(1, d.splits); break;
+    default: break;
+    }
+    const double by = ((double)d.M * d.K + (double)d.N * d.K) * e + mn * out;
+    return launch(c, nm, fl, by, [&] { return launch_gemm(d, c->stream); });
 }
 
 // weight gradient: out(f32 grads slice [M,N]) (+)= A^T-layout x B^T-layout over K tokens
-ncgpt_status wgrad(ncgpt_ctx* c, const void* dY, int ldy, const void* X, int ldx, int M, int N, float* g,
-                   int accumulate, int tile = -1, int variant = -1) {
+ncgpt_status wgrad(ncgpt_ctx* c, const char* tag, const void* dY, int ldy, const void* X, int ldx, int M, int N,
+                   float* g, int accumulate, int tile = -1, int variant = -1) {
     const int K = (int)c->N;
     WGrad w = pick_wgrad(c->dt, M, N, K);
     if (tile >= 0 && w.splits == 1) w.tile = tile;
@@ -289,16 +301,16 @@ ncgpt_status wgrad(ncgpt_ctx* c, const void* dY, int ldy, const void* X, int ldx
         d.epi = Epi::Grad;
         d.out = g;
         d.accumulate = accumulate;
-        return gemm(c, d);
+        return gemm(c, d, tag);
     }
     d.epi = Epi::SplitK;
     d.splits = w.splits;
     d.k_split = w.k_split;
     d.out = c->at<float>(c->pl.splitk);
     d.split_stride = (size_t)M * N;
-    TRY(gemm(c, d));
+    TRY(gemm(c, d, tag));
     const size_t n = (size_t)M * N;
-    return launch(c, "splitk_reduce", 0.0, (double)n * 4 * (w.splits + 1 + accumulate), [&] {
+    return launch(c, intern(std::string("splitk_reduce:") + tag), 0.0, (double)n * 4 * (w.splits + 1 + accumulate), [&] {
         return launch_splitk_reduce(c->at<float>(c->pl.splitk), w.splits, (size_t)M * N, g, n, accumulate, c->stream);
     });
 }
@@ -456,7 +468,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.M = N; d.N = QKV; d.K = C;
             d.epi = Epi::StoreCd; d.out = qkv; d.ldo = QKV;
             d.variant = 7;  // few tiles per CU: the non-persistent eight-wave ring measured fastest
-            TRY(gemm(c, d));
+            TRY(gemm(c, d, "qkv"));
         }
         TRY(launch(c, "rope_qknorm_fwd", 0.0, (double)N * (c->H + c->Hkv) * c->D * 2 * e, [&] {
             return launch_rope_qknorm_fwd(dt, qkv, c->at<float>(c->lay(l, p.l_rstdq)), c->at<float>(c->lay(l, p.l_rstdk)),
@@ -478,7 +490,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.A = y; d.lda = HD; d.B = weight(c, l, 3); d.ldb = HD;
             d.M = N; d.N = C; d.K = HD;
             d.epi = Epi::ResidualCd; d.out = c->ws + p.x; d.in = xin; d.ldo = C;
-            TRY(gemm(c, d));
+            TRY(gemm(c, d, "attn_out"));
         }
         TRY(launch(c, "rmsnorm_fwd", 0.0, norm_bytes, [&] {
             return launch_rmsnorm_fwd(dt, c->ws + p.x, xn2, c->at<float>(c->lay(l, p.l_rstd2)), N, C, eps, c->stream);
@@ -489,14 +501,14 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.M = N; d.N = F; d.K = C;
             d.epi = Epi::ReluSq; d.out = act; d.ldo = F;
             d.variant = 7;  // the non-persistent eight-wave ring measured fastest for this shape
-            TRY(gemm(c, d));
+            TRY(gemm(c, d, "fc"));
         }
         {
             GemmDesc d;
             d.A = act; d.lda = F; d.B = weight(c, l, 5); d.ldb = F;
             d.M = N; d.N = C; d.K = F;
             d.epi = Epi::ResidualCd; d.out = c->ws + p.x; d.in = c->ws + p.x; d.ldo = C;
-            TRY(gemm(c, d));
+            TRY(gemm(c, d, "proj"));
         }
     }
     TRY(launch(c, "rmsnorm_fwd", 0.0, norm_bytes, [&] {
@@ -507,7 +519,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
         d.A = c->ws + p.xf; d.lda = C; d.B = weight(c, -1, 1); d.ldb = C;
         d.M = N; d.N = V; d.K = C;
         d.epi = Epi::StoreCd; d.out = c->ws + p.logits; d.ldo = V;
-        TRY(gemm(c, d));
+        TRY(gemm(c, d, "lm_head"));
     }
     c->state = 1;
     return NCGPT_OK;
@@ -566,11 +578,11 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
         d.M = N; d.N = C; d.K = V;
         d.epi = Epi::StoreCd; d.out = dxn; d.ldo = C;  // compute dtype
         d.variant = 7;  // input gradients (NN): the non-persistent eight-wave ring measured fastest
-        TRY(gemm(c, d));
+        TRY(gemm(c, d, "dxf"));
     }
     // dWlm = dz^T xf: vocab x n_embd output over all tokens; 256 x 128 tiles, the four-wave persistent ring
     // measured fastest
-    TRY(wgrad(c, logits, V, c->ws + p.xf, C, V, C, gslice(-1, 1), acc, 1, 8));
+    TRY(wgrad(c, "dWlm", logits, V, c->ws + p.xf, C, V, C, gslice(-1, 1), acc, 1, 8));
     const double nb = (double)N * C * (e + e + 4 + (dt == Dt::BF16 ? 2 : 0)) + N * 4.0;
     TRY(launch(c, "rmsnorm_bwd", 0.0, nb, [&] {
         return launch_rmsnorm_bwd(dt, c->ws + p.xf, c->at<float>(p.rstdf), dxn, dx, dx_cd, N, C, 0, c->stream);
@@ -586,18 +598,18 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             d.A = dxg; d.lda = C; d.B = weight(c, l, 5); d.ldb = F; d.b_kcontig = false;
             d.M = N; d.N = F; d.K = C;
             d.epi = Epi::ReluSqBwd; d.out = c->ws + p.dh; d.in = act; d.ldo = F;
-            TRY(gemm(c, d));
+            TRY(gemm(c, d, "dh"));
         }
-        TRY(wgrad(c, dxg, C, act, F, C, F, gslice(l, 5), acc));  // dWproj = dx^T act
+        TRY(wgrad(c, "dWproj", dxg, C, act, F, C, F, gslice(l, 5), acc));  // dWproj = dx^T act
         {   // dxn2 = dh Wfc
             GemmDesc d;
             d.A = c->ws + p.dh; d.lda = F; d.B = weight(c, l, 4); d.ldb = C; d.b_kcontig = false;
             d.M = N; d.N = C; d.K = F;
             d.epi = Epi::StoreCd; d.out = dxn; d.ldo = C;  // compute dtype
             d.variant = 7;  // input gradients (NN): the non-persistent eight-wave ring measured fastest
-            TRY(gemm(c, d));
+            TRY(gemm(c, d, "dxn2"));
         }
-        TRY(wgrad(c, c->ws + p.dh, F, xn2, C, F, C, gslice(l, 4), acc));  // dWfc = dh^T xn2
+        TRY(wgrad(c, "dWfc", c->ws + p.dh, F, xn2, C, F, C, gslice(l, 4), acc));  // dWfc = dh^T xn2
         TRY(launch(c, "rmsnorm_bwd", 0.0, nb + (double)N * C * 4, [&] {
             return launch_rmsnorm_bwd(dt, xn2, c->at<float>(c->lay(l, p.l_rstd2)), dxn, dx, dx_cd, N, C, 1, c->stream);
         }));
@@ -606,9 +618,9 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             d.A = dxg; d.lda = C; d.B = weight(c, l, 3); d.ldb = HD; d.b_kcontig = false;
             d.M = N; d.N = HD; d.K = C;
             d.epi = Epi::StoreCd; d.out = c->ws + p.dy; d.ldo = HD;
-            TRY(gemm(c, d));
+            TRY(gemm(c, d, "dy"));
         }
-        TRY(wgrad(c, dxg, C, y, HD, C, HD, gslice(l, 3), acc));  // dWo = dx^T y
+        TRY(wgrad(c, "dWo", dxg, C, y, HD, C, HD, gslice(l, 3), acc));  // dWo = dx^T y
         {
             AttnDesc ad;
             ad.dt = dt; ad.B = (int)c->B; ad.T = (int)c->T; ad.H = (int)c->H; ad.Hkv = (int)c->Hkv; ad.D = (int)c->D;
@@ -643,9 +655,9 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             d.M = N; d.N = C; d.K = QKV;
             d.epi = Epi::StoreCd; d.out = dxn; d.ldo = C;  // compute dtype
             d.variant = 7;  // input gradients (NN): the non-persistent eight-wave ring measured fastest
-            TRY(gemm(c, d));
+            TRY(gemm(c, d, "dxn1"));
         }
-        TRY(wgrad(c, c->ws + p.dqkv, QKV, xn1, C, QKV, C, gslice(l, 0), acc));  // dWqkv = dqkv^T xn1
+        TRY(wgrad(c, "dWqkv", c->ws + p.dqkv, QKV, xn1, C, QKV, C, gslice(l, 0), acc));  // dWqkv = dqkv^T xn1
         TRY(launch(c, "rmsnorm_bwd", 0.0, nb + (double)N * C * 4, [&] {
             return launch_rmsnorm_bwd(dt, xn1, c->at<float>(c->lay(l, p.l_rstd1)), dxn, dx, dx_cd, N, C, 1, c->stream);
         }));
