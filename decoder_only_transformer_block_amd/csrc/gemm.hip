@@ -40,7 +40,7 @@ __device__ __forceinline__ void st8(bf16* p, const float (&v)[8]) {
 }
 
 template <typename T> struct EStoreCd {
-    static constexpr bool kWide = std::is_same<T, bf16>::value;
+    static constexpr bool kWide = std::is_same<T, bf16>::value, kLoads = false;
     T* out; int ldo;
     __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
         Vec4<T>::store(out + (size_t)m * ldo + n, v);
@@ -48,7 +48,7 @@ template <typename T> struct EStoreCd {
     __device__ void put8(int m, int n, int, const float (&v)[8]) const { st8(out + (size_t)m * ldo + n, v); }
 };
 struct EStoreF32 {
-    static constexpr bool kWide = false;
+    static constexpr bool kWide = false, kLoads = false;
     float* out; int ldo;
     __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
         Vec4<float>::store(out + (size_t)m * ldo + n, v);
@@ -56,8 +56,15 @@ struct EStoreF32 {
     __device__ void put8(int, int, int, const float (&)[8]) const {}
 };
 template <typename T> struct EResidual {
-    static constexpr bool kWide = std::is_same<T, bf16>::value;
+    static constexpr bool kWide = std::is_same<T, bf16>::value, kLoads = true;
     T* out; const T* in; int ldo;
+    __device__ bf16x8 fetch8(int m, int n) const { return *reinterpret_cast<const bf16x8*>(in + (size_t)m * ldo + n); }
+    __device__ void put8(int m, int n, int, const float (&v)[8], const bf16x8& x) const {
+        float r[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[i] = (float)x[i] + v[i];
+        st8(out + (size_t)m * ldo + n, r);
+    }
     __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
         size_t o = (size_t)m * ldo + n;
         float x[4];
@@ -78,7 +85,7 @@ template <typename T> struct EResidual {
 // act = a^2 with a = relu(v) rounded to the compute dtype: the only stored output of
 // the MLP's first linear; the backward recovers a as sqrt(act)
 template <typename T> struct EReluSq {
-    static constexpr bool kWide = std::is_same<T, bf16>::value;
+    static constexpr bool kWide = std::is_same<T, bf16>::value, kLoads = false;
     T* act; int ldo;
     __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
         float s[4];
@@ -101,8 +108,15 @@ template <typename T> struct EReluSq {
 };
 // dh = dact * d(relu(h)^2)/dh = dact * 2 relu(h), with relu(h) = sqrt(act)
 template <typename T> struct EReluSqBwd {
-    static constexpr bool kWide = std::is_same<T, bf16>::value;
+    static constexpr bool kWide = std::is_same<T, bf16>::value, kLoads = true;
     T* out; const T* act; int ldo;
+    __device__ bf16x8 fetch8(int m, int n) const { return *reinterpret_cast<const bf16x8*>(act + (size_t)m * ldo + n); }
+    __device__ void put8(int m, int n, int, const float (&v)[8], const bf16x8& x) const {
+        float r[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[i] = v[i] * 2.0f * __builtin_amdgcn_sqrtf((float)x[i]);
+        st8(out + (size_t)m * ldo + n, r);
+    }
     __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
         size_t o = (size_t)m * ldo + n;
         float x[4];
@@ -121,7 +135,7 @@ template <typename T> struct EReluSqBwd {
     }
 };
 struct EGrad {
-    static constexpr bool kWide = false;
+    static constexpr bool kWide = false, kLoads = false;
     float* out; int ldo; int acc;
     __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
         float* p = out + (size_t)m * ldo + n;
@@ -137,7 +151,7 @@ struct EGrad {
     __device__ void put8(int, int, int, const float (&)[8]) const {}
 };
 struct ESplitK {
-    static constexpr bool kWide = false;
+    static constexpr bool kWide = false, kLoads = false;
     float* out; int ldo; size_t stride;
     __device__ void operator()(int m, int n, int split, const float (&v)[4]) const {
         Vec4<float>::store(out + (size_t)split * stride + (size_t)m * ldo + n, v);
@@ -152,6 +166,39 @@ template <int FM, int FN, class E>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], int m0, int n0, int split, int M, int N,
                                            int lane, const E& epi) {
     const int h = lane >> 5, l32 = lane & 31;
+    if constexpr (E::kWide && E::kLoads) {
+        // epilogues that read a tensor: issue every load of the wave tile first, so the
+        // tile waits for memory once instead of once per column group
+        bf16x8 in[FM][FN][2];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const int m = m0 + 32 * i + l32, n = n0 + 32 * j + 16 * p + 8 * h;
+                    if (m < M && n < N) in[i][j][p] = epi.fetch8(m, n);
+                }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][j][8 * p + e]),
+                                                                        __float_as_uint(acc[i][j][8 * p + 4 + e]),
+                                                                        false, false);
+                        v[e] = __uint_as_float(r[0]);
+                        v[4 + e] = __uint_as_float(r[1]);
+                    }
+                    const int m = m0 + 32 * i + l32, n = n0 + 32 * j + 16 * p + 8 * h;
+                    if (m < M && n < N) epi.put8(m, n, split, v, in[i][j][p]);
+                }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int m = m0 + 32 * i + l32;

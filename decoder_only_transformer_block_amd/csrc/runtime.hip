@@ -490,6 +490,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.A = y; d.lda = HD; d.B = weight(c, l, 3); d.ldb = HD;
             d.M = N; d.N = C; d.K = HD;
             d.epi = Epi::ResidualCd; d.out = c->ws + p.x; d.in = xin; d.ldo = C;
+            d.variant = 7;  // epilogue reads the residual: the eight-wave ring without spills
             TRY(gemm(c, d, "attn_out"));
         }
         TRY(launch(c, "rmsnorm_fwd", 0.0, norm_bytes, [&] {
@@ -508,6 +509,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.A = act; d.lda = F; d.B = weight(c, l, 5); d.ldb = F;
             d.M = N; d.N = C; d.K = F;
             d.epi = Epi::ResidualCd; d.out = c->ws + p.x; d.in = c->ws + p.x; d.ldo = C;
+            d.variant = 7;
             TRY(gemm(c, d, "proj"));
         }
     }
@@ -598,6 +600,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             d.A = dxg; d.lda = C; d.B = weight(c, l, 5); d.ldb = F; d.b_kcontig = false;
             d.M = N; d.N = F; d.K = C;
             d.epi = Epi::ReluSqBwd; d.out = c->ws + p.dh; d.in = act; d.ldo = F;
+            d.variant = 7;  // epilogue reads act: the eight-wave ring without spills
             TRY(gemm(c, d, "dh"));
         }
         TRY(wgrad(c, "dWproj", dxg, C, act, F, C, F, gslice(l, 5), acc));  // dWproj = dx^T act
