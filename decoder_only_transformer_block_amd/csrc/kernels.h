@@ -23,8 +23,8 @@ enum class Epi : int {
     StoreCd,     // out[m*ldo+n] = cd(v)
     StoreF32,    // out(f32)[m*ldo+n] = v
     ResidualCd,  // out[m*ldo+n] = cd(in[m*ldo+n] + v)        (in may equal out)
-    ReluSq,      // a = cd(max(v,0)) -> out;  act = cd(a*a) -> out2
-    ReluSqBwd,   // out[m*ldo+n] = cd(v * 2 * in[m*ldo+n])      (in = saved a)
+    ReluSq,      // out[m*ldo+n] = cd(a * a), a = cd(max(v, 0))   (the MLP activation act)
+    ReluSqBwd,   // out[m*ldo+n] = cd(v * 2 * sqrt(in[m*ldo+n]))   (in = saved act; sqrt(act) recovers a to bf16 rounding)
     Grad,        // out(f32) = (accumulate ? out : 0) + v
     SplitK,      // out(f32)[split*split_stride + m*ldo + n] = v
 };
@@ -39,7 +39,6 @@ struct GemmDesc {
     Epi epi = Epi::StoreCd;
     void* out = nullptr;
     const void* in = nullptr;
-    void* out2 = nullptr;
     int ldo = 0;
     int accumulate = 0;
     int splits = 1;         // split-K: K is cut into ceil(K / k_split) ranges of k_split (grid.y)
