@@ -42,6 +42,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 // a bijection over 16 consecutive rows (row reads hit 16 distinct chunks) whose
 // high bits differ across 4 consecutive rows (transposed reads hit 4 distinct
 // 64-byte bank groups), so neither read conflicts on the 64-bank LDS.
+// rfrag / trfrag below are the definitional forms; the kernels read through the
+// closed-form offsets further down (rz, tz, frag_at, trfrag_at).
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -65,6 +67,32 @@ __device__ __forceinline__ bf16x8 trfrag(const bf16* S, int d0, int kbase, int l
     const int r = kbase + 4 * hh + (s >> 2);
     s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(S + toff(r, c) + o));
     s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(S + toff(r + 8, c) + o));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// The same fragments with their byte offsets in closed form.  Rows 16 apart share
+// swz, and the chunk bits (4..7 of the byte offset) sit apart from the row bits, so
+//   rfrag(S, r, 2 kk + hv) lies at rz(r, hv) ^ (kk << 5), and
+//   trfrag(S, 32 db, kbase, lane), kbase a multiple of 16, reads its low rows at
+//   256 kbase + (tz(lane) ^ (db << 6)) and its high rows (8 further) at
+//   256 kbase + 2048 + (tz(lane) ^ (db << 6) ^ 32).
+// A lane forms rz / tz once; a fragment then costs at most one XOR, and the row
+// block and the LDS array fold into the instruction's offset field.
+__device__ __forceinline__ int rz(int r, int hv) { return r * 256 | (((hv ^ swz(r)) & 15) << 4); }
+__device__ __forceinline__ int tz(int lane) {
+    const int s = lane & 15, rl = 4 * (lane >> 5) + (s >> 2), cl = 2 * ((lane >> 4) & 1) + ((s & 3) >> 1);
+    return rl * 256 + (((cl ^ swz(rl)) & 15) << 4) + 8 * (s & 1);
+}
+__device__ __forceinline__ bf16x8 frag_at(const bf16* S, int off) {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(S) + off);
+}
+// trfrag(S, 32 db, 0, lane) from t = tz(lane) (pass S + 128 kbase for a later row block)
+__device__ __forceinline__ bf16x8 trfrag_at(const bf16* S, int t, int db) {
+    const char* p = reinterpret_cast<const char*>(S);
+    s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + (t ^ (db << 6))));
+    s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 2048 + (t ^ (db << 6) ^ 32)));
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v);
@@ -226,6 +254,7 @@ attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restr
     const float c1 = kLog2e * rsqrtf((float)D), c2 = sqrtf((float)D) * kLog2e;
 
     const int nkt = min(q0 + QBLK, T) / 64;     // key tiles at or before the block's last query
+    const int zk = rz(l32, hh), tl = tz(lane);  // fragment offsets (rows l32 + 32 kb share them)
     const unsigned vo = dma_voff(QKV, lane, w);
     const bf16* kbase = qkv + rowbase * QKV + HD + g * D;
     auto issue = [&](int kt, bf16* Ks, bf16* Vs) {
@@ -242,9 +271,6 @@ attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restr
         const int kv0 = kt * 64;
         if (!active || kv0 > qw + QW - 1) return;  // wave-uniform: the whole tile lies after the wave's queries
         const bool diag = kv0 + 63 > qw;
-        int ln = threadIdx.x & 63;             // opaque lane: keeps fragment addresses out of loop-invariant registers
-        asm volatile("" : "+v"(ln));
-        const int hv = ln >> 5, lv32 = ln & 31;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             f32x16 sc[QB];
@@ -252,7 +278,7 @@ attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restr
             for (int qq = 0; qq < QB; ++qq) zero16(sc[qq]);
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
-                const bf16x8 kf = rfrag(Ks, 32 * kb + lv32, 2 * kk + hv);
+                const bf16x8 kf = frag_at(Ks + 32 * 128 * kb, zk ^ (kk << 5));
 #pragma unroll
                 for (int qq = 0; qq < QB; ++qq)
                     sc[qq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qq][kk], sc[qq], 0, 0, 0);
@@ -265,7 +291,7 @@ attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restr
                     for (int e = 0; e < 16; ++e) {
                         float p = __builtin_amdgcn_exp2f(sc[qq][e] * c1 - c2);
                         if constexpr (decltype(masked)::value)
-                            p = kv0 + 32 * kb + 8 * (e >> 2) + 4 * hv + (e & 3) > qw + 32 * qq + lv32 ? 0.0f : p;
+                            p = kv0 + 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3) > qw + 32 * qq + l32 ? 0.0f : p;
                         sc[qq][e] = p;
                         lsum[qq] += p;
                     }
@@ -281,7 +307,7 @@ attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restr
                 for (int qq = 0; qq < QB; ++qq) pf[qq] = pack8(sc[qq], 8 * j);
 #pragma unroll
                 for (int db = 0; db < 4; ++db) {
-                    const bf16x8 vf = trfrag(Vs, 32 * db, 32 * kb + 16 * j, ln);
+                    const bf16x8 vf = trfrag_at(Vs + 128 * (32 * kb + 16 * j), tl, db);
 #pragma unroll
                     for (int qq = 0; qq < QB; ++qq)
                         o[qq][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qq], o[qq][db], 0, 0, 0);
@@ -383,6 +409,7 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
     for (int db = 0; db < 4; ++db) zero16(dq[db]);
 
     const int nkt = min(q0 + QB, T) / 64;       // key tiles at or before the block's last query
+    const int zk = rz(l32, hh), tl = tz(lane);  // fragment offsets (rows l32 + 32 kb share them)
     const unsigned vo = dma_voff(QKV, lane, w);
     const bf16* kbase = qkv + rowbase * QKV + HD + g * D;
     auto issue = [&](int kt, bf16* Ks, bf16* Vs) {
@@ -399,9 +426,6 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
         const int kv0 = kt * 64;
         if (!active || kv0 > qw + 31) return;  // wave-uniform: the whole tile lies after the wave's queries
         const bool diag = kv0 + 63 > qw;
-        int ln = threadIdx.x & 63;             // opaque lane: keeps fragment addresses out of loop-invariant registers
-        asm volatile("" : "+v"(ln));
-        const int hv = ln >> 5, lv32 = ln & 31;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             f32x16 s, dp;
@@ -409,9 +433,10 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
             zero16(dp);
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(Ks, 32 * kb + lv32, 2 * kk + hv), qf[kk], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(Vs, 32 * kb + lv32, 2 * kk + hv), dof[kk], dp, 0, 0,
-                                                             0);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_at(Ks + 32 * 128 * kb, zk ^ (kk << 5)), qf[kk], s, 0,
+                                                            0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_at(Vs + 32 * 128 * kb, zk ^ (kk << 5)), dof[kk], dp,
+                                                             0, 0, 0);
             }
             // lane holds S[q][key = kv0 + 32kb + 8(e>>2) + 4hh + (e&3)] in s[e]
             auto softmax = [&](auto masked) {
@@ -419,7 +444,7 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
                 for (int e = 0; e < 16; ++e) {
                     float p = __builtin_amdgcn_exp2f(s[e] * c1 - l2);
                     if constexpr (decltype(masked)::value)
-                        p = kv0 + 32 * kb + 8 * (e >> 2) + 4 * hv + (e & 3) > qw + lv32 ? 0.0f : p;
+                        p = kv0 + 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3) > qw + l32 ? 0.0f : p;
                     dp[e] = p * (dp[e] - dl);
                 }
             };
@@ -432,8 +457,8 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
                 const bf16x8 dsf = pack8(dp, 8 * j);
 #pragma unroll
                 for (int db = 0; db < 4; ++db)
-                    dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(Ks, 32 * db, 32 * kb + 16 * j, ln), dsf,
-                                                                      dq[db], 0, 0, 0);
+                    dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        trfrag_at(Ks + 128 * (32 * kb + 16 * j), tl, db), dsf, dq[db], 0, 0, 0);
             }
         }
     };
@@ -520,6 +545,9 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
     for (int db = 0; db < 4; ++db) { zero16(dk[db]); zero16(dv[db]); }
 
     const int qt0 = k0 / 64, nqt = T / 64 - qt0;
+    // fragment offsets: the wave's query half (32 qh + l32) in the Q / dO tiles, its keys
+    // (32 kq + l32) in K / V, and the transposed reads of the query half
+    const int zq = rz(32 * qh + l32, hh), zk = rz(32 * kq + l32, hh), tq = tz(lane) + 32 * 256 * qh;
     const int total = r * nqt;
     const unsigned voq = dma_voff(QKV, lane, w), vod = dma_voff(HD, lane, w);
     // loads of tile it (query head g r + it / nqt, queries from (qt0 + it % nqt) 64) into one stage
@@ -544,28 +572,22 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
         const int q0 = (qt0 + it % nqt) * 64 + 32 * qh;  // the wave's 32 queries
         if (!active || q0 + 31 < kw) return;  // wave-uniform: every query precedes every key of the wave
         const bool diag = q0 < kw + 31;
-        // Re-derive the lane index per tile: the swizzled fragment addresses are then
-        // formed here (constant parts folded into the LDS offsets) instead of being
-        // hoisted out of the loop into many live registers.
-        int ln = threadIdx.x & 63;
-        asm volatile("" : "+v"(ln));
-        const int hv = ln >> 5, lv32 = ln & 31;
         f32x16 s, dp;
         zero16(s);
         zero16(dp);
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(Qs, 32 * qh + lv32, 2 * kk + hv),
-                                                        rfrag(sK, 32 * kq + lv32, 2 * kk + hv), s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rfrag(Os, 32 * qh + lv32, 2 * kk + hv),
-                                                         rfrag(sV, 32 * kq + lv32, 2 * kk + hv), dp, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_at(Qs, zq ^ (kk << 5)), frag_at(sK, zk ^ (kk << 5)), s,
+                                                        0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_at(Os, zq ^ (kk << 5)), frag_at(sV, zk ^ (kk << 5)), dp,
+                                                         0, 0, 0);
         }
         // lane holds S[q = q0 + 8(e>>2) + 4hh + (e&3)][key = kw + l32] in s[e]; P = exp2(S c1 - lse2),
         // dS / scale = P (dP - delta) (dK is scaled at the end); the mask only on diagonal tiles
         auto softmax = [&](auto masked) {
 #pragma unroll
             for (int gg = 0; gg < 4; ++gg) {
-                const int ql = 32 * qh + 8 * gg + 4 * hv;
+                const int ql = 32 * qh + 8 * gg + 4 * hh;
                 const float4 l4 = *reinterpret_cast<const float4*>(Ls + ql);
                 const float4 d4 = *reinterpret_cast<const float4*>(Ds + ql);
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
@@ -573,7 +595,7 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
                 for (int e = 0; e < 4; ++e) {
                     const int idx = 4 * gg + e;
                     float p = __builtin_amdgcn_exp2f(s[idx] * c1 - lv[e]);
-                    if constexpr (decltype(masked)::value) p = q0 + 8 * gg + 4 * hv + e < kw + lv32 ? 0.0f : p;
+                    if constexpr (decltype(masked)::value) p = q0 + 8 * gg + 4 * hh + e < kw + l32 ? 0.0f : p;
                     s[idx] = p;
                     dp[idx] = p * (dp[idx] - dv4[e]);
                 }
@@ -588,10 +610,10 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
             const bf16x8 pf = pack8(s, 8 * j2), dsf = pack8(dp, 8 * j2);
 #pragma unroll
             for (int db = 0; db < 4; ++db) {
-                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(Os, 32 * db, 32 * qh + 16 * j2, ln), pf,
-                                                                  dv[db], 0, 0, 0);
-                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag(Qs, 32 * db, 32 * qh + 16 * j2, ln), dsf,
-                                                                  dk[db], 0, 0, 0);
+                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag_at(Os + 128 * 16 * j2, tq, db), pf, dv[db],
+                                                                  0, 0, 0);
+                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag_at(Qs + 128 * 16 * j2, tq, db), dsf, dk[db],
+                                                                  0, 0, 0);
             }
         }
     };
