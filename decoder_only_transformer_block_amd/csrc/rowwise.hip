@@ -57,6 +57,36 @@ hipError_t launch_embed_fwd(Dt dt, const int32_t* ids, const float* wte, void* x
     return hipGetLastError();
 }
 
+// ---- row helpers: sums over lane groups, 8-element (16-byte in bf16) loads and stores
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void load8(const bf16* p, float (&v)[8]) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)a[e];
+}
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ void store8(bf16* p, const float (&v)[8]) {
+    bf16x8 a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = (bf16)v[e];
+    *reinterpret_cast<bf16x8*>(p) = a;
+}
+
+
 // ------------------------------------------------------------------ RMSNorm (one wave per row)
 // y = x / sqrt(mean(x^2) + eps), no weight ("nanochat 项目深度分析" §2.1 item 5).
 template <typename T>
@@ -85,7 +115,55 @@ rmsnorm_fwd_kernel(const T* __restrict__ x, T* __restrict__ y, float* __restrict
     if (lane == 0) rstd[row] = rs;
 }
 
+// The same map with each row held in registers (C = 256 NCH): 32 lanes per row, two rows
+// per wave; lane j holds the 8-element chunks j, j + 32, ..., j + 32 (NCH - 1), so every
+// access is 16 bytes wide in bf16, every load is issued before the reduction, and x is
+// read once.
+template <typename T, int NCH>
+__global__ void __launch_bounds__(256)
+rmsnorm_fwd_rows(const T* __restrict__ x, T* __restrict__ y, float* __restrict__ rstd, int rows, int C, float eps)
+{
+    const int row = blockIdx.x * 8 + (threadIdx.x >> 5), j = threadIdx.x & 31;
+    const bool live = row < rows;               // no early return: the lane-group sums stay uniform
+    const size_t base = (size_t)(live ? row : 0) * C + 8 * j;
+    float v[NCH][8];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) load8(x + base + 256 * i, v[i]);
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += v[i][e] * v[i][e];
+    ss = group_sum<32>(ss);
+    const float rs = 1.0f / sqrtf(ss / (float)C + eps);
+    if (!live) return;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[i][e] *= rs;
+        store8(y + base + 256 * i, v[i]);
+    }
+    if (j == 0) rstd[row] = rs;
+}
+
+template <typename T>
+static bool rmsnorm_fwd_rows_launch(const void* x, void* y, float* rstd, int rows, int C, float eps, hipStream_t s) {
+    const dim3 grid((rows + 7) / 8);
+    switch (C % 256 ? 0 : C / 256) {
+#define NCGPT_RMS_F(n)                                                                                              \
+    case n:                                                                                                          \
+        hipLaunchKernelGGL((rmsnorm_fwd_rows<T, n>), grid, dim3(256), 0, s, (const T*)x, (T*)y, rstd, rows, C, eps); \
+        return true;
+    NCGPT_RMS_F(1) NCGPT_RMS_F(2) NCGPT_RMS_F(3) NCGPT_RMS_F(4) NCGPT_RMS_F(5) NCGPT_RMS_F(6) NCGPT_RMS_F(8)
+#undef NCGPT_RMS_F
+    default: return false;
+    }
+}
+
 hipError_t launch_rmsnorm_fwd(Dt dt, const void* x, void* y, float* rstd, int rows, int C, float eps, hipStream_t s) {
+    if (dt == Dt::BF16 ? rmsnorm_fwd_rows_launch<bf16>(x, y, rstd, rows, C, eps, s)
+                       : rmsnorm_fwd_rows_launch<float>(x, y, rstd, rows, C, eps, s))
+        return hipGetLastError();
     dim3 grid((rows + 3) / 4);
     if (dt == Dt::BF16)
         hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)x, (bf16*)y, rstd, rows, C, eps);
@@ -127,8 +205,66 @@ rmsnorm_bwd_kernel(const T* __restrict__ y, const float* __restrict__ rstd, cons
     }
 }
 
+// The same derivative with each row held in registers, laid out as in rmsnorm_fwd_rows.
+template <typename T, int NCH>
+__global__ void __launch_bounds__(256)
+rmsnorm_bwd_rows(const T* __restrict__ y, const float* __restrict__ rstd, const T* __restrict__ dy,
+                 float* __restrict__ dx, T* __restrict__ dx_cd, int rows, int C, int accumulate)
+{
+    const int row = blockIdx.x * 8 + (threadIdx.x >> 5), j = threadIdx.x & 31;
+    const bool live = row < rows;
+    const int rr = live ? row : 0;
+    const size_t base = (size_t)rr * C + 8 * j;
+    float a[NCH][8], b[NCH][8], o[NCH][8];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        load8(y + base + 256 * i, a[i]);
+        load8(dy + base + 256 * i, b[i]);
+        if (accumulate) {
+            load8(dx + base + 256 * i, o[i]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[i][e] = 0.0f;
+        }
+    }
+    const float rs = rstd[rr];
+    float dot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot += a[i][e] * b[i][e];
+    dot = group_sum<32>(dot) / (float)C;
+    if (!live) return;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[i][e] += rs * (b[i][e] - a[i][e] * dot);
+        store8(dx + base + 256 * i, o[i]);
+        if (dx_cd) store8(dx_cd + base + 256 * i, o[i]);
+    }
+}
+
+template <typename T>
+static bool rmsnorm_bwd_rows_launch(const void* y, const float* rstd, const void* dy, float* dx, void* dx_cd,
+                                    int rows, int C, int accumulate, hipStream_t s) {
+    const dim3 grid((rows + 7) / 8);
+    switch (C % 256 ? 0 : C / 256) {
+#define NCGPT_RMS_B(n)                                                                                          \
+    case n:                                                                                                      \
+        hipLaunchKernelGGL((rmsnorm_bwd_rows<T, n>), grid, dim3(256), 0, s, (const T*)y, rstd, (const T*)dy, dx, \
+                           (T*)dx_cd, rows, C, accumulate);                                                      \
+        return true;
+    NCGPT_RMS_B(1) NCGPT_RMS_B(2) NCGPT_RMS_B(3) NCGPT_RMS_B(4) NCGPT_RMS_B(5) NCGPT_RMS_B(6) NCGPT_RMS_B(8)
+#undef NCGPT_RMS_B
+    default: return false;
+    }
+}
+
 hipError_t launch_rmsnorm_bwd(Dt dt, const void* y, const float* rstd, const void* dy, float* dx, void* dx_cd,
                               int rows, int C, int accumulate, hipStream_t s) {
+    if (dt == Dt::BF16 ? rmsnorm_bwd_rows_launch<bf16>(y, rstd, dy, dx, dx_cd, rows, C, accumulate, s)
+                       : rmsnorm_bwd_rows_launch<float>(y, rstd, dy, dx, dx_cd, rows, C, accumulate, s))
+        return hipGetLastError();
     dim3 grid((rows + 3) / 4);
     if (dt == Dt::BF16)
         hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)y, rstd, (const bf16*)dy, dx,
@@ -144,37 +280,9 @@ hipError_t launch_rmsnorm_bwd(Dt dt, const void* y, const float* rstd, const voi
 // (i, i + D/2) as y_i = x_i cos + x_{i+D/2} sin, y_{i+D/2} = -x_i sin +
 // x_{i+D/2} cos ("nanochat 项目深度分析" §2.1 item 1, §5.3), then RMS-normalise
 // the head (item 2).
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
-}
-
 // Each head is handled by L = D / 16 lanes; lane j of a head holds the 8
 // consecutive elements 8j..8j+7 of the first half and their rotation partners
 // D/2 + 8j.. of the second half, so every access is 16 bytes (bf16) wide.
-__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
-    const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-__device__ __forceinline__ void load8(const bf16* p, float (&v)[8]) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (float)a[e];
-}
-__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
-    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
-}
-__device__ __forceinline__ void store8(bf16* p, const float (&v)[8]) {
-    bf16x8 a;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) a[e] = (bf16)v[e];
-    *reinterpret_cast<bf16x8*>(p) = a;
-}
-
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 rope_qknorm_fwd_kernel(T* __restrict__ qkv, float* __restrict__ rstdq, float* __restrict__ rstdk,
