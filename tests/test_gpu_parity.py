@@ -142,21 +142,23 @@ def test_gradient_accumulation(dtype):
             assert cosine(a, b) >= 0.9999, name
 
 
-def test_full_depth12_step_sampled():
-    """The benchmark's launch configuration (depth 12, 32 x 2048 tokens, bf16):
-    per-token losses of the first 128 positions of two sequences against the
-    oracle run on those prefixes (position t sees only positions <= t of its
-    own sequence), plus properties of the whole step."""
-    w = WORKLOADS["d12"]
+@pytest.mark.parametrize("name", ["d12", "d20", "d24"])
+def test_full_config_step_sampled(name):
+    """The full-size configurations, bf16, in the launch configuration the benchmark
+    times (depth 12: 32 x 2048 tokens; depth 20, GQA 2:1, vocab 65536: 16 x 2048;
+    depth 24, GQA 3:1, vocab 65536: 8 x 2048): per-token losses of the first 128
+    positions of two sequences against the oracle run on those prefixes (position t
+    sees only positions <= t of its own sequence), plus properties of the whole step."""
+    w = WORKLOADS[name]
     ids, tg, params = make_inputs(w)
     s = GpuStep(w, "bf16", ids, params)
     loss, st = s.run(tg)
     assert st == ncgpt.OK
     lr = s.probe("loss_rows").reshape(w.batch, w.seq_len)
     P = 128
-    for b in (0, 17):
+    for b in (0, w.batch // 2 + 1):
         wp = w.with_(batch=1, seq_len=P)
-        say(f"[oracle] d12 prefix of sequence {b}")
+        say(f"[oracle] {name} prefix of sequence {b}")
         lo, acts = orc.forward(ocfg(wp), ids[b:b + 1, :P], tg[b:b + 1, :P], params)
         e = np.max(np.abs(lr[b, :P] - acts["loss_rows"])) / np.max(np.abs(acts["loss_rows"]))
         assert e <= 1e-2, (b, e)
