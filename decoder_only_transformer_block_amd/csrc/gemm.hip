@@ -239,7 +239,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], int m0, 
 // ------------------------------------------------------------------ tile order
 // Workgroups are dealt round-robin to the 8 XCDs; renumber them so each XCD
 // gets a contiguous range of tiles (shared A / B tiles stay in one L2), then
-// walk tiles in bands of GROUP_M tile-rows.
+// walk tiles in bands of group_m tile-rows (a per-call choice: GemmDesc::group_m).
 __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
     constexpr int NX = 8;
     int per = (nwg + NX - 1) / NX;
@@ -250,12 +250,11 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
     return tall * per + (xcd - tall) * (per - 1) + local;
 }
 
-__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
-    constexpr int GROUP_M = 8;
-    int in_group = GROUP_M * tiles_n;
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
+    int in_group = group_m * tiles_n;
     int gid = t / in_group;
-    int first_m = gid * GROUP_M;
-    int gsz = min(tiles_m - first_m, GROUP_M);
+    int first_m = gid * group_m;
+    int gsz = min(tiles_m - first_m, group_m);
     int r = t % in_group;
     tm = first_m + r % gsz;
     tn = r / gsz;
@@ -357,7 +356,7 @@ template <int R, int NT> struct Stage<R, false, NT> : StageMN<R, NT> {};
 template <int BM, int BN, bool AK, bool BK, class E>
 __global__ void __launch_bounds__(256, 1)
 gemm_bf16_mfma(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
-               int k_split, E epi)
+               int k_split, int group_m, E epi)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     constexpr int TA = BM * 64, TB = BN * 64;
@@ -369,7 +368,7 @@ gemm_bf16_mfma(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, in
 
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     int tm, tn;
-    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int split = blockIdx.y;
     const int kbeg = split * k_split;
@@ -448,7 +447,7 @@ gemm_bf16_mfma(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, in
 template <int BM, int BN, bool AK, bool BK, class E>
 __global__ void __launch_bounds__(256, 1)
 gemm_bf16_mfma_pipe(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
-                    int k_split, E epi)
+                    int k_split, int group_m, E epi)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     constexpr int TA = BM * 64, TB = BN * 64;
@@ -460,7 +459,7 @@ gemm_bf16_mfma_pipe(const bf16* __restrict__ A, const bf16* __restrict__ B, int 
 
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     int tm, tn;
-    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int split = blockIdx.y;
     const int kbeg = split * k_split;
@@ -564,7 +563,7 @@ gemm_bf16_mfma_pipe(const bf16* __restrict__ A, const bf16* __restrict__ B, int 
 template <int BM, int BN, bool AK, bool BK, class E>
 __global__ void __launch_bounds__(512, 1)
 gemm_bf16_mfma_w8(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
-                  int k_split, E epi)
+                  int k_split, int group_m, E epi)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     constexpr int TA = BM * 64, TB = BN * 64;
@@ -576,7 +575,7 @@ gemm_bf16_mfma_w8(const bf16* __restrict__ A, const bf16* __restrict__ B, int M,
 
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     int tm, tn;
-    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int split = blockIdx.y;
     const int kbeg = split * k_split;
@@ -721,7 +720,7 @@ struct DmaTile {
 template <int BM, int BN, int WGM, int WGN, bool AK, bool BK, class E>
 __global__ void __launch_bounds__(64 * WGM * WGN, 1)
 gemm_bf16_mfma_dma(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
-                   int k_split, E epi)
+                   int k_split, int group_m, E epi)
 {
     __shared__ __attribute__((aligned(1024))) bf16 sA0[BM * 64];
     __shared__ __attribute__((aligned(1024))) bf16 sB0[BN * 64];
@@ -736,7 +735,7 @@ gemm_bf16_mfma_dma(const bf16* __restrict__ A, const bf16* __restrict__ B, int M
 
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     int tm, tn;
-    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int split = blockIdx.y;
     const int kbeg = split * k_split;
@@ -889,7 +888,7 @@ __device__ __forceinline__ bf16x8 frag32(const bf16* S, int r0, int kk, int lane
 template <int BM, int BN, int WGM, int WGN, bool AK, bool BK, class E>
 __global__ void __launch_bounds__(64 * WGM * WGN, 1)
 gemm_bf16_mfma_ring(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
-                    int k_split, E epi)
+                    int k_split, int group_m, E epi)
 {
     __shared__ __attribute__((aligned(1024))) bf16 sA0[BM * 32];
     __shared__ __attribute__((aligned(1024))) bf16 sB0[BN * 32];
@@ -908,7 +907,7 @@ gemm_bf16_mfma_ring(const bf16* __restrict__ A, const bf16* __restrict__ B, int 
 
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     int tm, tn;
-    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int split = blockIdx.y;
     const int kbeg = split * k_split;
@@ -1005,7 +1004,7 @@ gemm_bf16_mfma_ring(const bf16* __restrict__ A, const bf16* __restrict__ B, int 
 template <int BM, int BN, int WGM, int WGN, bool AK, bool BK, class E>
 __global__ void __launch_bounds__(64 * WGM * WGN, 1)
 gemm_bf16_mfma_pring(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
-                     int k_split, int splits, E epi)
+                     int k_split, int splits, int group_m, E epi)
 {
     __shared__ __attribute__((aligned(1024))) bf16 sA0[BM * 32];
     __shared__ __attribute__((aligned(1024))) bf16 sB0[BN * 32];
@@ -1037,7 +1036,7 @@ gemm_bf16_mfma_pring(const bf16* __restrict__ A, const bf16* __restrict__ B, int
         const int Lc = it.valid ? L : 0;
         it.split = Lc / tiles;
         int tm, tn;
-        tile_coords(Lc % tiles, tiles_m, tiles_n, tm, tn);
+        tile_coords(Lc % tiles, tiles_m, tiles_n, group_m, tm, tn);
         it.m0 = tm * BM;
         it.n0 = tn * BN;
         it.kbeg = it.split * k_split;
@@ -1140,7 +1139,7 @@ gemm_bf16_mfma_pring(const bf16* __restrict__ A, const bf16* __restrict__ B, int
 template <int BM, int BN, bool AK, bool BK, class E>
 __global__ void __launch_bounds__(256, 1)
 gemm_bf16_mfma_db(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
-                  int k_split, E epi)
+                  int k_split, int group_m, E epi)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     constexpr int TA = BM * 64, TB = BN * 64;
@@ -1152,7 +1151,7 @@ gemm_bf16_mfma_db(const bf16* __restrict__ A, const bf16* __restrict__ B, int M,
 
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     int tm, tn;
-    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int split = blockIdx.y;
     const int kbeg = split * k_split;
@@ -1346,7 +1345,7 @@ static hipError_t run_mfma(const GemmDesc& d, E e, hipStream_t s) {
         const int items = ((d.M + BM - 1) / BM) * ((d.N + BN - 1) / BN) * splits;
         const int grid = std::min(items, occ * num_cus());
         hipLaunchKernelGGL(pk, dim3(grid), dim3(nt), 0, s, (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, d.K, d.lda,
-                           d.ldb, d.k_split, splits, e);
+                           d.ldb, d.k_split, splits, d.group_m, e);
         return hipGetLastError();
     }
     auto kern = v == 7   ? gemm_bf16_mfma_ring<BM, BN, 2, 4, AK, BK, E>
@@ -1369,7 +1368,7 @@ static hipError_t run_mfma(const GemmDesc& d, E e, hipStream_t s) {
     int tiles = ((d.M + BM - 1) / BM) * ((d.N + BN - 1) / BN);
     dim3 grid(tiles, (d.K + d.k_split - 1) / d.k_split);
     hipLaunchKernelGGL(kern, grid, dim3(nthreads), dyn, s, (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, d.K, d.lda,
-                       d.ldb, d.k_split, e);
+                       d.ldb, d.k_split, d.group_m, e);
     return hipGetLastError();
 }
 

@@ -45,6 +45,7 @@ struct GemmDesc {
     int k_split = 0;        // multiple of 64; 0 = K / splits
     size_t split_stride = 0;
     int tile = -1;    // MFMA tile: 0 = 256x256, 1 = 256x128, 2 = 128x128; -1 = chosen from the shape
+    int group_m = 4;  // tiles are walked in bands of group_m tile-rows (L2 reuse of the B tiles)
     int variant = -1; // MFMA main loop: 0 = plain two-stage, 1 = software-pipelined, 2 = two register stages,
                       // 3 = software-pipelined with 8 waves, 4 = direct-to-LDS loads, 5 = the same with 8 waves,
                       // 6 = four-stage ring of 32-deep direct-to-LDS stages, 7 = the same with 8 waves,

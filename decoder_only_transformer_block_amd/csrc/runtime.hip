@@ -468,6 +468,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.M = N; d.N = QKV; d.K = C;
             d.epi = Epi::StoreCd; d.out = qkv; d.ldo = QKV;
             d.variant = 7;  // few tiles per CU: the non-persistent eight-wave ring measured fastest
+            d.group_m = 8;  // bands of 8 tile-rows measured faster than bands of 4 for this shape
             TRY(gemm(c, d, "qkv"));
         }
         TRY(launch(c, "rope_qknorm_fwd", 0.0, (double)N * (c->H + c->Hkv) * c->D * 2 * e, [&] {
@@ -491,6 +492,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.M = N; d.N = C; d.K = HD;
             d.epi = Epi::ResidualCd; d.out = c->ws + p.x; d.in = xin; d.ldo = C;
             d.variant = 7;  // epilogue reads the residual: the eight-wave ring without spills
+            d.group_m = 8;
             TRY(gemm(c, d, "attn_out"));
         }
         TRY(launch(c, "rmsnorm_fwd", 0.0, norm_bytes, [&] {
@@ -521,6 +523,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
         d.A = c->ws + p.xf; d.lda = C; d.B = weight(c, -1, 1); d.ldb = C;
         d.M = N; d.N = V; d.K = C;
         d.epi = Epi::StoreCd; d.out = c->ws + p.logits; d.ldo = V;
+        d.group_m = 8;
         TRY(gemm(c, d, "lm_head"));
     }
     c->state = 1;
