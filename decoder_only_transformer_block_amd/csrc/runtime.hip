@@ -467,7 +467,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.A = xn1; d.lda = C; d.B = weight(c, l, 0); d.ldb = C;
             d.M = N; d.N = QKV; d.K = C;
             d.epi = Epi::StoreCd; d.out = qkv; d.ldo = QKV;
-            d.variant = 7;  // few tiles per CU: the non-persistent eight-wave ring measured fastest
+            d.variant = 9;  // the persistent eight-wave ring measured fastest for this shape
             d.group_m = 8;  // bands of 8 tile-rows measured faster than bands of 4 for this shape
             TRY(gemm(c, d, "qkv"));
         }
@@ -511,7 +511,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.A = act; d.lda = F; d.B = weight(c, l, 5); d.ldb = F;
             d.M = N; d.N = C; d.K = F;
             d.epi = Epi::ResidualCd; d.out = c->ws + p.x; d.in = c->ws + p.x; d.ldo = C;
-            d.variant = 7;
+            d.variant = 9;  // measured faster than the non-persistent ring despite a small spill
             TRY(gemm(c, d, "proj"));
         }
     }
