@@ -29,7 +29,18 @@ def flops_per_token(w):
     causal attention products, 6 * L * H * D * (T + 1)."""
     n_mm = w.n_layer * (w.n_embd * (w.n_head + 2 * w.n_kv_head) * w.head_dim + w.n_head * w.head_dim * w.n_embd
                         + 2 * w.n_embd * w.mlp_dim) + w.vocab_size * w.n_embd
-    return 6.0 * n_mm + 6.0 * w.n_layer * w.n_head * w.head_dim * (w.seq_len + 1)
+    return 6 * n_mm + 6 * w.n_layer * w.n_head * w.head_dim * (w.seq_len + 1)
+
+
+def six_n_flops_per_token(n_params):
+    """The pages' rule of thumb, 6 x N_params FLOPs per token (all parameters, attention ignored); reported
+    beside the primary count, not used for the MFU."""
+    return 6.0 * n_params
+
+
+def mfu(w, seconds_per_step):
+    """Model FLOPs utilisation of one step of workload w against the bf16 dense MFMA peak."""
+    return flops_per_token(w) * w.n_tokens / seconds_per_step / (PEAK_BF16_TFLOPS * 1e12)
 
 
 def cpu_baseline(w):
@@ -146,8 +157,7 @@ def main():
     ms = (t1 - t0) * 1e3 / args.steps
     tok_s = w.n_tokens / (ms / 1e3)
     fpt = flops_per_token(w)
-    step_flops = fpt * w.n_tokens
-    mfu = step_flops / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12)
+    step_mfu = mfu(w, ms / 1e3)
 
     # second region of the same K steps with a HIP event pair around every launch
     m.timing(True)
@@ -200,7 +210,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if dtype == "bf16" else "f32",
         "data": "synthetic",
-        "mfu": round(mfu, 4),
+        "mfu": round(step_mfu, 4),
         "flops_per_token": fpt,
         "config": {"workload": f"{w.name}: depth {w.n_layer}, n_embd {w.n_embd}, {w.n_head}x{w.head_dim} heads, "
                                f"{w.n_kv_head} kv heads, MLP {w.mlp_dim}, vocab {w.vocab_size}, "

@@ -796,8 +796,6 @@ attn_bwd_dkdv_f32(const float* __restrict__ qkv, const float* __restrict__ dy, c
 }
 
 // ======================================================================== host
-hipError_t attn_init_attributes() { return hipSuccess; }
-
 hipError_t launch_attn_fwd(const AttnDesc& a, hipStream_t s) {
     if (a.dt == Dt::BF16) {
         if (a.D != 128 || a.T % 64) return hipErrorInvalidValue;

@@ -1,13 +1,15 @@
 // GEMMs of the block stack: the bias-free linears y = x W^T (forward), their
 // input gradients dx = dy W and weight gradients dW = dy^T x (backward).
 //
-// bf16 path: one MFMA kernel (v_mfma_f32_32x32x16_bf16, fp32 accumulation)
-// for all three operand layouts.  Tiles of BM x BN x 64 are staged through
-// LDS (two stages, XOR-swizzled 16-byte chunks), 4 waves per workgroup in a
-// 2 x 2 grid.  Operands whose K index is not contiguous in memory (the
-// token-major activations of a weight gradient, the [out,in] weight of an
-// input gradient) are copied to LDS in their natural layout and their MFMA
-// fragments are read with gfx950's transposing LDS load (ds_read_b64_tr_b16).
+// bf16 path: MFMA kernels (v_mfma_f32_32x32x16_bf16, fp32 accumulation) for
+// all three operand layouts.  Operand tiles travel from memory straight into
+// LDS (buffer_load ... lds) in 32-deep stages held in a four-stage ring, three
+// stages ahead of the MFMAs; 4 or 8 waves per workgroup (2 x 2 or 2 x 4),
+// either one output tile per workgroup or persistent over (split, tile)
+// items.  Operands whose K index is not contiguous in memory (the token-major
+// activations of a weight gradient, the [out,in] weight of an input gradient)
+// stay in LDS in their natural layout and their MFMA fragments are read with
+// gfx950's transposing LDS load (ds_read_b64_tr_b16).
 //
 // The MFMA is issued with the two operands swapped (it computes C^T), which
 // leaves each lane holding 4 consecutive columns of one output row: the
@@ -46,14 +48,6 @@ template <typename T> struct EStoreCd {
         Vec4<T>::store(out + (size_t)m * ldo + n, v);
     }
     __device__ void put8(int m, int n, int, const float (&v)[8]) const { st8(out + (size_t)m * ldo + n, v); }
-};
-struct EStoreF32 {
-    static constexpr bool kWide = false, kLoads = false;
-    float* out; int ldo;
-    __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
-        Vec4<float>::store(out + (size_t)m * ldo + n, v);
-    }
-    __device__ void put8(int, int, int, const float (&)[8]) const {}
 };
 template <typename T> struct EResidual {
     static constexpr bool kWide = std::is_same<T, bf16>::value, kLoads = true;
@@ -260,559 +254,35 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
     tn = r / gsz;
 }
 
-// ------------------------------------------------------------------ LDS staging (bf16)
-// An LDS tile holds R rows x 64 k (bf16): 8 chunks of 16 bytes per row.  The
-// gfx950 LDS serves 16 lanes of a 16-byte access per cycle from 64 banks, so
-// the 16 consecutive rows read together must cover all (row parity, chunk)
-// pairs: the chunk index is XOR-ed with (row & 7) ^ ((row >> 3) & 1), which
-// gives the even rows of a 16-row group 8 distinct chunks and the odd rows 8
-// distinct chunks (bank-conflict counter reads 0 on the MFMA reads).
-__device__ __forceinline__ int lds_chunk(int row, int ch) { return row * 8 + (ch ^ ((row & 7) ^ ((row >> 3) & 1))); }
-
-// K-contiguous operand: element (r, k) at P[r*ld + k].
-template <int R, int NT = 256> struct StageK {
-    static constexpr int NC = R * 8 / NT;  // 16-byte chunks per thread
-    u32x4 v[NC];
-    __device__ __forceinline__ void load(const bf16* __restrict__ P, int ld, int r0, int rmax, int k0, int tid) {
-#pragma unroll
-        for (int i = 0; i < NC; ++i) {
-            int u = tid + NT * i;
-            int row = u >> 3, ch = u & 7;
-            int gr = min(r0 + row, rmax - 1);
-            v[i] = *reinterpret_cast<const u32x4*>(P + (size_t)gr * ld + k0 + ch * 8);
-        }
-    }
-    __device__ __forceinline__ void store(bf16* S, int tid) const {
-#pragma unroll
-        for (int i = 0; i < NC; ++i) {
-            int u = tid + NT * i;
-            int row = u >> 3, ch = u & 7;
-            *reinterpret_cast<u32x4*>(S + lds_chunk(row, ch) * 8) = v[i];
-        }
-    }
-};
-
-// MN-contiguous operand: element (r, k) at P[k*ld + r].  The tile is kept in
-// LDS in this natural layout, [64 k][R r] (16-byte chunks along r), and the
-// MFMA fragment (8 consecutive k of one r) is read with two
-// ds_read_b64_tr_b16.  A transposing read of one 16-lane group covers 4
-// consecutive k rows x 32 bytes; the chunk index is XOR-ed with
-// ((k & 3) << 2) so those 4 rows land in 4 different 64-byte bank groups.
+// ------------------------------------------------------------------ LDS layouts (bf16)
+// A K-strided operand (element (r, k) at P[k*ld + r]) is kept in LDS in its
+// natural layout, [k][R r] in 16-byte chunks along r, and the MFMA fragment (8
+// consecutive k of one r) is read with two ds_read_b64_tr_b16.  A transposing
+// read of one 16-lane group covers 4 consecutive k rows x 32 bytes; the chunk
+// index is XOR-ed with ((k & 3) << 2) so those 4 rows land in 4 different
+// 64-byte bank groups.
 __device__ __forceinline__ int mn_chunk(int k, int c, int R) { return k * (R / 8) + (c ^ ((k & 3) << 2)); }
-
-template <int R, int NT = 256> struct StageMN {
-    static constexpr int CPR = R / 8;            // 16-byte chunks per k row
-    static constexpr int NC = 64 * CPR / NT;     // chunks per thread
-    u32x4 v[NC];
-    __device__ __forceinline__ void load(const bf16* __restrict__ P, int ld, int r0, int rmax, int k0, int tid) {
-#pragma unroll
-        for (int i = 0; i < NC; ++i) {
-            int u = tid + NT * i;
-            int k = u / CPR, c = u % CPR;
-            int gr = min(r0 + c * 8, rmax - 8);
-            v[i] = *reinterpret_cast<const u32x4*>(P + (size_t)(k0 + k) * ld + gr);
-        }
-    }
-    __device__ __forceinline__ void store(bf16* S, int tid) const {
-#pragma unroll
-        for (int i = 0; i < NC; ++i) {
-            int u = tid + NT * i;
-            int k = u / CPR, c = u % CPR;
-            *reinterpret_cast<u32x4*>(S + mn_chunk(k, c, R) * 8) = v[i];
-        }
-    }
-};
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// MFMA fragment of lane `lane`: operand row r0 + (lane & 31), k = kk*16 + 8h .. +7.
-template <int R, bool KC>
-__device__ __forceinline__ bf16x8 frag(const bf16* S, int r0, int kk, int lane) {
-    const int h = lane >> 5;
-    if constexpr (KC) {
-        const int row = r0 + (lane & 31);
-        return *reinterpret_cast<const bf16x8*>(S + lds_chunk(row, kk * 2 + h) * 8);
-    } else {
-        // ds_read_b64_tr_b16: lane i of a 16-lane group receives element e of the
-        // 4-value row addressed by lane 4e + i/4, at position i % 4
-        const int sl = lane & 15;
-        const int r = r0 + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
-        const int c = r >> 3, o = r & 7;
-        const int k = kk * 16 + 8 * h + (sl >> 2);
-        s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(S + mn_chunk(k, c, R) * 8 + o));
-        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(S + mn_chunk(k + 4, c, R) * 8 + o));
-        s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        return __builtin_bit_cast(bf16x8, v);
-    }
-}
-
-template <int R, bool KC, int NT = 256> struct Stage;
-template <int R, int NT> struct Stage<R, true, NT> : StageK<R, NT> {};
-template <int R, int NT> struct Stage<R, false, NT> : StageMN<R, NT> {};
-
-// ------------------------------------------------------------------ bf16 MFMA kernel
-template <int BM, int BN, bool AK, bool BK, class E>
-__global__ void __launch_bounds__(256, 1)
-gemm_bf16_mfma(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
-               int k_split, int group_m, E epi)
-{
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    constexpr int TA = BM * 64, TB = BN * 64;
-    constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-    bf16* base = reinterpret_cast<bf16*>(smem);
-
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1, h = lane >> 5, l32 = lane & 31;
-
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    int tm, tn;
-    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int split = blockIdx.y;
-    const int kbeg = split * k_split;
-    const int nk = min(k_split, K - kbeg) / 64;
-
-    Stage<BM, AK> sa;
-    Stage<BN, BK> sb;
-    auto gload = [&](int k0) {
-        sa.load(A, lda, m0, M, k0, tid);
-        sb.load(B, ldb, n0, N, k0, tid);
-    };
-    auto lstore = [&](int st) {
-        sa.store(base + st * (TA + TB), tid);
-        sb.store(base + st * (TA + TB) + TA, tid);
-    };
-
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    if (nk > 0) {
-        gload(kbeg);
-        lstore(0);
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload(kbeg + (kt + 1) * 64);
-        const bf16* sA = base + cur * (TA + TB);
-        const bf16* sB = sA + TA;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            bf16x8 af[FM], bfr[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) af[i] = frag<BM, AK>(sA, wm * WM + 32 * i, kk, lane);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) bfr[j] = frag<BN, BK>(sB, wn * WN + 32 * j, kk, lane);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < nk) lstore(cur ^ 1);
-        __syncthreads();
-    }
-
-    // lane holds C[m0 + wm*WM + 32i + l32][n0 + wn*WN + 32j + 8g + 4h + (0..3)] = acc[i][j][4g + (0..3)]
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wm * WM + 32 * i + l32;
-        if (m >= M) continue;
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * WN + 32 * j + 8 * g + 4 * h;
-                if (n < N) {
-                    float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                    epi(m, n, split, v);
-                }
-            }
-    }
-}
-
-// ------------------------------------------------------------------ bf16 MFMA kernel, software-pipelined
-// Same tiling as above, with the LDS fragment reads of k-step kk+1 issued
-// while the MFMAs of k-step kk run (two fragment register sets), one
-// branch-free basic block per 64-deep stage (the prefetch of the stage after
-// the last one is clamped to a valid address and never stored), and
-// scheduling-group hints that interleave MFMAs with LDS reads and global loads.
-template <int BM, int BN, bool AK, bool BK, class E>
-__global__ void __launch_bounds__(256, 1)
-gemm_bf16_mfma_pipe(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
-                    int k_split, int group_m, E epi)
-{
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    constexpr int TA = BM * 64, TB = BN * 64;
-    constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-    bf16* base = reinterpret_cast<bf16*>(smem);
-
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1, h = lane >> 5, l32 = lane & 31;
-
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    int tm, tn;
-    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int split = blockIdx.y;
-    const int kbeg = split * k_split;
-    const int nk = min(k_split, K - kbeg) / 64;
-
-    Stage<BM, AK> sa;
-    Stage<BN, BK> sb;
-    auto gload = [&](int k0) {
-        sa.load(A, lda, m0, M, k0, tid);
-        sb.load(B, ldb, n0, N, k0, tid);
-    };
-    auto lstore = [&](int st) {
-        sa.store(base + st * (TA + TB), tid);
-        sb.store(base + st * (TA + TB) + TA, tid);
-    };
-    bf16x8 fa[2][FM], fb[2][FN];
-    auto lfrag = [&](int buf, int st, int kk) {
-        const bf16* sA = base + st * (TA + TB);
-        const bf16* sB = sA + TA;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) fa[buf][i] = frag<BM, AK>(sA, wm * WM + 32 * i, kk, lane);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) fb[buf][j] = frag<BN, BK>(sB, wn * WN + 32 * j, kk, lane);
-    };
-
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    if (nk > 0) {
-        gload(kbeg);
-        lstore(0);
-    }
-    __syncthreads();
-    if (nk > 0) lfrag(0, 0, 0);
-    const int klast = kbeg + (nk - 1) * 64;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        gload(min(kbeg + (kt + 1) * 64, klast));  // past the end: a harmless reload of the last stage
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int fc = kk & 1;
-            if (kk < 3) lfrag(fc ^ 1, cur, kk + 1);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fc][j], fa[fc][i], acc[i][j], 0, 0, 0);
-            if (kk == 0) {
-                // spread this stage's global loads over the first k-step's MFMAs
-#pragma unroll
-                for (int q = 0; q < FM + FN; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-                }
-#pragma unroll
-                for (int q = 0; q < FM * FN - (FM + FN); ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 global load
-                }
-            } else if (kk < 3) {
-#pragma unroll
-                for (int q = 0; q < FM + FN; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-            }
-        }
-        lstore(cur ^ 1);
-        __syncthreads();
-        lfrag(0, cur ^ 1, 0);
-    }
-
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wm * WM + 32 * i + l32;
-        if (m >= M) continue;
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * WN + 32 * j + 8 * g + 4 * h;
-                if (n < N) {
-                    float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                    epi(m, n, split, v);
-                }
-            }
-    }
-}
-
-// ------------------------------------------------------------------ bf16 MFMA kernel, 8 waves
-// The pipelined loop above with 512 threads: 8 waves in a 2 x 4 grid, each
-// owning a (BM/2) x (BN/4) sub-tile, so a wave holds half the accumulators and
-// fits in 256 registers.  Two waves then share each SIMD, and one wave's LDS
-// reads, barrier and memory waits overlap the other's MFMAs; the LDS read
-// traffic per MFMA grows by half, which the 64-bank LDS absorbs.
-template <int BM, int BN, bool AK, bool BK, class E>
-__global__ void __launch_bounds__(512, 1)
-gemm_bf16_mfma_w8(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
-                  int k_split, int group_m, E epi)
-{
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    constexpr int TA = BM * 64, TB = BN * 64;
-    constexpr int WM = BM / 2, WN = BN / 4, FM = WM / 32, FN = WN / 32;
-    bf16* base = reinterpret_cast<bf16*>(smem);
-
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 2, wn = w & 3, h = lane >> 5, l32 = lane & 31;
-
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    int tm, tn;
-    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int split = blockIdx.y;
-    const int kbeg = split * k_split;
-    const int nk = min(k_split, K - kbeg) / 64;
-
-    Stage<BM, AK, 512> sa;
-    Stage<BN, BK, 512> sb;
-    auto gload = [&](int k0) {
-        sa.load(A, lda, m0, M, k0, tid);
-        sb.load(B, ldb, n0, N, k0, tid);
-    };
-    auto lstore = [&](int st) {
-        sa.store(base + st * (TA + TB), tid);
-        sb.store(base + st * (TA + TB) + TA, tid);
-    };
-    bf16x8 fa[2][FM], fb[2][FN];
-    auto lfrag = [&](int buf, int st, int kk) {
-        const bf16* sA = base + st * (TA + TB);
-        const bf16* sB = sA + TA;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) fa[buf][i] = frag<BM, AK>(sA, wm * WM + 32 * i, kk, lane);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) fb[buf][j] = frag<BN, BK>(sB, wn * WN + 32 * j, kk, lane);
-    };
-
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    if (nk > 0) {
-        gload(kbeg);
-        lstore(0);
-    }
-    __syncthreads();
-    if (nk > 0) lfrag(0, 0, 0);
-    const int klast = kbeg + (nk - 1) * 64;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        gload(min(kbeg + (kt + 1) * 64, klast));  // past the end: a harmless reload of the last stage
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int fc = kk & 1;
-            if (kk < 3) lfrag(fc ^ 1, cur, kk + 1);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fc][j], fa[fc][i], acc[i][j], 0, 0, 0);
-        }
-        lstore(cur ^ 1);
-        __syncthreads();
-        lfrag(0, cur ^ 1, 0);
-    }
-
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wm * WM + 32 * i + l32;
-        if (m >= M) continue;
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * WN + 32 * j + 8 * g + 4 * h;
-                if (n < N) {
-                    float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                    epi(m, n, split, v);
-                }
-            }
-    }
-}
-
-// ------------------------------------------------------------------ bf16 MFMA kernel, direct-to-LDS loads
-// Tiles travel from memory straight into LDS (buffer_load_dwordx4 ... lds):
-// no registers stage them and no LDS store instructions are issued.  One
-// wave-instruction fills 1 KB of consecutive LDS chunk slots; each lane
-// fetches the global 16-byte chunk whose swizzled slot it fills, so the LDS
-// layouts are exactly those of the register-staged kernels.  A lane's byte
-// offset differs between its instructions only by a wave-uniform stride,
-// which goes into the scalar offset, and the buffer base moves with k, so a
-// lane keeps one offset register per operand.  Rows past the matrix end lie
-// past the buffer's record count and read as zeros; columns past a ragged
-// edge read neighbouring elements of the same matrix and only reach outputs
-// that are never stored.  The loads of stage k+1 run under the MFMAs of stage
-// k; each wave waits for its own loads and a barrier publishes the stage.
-// The two stages are distinct LDS arrays, which lets the compiler see that
-// fragment reads of one never wait for the loads into the other.
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int R, bool KC, int NW>
-struct DmaTile {
-    static constexpr int NI = R / (8 * NW);              // wave-instructions per wave and stage
-    static constexpr int CPR = R / 8;                    // 16-byte chunks per k-row (MN layout)
-    static_assert(NI >= 1 && (64 * NW / CPR) % 4 == 0, "tile too small for the wave count");
-    unsigned vo;                                         // lane's byte offset in its first instruction
-    int step;                                            // bytes between a lane's instructions
-    int w;                                               // wave index (uniform)
-
-    __device__ __forceinline__ void init(int ld, int tid) {
-        const int lane = tid & 63;
-        w = __builtin_amdgcn_readfirstlane(tid >> 6);
-        if constexpr (KC) {
-            // chunk q = 64 (w + NW i) + lane: row q / 8 (advances 8 NW per i), slot q % 8
-            const int row = 8 * w + (lane >> 3);
-            const int ch = (lane & 7) ^ ((lane >> 3) ^ (w & 1));
-            vo = (unsigned)(row * ld * 2 + ch * 16);
-            step = 8 * NW * ld * 2;
-        } else {
-            // chunk q: k-row q / CPR (advances 64 NW / CPR per i), slot q % CPR
-            const int k = (64 * w + lane) / CPR;
-            const int c = (lane % CPR) ^ ((k & 3) << 2);
-            vo = (unsigned)(k * ld * 2 + c * 16);
-            step = (64 * NW / CPR) * ld * 2;
-        }
-    }
-    // one 64-deep stage starting at k0 into S
-    __device__ __forceinline__ void load(const bf16* __restrict__ P, int ld, int r0, int rmax, int k0, bool valid,
-                                         bf16* S) const {
-        const bf16* base;
-        unsigned bytes;
-        if constexpr (KC) {
-            base = P + (size_t)r0 * ld + k0;
-            bytes = (unsigned)(((min(rmax - r0, R) - 1) * ld + 64) * 2);
-        } else {
-            base = P + (size_t)k0 * ld + r0;
-            bytes = (unsigned)((63 * ld + min(rmax - r0, R)) * 2);
-        }
-        if (!valid) bytes = 0;
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(S + 64 * (w + NW * i) * 8), 16, vo, i * step, 0,
-                                                     0);
-    }
-};
-
-// WGM x WGN waves (4 or 8); with 8, two waves share each SIMD and one wave's
-// memory-instruction stalls are covered by the other's MFMAs.
-template <int BM, int BN, int WGM, int WGN, bool AK, bool BK, class E>
-__global__ void __launch_bounds__(64 * WGM * WGN, 1)
-gemm_bf16_mfma_dma(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
-                   int k_split, int group_m, E epi)
-{
-    __shared__ __attribute__((aligned(1024))) bf16 sA0[BM * 64];
-    __shared__ __attribute__((aligned(1024))) bf16 sB0[BN * 64];
-    __shared__ __attribute__((aligned(1024))) bf16 sA1[BM * 64];
-    __shared__ __attribute__((aligned(1024))) bf16 sB1[BN * 64];
-    constexpr int NW = WGM * WGN;
-    constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
-    constexpr int NL = DmaTile<BM, AK, NW>::NI + DmaTile<BN, BK, NW>::NI;
-
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w / WGN, wn = w % WGN, h = lane >> 5, l32 = lane & 31;
-
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    int tm, tn;
-    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int split = blockIdx.y;
-    const int kbeg = split * k_split;
-    const int nk = min(k_split, K - kbeg) / 64;
-
-    DmaTile<BM, AK, NW> da;
-    DmaTile<BN, BK, NW> db;
-    da.init(lda, tid);
-    db.init(ldb, tid);
-    auto dma = [&](int kt, bf16* sA, bf16* sB) {
-        da.load(A, lda, m0, M, kbeg + kt * 64, kt < nk, sA);
-        db.load(B, ldb, n0, N, kbeg + kt * 64, kt < nk, sB);
-    };
-    bf16x8 fa[2][FM], fb[2][FN];
-    auto lfrag = [&](int buf, const bf16* sA, const bf16* sB, int kk) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) fa[buf][i] = frag<BM, AK>(sA, wm * WM + 32 * i, kk, lane);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) fb[buf][j] = frag<BN, BK>(sB, wn * WN + 32 * j, kk, lane);
-    };
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-    // the MFMAs of one stage (its first fragments already in registers), with the
-    // next stage's loads spread over the first k-step
-    auto compute = [&](const bf16* sA, const bf16* sB) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int fc = kk & 1;
-            if (kk < 3) lfrag(fc ^ 1, sA, sB, kk + 1);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fc][j], fa[fc][i], acc[i][j], 0, 0, 0);
-            if (kk < 3) {
-#pragma unroll
-                for (int q = 0; q < FM + FN; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-                }
-            }
-            if (kk == 0) {
-#pragma unroll
-                for (int q = 0; q < NL && q < FM * FN - (FM + FN); ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 memory load
-                }
-            }
-        }
-    };
-    auto publish = [&]() {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    };
-
-    // two stages per iteration; a stage past the end reads as zeros (its buffer
-    // holds no records), so an odd count costs one idle stage and no branch
-    dma(0, sA0, sB0);
-    publish();
-    lfrag(0, sA0, sB0, 0);
-    for (int kt = 0; kt < nk; kt += 2) {
-        dma(kt + 1, sA1, sB1);
-        compute(sA0, sB0);
-        publish();
-        lfrag(0, sA1, sB1, 0);
-        dma(kt + 2, sA0, sB0);
-        compute(sA1, sB1);
-        publish();
-        lfrag(0, sA0, sB0, 0);
-    }
-
-    store_tile<FM, FN>(acc, m0 + wm * WM, n0 + wn * WN, split, M, N, lane, epi);
+// MFMA fragment of lane `lane` from a [k][R] tile: operand row r0 + (lane & 31),
+// k = kk*16 + 8h .. +7 (h = lane >> 5).  ds_read_b64_tr_b16: lane i of a 16-lane
+// group receives element e of the 4-value row addressed by lane 4e + i/4, at
+// position i % 4.
+template <int R>
+__device__ __forceinline__ bf16x8 frag_mn(const bf16* S, int r0, int kk, int lane) {
+    const int h = lane >> 5;
+    const int sl = lane & 15;
+    const int r = r0 + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+    const int c = r >> 3, o = r & 7;
+    const int k = kk * 16 + 8 * h + (sl >> 2);
+    s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(S + mn_chunk(k, c, R) * 8 + o));
+    s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(S + mn_chunk(k + 4, c, R) * 8 + o));
+    s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel, four-stage ring
@@ -881,7 +351,7 @@ __device__ __forceinline__ bf16x8 frag32(const bf16* S, int r0, int kk, int lane
         const int row = r0 + (lane & 31);
         return *reinterpret_cast<const bf16x8*>(S + lds_chunk32(row, kk * 2 + (lane >> 5)) * 8);
     } else {
-        return frag<R, false>(S, r0, kk, lane);
+        return frag_mn<R>(S, r0, kk, lane);
     }
 }
 
@@ -1130,127 +600,6 @@ gemm_bf16_mfma_pring(const bf16* __restrict__ A, const bf16* __restrict__ B, int
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// ------------------------------------------------------------------ bf16 MFMA kernel, two register stages
-// The global loads of stage k+2 are issued while stage k is computed and
-// written to LDS only at the end of stage k+1, so every load has two stages of
-// MFMA work (~4k cycles) to arrive: the single-stage prefetch above leaves the
-// one wave per SIMD waiting on memory.  Two register sets alternate, so the
-// stage loop is unrolled by two.
-template <int BM, int BN, bool AK, bool BK, class E>
-__global__ void __launch_bounds__(256, 1)
-gemm_bf16_mfma_db(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
-                  int k_split, int group_m, E epi)
-{
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    constexpr int TA = BM * 64, TB = BN * 64;
-    constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-    bf16* base = reinterpret_cast<bf16*>(smem);
-
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1, h = lane >> 5, l32 = lane & 31;
-
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    int tm, tn;
-    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int split = blockIdx.y;
-    const int kbeg = split * k_split;
-    const int nk = min(k_split, K - kbeg) / 64;
-    const int klast = kbeg + (nk - 1) * 64;
-
-    Stage<BM, AK> sa0, sa1;
-    Stage<BN, BK> sb0, sb1;
-    bf16x8 fa[2][FM], fb[2][FN];
-    auto lfrag = [&](int buf, int st, int kk) {
-        const bf16* sA = base + st * (TA + TB);
-        const bf16* sB = sA + TA;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) fa[buf][i] = frag<BM, AK>(sA, wm * WM + 32 * i, kk, lane);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) fb[buf][j] = frag<BN, BK>(sB, wn * WN + 32 * j, kk, lane);
-    };
-
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    // one 64-deep stage out of LDS buffer st, with the fragment reads of the
-    // next k-step overlapping the MFMAs of the current one
-    auto compute = [&](int st) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int fc = kk & 1;
-            if (kk < 3) lfrag(fc ^ 1, st, kk + 1);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fc][j], fa[fc][i], acc[i][j], 0, 0, 0);
-            if (kk < 3) {
-#pragma unroll
-                for (int q = 0; q < FM + FN; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-                }
-            }
-        }
-    };
-
-    if (nk > 0) {
-        sa0.load(A, lda, m0, M, kbeg, tid);
-        sb0.load(B, ldb, n0, N, kbeg, tid);
-        sa0.store(base, tid);
-        sb0.store(base + TA, tid);
-        sa1.load(A, lda, m0, M, min(kbeg + 64, klast), tid);
-        sb1.load(B, ldb, n0, N, min(kbeg + 64, klast), tid);
-    }
-    __syncthreads();
-    if (nk > 0) lfrag(0, 0, 0);
-    for (int kt = 0; kt < nk; kt += 2) {
-        // even stage: buffer 0; prefetch stage kt+2 into set 0; publish stage kt+1 (set 1) to buffer 1
-        {
-            const int kn = min(kbeg + (kt + 2) * 64, klast);
-            sa0.load(A, lda, m0, M, kn, tid);
-            sb0.load(B, ldb, n0, N, kn, tid);
-            compute(0);
-            sa1.store(base + (TA + TB), tid);
-            sb1.store(base + (TA + TB) + TA, tid);
-            __syncthreads();
-            lfrag(0, 1, 0);
-        }
-        if (kt + 1 < nk) {
-            const int kn = min(kbeg + (kt + 3) * 64, klast);
-            sa1.load(A, lda, m0, M, kn, tid);
-            sb1.load(B, ldb, n0, N, kn, tid);
-            compute(1);
-            sa0.store(base, tid);
-            sb0.store(base + TA, tid);
-            __syncthreads();
-            lfrag(0, 0, 0);
-        }
-    }
-
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wm * WM + 32 * i + l32;
-        if (m >= M) continue;
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * WN + 32 * j + 8 * g + 4 * h;
-                if (n < N) {
-                    float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                    epi(m, n, split, v);
-                }
-            }
-    }
-}
-
 // ------------------------------------------------------------------ fp32 SIMT kernel
 template <bool AK, bool BK, class E>
 __global__ void __launch_bounds__(256)
@@ -1312,9 +661,6 @@ gemm_f32_simt(const float* __restrict__ A, const float* __restrict__ B, int M, i
 }
 
 // ------------------------------------------------------------------ host side
-static int g_variant = 9;
-void gemm_set_variant(int v) { g_variant = v; }
-
 // compute units of the current device (queried once per process)
 static int num_cus() {
     static int n = 0;
@@ -1329,46 +675,26 @@ static int num_cus() {
 
 template <int BM, int BN, bool AK, bool BK, class E>
 static hipError_t run_mfma(const GemmDesc& d, E e, hipStream_t s) {
-    constexpr size_t lds = 2 * (size_t)(BM + BN) * 64 * sizeof(bf16);
-    const int v = d.variant >= 0 && d.variant <= 9 ? d.variant : g_variant;
-    if (v >= 8) {
-        auto pk = v == 9 ? gemm_bf16_mfma_pring<BM, BN, 2, 4, AK, BK, E> : gemm_bf16_mfma_pring<BM, BN, 2, 2, AK, BK, E>;
-        const int nt = v == 9 ? 512 : 256;
-        static int resident[2] = {0, 0};  // workgroups per CU, from the occupancy query
-        int& occ = resident[v - 8];
-        if (occ == 0) {
-            hipError_t st = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(pk), nt, 0);
-            if (st != hipSuccess) return st;
-            if (occ < 1) occ = 1;
-        }
-        const int splits = (d.K + d.k_split - 1) / d.k_split;
-        const int items = ((d.M + BM - 1) / BM) * ((d.N + BN - 1) / BN) * splits;
-        const int grid = std::min(items, occ * num_cus());
-        hipLaunchKernelGGL(pk, dim3(grid), dim3(nt), 0, s, (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, d.K, d.lda,
-                           d.ldb, d.k_split, splits, d.group_m, e);
+    const int splits = (d.K + d.k_split - 1) / d.k_split;
+    const int tiles = ((d.M + BM - 1) / BM) * ((d.N + BN - 1) / BN);
+    if (d.loop == GemmLoop::Ring8) {
+        hipLaunchKernelGGL((gemm_bf16_mfma_ring<BM, BN, 2, 4, AK, BK, E>), dim3(tiles, splits), dim3(512), 0, s,
+                           (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, d.K, d.lda, d.ldb, d.k_split, d.group_m, e);
         return hipGetLastError();
     }
-    auto kern = v == 7   ? gemm_bf16_mfma_ring<BM, BN, 2, 4, AK, BK, E>
-                : v == 6 ? gemm_bf16_mfma_ring<BM, BN, 2, 2, AK, BK, E>
-                : v == 5 ? gemm_bf16_mfma_dma<BM, BN, 2, 4, AK, BK, E>
-                : v == 4 ? gemm_bf16_mfma_dma<BM, BN, 2, 2, AK, BK, E>
-                : v == 3 ? gemm_bf16_mfma_w8<BM, BN, AK, BK, E>
-                : v == 2 ? gemm_bf16_mfma_db<BM, BN, AK, BK, E>
-                : v == 1 ? gemm_bf16_mfma_pipe<BM, BN, AK, BK, E>
-                         : gemm_bf16_mfma<BM, BN, AK, BK, E>;
-    const int nthreads = v == 3 || v == 5 || v == 7 ? 512 : 256;
-    const size_t dyn = v >= 4 ? 0 : lds;  // the direct-to-LDS kernels use static LDS
-    static bool attr_done[4] = {false, false, false, false};
-    if (v < 4 && !attr_done[v]) {
-        hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const bool eight = d.loop == GemmLoop::Persist8;
+    auto pk = eight ? gemm_bf16_mfma_pring<BM, BN, 2, 4, AK, BK, E> : gemm_bf16_mfma_pring<BM, BN, 2, 2, AK, BK, E>;
+    const int nt = eight ? 512 : 256;
+    static int resident[2] = {0, 0};  // workgroups per CU, from the occupancy query
+    int& occ = resident[eight ? 1 : 0];
+    if (occ == 0) {
+        hipError_t st = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(pk), nt, 0);
         if (st != hipSuccess) return st;
-        attr_done[v] = true;
+        if (occ < 1) occ = 1;
     }
-    int tiles = ((d.M + BM - 1) / BM) * ((d.N + BN - 1) / BN);
-    dim3 grid(tiles, (d.K + d.k_split - 1) / d.k_split);
-    hipLaunchKernelGGL(kern, grid, dim3(nthreads), dyn, s, (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, d.K, d.lda,
-                       d.ldb, d.k_split, d.group_m, e);
+    const int grid = std::min(tiles * splits, occ * num_cus());
+    hipLaunchKernelGGL(pk, dim3(grid), dim3(nt), 0, s, (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, d.K, d.lda,
+                       d.ldb, d.k_split, splits, d.group_m, e);
     return hipGetLastError();
 }
 
@@ -1390,20 +716,35 @@ static hipError_t run_f32(const GemmDesc& d, E e, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Only the (layout, epilogue) pairs of the block stack are instantiated:
+//   NT  (x W^T, forward):           store, residual add, ReLU^2
+//   NN  (dY W, input gradients):    store, ReLU^2 backward
+//   TN  (dY^T X, weight gradients): fp32 gradient, split-K partial
 template <typename T, bool AK, bool BK>
 static hipError_t dispatch_epi(const GemmDesc& d, hipStream_t s) {
     auto run = [&](auto e) -> hipError_t {
         if constexpr (sizeof(T) == 2) return run_bf16<AK, BK>(d, e, s);
         else return run_f32<AK, BK>(d, e, s);
     };
-    switch (d.epi) {
-    case Epi::StoreCd: return run(EStoreCd<T>{(T*)d.out, d.ldo});
-    case Epi::StoreF32: return run(EStoreF32{(float*)d.out, d.ldo});
-    case Epi::ResidualCd: return run(EResidual<T>{(T*)d.out, (const T*)d.in, d.ldo});
-    case Epi::ReluSq: return run(EReluSq<T>{(T*)d.out, d.ldo});
-    case Epi::ReluSqBwd: return run(EReluSqBwd<T>{(T*)d.out, (const T*)d.in, d.ldo});
-    case Epi::Grad: return run(EGrad{(float*)d.out, d.ldo, d.accumulate});
-    case Epi::SplitK: return run(ESplitK{(float*)d.out, d.ldo, d.split_stride});
+    if constexpr (AK && BK) {
+        switch (d.epi) {
+        case Epi::StoreCd: return run(EStoreCd<T>{(T*)d.out, d.ldo});
+        case Epi::ResidualCd: return run(EResidual<T>{(T*)d.out, (const T*)d.in, d.ldo});
+        case Epi::ReluSq: return run(EReluSq<T>{(T*)d.out, d.ldo});
+        default: break;
+        }
+    } else if constexpr (AK && !BK) {
+        switch (d.epi) {
+        case Epi::StoreCd: return run(EStoreCd<T>{(T*)d.out, d.ldo});
+        case Epi::ReluSqBwd: return run(EReluSqBwd<T>{(T*)d.out, (const T*)d.in, d.ldo});
+        default: break;
+        }
+    } else if constexpr (!AK && !BK) {
+        switch (d.epi) {
+        case Epi::Grad: return run(EGrad{(float*)d.out, d.ldo, d.accumulate});
+        case Epi::SplitK: return run(ESplitK{(float*)d.out, d.ldo, d.split_stride});
+        default: break;
+        }
     }
     return hipErrorInvalidValue;
 }
@@ -1413,7 +754,7 @@ static hipError_t dispatch_layout(const GemmDesc& d, hipStream_t s) {
     if (d.a_kcontig && d.b_kcontig) return dispatch_epi<T, true, true>(d, s);
     if (d.a_kcontig && !d.b_kcontig) return dispatch_epi<T, true, false>(d, s);
     if (!d.a_kcontig && !d.b_kcontig) return dispatch_epi<T, false, false>(d, s);
-    return dispatch_epi<T, false, true>(d, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(const GemmDesc& in, hipStream_t s) {
@@ -1430,9 +771,7 @@ hipError_t launch_gemm(const GemmDesc& in, hipStream_t s) {
 }
 
 const char* gemm_kernel_name(const GemmDesc& d) {
-    static const char* lay[4] = {"tn", "tk", "nt_mn", "nt"};
     int li = (d.a_kcontig ? 2 : 0) + (d.b_kcontig ? 1 : 0);
-    (void)lay;
     if (d.dt == Dt::F32) return li == 3 ? "gemm_f32_nt" : (li == 2 ? "gemm_f32_nn" : "gemm_f32_tn");
     static const char* names[3][3] = {
         {"gemm_bf16_nt_256x256", "gemm_bf16_nt_256x128", "gemm_bf16_nt_128x128"},
@@ -1440,11 +779,8 @@ const char* gemm_kernel_name(const GemmDesc& d) {
         {"gemm_bf16_tn_256x256", "gemm_bf16_tn_256x128", "gemm_bf16_tn_128x128"}};
     int r = li == 3 ? 0 : (li == 2 ? 1 : 2);
     int t = d.tile < 0 ? 0 : (d.tile > 2 ? 2 : d.tile);
-    (void)lay;
     return names[r][t];
 }
-
-hipError_t gemm_init_attributes() { return hipSuccess; }
 
 // ------------------------------------------------------------------ split-K reduction
 __global__ void __launch_bounds__(256)

@@ -21,13 +21,18 @@ enum : uint32_t { kErrBadToken = 1u, kErrNoTargets = 2u, kErrBadTarget = 4u };
 // (SIMT kernel).  K must be a multiple of 64; M and N multiples of 8.
 enum class Epi : int {
     StoreCd,     // out[m*ldo+n] = cd(v)
-    StoreF32,    // out(f32)[m*ldo+n] = v
     ResidualCd,  // out[m*ldo+n] = cd(in[m*ldo+n] + v)        (in may equal out)
     ReluSq,      // out[m*ldo+n] = cd(a * a), a = cd(max(v, 0))   (the MLP activation act)
     ReluSqBwd,   // out[m*ldo+n] = cd(v * 2 * sqrt(in[m*ldo+n]))   (in = saved act; sqrt(act) recovers a to bf16 rounding)
     Grad,        // out(f32) = (accumulate ? out : 0) + v
     SplitK,      // out(f32)[split*split_stride + m*ldo + n] = v
 };
+
+// MFMA main loop (all three stream 32-deep stages straight into a four-stage LDS ring):
+//   Ring8    eight waves, one output tile per workgroup;
+//   Persist4 four waves, persistent (the grid is the resident workgroups, walking (split, tile) items);
+//   Persist8 eight waves, persistent.
+enum class GemmLoop : int { Ring8 = 0, Persist4 = 1, Persist8 = 2 };
 
 struct GemmDesc {
     Dt dt = Dt::BF16;
@@ -46,11 +51,7 @@ struct GemmDesc {
     size_t split_stride = 0;
     int tile = -1;    // MFMA tile: 0 = 256x256, 1 = 256x128, 2 = 128x128; -1 = chosen from the shape
     int group_m = 4;  // tiles are walked in bands of group_m tile-rows (L2 reuse of the B tiles)
-    int variant = -1; // MFMA main loop: 0 = plain two-stage, 1 = software-pipelined, 2 = two register stages,
-                      // 3 = software-pipelined with 8 waves, 4 = direct-to-LDS loads, 5 = the same with 8 waves,
-                      // 6 = four-stage ring of 32-deep direct-to-LDS stages, 7 = the same with 8 waves,
-                      // 8 = persistent four-stage ring, 9 = the same with 8 waves;
-                      // -1 = the default (gemm_set_variant)
+    GemmLoop loop = GemmLoop::Persist8;
 };
 
 const char* gemm_kernel_name(const GemmDesc& d);
@@ -58,10 +59,6 @@ hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
 // grads = (accumulate ? grads : 0) + sum_s part[s]   (n elements, n % 4 == 0)
 hipError_t launch_splitk_reduce(const float* part, int splits, size_t stride, float* grads, size_t n,
                                 int accumulate, hipStream_t s);
-// MFMA kernels need more than the default 64 KB of dynamic LDS; call once per device.
-hipError_t gemm_init_attributes();
-// kernel variant of the bf16 GEMM (numbering as GemmDesc::variant; 9, the persistent 8-wave ring, is the default)
-void gemm_set_variant(int v);
 
 // ---------------------------------------------------------------- attention
 struct AttnDesc {
@@ -83,7 +80,6 @@ hipError_t launch_attn_fwd(const AttnDesc& a, hipStream_t s);
 // part 0: dQ (and delta = rowsum(dy * y), which part 1 reads); part 1: dK, dV -- in this order.  In bf16
 // the q and k gradients leave already taken back through QK-norm and RoPE (rstdq/rstdk/cosv/sinv).
 hipError_t launch_attn_bwd(const AttnDesc& a, hipStream_t s, int part);
-hipError_t attn_init_attributes();
 
 // ---------------------------------------------------------------- row-wise / elementwise
 hipError_t launch_cast_bf16(const float* src, void* dst, size_t n, hipStream_t s);

@@ -63,7 +63,6 @@ struct ncgpt_ctx {
     std::vector<Timed> pending;
     std::vector<hipEvent_t> pool;
     std::vector<Agg> agg;
-    bool attrs_done = false;
 
     template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
     size_t lay(int l, size_t o) const { return pl.layer0 + (size_t)l * pl.layer_stride + o; }
@@ -243,7 +242,6 @@ ncgpt_status fold_timing(ncgpt_ctx* c) {
 const char* epi_name(Epi e) {
     switch (e) {
     case Epi::StoreCd: return "store";
-    case Epi::StoreF32: return "store_f32";
     case Epi::ResidualCd: return "residual";
     case Epi::ReluSq: return "relusq";
     case Epi::ReluSqBwd: return "relusq_bwd";
@@ -272,7 +270,6 @@ ncgpt_status gemm(ncgpt_ctx* c, GemmDesc d, const char* tag) {
     const double e = d.dt == Dt::BF16 ? 2.0 : 4.0, mn = (double)d.M * d.N;
     double out = e;
     switch (d.epi) {
-    case Epi::StoreF32: out = 4.0; break;
     case Epi::ResidualCd: case Epi::ReluSqBwd: out = 2.0 * e; break;
     case Epi::Grad: out = d.accumulate ? 8.0 : 4.0; break;
     case Epi::SplitK: out = 4.0 * std::max(1, d.splits); break;
@@ -284,14 +281,14 @@ ncgpt_status gemm(ncgpt_ctx* c, GemmDesc d, const char* tag) {
 
 // weight gradient: out(f32 grads slice [M,N]) (+)= A^T-layout x B^T-layout over K tokens
 ncgpt_status wgrad(ncgpt_ctx* c, const char* tag, const void* dY, int ldy, const void* X, int ldx, int M, int N,
-                   float* g, int accumulate, int tile = -1, int variant = -1) {
+                   float* g, int accumulate, int tile = -1) {
     const int K = (int)c->N;
     WGrad w = pick_wgrad(c->dt, M, N, K);
     if (tile >= 0 && w.splits == 1) w.tile = tile;
     GemmDesc d;
     // both operands are read through transposing LDS reads (half rate): the four-wave persistent
     // ring, which reads fewer fragments per MFMA, measured fastest
-    d.variant = variant >= 0 ? variant : 8;
+    d.loop = GemmLoop::Persist4;
     d.A = dY; d.lda = ldy; d.a_kcontig = false;
     d.B = X; d.ldb = ldx; d.b_kcontig = false;
     d.M = M; d.N = N; d.K = K;
@@ -407,13 +404,6 @@ ncgpt_status ncgpt_bind(ncgpt_ctx* c, void* workspace, size_t bytes, void* strea
     if (!workspace) return fail(c, NCGPT_EINVAL, "null workspace");
     if (bytes < c->pl.total) return fail(c, NCGPT_ENOMEM, "workspace smaller than ncgpt_workspace_size");
     if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(c, NCGPT_EINVAL, "workspace not 256-byte aligned");
-    if (!c->attrs_done) {
-        hipError_t e = attn_init_attributes();
-        if (e != hipSuccess) return hip_fail(c, e, "attention kernel attributes");
-        e = gemm_init_attributes();
-        if (e != hipSuccess) return hip_fail(c, e, "gemm kernel attributes");
-        c->attrs_done = true;
-    }
     c->ws = static_cast<uint8_t*>(workspace);
     c->ws_bytes = bytes;
     c->stream = static_cast<hipStream_t>(stream);
@@ -467,7 +457,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.A = xn1; d.lda = C; d.B = weight(c, l, 0); d.ldb = C;
             d.M = N; d.N = QKV; d.K = C;
             d.epi = Epi::StoreCd; d.out = qkv; d.ldo = QKV;
-            d.variant = 9;  // the persistent eight-wave ring measured fastest for this shape
+            d.loop = GemmLoop::Persist8;  // the persistent eight-wave ring measured fastest for this shape
             d.group_m = 8;  // bands of 8 tile-rows measured faster than bands of 4 for this shape
             TRY(gemm(c, d, "qkv"));
         }
@@ -491,7 +481,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.A = y; d.lda = HD; d.B = weight(c, l, 3); d.ldb = HD;
             d.M = N; d.N = C; d.K = HD;
             d.epi = Epi::ResidualCd; d.out = c->ws + p.x; d.in = xin; d.ldo = C;
-            d.variant = 7;  // epilogue reads the residual: the eight-wave ring without spills
+            d.loop = GemmLoop::Ring8;  // epilogue reads the residual: the eight-wave ring without spills
             d.group_m = 8;
             TRY(gemm(c, d, "attn_out"));
         }
@@ -503,7 +493,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.A = xn2; d.lda = C; d.B = weight(c, l, 4); d.ldb = C;
             d.M = N; d.N = F; d.K = C;
             d.epi = Epi::ReluSq; d.out = act; d.ldo = F;
-            d.variant = 7;  // the non-persistent eight-wave ring measured fastest for this shape
+            d.loop = GemmLoop::Ring8;  // the non-persistent eight-wave ring measured fastest for this shape
             TRY(gemm(c, d, "fc"));
         }
         {
@@ -511,7 +501,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.A = act; d.lda = F; d.B = weight(c, l, 5); d.ldb = F;
             d.M = N; d.N = C; d.K = F;
             d.epi = Epi::ResidualCd; d.out = c->ws + p.x; d.in = c->ws + p.x; d.ldo = C;
-            d.variant = 9;  // measured faster than the non-persistent ring despite a small spill
+            d.loop = GemmLoop::Persist8;  // measured faster than the non-persistent ring despite a small spill
             TRY(gemm(c, d, "proj"));
         }
     }
@@ -582,12 +572,12 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
         d.A = logits; d.lda = V; d.B = weight(c, -1, 1); d.ldb = C; d.b_kcontig = false;
         d.M = N; d.N = C; d.K = V;
         d.epi = Epi::StoreCd; d.out = dxn; d.ldo = C;  // compute dtype
-        d.variant = 7;  // input gradients (NN): the non-persistent eight-wave ring measured fastest
+        d.loop = GemmLoop::Ring8;  // input gradients (NN): the non-persistent eight-wave ring measured fastest
         TRY(gemm(c, d, "dxf"));
     }
     // dWlm = dz^T xf: vocab x n_embd output over all tokens; 256 x 128 tiles, the four-wave persistent ring
     // measured fastest
-    TRY(wgrad(c, "dWlm", logits, V, c->ws + p.xf, C, V, C, gslice(-1, 1), acc, 1, 8));
+    TRY(wgrad(c, "dWlm", logits, V, c->ws + p.xf, C, V, C, gslice(-1, 1), acc, 1));
     const double nb = (double)N * C * (e + e + 4 + (dt == Dt::BF16 ? 2 : 0)) + N * 4.0;
     TRY(launch(c, "rmsnorm_bwd", 0.0, nb, [&] {
         return launch_rmsnorm_bwd(dt, c->ws + p.xf, c->at<float>(p.rstdf), dxn, dx, dx_cd, N, C, 0, c->stream);
@@ -603,7 +593,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             d.A = dxg; d.lda = C; d.B = weight(c, l, 5); d.ldb = F; d.b_kcontig = false;
             d.M = N; d.N = F; d.K = C;
             d.epi = Epi::ReluSqBwd; d.out = c->ws + p.dh; d.in = act; d.ldo = F;
-            d.variant = 7;  // epilogue reads act: the eight-wave ring without spills
+            d.loop = GemmLoop::Ring8;  // epilogue reads act: the eight-wave ring without spills
             TRY(gemm(c, d, "dh"));
         }
         TRY(wgrad(c, "dWproj", dxg, C, act, F, C, F, gslice(l, 5), acc));  // dWproj = dx^T act
@@ -612,7 +602,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             d.A = c->ws + p.dh; d.lda = F; d.B = weight(c, l, 4); d.ldb = C; d.b_kcontig = false;
             d.M = N; d.N = C; d.K = F;
             d.epi = Epi::StoreCd; d.out = dxn; d.ldo = C;  // compute dtype
-            d.variant = 7;  // input gradients (NN): the non-persistent eight-wave ring measured fastest
+            d.loop = GemmLoop::Ring8;  // input gradients (NN): the non-persistent eight-wave ring measured fastest
             TRY(gemm(c, d, "dxn2"));
         }
         TRY(wgrad(c, "dWfc", c->ws + p.dh, F, xn2, C, F, C, gslice(l, 4), acc));  // dWfc = dh^T xn2
@@ -660,7 +650,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             d.A = c->ws + p.dqkv; d.lda = QKV; d.B = weight(c, l, 0); d.ldb = C; d.b_kcontig = false;
             d.M = N; d.N = C; d.K = QKV;
             d.epi = Epi::StoreCd; d.out = dxn; d.ldo = C;  // compute dtype
-            d.variant = 7;  // input gradients (NN): the non-persistent eight-wave ring measured fastest
+            d.loop = GemmLoop::Ring8;  // input gradients (NN): the non-persistent eight-wave ring measured fastest
             TRY(gemm(c, d, "dxn1"));
         }
         TRY(wgrad(c, "dWqkv", c->ws + p.dqkv, QKV, xn1, C, QKV, C, gslice(l, 0), acc));  // dWqkv = dqkv^T xn1

@@ -140,8 +140,9 @@ def test_model_sizes_match_pages():
 # ------------------------------------------------------------------ independent second opinion
 
 def torch_model_loss(cfg, ids, tg, params64):
-    """The same model written with PyTorch library routines (fp64, CPU):
-    F.rms_norm, F.scaled_dot_product_attention(enable_gqa), F.cross_entropy."""
+    """The same model written with PyTorch (fp64, CPU, autograd for the gradient): RMSNorm and RoPE from
+    their formulas (RoPE as a complex product), and the library's F.scaled_dot_product_attention
+    (enable_gqa) and F.cross_entropy."""
     P = torch.tensor(params64, dtype=torch.float64, requires_grad=True)
     B, T, C, H, Hkv, D = cfg.batch, cfg.seq_len, cfg.n_embd, cfg.n_head, cfg.n_kv_head, cfg.head_dim
     eps = 2.0 ** -23
@@ -151,17 +152,18 @@ def torch_model_loss(cfg, ids, tg, params64):
         return P[o:o + r * c].view(r, c)
 
     def norm(x):
-        return F.rms_norm(x, (x.size(-1),), eps=eps)
+        # parameter-free RMSNorm over the last dim ("nanochat 项目深度分析" §2.1 item 5)
+        return x * torch.rsqrt(x.pow(2).mean(-1, keepdim=True) + eps)
 
+    # RoPE as complex multiplication: the pair (x_i, x_{i+D/2}) read as x_i + i x_{i+D/2} is multiplied by
+    # exp(-i t theta_i), the rotation whose sign the pages fix (§2.1 item 1, §5.3)
     pos = torch.arange(T, dtype=torch.float64)
-    inv = 10000.0 ** (-torch.arange(0, D, 2, dtype=torch.float64) / D)
-    ang = pos[:, None] * inv[None, :]
-    cos, sin = ang.cos()[None, :, None, :], ang.sin()[None, :, None, :]
+    theta = 10000.0 ** (-torch.arange(0, D, 2, dtype=torch.float64) / D)
+    rot = torch.polar(torch.ones(T, D // 2, dtype=torch.float64), -pos[:, None] * theta[None, :])
 
     def rope(x):
-        d = x.shape[3] // 2
-        x1, x2 = x[..., :d], x[..., d:]
-        return torch.cat([x1 * cos + x2 * sin, -x1 * sin + x2 * cos], 3)
+        z = torch.complex(x[..., : D // 2], x[..., D // 2:]) * rot[None, :, None, :]
+        return torch.cat([z.real, z.imag], -1)
 
     idx = torch.tensor(ids, dtype=torch.long)
     x = W(-1, 0)[idx]
@@ -175,7 +177,7 @@ def torch_model_loss(cfg, ids, tg, params64):
                                            is_causal=True, enable_gqa=True)
         x = x + F.linear(y.transpose(1, 2).reshape(B, T, H * D), W(l, 3))
         u = norm(x)
-        x = x + F.linear(F.relu(F.linear(u, W(l, 4))).square(), W(l, 5))
+        x = x + F.linear(F.linear(u, W(l, 4)).clamp_min(0.0) ** 2, W(l, 5))  # ReLU^2 (§2.1 item 4)
     z = F.linear(norm(x), W(-1, 1))
     t = torch.tensor(tg, dtype=torch.long)
     t = torch.where(t < 0, torch.full_like(t, -100), t)
