@@ -108,5 +108,6 @@ size_t embed_bwd_scratch_ints(int N, int V);
 hipError_t launch_embed_bwd(const int32_t* ids, const float* dx, float* dwte, int N, int C, int V, int accumulate,
                             int32_t* iscratch, float* partial, hipStream_t s);
 hipError_t launch_to_f32(Dt dt, const void* src, float* dst, size_t n, hipStream_t s);
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);
 
 }  // namespace ncgpt

@@ -724,6 +724,21 @@ hipError_t launch_embed_bwd(const int32_t* ids, const float* dx, float* dwte, in
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ zero fill
+// Clears n 32-bit words with ordinary stores (a kernel rather than a memset node, so
+// that a caller may capture the call in a HIP graph).
+__global__ void __launch_bounds__(256) zero_u32_kernel(uint32_t* __restrict__ p, size_t n)
+{
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ probe helper
 template <typename T>
 __global__ void __launch_bounds__(256) to_f32_kernel(const T* __restrict__ src, float* __restrict__ dst, size_t n)

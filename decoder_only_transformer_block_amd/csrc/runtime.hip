@@ -1,9 +1,11 @@
 // Host runtime behind include/ncgpt.h: shape validation, the workspace plan,
 // and the launch sequence of one forward / loss / backward on the bound stream.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -54,6 +56,7 @@ struct ncgpt_ctx {
     size_t ws_bytes = 0;
     hipStream_t stream = nullptr;
     bool bound = false;
+    int static_dev = -1;  // device whose static scratch holds the workspace (ncgpt_bind_static), else -1
     const int32_t* ids = nullptr;
     const float* params = nullptr;
     const int32_t* targets = nullptr;
@@ -67,6 +70,21 @@ struct ncgpt_ctx {
     template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
     size_t lay(int l, size_t o) const { return pl.layer0 + (size_t)l * pl.layer_stride + o; }
 };
+
+// ---------------------------------------------------------------- static scratch (ncgpt_bind_static)
+// A workspace that lives in the library itself, for callers that cannot allocate device memory.  Each GPU
+// the library runs on holds its own copy of the array until the process ends.  In host code `scratch` is
+// only a host-side stand-in for the symbol: its device address on a device comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only that address is used.
+static constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];                        // device address of `scratch`, per device
+std::atomic<const ncgpt_ctx*> g_scratch_owner[kMaxDevices];  // context last bound to that device's array
+}  // namespace
 
 namespace {
 
@@ -320,6 +338,45 @@ const void* weight(ncgpt_ctx* c, int layer, int which) {
     return c->params + off;
 }
 
+// Attach a workspace and stream: upload the RoPE tables, clear the device error flag (a kernel, not a
+// memset node), reset the call-order state.
+ncgpt_status bind_common(ncgpt_ctx* c, uint8_t* ws, size_t bytes, void* stream) {
+    c->ws = ws;
+    c->ws_bytes = bytes;
+    c->stream = static_cast<hipStream_t>(stream);
+    c->bound = false;
+    hipError_t e = hipMemcpyAsync(c->ws + c->pl.cosv, c->cos_host.data(), c->cos_host.size() * 4,
+                                  hipMemcpyHostToDevice, c->stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(c->ws + c->pl.sinv, c->sin_host.data(), c->sin_host.size() * 4, hipMemcpyHostToDevice,
+                           c->stream);
+    if (e == hipSuccess) e = launch_zero_u32(c->at<uint32_t>(c->pl.flag), 64, c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, "bind uploads");
+    c->bound = true;
+    c->state = 0;
+    return NCGPT_OK;
+}
+
+// A context bound to a device's static scratch gives the array up (when it still owns it).
+void release_static(ncgpt_ctx* c) {
+    if (c->static_dev >= 0) {
+        const ncgpt_ctx* me = c;
+        g_scratch_owner[c->static_dev].compare_exchange_strong(me, nullptr);
+        c->static_dev = -1;
+    }
+}
+
+// Bound, and (for the static scratch) still the array's owner.
+ncgpt_status check_bound(ncgpt_ctx* c) {
+    if (!c->bound) return fail(c, NCGPT_ESTATE, "ncgpt_bind has not been called");
+    if (c->static_dev >= 0 && g_scratch_owner[c->static_dev].load() != c) {
+        c->bound = false;
+        c->state = 0;
+        return fail(c, NCGPT_ESTATE, "another context has been bound to this device's static scratch since");
+    }
+    return NCGPT_OK;
+}
+
 }  // namespace
 
 // ====================================================================== C ABI
@@ -404,24 +461,42 @@ ncgpt_status ncgpt_bind(ncgpt_ctx* c, void* workspace, size_t bytes, void* strea
     if (!workspace) return fail(c, NCGPT_EINVAL, "null workspace");
     if (bytes < c->pl.total) return fail(c, NCGPT_ENOMEM, "workspace smaller than ncgpt_workspace_size");
     if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(c, NCGPT_EINVAL, "workspace not 256-byte aligned");
-    c->ws = static_cast<uint8_t*>(workspace);
-    c->ws_bytes = bytes;
-    c->stream = static_cast<hipStream_t>(stream);
-    hipError_t e = hipMemcpyAsync(c->ws + c->pl.cosv, c->cos_host.data(), c->cos_host.size() * 4,
-                                  hipMemcpyHostToDevice, c->stream);
-    if (e == hipSuccess)
-        e = hipMemcpyAsync(c->ws + c->pl.sinv, c->sin_host.data(), c->sin_host.size() * 4, hipMemcpyHostToDevice,
-                           c->stream);
-    if (e == hipSuccess) e = hipMemsetAsync(c->ws + c->pl.flag, 0, 256, c->stream);
-    if (e != hipSuccess) return hip_fail(c, e, "bind uploads");
-    c->bound = true;
-    c->state = 0;
+    release_static(c);
+    return bind_common(c, static_cast<uint8_t*>(workspace), bytes, stream);
+}
+
+ncgpt_status ncgpt_bind_static(ncgpt_ctx* c, void* stream) {
+    if (!c) return NCGPT_EINVAL;
+    if (c->pl.total > kStaticScratchBytes)
+        return fail(c, NCGPT_ENOMEM, "workspace of " + std::to_string(c->pl.total) + " bytes exceeds the " +
+                                         std::to_string(kStaticScratchBytes) + "-byte static scratch");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(c, e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(c, NCGPT_EUNSUPPORTED, "device index beyond the static scratch table");
+    void* ptr = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        if (!g_scratch_ptr[dev]) {
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return hip_fail(c, e, "hipGetSymbolAddress(scratch)");
+            if (!ptr || (reinterpret_cast<uintptr_t>(ptr) & 255))
+                return fail(c, NCGPT_EHIP, "static scratch has no 256-byte aligned device address");
+            g_scratch_ptr[dev] = ptr;
+        }
+        ptr = g_scratch_ptr[dev];
+    }
+    release_static(c);
+    ncgpt_status st = bind_common(c, static_cast<uint8_t*>(ptr), kStaticScratchBytes, stream);
+    if (st != NCGPT_OK) return st;
+    c->static_dev = dev;
+    g_scratch_owner[dev].store(c);
     return NCGPT_OK;
 }
 
 ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params) {
     if (!c) return NCGPT_EINVAL;
-    if (!c->bound) return fail(c, NCGPT_ESTATE, "ncgpt_bind has not been called");
+    TRY(check_bound(c));
     if (!ids || !params) return fail(c, NCGPT_EINVAL, "null ids or params");
     c->ids = ids;
     c->params = params;
@@ -522,6 +597,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
 
 ncgpt_status ncgpt_loss(ncgpt_ctx* c, const int32_t* targets, float* loss) {
     if (!c) return NCGPT_EINVAL;
+    TRY(check_bound(c));
     if (c->state < 1) return fail(c, NCGPT_ESTATE, "ncgpt_loss before ncgpt_forward");
     if (!targets || !loss) return fail(c, NCGPT_EINVAL, "null targets or loss");
     const Plan& p = c->pl;
@@ -542,6 +618,7 @@ ncgpt_status ncgpt_loss(ncgpt_ctx* c, const int32_t* targets, float* loss) {
 
 ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float grad_scale) {
     if (!c) return NCGPT_EINVAL;
+    TRY(check_bound(c));
     if (c->state != 2) return fail(c, NCGPT_ESTATE, "ncgpt_backward needs ncgpt_loss after the last ncgpt_forward");
     if (!grads) return fail(c, NCGPT_EINVAL, "null grads");
     const Plan& p = c->pl;
@@ -667,7 +744,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
 
 ncgpt_status ncgpt_check(ncgpt_ctx* c) {
     if (!c) return NCGPT_EINVAL;
-    if (!c->bound) return fail(c, NCGPT_ESTATE, "ncgpt_bind has not been called");
+    TRY(check_bound(c));
     hipError_t e = hipStreamSynchronize(c->stream);
     if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
     uint32_t flag = 0;
@@ -700,6 +777,7 @@ ncgpt_status ncgpt_probe_numel(const ncgpt_ctx* c, int what, size_t* numel) {
 
 ncgpt_status ncgpt_probe(ncgpt_ctx* c, int what, int layer, float* dst) {
     if (!c || !dst) return NCGPT_EINVAL;
+    TRY(check_bound(c));
     size_t n;
     if (ncgpt_probe_numel(c, what, &n) != NCGPT_OK) return fail(c, NCGPT_EINVAL, "unknown probe");
     const bool per_layer = what >= 1 && what <= 6;
@@ -766,6 +844,7 @@ const char* ncgpt_last_error(const ncgpt_ctx* c) { return c ? c->err.c_str() : "
 
 void ncgpt_destroy(ncgpt_ctx* c) {
     if (!c) return;
+    release_static(c);
     for (auto& t : c->pending) {
         (void)hipEventDestroy(t.a);
         (void)hipEventDestroy(t.b);

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libncgpt.so")
 
 OK, EINVAL, EUNSUPPORTED, ENOMEM, EHIP, ESTATE, EDEVICE = 0, -1, -2, -3, -4, -5, -6
 F32, BF16 = 0, 1
+STATIC_SCRATCH_BYTES = 64 << 20   # NCGPT_STATIC_SCRATCH_BYTES
 _STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "ENOMEM", -4: "EHIP", -5: "ESTATE", -6: "EDEVICE"}
 
 # probe ids (ncgpt_probe)
@@ -65,6 +66,7 @@ class Config:
 _lib = None
 
 EXPORTS = ["ncgpt_num_params", "ncgpt_param_slice", "ncgpt_create", "ncgpt_workspace_size", "ncgpt_bind",
+           "ncgpt_bind_static",
            "ncgpt_forward", "ncgpt_loss", "ncgpt_backward", "ncgpt_check", "ncgpt_probe_numel", "ncgpt_probe",
            "ncgpt_timing_enable", "ncgpt_timing_reset", "ncgpt_timing_count", "ncgpt_timing_get",
            "ncgpt_last_error", "ncgpt_destroy"]
@@ -85,6 +87,7 @@ def lib():
         L.ncgpt_create.argtypes = [P(_Config), ct.c_int, P(vp)]
         L.ncgpt_workspace_size.argtypes = [vp, P(ct.c_size_t)]
         L.ncgpt_bind.argtypes = [vp, vp, ct.c_size_t, vp]
+        L.ncgpt_bind_static.argtypes = [vp, vp]
         L.ncgpt_forward.argtypes = [vp, vp, vp]
         L.ncgpt_loss.argtypes = [vp, vp, vp]
         L.ncgpt_backward.argtypes = [vp, vp, ct.c_int, ct.c_float]
@@ -130,9 +133,12 @@ def _ptr(t: torch.Tensor, dtype, numel, name):
 class Model:
     """One context of the library bound to a workspace and a stream.
 
-    dtype: "bf16" (bf16 compute, fp32 master weights) or "f32"."""
+    dtype: "bf16" (bf16 compute, fp32 master weights) or "f32".
+    static_scratch: bind to the library's own per-GPU scratch array (ncgpt_bind_static) instead of a
+    workspace allocated here; only workspaces up to STATIC_SCRATCH_BYTES fit."""
 
-    def __init__(self, cfg: Config, dtype: str = "bf16", stream: torch.cuda.Stream = None):
+    def __init__(self, cfg: Config, dtype: str = "bf16", stream: torch.cuda.Stream = None,
+                 static_scratch: bool = False):
         self.cfg = cfg
         self.dtype = {"bf16": BF16, "f32": F32}[dtype]
         self._ctx = ct.c_void_p()
@@ -145,9 +151,13 @@ class Model:
         self._check(lib().ncgpt_workspace_size(self._ctx, ct.byref(nbytes)))
         self.workspace_bytes = nbytes.value
         self.stream = stream if stream is not None else torch.cuda.current_stream()
-        self.workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device="cuda")
-        self._check(lib().ncgpt_bind(self._ctx, ct.c_void_p(self.workspace.data_ptr()), self.workspace_bytes,
-                                     ct.c_void_p(self.stream.cuda_stream)))
+        if static_scratch:
+            self.workspace = None
+            self._check(lib().ncgpt_bind_static(self._ctx, ct.c_void_p(self.stream.cuda_stream)))
+        else:
+            self.workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device="cuda")
+            self._check(lib().ncgpt_bind(self._ctx, ct.c_void_p(self.workspace.data_ptr()), self.workspace_bytes,
+                                         ct.c_void_p(self.stream.cuda_stream)))
         self._keep = {}
 
     def _check(self, st):

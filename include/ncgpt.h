@@ -89,6 +89,20 @@ ncgpt_status ncgpt_workspace_size(const ncgpt_ctx* ctx, size_t* bytes);
  * tables and clears the device error flag (asynchronously on that stream).  May be called again to rebind. */
 ncgpt_status ncgpt_bind(ncgpt_ctx* ctx, void* workspace, size_t bytes, void* hip_stream);
 
+/* Variant of ncgpt_bind for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the workspace is a file-scope device array
+ * inside the library, 64 MiB (NCGPT_STATIC_SCRATCH_BYTES) on each GPU it runs on, held until the process
+ * ends.  Binds ctx to that array on the device current at the call (the stream must belong to it) and
+ * allocates nothing: no hipMalloc, no hipFree, no allocating library routine.  The caller still passes
+ * ids, params, targets, loss and grads to the other calls.  Returns NCGPT_ENOMEM, with a message naming
+ * both sizes, when ncgpt_workspace_size exceeds the array; nothing is bound then.
+ * One array per GPU is shared by every context bound to it and keeps the last call's contents (the
+ * error flag is cleared here).  Binding a second context to it takes the array over: the first context's
+ * later calls return NCGPT_ESTATE until it is bound again.  Calls of contexts bound to the same GPU's
+ * array that overlap in time (other threads or streams) race on its contents. */
+#define NCGPT_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+ncgpt_status ncgpt_bind_static(ncgpt_ctx* ctx, void* hip_stream);
+
 /* Forward pass.  ids: int32 [batch*seq_len] (row b*seq_len + t).  params: fp32 [P] packed as above.
  * Both must stay valid and unmodified until ncgpt_backward has been enqueued: the context remembers them. */
 ncgpt_status ncgpt_forward(ncgpt_ctx* ctx, const int32_t* ids, const float* params);
