@@ -115,6 +115,8 @@ def main():
     ap.add_argument("--workload", default="d12")
     ap.add_argument("--dtype", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lm-head", choices=["stored", "recomputed"], default="stored",
+                    help="where the backward's dz comes from: stored logits (default) or a second LM-head GEMM")
     ap.add_argument("--kernels", action="store_true", help="print the per-kernel table to stderr")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -131,6 +133,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     m = ncgpt.Model(cfg, dtype)
+    if args.lm_head == "recomputed":
+        m.set_lm_head_mode(ncgpt.LOGITS_RECOMPUTED)
     ids, tg = split_stream(token_stream(w.vocab_size, w.batch, w.seq_len, w.tokens, 1))
     ids_d = torch.from_numpy(ids.reshape(-1)).to(dev)
     tg_d = torch.from_numpy(tg.reshape(-1)).to(dev)

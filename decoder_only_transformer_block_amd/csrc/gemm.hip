@@ -153,44 +153,64 @@ struct ESplitK {
     __device__ void put8(int, int, int, const float (&)[8]) const {}
 };
 
+// The 8 consecutive columns n0w + 32 j + 16 p + 8 (lane >> 5) + 0..7 of row block i for this lane: the
+// registers of column groups 2p and 2p+1 trade halves between lanes l and l + 32.
+template <int FM, int FN>
+__device__ __forceinline__ void wide8(const f32x16 (&acc)[FM][FN], int i, int j, int p, float (&v)[8]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][j][8 * p + e]),
+                                                        __float_as_uint(acc[i][j][8 * p + 4 + e]), false, false);
+        v[e] = __uint_as_float(r[0]);
+        v[4 + e] = __uint_as_float(r[1]);
+    }
+}
+
 // Epilogue of an MFMA wave tile: FM x FN accumulators of 32 x 32 (operand-swapped
 // layout: lane l holds row l % 32 and, in registers 4g..4g+3, columns
 // 8g + 4(l / 32) + 0..3).  m0, n0: the wave tile's first row and column.
-template <int FM, int FN, class E>
+// RG: row blocks whose epilogue inputs are fetched together (FM by default; the
+// persistent kernels, which keep more registers live, fetch half as many at once).
+template <int FM, int FN, class E, int RG = FM>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], int m0, int n0, int split, int M, int N,
                                            int lane, const E& epi) {
     const int h = lane >> 5, l32 = lane & 31;
     if constexpr (E::kWide && E::kLoads) {
-        // epilogues that read a tensor: issue every load of the wave tile first, so the
-        // tile waits for memory once instead of once per column group
-        bf16x8 in[FM][FN][2];
+        // epilogues that read a tensor: issue every load of RG row blocks first, so the
+        // tile waits for memory once per group instead of once per column group
+        static_assert(FM % RG == 0, "row groups must divide the row blocks");
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int i0 = 0; i0 < FM; i0 += RG) {
+            bf16x8 in[RG][FN][2];
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
+            for (int ii = 0; ii < RG; ++ii)
 #pragma unroll
-                for (int p = 0; p < 2; ++p) {
-                    const int m = m0 + 32 * i + l32, n = n0 + 32 * j + 16 * p + 8 * h;
-                    if (m < M && n < N) in[i][j][p] = epi.fetch8(m, n);
-                }
+                for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int p = 0; p < 2; ++p) {
-                    float v[8];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][j][8 * p + e]),
-                                                                        __float_as_uint(acc[i][j][8 * p + 4 + e]),
-                                                                        false, false);
-                        v[e] = __uint_as_float(r[0]);
-                        v[4 + e] = __uint_as_float(r[1]);
+                    for (int p = 0; p < 2; ++p) {
+                        const int m = m0 + 32 * (i0 + ii) + l32, n = n0 + 32 * j + 16 * p + 8 * h;
+                        if (m < M && n < N) in[ii][j][p] = epi.fetch8(m, n);
                     }
-                    const int m = m0 + 32 * i + l32, n = n0 + 32 * j + 16 * p + 8 * h;
-                    if (m < M && n < N) epi.put8(m, n, split, v, in[i][j][p]);
-                }
+#pragma unroll
+            for (int ii = 0; ii < RG; ++ii)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) {
+                        const int i = i0 + ii;
+                        float v[8];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][j][8 * p + e]),
+                                                                            __float_as_uint(acc[i][j][8 * p + 4 + e]),
+                                                                            false, false);
+                            v[e] = __uint_as_float(r[0]);
+                            v[4 + e] = __uint_as_float(r[1]);
+                        }
+                        const int m = m0 + 32 * i + l32, n = n0 + 32 * j + 16 * p + 8 * h;
+                        if (m < M && n < N) epi.put8(m, n, split, v, in[ii][j][p]);
+                    }
+        }
         return;
     }
 #pragma unroll
@@ -228,6 +248,175 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], int m0, 
             }
         }
     }
+}
+
+// ------------------------------------------------------------------ LM-head epilogues (bf16)
+// The cross-entropy needs, per row of logits z, lse = log sum exp z and z[target].  The LM-head GEMM
+// forms them from its accumulators, so no pass over the [N, V] logits is needed for the loss: per row and
+// per wave column block (32 FN columns), the max of z log2(e) and the sum of 2^(z log2(e) - max), and the
+// logit at the row's target when the block holds it.  Statistics use the bf16-rounded logits, the values
+// the backward turns into dz, so loss and gradient see the same logits (the shift is the max of the
+// unrounded values: any shift near the max keeps the sum in range, and the merge is exact for any shift).
+constexpr float kLog2eF = 1.4426950408889634f;
+
+__device__ __forceinline__ float rnd_bf16(float v) { return (float)(bf16)v; }
+
+// Max and sum over lanes l and l ^ 32 (the two halves of one accumulator row).  The swap leaves lanes
+// 0..31 with (own, partner) and lanes 32..63 with (partner, own); both orders give the same result.
+__device__ __forceinline__ float pair_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Detects epilogues that take the whole wave tile (kTile) instead of per-element stores.
+template <class E, class = void> struct TileEpi : std::false_type {};
+template <class E> struct TileEpi<E, std::void_t<decltype(E::kTile)>> : std::bool_constant<E::kTile> {};
+
+// Round the 16 accumulators of one 32x32 block to bf16 and back (v_cvt_pk_bf16_f32 rounds two at once).
+__device__ __forceinline__ void round16(const f32x16& a, float (&z)[16]) {
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+        typedef float f32x2_t __attribute__((ext_vector_type(2)));
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        const f32x2_t f = {a[r], a[r + 1]};
+        const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+        z[r] = __uint_as_float(u << 16);
+        z[r + 1] = __uint_as_float(u & 0xffff0000u);
+    }
+}
+
+struct ECeStats {
+    static constexpr bool kTile = true;
+    bf16* out;               // [M][ldo] rounded logits, or null (not stored)
+    int ldo;
+    float2* part;            // [nblk][M]: a wave's 32 rows of one block are 256 contiguous bytes
+    int nblk;
+    float* zt;               // [M]
+    const int32_t* targets;  // [M]
+
+    template <int FM, int FN>
+    __device__ void tile(const f32x16 (&acc)[FM][FN], int m0, int n0, int M, int N, int lane) const {
+        const int h = lane >> 5, l32 = lane & 31;
+        // the rounded logits leave first, so their stores drain while the statistics are formed
+        if (out) store_tile<FM, FN>(acc, m0, n0, 0, M, N, lane, EStoreCd<bf16>{out, ldo});
+        if (n0 >= N) return;                      // wave-uniform: the block lies past a ragged vocab edge
+        const bool full = n0 + 32 * FN <= N;      // wave-uniform: no column of the block is past the edge
+        const int blk = n0 / (32 * FN);
+        int tv[FM];  // every row's target, fetched before any is needed (one memory wait per tile)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) tv[i] = m0 + 32 * i + l32 < M ? targets[m0 + 32 * i + l32] : -1;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = m0 + 32 * i + l32;
+            float z[FN][16];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) round16(acc[i][j], z[j]);
+            if (!full) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (n0 + 32 * j + 8 * (r >> 2) + 4 * h + (r & 3) >= N) z[j][r] = -INFINITY;
+            }
+            float mx = z[0][0];
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, z[j][r]);
+            mx = pair_max(mx) * kLog2eF;
+            float sum = 0.0f;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(z[j][r] * kLog2eF - mx);
+            sum = pair_sum(sum);
+            if (m < M && h == 0) part[(size_t)blk * M + m] = make_float2(mx, sum);
+            // the target logit: only a lane whose half-row holds the target column takes this branch
+            // (rare: the block is 32 FN of the vocab's columns)
+            const int c = tv[i] - n0;
+            if (c >= 0 && c < 32 * FN && ((c >> 2) & 1) == h && m < M) {
+                float v = 0.0f;
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (c == 32 * j + 8 * (r >> 2) + 4 * h + (r & 3)) v = z[j][r];
+                zt[m] = v;
+            }
+        }
+    }
+};
+
+// dz = grad_scale * inv_valid * (softmax(z) - onehot(target)) from recomputed logits, rounded to bf16
+// first exactly as the stored logits are, so the result equals the stored-logit backward's.
+struct EDz {
+    static constexpr bool kTile = true;
+    bf16* out;
+    int ldo;
+    const float* lse;
+    const int32_t* targets;
+    const float* inv_valid;
+    float grad_scale;
+
+    template <int FM, int FN>
+    __device__ void tile(const f32x16 (&acc)[FM][FN], int m0, int n0, int M, int N, int lane) const {
+        const int h = lane >> 5, l32 = lane & 31;
+        // every row's target and log2-domain lse first (one memory wait per tile)
+        int tv[FM];
+        float l2v[FM];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = m0 + 32 * i + l32;
+            tv[i] = m < M ? targets[m] : -1;
+            l2v[i] = m < M ? lse[m] : 0.0f;
+        }
+        const float kv = grad_scale * (*inv_valid);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = m0 + 32 * i + l32, t = tv[i];
+            const bool valid = t >= 0 && t < N;
+            const float k = valid ? kv : 0.0f, l2 = valid ? l2v[i] * kLog2eF : 0.0f;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    float v[8];
+                    wide8<FM, FN>(acc, i, j, p, v);
+                    const int n = n0 + 32 * j + 16 * p + 8 * h;
+                    float z[8];
+#pragma unroll
+                    for (int e = 0; e < 8; e += 2) {
+                        typedef float f32x2_t __attribute__((ext_vector_type(2)));
+                        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+                        const f32x2_t f = {v[e], v[e + 1]};
+                        const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+                        z[e] = __uint_as_float(u << 16);
+                        z[e + 1] = __uint_as_float(u & 0xffff0000u);
+                    }
+                    float r[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) r[e] = valid ? k * __builtin_amdgcn_exp2f(z[e] * kLog2eF - l2) : 0.0f;
+                    // the target column (rare): k (p - 1) instead of k p, the same expression as ce_bwd's
+                    if (t >= n && t < n + 8) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (n + e == t) r[e] = k * (__builtin_amdgcn_exp2f(z[e] * kLog2eF - l2) - 1.0f);
+                    }
+                    if (m < M && n < N) st8(out + (size_t)m * ldo + n, r);
+                }
+        }
+    }
+};
+
+template <int FM, int FN, class E, int RG = FM>
+__device__ __forceinline__ void epilogue(const f32x16 (&acc)[FM][FN], int m0, int n0, int split, int M, int N,
+                                         int lane, const E& epi) {
+    if constexpr (TileEpi<E>::value) epi.template tile<FM, FN>(acc, m0, n0, M, N, lane);
+    else store_tile<FM, FN, E, RG>(acc, m0, n0, split, M, N, lane, epi);
 }
 
 // ------------------------------------------------------------------ tile order
@@ -459,7 +648,7 @@ gemm_bf16_mfma_ring(const bf16* __restrict__ A, const bf16* __restrict__ B, int 
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the loads past the end before the stores
 
-    store_tile<FM, FN>(acc, m0 + wm * WM, n0 + wn * WN, split, M, N, lane, epi);
+    epilogue<FM, FN>(acc, m0 + wm * WM, n0 + wn * WN, split, M, N, lane, epi);
 }
 
 // ------------------------------------------------------------------ persistent four-stage ring
@@ -593,7 +782,8 @@ gemm_bf16_mfma_pring(const bf16* __restrict__ A, const bf16* __restrict__ B, int
             stage(kt + 2, sA2, sB2, sA3, sB3, sA1, sB1);
             stage(kt + 3, sA3, sB3, sA0, sB0, sA2, sB2);
         }
-        store_tile<FM, FN>(acc, cur.m0 + wm * WM, cur.n0 + wn * WN, cur.split, M, N, lane, epi);
+        epilogue<FM, FN, E, (FM >= 2 ? FM / 2 : FM)>(acc, cur.m0 + wm * WM, cur.n0 + wn * WN, cur.split, M, N,
+                                                    lane, epi);
         cur = nxt;
         nxt = item(r + 2);
     }
@@ -731,6 +921,14 @@ static hipError_t dispatch_epi(const GemmDesc& d, hipStream_t s) {
         case Epi::StoreCd: return run(EStoreCd<T>{(T*)d.out, d.ldo});
         case Epi::ResidualCd: return run(EResidual<T>{(T*)d.out, (const T*)d.in, d.ldo});
         case Epi::ReluSq: return run(EReluSq<T>{(T*)d.out, d.ldo});
+        case Epi::CeStats:
+            if constexpr (sizeof(T) == 2)
+                return run(ECeStats{(bf16*)d.out, d.ldo, (float2*)d.part, d.nblk, d.zt, d.targets});
+            break;
+        case Epi::Dz:
+            if constexpr (sizeof(T) == 2)
+                return run(EDz{(bf16*)d.out, d.ldo, d.lse, d.targets, d.inv_valid, d.grad_scale});
+            break;
         default: break;
         }
     } else if constexpr (AK && !BK) {
@@ -768,6 +966,12 @@ hipError_t launch_gemm(const GemmDesc& in, hipStream_t s) {
     if (d.epi != Epi::SplitK && d.k_split < d.K) return hipErrorInvalidValue;  // only SplitK writes partials
     if (d.dt == Dt::BF16) return dispatch_layout<bf16>(d, s);
     return dispatch_layout<float>(d, s);
+}
+
+int gemm_wave_cols(const GemmDesc& d) {
+    static const int bn[3] = {256, 128, 128};
+    const int t = d.tile < 0 ? 0 : (d.tile > 2 ? 2 : d.tile);
+    return bn[t] / (d.loop == GemmLoop::Persist4 ? 2 : 4);
 }
 
 const char* gemm_kernel_name(const GemmDesc& d) {

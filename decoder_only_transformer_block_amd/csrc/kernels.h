@@ -26,6 +26,10 @@ enum class Epi : int {
     ReluSqBwd,   // out[m*ldo+n] = cd(v * 2 * sqrt(in[m*ldo+n]))   (in = saved act; sqrt(act) recovers a to bf16 rounding)
     Grad,        // out(f32) = (accumulate ? out : 0) + v
     SplitK,      // out(f32)[split*split_stride + m*ldo + n] = v
+    CeStats,     // bf16 LM head: per row and wave column block the (max, sum) of the softmax in the log2
+                 // domain (part), the logit at the row's target (zt); the rounded logits too when out != 0
+    Dz,          // bf16 LM head recomputed in the backward: out = bf16(scale (softmax(z) - onehot(target))),
+                 // scale = grad_scale * inv_valid on rows with a valid target, 0 elsewhere
 };
 
 // MFMA main loop (all three stream 32-deep stages straight into a four-stage LDS ring):
@@ -49,12 +53,22 @@ struct GemmDesc {
     int splits = 1;         // split-K: K is cut into ceil(K / k_split) ranges of k_split (grid.y)
     int k_split = 0;        // multiple of 64; 0 = K / splits
     size_t split_stride = 0;
+    // LM-head epilogues (CeStats, Dz)
+    void* part = nullptr;            // float2 [nblk][M]
+    int nblk = 0;                    // column blocks per row = ceil(N / gemm_wave_cols)
+    float* zt = nullptr;             // [M]
+    const int32_t* targets = nullptr;
+    const float* lse = nullptr;      // [M] natural-log LSE (Dz)
+    const float* inv_valid = nullptr;
+    float grad_scale = 1.0f;
     int tile = -1;    // MFMA tile: 0 = 256x256, 1 = 256x128, 2 = 128x128; -1 = chosen from the shape
     int group_m = 4;  // tiles are walked in bands of group_m tile-rows (L2 reuse of the B tiles)
     GemmLoop loop = GemmLoop::Persist8;
 };
 
 const char* gemm_kernel_name(const GemmDesc& d);
+// columns of one wave's share of an output tile (the CeStats column block) for d's tile and loop
+int gemm_wave_cols(const GemmDesc& d);
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
 // grads = (accumulate ? grads : 0) + sum_s part[s]   (n elements, n % 4 == 0)
 hipError_t launch_splitk_reduce(const float* part, int splits, size_t stride, float* grads, size_t n,
@@ -97,6 +111,9 @@ hipError_t launch_rope_qknorm_bwd(Dt dt, void* dqkv, const void* qkv, const floa
                                   hipStream_t s);
 hipError_t launch_ce_fwd_rows(Dt dt, const void* logits, const int32_t* targets, float* lse, float* loss_rows,
                               int N, int V, uint32_t* err, hipStream_t s);
+// lse and per-row loss from the LM-head epilogue's partials (CeStats)
+hipError_t launch_ce_merge(const void* part, int nblk, const float* zt, const int32_t* targets, float* lse,
+                           float* loss_rows, int N, int V, uint32_t* err, hipStream_t s);
 hipError_t launch_loss_reduce(const float* loss_rows, const int32_t* targets, int N, int V, float* loss,
                               float* inv_valid, uint32_t* err, hipStream_t s);
 hipError_t launch_ce_bwd(Dt dt, void* logits, const float* lse, const int32_t* targets, const float* inv_valid,

@@ -473,6 +473,43 @@ hipError_t launch_ce_fwd_rows(Dt dt, const void* logits, const int32_t* targets,
     return hipGetLastError();
 }
 
+// The same lse and per-row loss from the LM-head GEMM's per-block statistics (its CeStats epilogue):
+// part[b][n] = (max of z log2 e over block b of row n, sum of 2^(z log2 e - max)), zt[n] = z[target].
+// One lane per row merges the row's blocks in order with the running (max, sum) rule above; a wave's
+// reads of one block are 512 contiguous bytes.
+__global__ void __launch_bounds__(64)
+ce_merge_kernel(const float2* __restrict__ part, int nblk, const float* __restrict__ zt,
+                const int32_t* __restrict__ targets, float* __restrict__ lse, float* __restrict__ loss_rows, int N,
+                int V, uint32_t* err)
+{
+    constexpr float kLn2 = 0.6931471805599453f;
+    const int n = blockIdx.x * 64 + threadIdx.x;
+    if (n >= N) return;
+    float m = -INFINITY, s = 0.0f;
+#pragma unroll 8
+    for (int b = 0; b < nblk; ++b) {
+        const float2 p = part[(size_t)b * N + n];
+        const float mn = fmaxf(m, p.x);
+        s = (m == -INFINITY ? 0.0f : s * __builtin_amdgcn_exp2f(m - mn)) + p.y * __builtin_amdgcn_exp2f(p.x - mn);
+        m = mn;
+    }
+    const float l = (m + __builtin_amdgcn_logf(s)) * kLn2;
+    lse[n] = l;
+    const int t = targets[n];
+    float lr = 0.0f;
+    if (t >= V) raise_error(err, kErrBadTarget);
+    else if (t >= 0) lr = l - zt[n];
+    loss_rows[n] = lr;
+}
+
+hipError_t launch_ce_merge(const void* part, int nblk, const float* zt, const int32_t* targets, float* lse,
+                           float* loss_rows, int N, int V, uint32_t* err, hipStream_t s) {
+    if (nblk < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(ce_merge_kernel, dim3((N + 63) / 64), dim3(64), 0, s, (const float2*)part, nblk, zt,
+                       targets, lse, loss_rows, N, V, err);
+    return hipGetLastError();
+}
+
 // loss = sum(loss_rows over valid targets) / #valid, in a fixed order (one
 // workgroup); inv_valid = 1/#valid is kept for the backward.  No valid
 // target raises kErrNoTargets and yields loss = NaN, inv_valid = 0.

@@ -24,7 +24,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Plan {
     size_t flag, cosv, sinv, wcast, x0, x, layer0, layer_stride;
     size_t l_xn1, l_rstd1, l_qkv, l_rstdq, l_rstdk, l_y, l_lse, l_xn2, l_rstd2, l_act;
-    size_t xf, rstdf, logits, lse, loss_rows, dxn, dx, dx_cd, dh, dy, dqkv, delta, splitk, iscr, total;
+    size_t xf, rstdf, logits, cepart, zt, lse, loss_rows, dxn, dx, dx_cd, dh, dy, dqkv, delta, splitk, iscr, total;
+    int ce_nblk;
 };
 
 struct Timed {
@@ -57,6 +58,8 @@ struct ncgpt_ctx {
     hipStream_t stream = nullptr;
     bool bound = false;
     int static_dev = -1;  // device whose static scratch holds the workspace (ncgpt_bind_static), else -1
+    int lm_mode = NCGPT_LOGITS_STORED;  // ncgpt_set_lm_head_mode
+    int loss_mode = NCGPT_LOGITS_STORED;  // the mode the last ncgpt_loss ran in
     const int32_t* ids = nullptr;
     const float* params = nullptr;
     const int32_t* targets = nullptr;
@@ -154,6 +157,21 @@ WGrad pick_wgrad(Dt dt, int64_t M, int64_t N, int64_t K) {
     return w;
 }
 
+// The bf16 LM-head GEMM z = xf Wlm^T (tokens x vocab, K = n_embd): its tile, loop and band height are
+// fixed here so that the workspace plan (the CeStats column blocks) and the launches agree.
+GemmDesc lm_head_desc(const ncgpt_ctx* c) {
+    GemmDesc d;
+    d.dt = c->dt;
+    d.lda = (int)c->C; d.ldb = (int)c->C;
+    d.M = (int)c->N; d.N = (int)c->V; d.K = (int)c->C;
+    d.ldo = (int)c->V;
+    d.tile = pick_tile(d.M, d.N);
+    d.group_m = 8;
+    // 32768 tiles at depth 12: the persistent ring measured 0.8 ms faster than one workgroup per tile
+    d.loop = GemmLoop::Persist8;
+    return d;
+}
+
 void make_plan(ncgpt_ctx* c) {
     Plan& p = c->pl;
     size_t off = 0;
@@ -183,6 +201,10 @@ void make_plan(ncgpt_ctx* c) {
     p.xf = A(N * c->C * e);
     p.rstdf = A(N * 4);
     p.logits = A(N * c->V * e);
+    const GemmDesc lm = lm_head_desc(c);
+    p.ce_nblk = (int)((c->V + gemm_wave_cols(lm) - 1) / gemm_wave_cols(lm));
+    p.cepart = A(c->dt == Dt::BF16 ? N * p.ce_nblk * 8 : 0);
+    p.zt = A(N * 4);
     p.lse = A(N * 4);
     p.loss_rows = A(N * 4);
     p.dxn = A(N * c->C * 4);
@@ -265,6 +287,8 @@ const char* epi_name(Epi e) {
     case Epi::ReluSqBwd: return "relusq_bwd";
     case Epi::Grad: return "grad";
     case Epi::SplitK: return "splitk";
+    case Epi::CeStats: return "ce_stats";
+    case Epi::Dz: return "dz";
     }
     return "?";
 }
@@ -289,6 +313,7 @@ ncgpt_status gemm(ncgpt_ctx* c, GemmDesc d, const char* tag) {
     double out = e;
     switch (d.epi) {
     case Epi::ResidualCd: case Epi::ReluSqBwd: out = 2.0 * e; break;
+    case Epi::CeStats: out = (d.out ? e : 0.0) + 8.0 * d.nblk / d.N; break;
     case Epi::Grad: out = d.accumulate ? 8.0 : 4.0; break;
     case Epi::SplitK: out = 4.0 * std::max(1, d.splits); break;
     default: break;
@@ -583,14 +608,6 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
     TRY(launch(c, "rmsnorm_fwd", 0.0, norm_bytes, [&] {
         return launch_rmsnorm_fwd(dt, c->ws + p.x, c->ws + p.xf, c->at<float>(p.rstdf), N, C, eps, c->stream);
     }));
-    {
-        GemmDesc d;
-        d.A = c->ws + p.xf; d.lda = C; d.B = weight(c, -1, 1); d.ldb = C;
-        d.M = N; d.N = V; d.K = C;
-        d.epi = Epi::StoreCd; d.out = c->ws + p.logits; d.ldo = V;
-        d.group_m = 8;
-        TRY(gemm(c, d, "lm_head"));
-    }
     c->state = 1;
     return NCGPT_OK;
 }
@@ -604,15 +621,44 @@ ncgpt_status ncgpt_loss(ncgpt_ctx* c, const int32_t* targets, float* loss) {
     const int N = (int)c->N, V = (int)c->V;
     uint32_t* flag = c->at<uint32_t>(p.flag);
     c->targets = targets;
-    TRY(launch(c, "ce_fwd_rows", 0.0, (double)N * V * c->esz + N * 12.0, [&] {
-        return launch_ce_fwd_rows(c->dt, c->ws + p.logits, targets, c->at<float>(p.lse), c->at<float>(p.loss_rows), N,
-                                  V, flag, c->stream);
-    }));
+    c->state = 1;
+    GemmDesc d = lm_head_desc(c);
+    d.A = c->ws + p.xf; d.B = weight(c, -1, 1);
+    if (c->dt == Dt::BF16) {
+        // logits, their softmax statistics and the target logit in one pass; the logits are stored for the
+        // backward only in the stored-logit mode
+        d.epi = Epi::CeStats;
+        d.out = c->lm_mode == NCGPT_LOGITS_STORED ? (void*)(c->ws + p.logits) : nullptr;
+        d.part = c->ws + p.cepart; d.nblk = p.ce_nblk;
+        d.zt = c->at<float>(p.zt); d.targets = targets;
+        TRY(gemm(c, d, c->lm_mode == NCGPT_LOGITS_STORED ? "lm_head" : "lm_head_nostore"));
+        TRY(launch(c, "ce_merge", 0.0, (double)N * p.ce_nblk * 8 + N * 16.0, [&] {
+            return launch_ce_merge(c->ws + p.cepart, p.ce_nblk, c->at<float>(p.zt), targets, c->at<float>(p.lse),
+                                   c->at<float>(p.loss_rows), N, V, flag, c->stream);
+        }));
+    } else {
+        d.epi = Epi::StoreCd; d.out = c->ws + p.logits;
+        TRY(gemm(c, d, "lm_head"));
+        TRY(launch(c, "ce_fwd_rows", 0.0, (double)N * V * c->esz + N * 12.0, [&] {
+            return launch_ce_fwd_rows(c->dt, c->ws + p.logits, targets, c->at<float>(p.lse), c->at<float>(p.loss_rows),
+                                      N, V, flag, c->stream);
+        }));
+    }
     TRY(launch(c, "loss_reduce", 0.0, N * 8.0, [&] {
         return launch_loss_reduce(c->at<float>(p.loss_rows), targets, N, V, loss, c->at<float>(p.flag + 4), flag,
                                   c->stream);
     }));
+    c->loss_mode = c->dt == Dt::BF16 ? c->lm_mode : NCGPT_LOGITS_STORED;
     c->state = 2;
+    return NCGPT_OK;
+}
+
+ncgpt_status ncgpt_set_lm_head_mode(ncgpt_ctx* c, int mode) {
+    if (!c) return NCGPT_EINVAL;
+    if (mode != NCGPT_LOGITS_STORED && mode != NCGPT_LOGITS_RECOMPUTED) return fail(c, NCGPT_EINVAL, "unknown mode");
+    if (mode == NCGPT_LOGITS_RECOMPUTED && c->dt != Dt::BF16)
+        return fail(c, NCGPT_EUNSUPPORTED, "the recomputed-logit mode is built for the bf16 compute dtype");
+    c->lm_mode = mode;
     return NCGPT_OK;
 }
 
@@ -639,11 +685,21 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
         return grads + off;
     };
 
-    // cross-entropy -> dz (in place over the logits)
-    TRY(launch(c, "ce_bwd", 0.0, (double)N * V * 2 * e, [&] {
-        return launch_ce_bwd(dt, logits, c->at<float>(p.lse), c->targets, c->at<float>(p.flag + 4), grad_scale, N, V,
-                             c->stream);
-    }));
+    if (c->loss_mode == NCGPT_LOGITS_RECOMPUTED) {
+        // the logits again, turned into dz by the GEMM's epilogue (nothing was stored by ncgpt_loss)
+        GemmDesc d = lm_head_desc(c);
+        d.A = c->ws + p.xf; d.B = weight(c, -1, 1);
+        d.epi = Epi::Dz; d.out = logits;
+        d.lse = c->at<float>(p.lse); d.targets = c->targets; d.inv_valid = c->at<float>(p.flag + 4);
+        d.grad_scale = grad_scale;
+        TRY(gemm(c, d, "lm_head_dz"));
+    } else {
+        // cross-entropy -> dz (in place over the logits)
+        TRY(launch(c, "ce_bwd", 0.0, (double)N * V * 2 * e, [&] {
+            return launch_ce_bwd(dt, logits, c->at<float>(p.lse), c->targets, c->at<float>(p.flag + 4), grad_scale, N,
+                                 V, c->stream);
+        }));
+    }
     {   // dxf = dz Wlm
         GemmDesc d;
         d.A = logits; d.lda = V; d.B = weight(c, -1, 1); d.ldb = C; d.b_kcontig = false;

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libncgpt.so")
 OK, EINVAL, EUNSUPPORTED, ENOMEM, EHIP, ESTATE, EDEVICE = 0, -1, -2, -3, -4, -5, -6
 F32, BF16 = 0, 1
 STATIC_SCRATCH_BYTES = 64 << 20   # NCGPT_STATIC_SCRATCH_BYTES
+LOGITS_STORED, LOGITS_RECOMPUTED = 0, 1
 _STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "ENOMEM", -4: "EHIP", -5: "ESTATE", -6: "EDEVICE"}
 
 # probe ids (ncgpt_probe)
@@ -66,7 +67,7 @@ class Config:
 _lib = None
 
 EXPORTS = ["ncgpt_num_params", "ncgpt_param_slice", "ncgpt_create", "ncgpt_workspace_size", "ncgpt_bind",
-           "ncgpt_bind_static",
+           "ncgpt_bind_static", "ncgpt_set_lm_head_mode",
            "ncgpt_forward", "ncgpt_loss", "ncgpt_backward", "ncgpt_check", "ncgpt_probe_numel", "ncgpt_probe",
            "ncgpt_timing_enable", "ncgpt_timing_reset", "ncgpt_timing_count", "ncgpt_timing_get",
            "ncgpt_last_error", "ncgpt_destroy"]
@@ -88,6 +89,7 @@ def lib():
         L.ncgpt_workspace_size.argtypes = [vp, P(ct.c_size_t)]
         L.ncgpt_bind.argtypes = [vp, vp, ct.c_size_t, vp]
         L.ncgpt_bind_static.argtypes = [vp, vp]
+        L.ncgpt_set_lm_head_mode.argtypes = [vp, ct.c_int]
         L.ncgpt_forward.argtypes = [vp, vp, vp]
         L.ncgpt_loss.argtypes = [vp, vp, vp]
         L.ncgpt_backward.argtypes = [vp, vp, ct.c_int, ct.c_float]
@@ -183,6 +185,10 @@ class Model:
     def backward(self, grads: torch.Tensor, accumulate: bool = False, grad_scale: float = 1.0):
         pg = _ptr(grads, torch.float32, self.n_params, "grads")
         self._check(lib().ncgpt_backward(self._ctx, pg, 1 if accumulate else 0, float(grad_scale)))
+
+    def set_lm_head_mode(self, mode: int):
+        """LOGITS_STORED (default) or LOGITS_RECOMPUTED: where the backward's dz comes from."""
+        self._check(lib().ncgpt_set_lm_head_mode(self._ctx, int(mode)))
 
     def check(self):
         self._check(lib().ncgpt_check(self._ctx))

@@ -103,18 +103,33 @@ ncgpt_status ncgpt_bind(ncgpt_ctx* ctx, void* workspace, size_t bytes, void* hip
 #define NCGPT_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
 ncgpt_status ncgpt_bind_static(ncgpt_ctx* ctx, void* hip_stream);
 
-/* Forward pass.  ids: int32 [batch*seq_len] (row b*seq_len + t).  params: fp32 [P] packed as above.
+/* Forward pass of the block stack up to the final RMSNorm (the LM head runs in ncgpt_loss, where the
+ * targets are known).  ids: int32 [batch*seq_len] (row b*seq_len + t).  params: fp32 [P] packed as above.
  * Both must stay valid and unmodified until ncgpt_backward has been enqueued: the context remembers them. */
 ncgpt_status ncgpt_forward(ncgpt_ctx* ctx, const int32_t* ids, const float* params);
 
-/* Cross-entropy of the last forward's logits.  targets: int32 [batch*seq_len]; a negative target is
- * ignored.  loss: fp32 [1], receives the mean over valid targets (NaN if none, with the device flag set).
- * targets must stay valid until ncgpt_backward has been enqueued.  ESTATE before ncgpt_forward. */
+/* LM head and cross-entropy of the last forward ("nanochat 项目深度分析" §2.1 item 3, §2.3; woshipm.com §三
+ * item 1).  targets: int32 [batch*seq_len]; a negative target is ignored.  loss: fp32 [1], receives the mean
+ * over valid targets of logsumexp(z) - z[target] (NaN if none, with the device flag set; a target >= vocab
+ * also sets the flag).  In NCGPT_BF16 the LM-head GEMM's epilogue forms each row's softmax statistics and
+ * target logit from its accumulators, so no pass over the [N, vocab] logits is needed for the loss; the
+ * logits are kept for the backward only in NCGPT_LOGITS_STORED mode.  targets must stay valid until
+ * ncgpt_backward has been enqueued.  ESTATE before ncgpt_forward. */
 ncgpt_status ncgpt_loss(ncgpt_ctx* ctx, const int32_t* targets, float* loss);
+
+/* Where the backward's dz = softmax(z) - onehot(target) comes from (NCGPT_BF16 only; takes effect at the
+ * next ncgpt_loss):
+ *   NCGPT_LOGITS_STORED      ncgpt_loss stores the bf16 logits; ncgpt_backward turns them into dz in place
+ *                            (one read + one write of [N, vocab]).  The default.
+ *   NCGPT_LOGITS_RECOMPUTED  ncgpt_loss stores no logits; ncgpt_backward recomputes them with the LM-head
+ *                            GEMM, whose epilogue writes dz directly (one more GEMM, no logit read).
+ * Both give bitwise identical results.  EINVAL for another value, EUNSUPPORTED for RECOMPUTED in NCGPT_F32. */
+typedef enum { NCGPT_LOGITS_STORED = 0, NCGPT_LOGITS_RECOMPUTED = 1 } ncgpt_lm_head_mode;
+ncgpt_status ncgpt_set_lm_head_mode(ncgpt_ctx* ctx, int mode);
 
 /* Backward of the last loss.  grads: fp32 [P] receives grad_scale * d loss / d params (accumulate = 0) or
  * has it added (accumulate = 1).  For k micro-batches of gradient accumulation pass grad_scale = 1/k and
- * accumulate = 1 after the first ("nanochat 项目深度分析" §4.3).  The logits in the workspace are consumed.
+ * accumulate = 1 after the first ("nanochat 项目深度分析" §4.3).  The stored logits (if any) are consumed.
  * ESTATE unless ncgpt_loss followed the last ncgpt_forward. */
 ncgpt_status ncgpt_backward(ncgpt_ctx* ctx, float* grads, int accumulate, float grad_scale);
 

@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = ncgpt.lib()
     names = declared_functions()
-    assert len(names) >= 18
+    assert len(names) >= 19
     for n in names:
         assert hasattr(L, n), n
     assert sorted(ncgpt.EXPORTS) == names
@@ -93,6 +93,21 @@ def test_create_validates_shapes_and_plans_workspace():
         assert not ctx.value
     st, _ = create(base, 7)
     assert st == ncgpt.EINVAL
+
+
+def test_lm_head_mode_validation():
+    L = ncgpt.lib()
+    cfg = ncgpt.Config.from_workload(WORKLOADS["tiny"])
+    st, ctx = create(cfg, ncgpt.F32)
+    assert st == ncgpt.OK
+    assert L.ncgpt_set_lm_head_mode(ctx, ncgpt.LOGITS_STORED) == ncgpt.OK
+    assert L.ncgpt_set_lm_head_mode(ctx, ncgpt.LOGITS_RECOMPUTED) == ncgpt.EUNSUPPORTED  # bf16 only
+    assert L.ncgpt_set_lm_head_mode(ctx, 2) == ncgpt.EINVAL
+    L.ncgpt_destroy(ctx)
+    st, ctx = create(ncgpt.Config.from_workload(WORKLOADS["small"]), ncgpt.BF16)
+    assert L.ncgpt_set_lm_head_mode(ctx, ncgpt.LOGITS_RECOMPUTED) == ncgpt.OK
+    assert L.ncgpt_set_lm_head_mode(None, 0) == ncgpt.EINVAL
+    L.ncgpt_destroy(ctx)
 
 
 def test_null_arguments_are_rejected():

@@ -167,6 +167,32 @@ def test_gradient_accumulation(dtype):
             assert cosine(a, b) >= 0.9999, name
 
 
+@pytest.mark.parametrize("name", ["small", "gqa3", "d12"])
+def test_lm_head_modes_bitwise_equal(name):
+    """The recomputed-logit backward (no logits stored by the loss; the LM-head GEMM runs again and its
+    epilogue writes dz) gives bitwise the stored-logit backward's loss, per-token losses and gradients:
+    both round the same fp32 accumulators to bf16 before the softmax.  gqa3 has a ragged last vocab tile
+    (4160 = 32 x 130 columns); d12 is the benchmark step."""
+    w = GQA3 if name == "gqa3" else WORKLOADS[name]
+    ids, tg, params = make_inputs(w)
+    tg = tg.copy()
+    tg[0, ::5] = -1
+    out = []
+    for mode in (ncgpt.LOGITS_STORED, ncgpt.LOGITS_RECOMPUTED):
+        s = GpuStep(w, "bf16", ids, params)
+        s.m.set_lm_head_mode(mode)
+        loss, st = s.run(tg)
+        assert st == ncgpt.OK
+        out.append((loss, s.probe("loss_rows"), s.probe("lse"), s.grads_np()))
+        del s
+        torch.cuda.empty_cache()
+    (l0, r0, e0, g0), (l1, r1, e1, g1) = out
+    say(f"  loss stored {l0:.7f} recomputed {l1:.7f}")
+    assert l0 == l1
+    assert np.array_equal(r0, r1) and np.array_equal(e0, e1)
+    assert np.array_equal(g0, g1)
+
+
 # Gradient parity at the widths and sequence lengths the benchmark runs, with the batch cut so the oracle
 # finishes in about a minute: depth 12 at T = 2048 (long-sequence attention tiles, split-K weight gradients
 # over 4096 tokens, the persistent GEMM rings walking several items per workgroup); depth 20 (GQA 2:1,
