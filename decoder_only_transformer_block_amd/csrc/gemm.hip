@@ -412,6 +412,97 @@ struct EDz {
     }
 };
 
+// ------------------------------------------------------------------ qkv epilogue: RoPE + QK-norm (bf16)
+// The qkv projection's output leaves already rotated and normalised ("nanochat 项目深度分析" §2.1 items 1-2):
+// for token m (position t = m mod T) and each q or k head, pair (i, i + 64) is rotated by the angle of
+// (t, i) as y_i = x_i cos + x_{i+64} sin, y_{i+64} = -x_i sin + x_{i+64} cos, and the head is divided by
+// its RMS, sqrt(mean(y^2) + eps).  The rotation preserves each pair's norm, so the RMS is taken from the
+// unrotated accumulators (equal up to rounding).  The head is rounded to bf16 once, at the store; 1/rms
+// is saved for the backward.  With the 4 x 2 wave grid a wave owns 128 columns = one head, and in the
+// accumulator layout the pair (i, i + 64) sits in one lane (column blocks j and j + 2), so everything is
+// lane-local except the head sum, which adds the two lane halves of a row.
+struct ERopeNorm {
+    static constexpr bool kTile = true;
+    bf16* out;
+    int ldo;
+    const float* cosv;   // [T][64]
+    const float* sinv;
+    float* rstdq;        // [M][H]
+    float* rstdk;        // [M][Hkv]
+    int T, H, Hkv;
+    float eps;
+
+    // 8 consecutive columns (16 p + 8 h .. + 7 of a 32-column block) of a per-lane array in the accumulator
+    // layout: registers of column groups 2p and 2p+1 trade halves between lanes l and l + 32
+    __device__ static void swap8(const float (&y)[16], int p, float (&v)[8]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(y[8 * p + e]),
+                                                            __float_as_uint(y[8 * p + 4 + e]), false, false);
+            v[e] = __uint_as_float(r[0]);
+            v[4 + e] = __uint_as_float(r[1]);
+        }
+    }
+
+    template <int FM, int FN>
+    __device__ void tile(const f32x16 (&acc)[FM][FN], int m0, int n0, int M, int N, int lane) const {
+        static_assert(FN == 4, "a wave must own one 128-column head");
+        if (n0 >= N) return;                 // wave-uniform: past the last head
+        const int head = n0 >> 7;
+        if (head >= H + Hkv) {               // v head: stored as computed
+            store_tile<FM, FN>(acc, m0, n0, 0, M, N, lane, EStoreCd<bf16>{out, ldo});
+            return;
+        }
+        const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = m0 + 32 * i + l32;
+            const bool live = m < M;
+            const int t = (live ? m : 0) % T;
+            float ss = 0.0f;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) ss += acc[i][j][r] * acc[i][j][r];
+            const float rs = 1.0f / sqrtf(pair_sum(ss) * (1.0f / 128.0f) + eps);
+            if (live && h == 0) {
+                if (head < H) rstdq[(size_t)m * H + head] = rs;
+                else rstdk[(size_t)m * Hkv + head - H] = rs;
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                // this lane's cos / sin: pair index 32 j + 8 g + 4 h + e sits in register 4 g + e of block j
+                float cs[16], sn[16];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float4 c4 = *reinterpret_cast<const float4*>(cosv + t * 64 + 32 * j + 8 * g + 4 * h);
+                    const float4 s4 = *reinterpret_cast<const float4*>(sinv + t * 64 + 32 * j + 8 * g + 4 * h);
+                    cs[4 * g] = c4.x; cs[4 * g + 1] = c4.y; cs[4 * g + 2] = c4.z; cs[4 * g + 3] = c4.w;
+                    sn[4 * g] = s4.x; sn[4 * g + 1] = s4.y; sn[4 * g + 2] = s4.z; sn[4 * g + 3] = s4.w;
+                }
+                float y1[16], y2[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float x1 = acc[i][j][r], x2 = acc[i][j + 2][r];
+                    y1[r] = (x1 * cs[r] + x2 * sn[r]) * rs;
+                    y2[r] = (-x1 * sn[r] + x2 * cs[r]) * rs;
+                }
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    float v1[8], v2[8];
+                    swap8(y1, p, v1);
+                    swap8(y2, p, v2);
+                    if (live) {
+                        bf16* row = out + (size_t)m * ldo + n0 + 16 * p + 8 * h;
+                        st8(row + 32 * j, v1);
+                        st8(row + 32 * (j + 2), v2);
+                    }
+                }
+            }
+        }
+    }
+};
+
 template <int FM, int FN, class E, int RG = FM>
 __device__ __forceinline__ void epilogue(const f32x16 (&acc)[FM][FN], int m0, int n0, int split, int M, int N,
                                          int lane, const E& epi) {
@@ -867,6 +958,25 @@ template <int BM, int BN, bool AK, bool BK, class E>
 static hipError_t run_mfma(const GemmDesc& d, E e, hipStream_t s) {
     const int splits = (d.K + d.k_split - 1) / d.k_split;
     const int tiles = ((d.M + BM - 1) / BM) * ((d.N + BN - 1) / BN);
+    if constexpr (std::is_same<E, ERopeNorm>::value) {
+        if constexpr (BM == 256 && BN == 256) {
+            if (d.loop != GemmLoop::Persist8Heads) return hipErrorInvalidValue;
+            auto pk = gemm_bf16_mfma_pring<256, 256, 4, 2, AK, BK, E>;
+            static int occ = 0;
+            if (occ == 0) {
+                hipError_t st = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(pk), 512, 0);
+                if (st != hipSuccess) return st;
+                if (occ < 1) occ = 1;
+            }
+            const int grid = std::min(tiles * splits, occ * num_cus());
+            hipLaunchKernelGGL(pk, dim3(grid), dim3(512), 0, s, (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, d.K,
+                               d.lda, d.ldb, d.k_split, splits, d.group_m, e);
+            return hipGetLastError();
+        } else {
+            return hipErrorInvalidValue;
+        }
+    } else {
+    if (d.loop == GemmLoop::Persist8Heads) return hipErrorInvalidValue;
     if (d.loop == GemmLoop::Ring8) {
         hipLaunchKernelGGL((gemm_bf16_mfma_ring<BM, BN, 2, 4, AK, BK, E>), dim3(tiles, splits), dim3(512), 0, s,
                            (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, d.K, d.lda, d.ldb, d.k_split, d.group_m, e);
@@ -886,6 +996,7 @@ static hipError_t run_mfma(const GemmDesc& d, E e, hipStream_t s) {
     hipLaunchKernelGGL(pk, dim3(grid), dim3(nt), 0, s, (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, d.K, d.lda,
                        d.ldb, d.k_split, splits, d.group_m, e);
     return hipGetLastError();
+    }
 }
 
 template <bool AK, bool BK, class E>
@@ -929,6 +1040,14 @@ static hipError_t dispatch_epi(const GemmDesc& d, hipStream_t s) {
             if constexpr (sizeof(T) == 2)
                 return run(EDz{(bf16*)d.out, d.ldo, d.lse, d.targets, d.inv_valid, d.grad_scale});
             break;
+        case Epi::RopeNorm:
+            if constexpr (sizeof(T) == 2) {
+                if (d.T <= 0 || d.H <= 0 || d.Hkv <= 0 || !d.cosv || !d.sinv || !d.rstdq || !d.rstdk ||
+                    d.N != (d.H + 2 * d.Hkv) * 128 || d.tile != 0)
+                    return hipErrorInvalidValue;
+                return run(ERopeNorm{(bf16*)d.out, d.ldo, d.cosv, d.sinv, d.rstdq, d.rstdk, d.T, d.H, d.Hkv, d.eps});
+            }
+            break;
         default: break;
         }
     } else if constexpr (AK && !BK) {
@@ -971,7 +1090,7 @@ hipError_t launch_gemm(const GemmDesc& in, hipStream_t s) {
 int gemm_wave_cols(const GemmDesc& d) {
     static const int bn[3] = {256, 128, 128};
     const int t = d.tile < 0 ? 0 : (d.tile > 2 ? 2 : d.tile);
-    return bn[t] / (d.loop == GemmLoop::Persist4 ? 2 : 4);
+    return bn[t] / (d.loop == GemmLoop::Persist4 || d.loop == GemmLoop::Persist8Heads ? 2 : 4);
 }
 
 const char* gemm_kernel_name(const GemmDesc& d) {

@@ -30,13 +30,17 @@ enum class Epi : int {
                  // domain (part), the logit at the row's target (zt); the rounded logits too when out != 0
     Dz,          // bf16 LM head recomputed in the backward: out = bf16(scale (softmax(z) - onehot(target))),
                  // scale = grad_scale * inv_valid on rows with a valid target, 0 elsewhere
+    RopeNorm,    // bf16 qkv projection (head_dim 128, Persist8Heads, 256 x 256 tiles): q and k heads rotated
+                 // (RoPE) and RMS-normalised over the head, 1/rms saved; v heads stored as they are
 };
 
 // MFMA main loop (all three stream 32-deep stages straight into a four-stage LDS ring):
 //   Ring8    eight waves, one output tile per workgroup;
 //   Persist4 four waves, persistent (the grid is the resident workgroups, walking (split, tile) items);
-//   Persist8 eight waves, persistent.
-enum class GemmLoop : int { Ring8 = 0, Persist4 = 1, Persist8 = 2 };
+//   Persist8 eight waves, persistent;
+//   Persist8Heads eight waves, persistent, in a 4 x 2 grid: on a 256 x 256 tile each wave owns 64 rows x 128
+//            columns, i.e. whole attention heads of the qkv projection (the RopeNorm epilogue needs that).
+enum class GemmLoop : int { Ring8 = 0, Persist4 = 1, Persist8 = 2, Persist8Heads = 3 };
 
 struct GemmDesc {
     Dt dt = Dt::BF16;
@@ -61,6 +65,13 @@ struct GemmDesc {
     const float* lse = nullptr;      // [M] natural-log LSE (Dz)
     const float* inv_valid = nullptr;
     float grad_scale = 1.0f;
+    // RopeNorm epilogue
+    const float* cosv = nullptr;     // [T, 64] rotation tables
+    const float* sinv = nullptr;
+    float* rstdq = nullptr;          // [M, H]
+    float* rstdk = nullptr;          // [M, Hkv]
+    int T = 0, H = 0, Hkv = 0;
+    float eps = 0.0f;
     int tile = -1;    // MFMA tile: 0 = 256x256, 1 = 256x128, 2 = 128x128; -1 = chosen from the shape
     int group_m = 4;  // tiles are walked in bands of group_m tile-rows (L2 reuse of the B tiles)
     GemmLoop loop = GemmLoop::Persist8;

@@ -289,6 +289,7 @@ const char* epi_name(Epi e) {
     case Epi::SplitK: return "splitk";
     case Epi::CeStats: return "ce_stats";
     case Epi::Dz: return "dz";
+    case Epi::RopeNorm: return "rope_qknorm";
     }
     return "?";
 }
@@ -556,16 +557,26 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             GemmDesc d;
             d.A = xn1; d.lda = C; d.B = weight(c, l, 0); d.ldb = C;
             d.M = N; d.N = QKV; d.K = C;
-            d.epi = Epi::StoreCd; d.out = qkv; d.ldo = QKV;
-            d.loop = GemmLoop::Persist8;  // the persistent eight-wave ring measured fastest for this shape
+            d.out = qkv; d.ldo = QKV;
             d.group_m = 8;  // bands of 8 tile-rows measured faster than bands of 4 for this shape
-            TRY(gemm(c, d, "qkv"));
+            if (dt == Dt::BF16) {
+                // RoPE + QK-norm in the epilogue: each wave of the 4 x 2 grid owns one head
+                d.epi = Epi::RopeNorm; d.loop = GemmLoop::Persist8Heads; d.tile = 0;
+                d.cosv = c->at<float>(p.cosv); d.sinv = c->at<float>(p.sinv);
+                d.rstdq = c->at<float>(c->lay(l, p.l_rstdq)); d.rstdk = c->at<float>(c->lay(l, p.l_rstdk));
+                d.T = (int)c->T; d.H = (int)c->H; d.Hkv = (int)c->Hkv; d.eps = eps;
+                TRY(gemm(c, d, "qkv"));
+            } else {
+                d.epi = Epi::StoreCd;
+                TRY(gemm(c, d, "qkv"));
+                TRY(launch(c, "rope_qknorm_fwd", 0.0, (double)N * (c->H + c->Hkv) * c->D * 2 * e, [&] {
+                    return launch_rope_qknorm_fwd(dt, qkv, c->at<float>(c->lay(l, p.l_rstdq)),
+                                                  c->at<float>(c->lay(l, p.l_rstdk)), c->at<float>(p.cosv),
+                                                  c->at<float>(p.sinv), N, (int)c->T, (int)c->H, (int)c->Hkv,
+                                                  (int)c->D, eps, c->stream);
+                }));
+            }
         }
-        TRY(launch(c, "rope_qknorm_fwd", 0.0, (double)N * (c->H + c->Hkv) * c->D * 2 * e, [&] {
-            return launch_rope_qknorm_fwd(dt, qkv, c->at<float>(c->lay(l, p.l_rstdq)), c->at<float>(c->lay(l, p.l_rstdk)),
-                                          c->at<float>(p.cosv), c->at<float>(p.sinv), N, (int)c->T, (int)c->H,
-                                          (int)c->Hkv, (int)c->D, eps, c->stream);
-        }));
         {
             AttnDesc ad;
             ad.dt = dt; ad.B = (int)c->B; ad.T = (int)c->T; ad.H = (int)c->H; ad.Hkv = (int)c->Hkv; ad.D = (int)c->D;
