@@ -118,6 +118,7 @@ def main():
     ap.add_argument("--lm-head", choices=["stored", "recomputed"], default="stored",
                     help="where the backward's dz comes from: stored logits (default) or a second LM-head GEMM")
     ap.add_argument("--kernels", action="store_true", help="print the per-kernel table to stderr")
+    ap.add_argument("--no-optim", action="store_true", help="skip timing the optimizer step")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -198,6 +199,36 @@ def main():
                   f"{(f / (t / 1e3) / 1e12) if f else 0:7.1f} {(b / (t / 1e3) / 1e9) if b else 0:7.1f}",
                   file=sys.stderr)
 
+    # the optimizer step (Muon + AdamW) that follows the gradients: timed on its own, not part of `value`
+    optim = None
+    if not args.no_optim:
+        st = torch.zeros(ncgpt.optim_state_size(cfg), dtype=torch.float32, device=dev)
+        p2 = params.clone()
+        m.optim_step(p2, grads, st, 1)
+        torch.cuda.synchronize()
+        o0 = time.perf_counter()
+        for t in range(2, 2 + args.steps):
+            m.optim_step(p2, grads, st, t)
+        torch.cuda.synchronize()
+        o1 = time.perf_counter()
+        m.timing(True)
+        m.timing_reset()
+        m.optim_step(p2, grads, st, 2 + args.steps)
+        otab = m.timing_read()
+        m.timing(False)
+        m.check()
+        gemm_fl = sum(v[2] for k, v in otab.items() if k.startswith("gemm"))
+        gemm_ms = sum(v[1] for k, v in otab.items() if k.startswith("gemm"))
+        optim = {"ms_per_step": round((o1 - o0) * 1e3 / args.steps, 3),
+                 "newton_schulz_tflop": round(gemm_fl / 1e12, 3),
+                 "newton_schulz_gemm_ms": round(gemm_ms, 3),
+                 "newton_schulz_tflops": round(gemm_fl / (gemm_ms / 1e3) / 1e12, 1) if gemm_ms else None}
+        if args.kernels:
+            print("optimizer step:", file=sys.stderr)
+            for k, (n, t_, f, b) in sorted(otab.items(), key=lambda kv: -kv[1][1]):
+                print(f"  {k:44s} {n:6d} {t_:8.3f} {(f / (t_ / 1e3) / 1e12) if f else 0:7.1f} "
+                      f"{(b / (t_ / 1e3) / 1e9) if b else 0:7.1f}", file=sys.stderr)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w)
@@ -221,6 +252,7 @@ def main():
                                f"{w.tokens} tokens", "global_batch": w.batch, "seq_len": w.seq_len,
                    "parallelism": "single GPU"},
         "roofline": roof,
+        "optimizer": optim,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

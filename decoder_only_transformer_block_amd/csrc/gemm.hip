@@ -44,6 +44,8 @@ __device__ __forceinline__ void st8(bf16* p, const float (&v)[8]) {
 template <typename T> struct EStoreCd {
     static constexpr bool kWide = std::is_same<T, bf16>::value, kLoads = false;
     T* out; int ldo;
+    int64_t sOut = 0;  // batch stride (elements) of a batched GEMM
+    __device__ EStoreCd at(int z) const { EStoreCd e = *this; e.out += z * sOut; return e; }
     __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
         Vec4<T>::store(out + (size_t)m * ldo + n, v);
     }
@@ -76,6 +78,37 @@ template <typename T> struct EResidual {
         st8(out + o, x);
     }
 };
+// out = cd(alpha in + beta v): the Newton-Schulz steps B = b A + c A A and X = a X + B X (bf16)
+struct EAxpby {
+    static constexpr bool kWide = true, kLoads = true;
+    bf16* out; const bf16* in; int ldo;
+    float alpha, beta;
+    int64_t sOut, sIn;  // batch strides (elements)
+    __device__ EAxpby at(int z) const {
+        EAxpby e = *this;
+        e.out += z * sOut;
+        e.in += z * sIn;
+        return e;
+    }
+    __device__ bf16x8 fetch8(int m, int n) const { return *reinterpret_cast<const bf16x8*>(in + (size_t)m * ldo + n); }
+    __device__ void put8(int m, int n, int, const float (&v)[8], const bf16x8& x) const {
+        float r[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[i] = alpha * (float)x[i] + beta * v[i];
+        st8(out + (size_t)m * ldo + n, r);
+    }
+    __device__ void put8(int, int, int, const float (&)[8]) const {}
+    __device__ void operator()(int, int, int, const float (&)[4]) const {}
+};
+
+// Epilogues of batched GEMMs shift their pointers to batch item z (at()); the others take z = 0 only.
+template <class E, class = void> struct BatchEpi : std::false_type {};
+template <class E> struct BatchEpi<E, std::void_t<decltype(std::declval<const E&>().at(0))>> : std::true_type {};
+template <class E> __device__ __forceinline__ E epi_at(const E& e, int z) {
+    if constexpr (BatchEpi<E>::value) return e.at(z);
+    else return e;
+}
+
 // act = a^2 with a = relu(v) rounded to the compute dtype: the only stored output of
 // the MLP's first linear; the backward recovers a as sqrt(act)
 template <typename T> struct EReluSq {
@@ -638,8 +671,12 @@ __device__ __forceinline__ bf16x8 frag32(const bf16* S, int r0, int kk, int lane
 template <int BM, int BN, int WGM, int WGN, bool AK, bool BK, class E>
 __global__ void __launch_bounds__(64 * WGM * WGN, 1)
 gemm_bf16_mfma_ring(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
-                    int k_split, int group_m, E epi)
+                    int k_split, int group_m, E epi_, int64_t sA, int64_t sB)
 {
+    // batched GEMMs: item blockIdx.z reads A + z sA and B + z sB and writes through its shifted epilogue
+    A += blockIdx.z * sA;
+    B += blockIdx.z * sB;
+    const E epi = epi_at(epi_, blockIdx.z);
     __shared__ __attribute__((aligned(1024))) bf16 sA0[BM * 32];
     __shared__ __attribute__((aligned(1024))) bf16 sB0[BN * 32];
     __shared__ __attribute__((aligned(1024))) bf16 sA1[BM * 32];
@@ -977,9 +1014,12 @@ static hipError_t run_mfma(const GemmDesc& d, E e, hipStream_t s) {
         }
     } else {
     if (d.loop == GemmLoop::Persist8Heads) return hipErrorInvalidValue;
+    if (d.batch > 1 && d.loop != GemmLoop::Ring8) return hipErrorInvalidValue;  // batches run on the ring only
     if (d.loop == GemmLoop::Ring8) {
-        hipLaunchKernelGGL((gemm_bf16_mfma_ring<BM, BN, 2, 4, AK, BK, E>), dim3(tiles, splits), dim3(512), 0, s,
-                           (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, d.K, d.lda, d.ldb, d.k_split, d.group_m, e);
+        if (d.batch > 1 && !BatchEpi<E>::value) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((gemm_bf16_mfma_ring<BM, BN, 2, 4, AK, BK, E>), dim3(tiles, splits, d.batch), dim3(512), 0,
+                           s, (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, d.K, d.lda, d.ldb, d.k_split, d.group_m, e,
+                           (int64_t)d.sA, (int64_t)d.sB);
         return hipGetLastError();
     }
     const bool eight = d.loop == GemmLoop::Persist8;
@@ -1029,7 +1069,7 @@ static hipError_t dispatch_epi(const GemmDesc& d, hipStream_t s) {
     };
     if constexpr (AK && BK) {
         switch (d.epi) {
-        case Epi::StoreCd: return run(EStoreCd<T>{(T*)d.out, d.ldo});
+        case Epi::StoreCd: return run(EStoreCd<T>{(T*)d.out, d.ldo, d.sOut});
         case Epi::ResidualCd: return run(EResidual<T>{(T*)d.out, (const T*)d.in, d.ldo});
         case Epi::ReluSq: return run(EReluSq<T>{(T*)d.out, d.ldo});
         case Epi::CeStats:
@@ -1052,12 +1092,19 @@ static hipError_t dispatch_epi(const GemmDesc& d, hipStream_t s) {
         }
     } else if constexpr (AK && !BK) {
         switch (d.epi) {
-        case Epi::StoreCd: return run(EStoreCd<T>{(T*)d.out, d.ldo});
+        case Epi::StoreCd: return run(EStoreCd<T>{(T*)d.out, d.ldo, d.sOut});
         case Epi::ReluSqBwd: return run(EReluSqBwd<T>{(T*)d.out, (const T*)d.in, d.ldo});
+        case Epi::Axpby:
+            if constexpr (sizeof(T) == 2)
+                return run(EAxpby{(bf16*)d.out, (const bf16*)d.in, d.ldo, d.alpha, d.beta, d.sOut, d.sIn});
+            break;
         default: break;
         }
     } else if constexpr (!AK && !BK) {
         switch (d.epi) {
+        case Epi::StoreCd:
+            if constexpr (sizeof(T) == 2) return run(EStoreCd<T>{(T*)d.out, d.ldo, d.sOut});
+            break;
         case Epi::Grad: return run(EGrad{(float*)d.out, d.ldo, d.accumulate});
         case Epi::SplitK: return run(ESplitK{(float*)d.out, d.ldo, d.split_stride});
         default: break;

@@ -30,6 +30,7 @@ enum class Epi : int {
                  // domain (part), the logit at the row's target (zt); the rounded logits too when out != 0
     Dz,          // bf16 LM head recomputed in the backward: out = bf16(scale (softmax(z) - onehot(target))),
                  // scale = grad_scale * inv_valid on rows with a valid target, 0 elsewhere
+    Axpby,       // bf16: out = cd(alpha in + beta v) (the Newton-Schulz steps); NN layout, batches allowed
     RopeNorm,    // bf16 qkv projection (head_dim 128, Persist8Heads, 256 x 256 tiles): q and k heads rotated
                  // (RoPE) and RMS-normalised over the head, 1/rms saved; v heads stored as they are
 };
@@ -72,6 +73,12 @@ struct GemmDesc {
     float* rstdk = nullptr;          // [M, Hkv]
     int T = 0, H = 0, Hkv = 0;
     float eps = 0.0f;
+    // Axpby epilogue
+    float alpha = 0.0f, beta = 1.0f;
+    // batched GEMM (the Ring8 loop only; StoreCd and Axpby epilogues): item z reads A + z sA and B + z sB and
+    // writes out + z sOut (reading in + z sIn); strides in elements
+    int batch = 1;
+    int64_t sA = 0, sB = 0, sOut = 0, sIn = 0;
     int tile = -1;    // MFMA tile: 0 = 256x256, 1 = 256x128, 2 = 128x128; -1 = chosen from the shape
     int group_m = 4;  // tiles are walked in bands of group_m tile-rows (L2 reuse of the B tiles)
     GemmLoop loop = GemmLoop::Persist8;
@@ -137,5 +144,30 @@ hipError_t launch_embed_bwd(const int32_t* ids, const float* dx, float* dwte, in
                             int32_t* iscratch, float* partial, hipStream_t s);
 hipError_t launch_to_f32(Dt dt, const void* src, float* dst, size_t n, hipStream_t s);
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);
+
+// ---------------------------------------------------------------- optimizer step (optim.hip)
+// The six matrices of a layer (Wq, Wk, Wv, Wo, Wfc, Wproj) inside the packed matrix range: layer stride,
+// offset and size of each, and its place in the Newton-Schulz batch of its shape (matrices of equal shape
+// form one batch: layer-major, group_count per layer, this one at group_slot).
+struct MuonShapes {
+    int64_t layer;
+    int64_t off[6], size[6];
+    int group_count[6], group_slot[6];
+};
+struct AdamArgs {
+    float lr, b1, b2, eps, bc1, bc2, decay;
+};
+// buf = mu buf + (1 - mu) g over the n-element matrix range (n % 4096 == 0); part[n / 4096] chunk sums of u^2
+hipError_t launch_muon_momentum(const float* g, float* buf, float* part, size_t n, float mu, int nesterov,
+                                hipStream_t s);
+// inv[layer * 6 + w] = 1 / max(||u||_F, eps)
+hipError_t launch_muon_norm(const float* part, float* inv, const MuonShapes& sh, int layers, float eps, hipStream_t s);
+// x (bf16, the shape group of matrix w): u * inv for every layer
+hipError_t launch_muon_init(const float* g, const float* buf, const float* inv, void* x, const MuonShapes& sh, int w,
+                            int layers, float mu, int nesterov, hipStream_t s);
+// p = p decay - step x for matrix w of every layer
+hipError_t launch_muon_apply(float* p, const void* x, const MuonShapes& sh, int w, int layers, float decay, float step,
+                             hipStream_t s);
+hipError_t launch_adamw(float* p, const float* g, float* m, float* v, size_t n, const AdamArgs& a, hipStream_t s);
 
 }  // namespace ncgpt

@@ -26,6 +26,14 @@ struct Plan {
     size_t l_xn1, l_rstd1, l_qkv, l_rstdq, l_rstdk, l_y, l_lse, l_xn2, l_rstd2, l_act;
     size_t xf, rstdf, logits, cepart, zt, lse, loss_rows, dxn, dx, dx_cd, dh, dy, dqkv, delta, splitk, iscr, total;
     int ce_nblk;
+    // optimizer step scratch (overlays the saved activations from layer0 on)
+    size_t o_part, o_inv;
+    int n_groups;
+    int64_t g_rows[6], g_cols[6];
+    int g_count[6];
+    size_t g_x0[6], g_x1[6], g_a[6], g_b[6];
+    int w_group[6];
+    MuonShapes shapes;
 };
 
 struct Timed {
@@ -224,6 +232,42 @@ void make_plan(ncgpt_ctx* c) {
     p.splitk = A(sk);
     p.iscr = A(embed_bwd_scratch_ints((int)N, (int)c->V) * 4);
     p.total = off;
+
+    // optimizer step: Newton-Schulz buffers per shape group, laid over the saved activations
+    const int64_t r6[6] = {c->HD, c->KD, c->KD, c->C, c->F, c->C}, k6[6] = {c->C, c->C, c->C, c->HD, c->C, c->F};
+    MuonShapes& sh = p.shapes;
+    int64_t o = 0;
+    for (int w = 0; w < 6; ++w) {
+        sh.off[w] = o;
+        sh.size[w] = r6[w] * k6[w];
+        o += sh.size[w];
+    }
+    sh.layer = o;
+    p.n_groups = 0;
+    for (int w = 0; w < 6; ++w) {
+        int g = 0;
+        while (g < p.n_groups && !(p.g_rows[g] == r6[w] && p.g_cols[g] == k6[w])) ++g;
+        if (g == p.n_groups) {
+            p.g_rows[g] = r6[w];
+            p.g_cols[g] = k6[w];
+            p.g_count[g] = 0;
+            ++p.n_groups;
+        }
+        p.w_group[w] = g;
+        sh.group_slot[w] = p.g_count[g]++;
+    }
+    for (int w = 0; w < 6; ++w) sh.group_count[w] = p.g_count[p.w_group[w]];
+    off = p.layer0;
+    p.o_part = A((size_t)(c->L * sh.layer / 4096) * 4);
+    p.o_inv = A((size_t)c->L * 6 * 4);
+    for (int g = 0; g < p.n_groups; ++g) {
+        const size_t items = (size_t)c->L * p.g_count[g], mm = (size_t)std::min(p.g_rows[g], p.g_cols[g]);
+        p.g_x0[g] = A(items * p.g_rows[g] * p.g_cols[g] * 2);
+        p.g_x1[g] = A(items * p.g_rows[g] * p.g_cols[g] * 2);
+        p.g_a[g] = A(items * mm * mm * 2);
+        p.g_b[g] = A(items * mm * mm * 2);
+    }
+    p.total = std::max(p.total, off);
 }
 
 // ---------------------------------------------------------------- launch wrapper with optional timing
@@ -290,6 +334,7 @@ const char* epi_name(Epi e) {
     case Epi::CeStats: return "ce_stats";
     case Epi::Dz: return "dz";
     case Epi::RopeNorm: return "rope_qknorm";
+    case Epi::Axpby: return "axpby";
     }
     return "?";
 }
@@ -304,22 +349,23 @@ const char* intern(const std::string& s) {
 }
 
 // tag: the call site (qkv, lm_head, dWfc, ...), so every timing row is one shape
-ncgpt_status gemm(ncgpt_ctx* c, GemmDesc d, const char* tag) {
-    d.dt = c->dt;
+ncgpt_status gemm(ncgpt_ctx* c, GemmDesc d, const char* tag, bool bf16_always = false) {
+    d.dt = bf16_always ? Dt::BF16 : c->dt;
     if (d.tile < 0) d.tile = pick_tile(d.M, d.N);
     const char* nm = intern(std::string(gemm_kernel_name(d)) + ":" + epi_name(d.epi) + ":" + tag);
-    const double fl = 2.0 * d.M * d.N * d.K;
+    const double fl = 2.0 * d.M * d.N * d.K * d.batch;
     // algorithmic bytes: both operands once, the output (and what the epilogue reads) once
     const double e = d.dt == Dt::BF16 ? 2.0 : 4.0, mn = (double)d.M * d.N;
     double out = e;
     switch (d.epi) {
     case Epi::ResidualCd: case Epi::ReluSqBwd: out = 2.0 * e; break;
     case Epi::CeStats: out = (d.out ? e : 0.0) + 8.0 * d.nblk / d.N; break;
+    case Epi::Axpby: out = 4.0; break;
     case Epi::Grad: out = d.accumulate ? 8.0 : 4.0; break;
     case Epi::SplitK: out = 4.0 * std::max(1, d.splits); break;
     default: break;
     }
-    const double by = ((double)d.M * d.K + (double)d.N * d.K) * e + mn * out;
+    const double by = (((double)d.M * d.K + (double)d.N * d.K) * e + mn * out) * d.batch;
     return launch(c, nm, fl, by, [&] { return launch_gemm(d, c->stream); });
 }
 
@@ -806,6 +852,118 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
         return launch_embed_bwd(c->ids, dx, gslice(-1, 0), N, C, V, acc, c->at<int32_t>(p.iscr), dxn, c->stream);
     }));
     c->state = 3;
+    return NCGPT_OK;
+}
+
+size_t ncgpt_optim_state_size(const ncgpt_config* g) {
+    if (!valid_cfg(g)) return 0;
+    const int64_t VC = (int64_t)g->vocab_size * g->n_embd;
+    return (size_t)((int64_t)g->n_layer * layer_params(g) + 4 * VC);
+}
+
+ncgpt_status ncgpt_optim_step(ncgpt_ctx* c, float* params, const float* grads, float* state, int64_t step,
+                              const ncgpt_optim_config* oc) {
+    if (!c) return NCGPT_EINVAL;
+    TRY(check_bound(c));
+    if (c->state == 1 || c->state == 2)
+        return fail(c, NCGPT_ESTATE, "ncgpt_optim_step between ncgpt_forward and ncgpt_backward");
+    if (!params || !grads || !state || !oc) return fail(c, NCGPT_EINVAL, "null params, grads, state or config");
+    if (step < 1 || oc->ns_steps < 0 || oc->ns_steps > 20 || !(oc->muon_momentum >= 0.0f && oc->muon_momentum < 1.0f) ||
+        !(oc->adam_beta1 >= 0.0f && oc->adam_beta1 < 1.0f) || !(oc->adam_beta2 >= 0.0f && oc->adam_beta2 < 1.0f) ||
+        !(oc->ns_eps > 0.0f))
+        return fail(c, NCGPT_EINVAL, "optimizer step or constants out of range");
+    const Plan& p = c->pl;
+    const MuonShapes& sh = p.shapes;
+    const int L = (int)c->L;
+    const int64_t VC = c->VC, nmat = (int64_t)L * sh.layer;
+    const float mu = oc->muon_momentum;
+    const int nest = oc->muon_nesterov ? 1 : 0;
+    c->state = 0;   // the Newton-Schulz scratch overwrites the saved activations
+    float* gm = const_cast<float*>(grads) + VC;   // the packed matrix range
+    float* pm = params + VC;
+    float* part = c->at<float>(p.o_part);
+    float* inv = c->at<float>(p.o_inv);
+    TRY(launch(c, "muon_momentum", 0.0, (double)nmat * 12, [&] {
+        return launch_muon_momentum(gm, state, part, (size_t)nmat, mu, nest, c->stream);
+    }));
+    TRY(launch(c, "muon_norm", 0.0, (double)nmat / 4096 * 4, [&] {
+        return launch_muon_norm(part, inv, sh, L, oc->ns_eps, c->stream);
+    }));
+    for (int w = 0; w < 6; ++w) {
+        const int g = p.w_group[w];
+        TRY(launch(c, "muon_init", 0.0, (double)L * sh.size[w] * 10, [&] {
+            return launch_muon_init(gm, state, inv, c->ws + p.g_x0[g], sh, w, L, mu, nest, c->stream);
+        }));
+    }
+    // Newton-Schulz on each shape group, batched over its L * count matrices
+    for (int g = 0; g < p.n_groups; ++g) {
+        const int R = (int)p.g_rows[g], Cc = (int)p.g_cols[g], batch = L * p.g_count[g];
+        const bool tall = R > Cc;
+        const int m = tall ? Cc : R;
+        uint8_t* X[2] = {c->ws + p.g_x0[g], c->ws + p.g_x1[g]};
+        uint8_t* Am = c->ws + p.g_a[g];
+        uint8_t* Bm = c->ws + p.g_b[g];
+        const int64_t sx = (int64_t)R * Cc, sm = (int64_t)m * m;
+        for (int it = 0; it < oc->ns_steps; ++it) {
+            uint8_t* x = X[it & 1];
+            uint8_t* xn = X[(it + 1) & 1];
+            {   // A = X X^T (wide) or X^T X (tall)
+                GemmDesc d;
+                d.A = x; d.B = x; d.lda = Cc; d.ldb = Cc;
+                d.a_kcontig = !tall; d.b_kcontig = !tall;
+                d.M = m; d.N = m; d.K = tall ? R : Cc;
+                d.epi = Epi::StoreCd; d.out = Am; d.ldo = m;
+                d.loop = GemmLoop::Ring8; d.tile = 2;
+                d.batch = batch; d.sA = sx; d.sB = sx; d.sOut = sm;
+                TRY(gemm(c, d, "ns_gram", true));
+            }
+            {   // B = b A + c A A
+                GemmDesc d;
+                d.A = Am; d.B = Am; d.lda = m; d.ldb = m; d.b_kcontig = false;
+                d.M = m; d.N = m; d.K = m;
+                d.epi = Epi::Axpby; d.out = Bm; d.in = Am; d.ldo = m; d.alpha = oc->ns_b; d.beta = oc->ns_c;
+                d.loop = GemmLoop::Ring8; d.tile = 2;
+                d.batch = batch; d.sA = sm; d.sB = sm; d.sOut = sm; d.sIn = sm;
+                TRY(gemm(c, d, "ns_poly", true));
+            }
+            {   // X = a X + B X (wide) or a X + X B (tall)
+                GemmDesc d;
+                if (tall) { d.A = x; d.lda = Cc; d.B = Bm; d.ldb = m; d.sA = sx; d.sB = sm; d.K = Cc; }
+                else { d.A = Bm; d.lda = m; d.B = x; d.ldb = Cc; d.sA = sm; d.sB = sx; d.K = R; }
+                d.b_kcontig = false;
+                d.M = R; d.N = Cc;
+                d.epi = Epi::Axpby; d.out = xn; d.in = x; d.ldo = Cc; d.alpha = oc->ns_a; d.beta = 1.0f;
+                d.loop = GemmLoop::Ring8; d.tile = pick_tile((int64_t)R * batch, Cc);
+                d.batch = batch; d.sOut = sx; d.sIn = sx;
+                TRY(gemm(c, d, "ns_update", true));
+            }
+        }
+    }
+    const float decay = 1.0f - oc->matrix_lr * oc->weight_decay;
+    for (int w = 0; w < 6; ++w) {
+        const int g = p.w_group[w];
+        const double ratio = (double)p.g_rows[g] / (double)p.g_cols[g];
+        const float scaled = (float)(oc->matrix_lr * std::sqrt(std::max(1.0, ratio)));
+        TRY(launch(c, "muon_apply", 0.0, (double)L * sh.size[w] * 10, [&] {
+            return launch_muon_apply(pm, c->ws + (oc->ns_steps & 1 ? p.g_x1[g] : p.g_x0[g]), sh, w, L, decay, scaled,
+                                     c->stream);
+        }));
+    }
+    // AdamW on wte and lm_head
+    const double bc1 = 1.0 - std::pow((double)oc->adam_beta1, (double)step);
+    const double bc2 = 1.0 - std::pow((double)oc->adam_beta2, (double)step);
+    for (int which = 0; which < 2; ++which) {
+        size_t off;
+        int64_t r, k;
+        ncgpt_param_slice(&c->cfg, -1, which, &off, &r, &k);
+        const float lr = which == 0 ? oc->embedding_lr : oc->unembedding_lr;
+        AdamArgs a{lr, oc->adam_beta1, oc->adam_beta2, oc->adam_eps, (float)bc1, (float)bc2,
+                   1.0f - lr * oc->weight_decay};
+        float* mo = state + nmat + (size_t)which * 2 * VC;
+        TRY(launch(c, "adamw", 0.0, (double)VC * 28, [&] {
+            return launch_adamw(params + off, grads + off, mo, mo + VC, (size_t)VC, a, c->stream);
+        }));
+    }
     return NCGPT_OK;
 }
 

@@ -64,10 +64,42 @@ class Config:
                        self.vocab_size, self.batch, self.seq_len, self.rope_base, self.norm_eps)
 
 
+class _OptimConfig(ct.Structure):
+    _fields_ = [("matrix_lr", ct.c_float), ("embedding_lr", ct.c_float), ("unembedding_lr", ct.c_float),
+                ("muon_momentum", ct.c_float), ("muon_nesterov", ct.c_int32), ("ns_steps", ct.c_int32),
+                ("ns_a", ct.c_float), ("ns_b", ct.c_float), ("ns_c", ct.c_float), ("ns_eps", ct.c_float),
+                ("adam_beta1", ct.c_float), ("adam_beta2", ct.c_float), ("adam_eps", ct.c_float),
+                ("weight_decay", ct.c_float)]
+
+
+@dataclass(frozen=True)
+class OptimConfig:
+    """ncgpt_optim_config.  Learning rates as on the pages ("nanochat 项目深度分析" §2.2, §4.2); Muon's
+    momentum and Newton-Schulz constants as in the published Muon description; AdamW's moment constants are
+    not on the pages (PyTorch's AdamW defaults)."""
+    matrix_lr: float = 0.02
+    embedding_lr: float = 0.2
+    unembedding_lr: float = 0.004
+    muon_momentum: float = 0.95
+    muon_nesterov: int = 1
+    ns_steps: int = 5
+    ns_a: float = 3.4445
+    ns_b: float = -4.7750
+    ns_c: float = 2.0315
+    ns_eps: float = 1e-7
+    adam_beta1: float = 0.9
+    adam_beta2: float = 0.999
+    adam_eps: float = 1e-8
+    weight_decay: float = 0.0
+
+    def _c(self):
+        return _OptimConfig(*[getattr(self, f) for f, _ in _OptimConfig._fields_])
+
+
 _lib = None
 
 EXPORTS = ["ncgpt_num_params", "ncgpt_param_slice", "ncgpt_create", "ncgpt_workspace_size", "ncgpt_bind",
-           "ncgpt_bind_static", "ncgpt_set_lm_head_mode",
+           "ncgpt_bind_static", "ncgpt_set_lm_head_mode", "ncgpt_optim_state_size", "ncgpt_optim_step",
            "ncgpt_forward", "ncgpt_loss", "ncgpt_backward", "ncgpt_check", "ncgpt_probe_numel", "ncgpt_probe",
            "ncgpt_timing_enable", "ncgpt_timing_reset", "ncgpt_timing_count", "ncgpt_timing_get",
            "ncgpt_last_error", "ncgpt_destroy"]
@@ -90,6 +122,9 @@ def lib():
         L.ncgpt_bind.argtypes = [vp, vp, ct.c_size_t, vp]
         L.ncgpt_bind_static.argtypes = [vp, vp]
         L.ncgpt_set_lm_head_mode.argtypes = [vp, ct.c_int]
+        L.ncgpt_optim_state_size.argtypes = [P(_Config)]
+        L.ncgpt_optim_state_size.restype = ct.c_size_t
+        L.ncgpt_optim_step.argtypes = [vp, vp, vp, vp, ct.c_int64, P(_OptimConfig)]
         L.ncgpt_forward.argtypes = [vp, vp, vp]
         L.ncgpt_loss.argtypes = [vp, vp, vp]
         L.ncgpt_backward.argtypes = [vp, vp, ct.c_int, ct.c_float]
@@ -106,7 +141,7 @@ def lib():
         L.ncgpt_destroy.argtypes = [vp]
         L.ncgpt_destroy.restype = None
         for name in EXPORTS:
-            if name not in ("ncgpt_num_params", "ncgpt_last_error", "ncgpt_destroy"):
+            if name not in ("ncgpt_num_params", "ncgpt_last_error", "ncgpt_destroy", "ncgpt_optim_state_size"):
                 getattr(L, name).restype = ct.c_int
         _lib = L
     return _lib
@@ -114,6 +149,10 @@ def lib():
 
 def num_params(cfg: Config) -> int:
     return int(lib().ncgpt_num_params(ct.byref(cfg._c())))
+
+
+def optim_state_size(cfg: Config) -> int:
+    return int(lib().ncgpt_optim_state_size(ct.byref(cfg._c())))
 
 
 def param_slice(cfg: Config, layer: int, which: int):
@@ -185,6 +224,15 @@ class Model:
     def backward(self, grads: torch.Tensor, accumulate: bool = False, grad_scale: float = 1.0):
         pg = _ptr(grads, torch.float32, self.n_params, "grads")
         self._check(lib().ncgpt_backward(self._ctx, pg, 1 if accumulate else 0, float(grad_scale)))
+
+    def optim_step(self, params: torch.Tensor, grads: torch.Tensor, state: torch.Tensor, step: int,
+                   opt: "OptimConfig" = None):
+        """One optimizer step in place on params and state (ncgpt_optim_step)."""
+        opt = opt or OptimConfig()
+        pp = _ptr(params, torch.float32, self.n_params, "params")
+        pg = _ptr(grads, torch.float32, self.n_params, "grads")
+        ps = _ptr(state, torch.float32, optim_state_size(self.cfg), "state")
+        self._check(lib().ncgpt_optim_step(self._ctx, pp, pg, ps, int(step), ct.byref(opt._c())))
 
     def set_lm_head_mode(self, mode: int):
         """LOGITS_STORED (default) or LOGITS_RECOMPUTED: where the backward's dz comes from."""

@@ -133,6 +133,40 @@ ncgpt_status ncgpt_set_lm_head_mode(ncgpt_ctx* ctx, int mode);
  * ESTATE unless ncgpt_loss followed the last ncgpt_forward. */
 ncgpt_status ncgpt_backward(ncgpt_ctx* ctx, float* grads, int accumulate, float grad_scale);
 
+/* The optimizer step that follows the backward ("nanochat 项目深度分析" §2.2 and §4.2): Muon for every layer
+ * matrix (Wq, Wk, Wv, Wo, Wfc, Wproj), AdamW for wte and lm_head, each group at its own learning rate.
+ * Muon is taken in the form of the published Muon description (the pages leave the iteration out):
+ *   buf = mu buf + (1 - mu) g;  u = (1 - mu) g + mu buf (muon_nesterov) or buf;
+ *   X = u / max(||u||_F, ns_eps) in bf16, then ns_steps times: A = X X^T (X^T X when rows > cols),
+ *   B = ns_b A + ns_c A A, X = ns_a X + B X (X B when rows > cols), all bf16 MFMA products;
+ *   p = p (1 - matrix_lr weight_decay) - matrix_lr sqrt(max(1, rows / cols)) X.
+ * AdamW (decoupled weight decay, bias-corrected, fp32): m = b1 m + (1 - b1) g, v = b2 v + (1 - b2) g^2,
+ *   p = p (1 - lr weight_decay) - lr (m / (1 - b1^step)) / (sqrt(v / (1 - b2^step)) + adam_eps).
+ * Typical values: matrix_lr 0.02, embedding_lr 0.2, unembedding_lr 0.004 (the pages); muon_momentum 0.95,
+ * ns_steps 5, (ns_a, ns_b, ns_c) = (3.4445, -4.7750, 2.0315), ns_eps 1e-7 (the Muon description). */
+typedef struct {
+    float matrix_lr, embedding_lr, unembedding_lr;
+    float muon_momentum;
+    int32_t muon_nesterov, ns_steps;
+    float ns_a, ns_b, ns_c, ns_eps;
+    float adam_beta1, adam_beta2, adam_eps;
+    float weight_decay;
+} ncgpt_optim_config;
+
+/* fp32 elements of the optimizer state: a momentum buffer per layer matrix (the packed matrix range, in
+ * packing order), then AdamW's m and v for wte, then m and v for lm_head.  The caller zeroes it before the
+ * first step.  0 for an invalid config. */
+size_t ncgpt_optim_state_size(const ncgpt_config* cfg);
+
+/* One optimizer step, in place on params (fp32 [P]) and state (fp32 [ncgpt_optim_state_size]), from grads
+ * (fp32 [P], e.g. those of ncgpt_backward).  step counts from 1 (AdamW's bias correction).  Runs on the bound
+ * stream; its Newton-Schulz scratch overlays the workspace's saved activations, so the next call on the
+ * context must be ncgpt_forward (probes of the last forward are lost).  ESTATE between ncgpt_forward and
+ * ncgpt_backward; EINVAL for null pointers, step < 1, ns_steps outside [0, 20] or a momentum / beta outside
+ * [0, 1). */
+ncgpt_status ncgpt_optim_step(ncgpt_ctx* ctx, float* params, const float* grads, float* state, int64_t step,
+                              const ncgpt_optim_config* oc);
+
 /* Synchronise the bound stream and report device-side errors: EDEVICE if the flag is set (the flag is then
  * cleared), EHIP on an asynchronous HIP error, OK otherwise. */
 ncgpt_status ncgpt_check(ncgpt_ctx* ctx);

@@ -9,13 +9,13 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "ncgpt_oracle.c")
+SRCS = [os.path.join(HERE, "ncgpt_oracle.c"), os.path.join(HERE, "optim_oracle.c")]
 OUT = os.path.join(HERE, "liboracle.so")
 
 
 def build(verbose: bool = False) -> str:
     cmd = ["gcc", "-std=c99", "-O2", "-ftree-vectorize", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
-           "-Wall", "-Wextra", "-o", OUT + ".tmp", SRC, "-lm"]
+           "-Wall", "-Wextra", "-o", OUT + ".tmp", *SRCS, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.check_call(cmd)

@@ -33,6 +33,40 @@ class _Layout(ct.Structure):
                 ("lse", ct.c_int64), ("loss_rows", ct.c_int64), ("total", ct.c_int64)]
 
 
+class _Optim(ct.Structure):
+    _fields_ = [("matrix_lr", ct.c_double), ("embedding_lr", ct.c_double), ("unembedding_lr", ct.c_double),
+                ("muon_momentum", ct.c_double), ("muon_nesterov", ct.c_int32), ("ns_steps", ct.c_int32),
+                ("ns_a", ct.c_double), ("ns_b", ct.c_double), ("ns_c", ct.c_double), ("ns_eps", ct.c_double),
+                ("adam_beta1", ct.c_double), ("adam_beta2", ct.c_double), ("adam_eps", ct.c_double),
+                ("weight_decay", ct.c_double)]
+
+
+@dataclass(frozen=True)
+class OptimConfig:
+    """Hyper-parameters of the optimizer step.  Learning rates: "nanochat 项目深度分析" §2.2 / §4.2.  The
+    Newton-Schulz constants and the momentum form: the published Muon description.  The AdamW moments'
+    constants are not on the pages (PyTorch's AdamW defaults)."""
+    matrix_lr: float = 0.02
+    embedding_lr: float = 0.2
+    unembedding_lr: float = 0.004
+    muon_momentum: float = 0.95
+    muon_nesterov: int = 1
+    ns_steps: int = 5
+    ns_a: float = 3.4445
+    ns_b: float = -4.7750
+    ns_c: float = 2.0315
+    ns_eps: float = 1e-7
+    adam_beta1: float = 0.9
+    adam_beta2: float = 0.999
+    adam_eps: float = 1e-8
+    weight_decay: float = 0.0
+
+    def _c(self):
+        return _Optim(self.matrix_lr, self.embedding_lr, self.unembedding_lr, self.muon_momentum,
+                      self.muon_nesterov, self.ns_steps, self.ns_a, self.ns_b, self.ns_c, self.ns_eps,
+                      self.adam_beta1, self.adam_beta2, self.adam_eps, self.weight_decay)
+
+
 @dataclass(frozen=True)
 class OracleConfig:
     n_layer: int
@@ -86,6 +120,15 @@ def lib():
         L.orc_forward_f64.restype = ct.c_int64
         L.orc_grad_f64.argtypes = [P(_Cfg), i32, i32, d, ct.c_double, d, d]
         L.orc_grad_f64.restype = ct.c_int64
+        L.orc_newton_schulz.argtypes = [d, ct.c_int64, ct.c_int64, ct.c_int, ct.c_double, ct.c_double, ct.c_double,
+                                        ct.c_double, d]
+        L.orc_muon_update.argtypes = [d, d, d, ct.c_int64, ct.c_int64, ct.c_double, ct.c_double, ct.c_int,
+                                      ct.c_double, ct.c_int, ct.c_double, ct.c_double, ct.c_double, ct.c_double]
+        L.orc_adamw_update.argtypes = [d, d, d, d, ct.c_int64, ct.c_int64, ct.c_double, ct.c_double, ct.c_double,
+                                       ct.c_double, ct.c_double]
+        L.orc_optim_state_size.argtypes = [P(_Cfg)]
+        L.orc_optim_state_size.restype = ct.c_int64
+        L.orc_optim_step.argtypes = [P(_Cfg), d, d, d, ct.c_int64, P(_Optim)]
         _lib = L
     return _lib
 
@@ -300,3 +343,51 @@ def grad(cfg: OracleConfig, ids, targets, params, grad_scale=1.0):
     if valid < 0:
         raise ValueError("oracle rejected the inputs (bad config or token id)")
     return loss.value, g
+
+
+# ---------------------------------------------------------------- optimizer step
+
+def newton_schulz(G, steps=5, a=3.4445, b=-4.7750, c=2.0315, eps=1e-7):
+    G, pg = _f64(G)
+    rows, cols = G.shape
+    out, po = _out((rows, cols))
+    lib().orc_newton_schulz(pg, rows, cols, steps, a, b, c, eps, po)
+    return out
+
+
+def muon_update(p, g, buf, lr, momentum=0.95, nesterov=True, wd=0.0, steps=5, a=3.4445, b=-4.7750, c=2.0315,
+                eps=1e-7):
+    """Returns (new p, new buf); inputs are not modified."""
+    p = np.array(p, dtype=np.float64, order="C")
+    buf = np.array(buf, dtype=np.float64, order="C")
+    g, pg = _f64(g)
+    rows, cols = p.shape
+    lib().orc_muon_update(p.ctypes.data_as(ct.POINTER(ct.c_double)), pg, buf.ctypes.data_as(ct.POINTER(ct.c_double)),
+                          rows, cols, lr, momentum, int(nesterov), wd, steps, a, b, c, eps)
+    return p, buf
+
+
+def adamw_update(p, g, m, v, t, lr, b1=0.9, b2=0.999, eps=1e-8, wd=0.0):
+    """Returns (new p, new m, new v)."""
+    p = np.array(p, dtype=np.float64).ravel()
+    m = np.array(m, dtype=np.float64).ravel()
+    v = np.array(v, dtype=np.float64).ravel()
+    g, pg = _f64(np.ravel(g))
+    D = ct.POINTER(ct.c_double)
+    lib().orc_adamw_update(p.ctypes.data_as(D), pg, m.ctypes.data_as(D), v.ctypes.data_as(D), p.size, t, lr, b1, b2,
+                           eps, wd)
+    return p, m, v
+
+
+def optim_state_size(cfg: OracleConfig) -> int:
+    return int(lib().orc_optim_state_size(ct.byref(cfg._c())))
+
+
+def optim_step(cfg: OracleConfig, params, grads, state, t, opt: OptimConfig = OptimConfig()):
+    """One optimizer step over packed parameters.  Returns (new params, new state) as float64."""
+    p = np.array(params, dtype=np.float64)
+    st = np.array(state, dtype=np.float64)
+    g, pg = _f64(grads)
+    D = ct.POINTER(ct.c_double)
+    lib().orc_optim_step(ct.byref(cfg._c()), p.ctypes.data_as(D), pg, st.ctypes.data_as(D), t, ct.byref(opt._c()))
+    return p, st

@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = ncgpt.lib()
     names = declared_functions()
-    assert len(names) >= 19
+    assert len(names) >= 21
     for n in names:
         assert hasattr(L, n), n
     assert sorted(ncgpt.EXPORTS) == names
@@ -46,6 +46,12 @@ def test_packing_matches_oracle(name):
         ncgpt.param_slice(cfg, w.n_layer, 0)
     with pytest.raises(ncgpt.NcgptError):
         ncgpt.param_slice(cfg, -1, 2)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_optim_state_size_matches_oracle(name):
+    w = WORKLOADS[name]
+    assert ncgpt.optim_state_size(ncgpt.Config.from_workload(w)) == orc.optim_state_size(ocfg(w))
 
 
 def create(cfg, dtype):
