@@ -119,6 +119,7 @@ def main():
                     help="where the backward's dz comes from: stored logits (default) or a second LM-head GEMM")
     ap.add_argument("--kernels", action="store_true", help="print the per-kernel table to stderr")
     ap.add_argument("--no-optim", action="store_true", help="skip timing the optimizer step")
+    ap.add_argument("--no-decode", action="store_true", help="skip timing the KV-cache decode step")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -229,6 +230,40 @@ def main():
                 print(f"  {k:44s} {n:6d} {t_:8.3f} {(f / (t_ / 1e3) / 1e12) if f else 0:7.1f} "
                       f"{(b / (t_ / 1e3) / 1e9) if b else 0:7.1f}", file=sys.stderr)
 
+    # KV-cache decode at the end of the context: B sequences, one token each, against seq_len - 1 cached positions
+    decode = None
+    if not args.no_decode:
+        cache = m.kv_cache()
+        m.forward(ids_d, params)
+        m.kv_fill(cache, w.seq_len - 1)
+        tok = ids_d.view(w.batch, w.seq_len)[:, -1].contiguous()
+        lg = torch.empty(w.batch * w.vocab_size, dtype=torch.float32, device=dev)
+        m.decode_step(tok, params, cache, w.seq_len - 1, lg, recast=True)
+        torch.cuda.synchronize()
+        d0 = time.perf_counter()
+        for _ in range(args.steps):
+            m.decode_step(tok, params, cache, w.seq_len - 1, lg, recast=False)
+        torch.cuda.synchronize()
+        d1 = time.perf_counter()
+        m.timing(True)
+        m.timing_reset()
+        m.decode_step(tok, params, cache, w.seq_len - 1, lg, recast=False)
+        dtab = m.timing_read()
+        m.timing(False)
+        m.check()
+        att = dtab.get("decode_attn")
+        dms = (d1 - d0) * 1e3 / args.steps
+        decode = {"ms_per_step": round(dms, 3), "tokens_per_s": round(w.batch / (dms / 1e3), 1),
+                  "context": w.seq_len, "batch": w.batch,
+                  "attention_ms": round(att[1], 3) if att else None,
+                  "attention_gbs": round(att[3] / (att[1] / 1e3) / 1e9, 1) if att else None,
+                  "kv_cache_bytes": m.kv_cache_bytes()}
+        if args.kernels:
+            print("decode step:", file=sys.stderr)
+            for k, (n, t_, f, b) in sorted(dtab.items(), key=lambda kv: -kv[1][1]):
+                print(f"  {k:44s} {n:6d} {t_:8.3f} {(f / (t_ / 1e3) / 1e12) if f else 0:7.1f} "
+                      f"{(b / (t_ / 1e3) / 1e9) if b else 0:7.1f}", file=sys.stderr)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w)
@@ -253,6 +288,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof,
         "optimizer": optim,
+        "decode": decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

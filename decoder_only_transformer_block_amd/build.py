@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(PKG, "libncgpt.so")
-SOURCES = ["gemm.hip", "attention.hip", "rowwise.hip", "optim.hip", "runtime.hip"]
+SOURCES = ["gemm.hip", "attention.hip", "rowwise.hip", "optim.hip", "decode.hip", "runtime.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -1058,9 +1058,10 @@ static hipError_t run_f32(const GemmDesc& d, E e, hipStream_t s) {
 }
 
 // Only the (layout, epilogue) pairs of the block stack are instantiated:
-//   NT  (x W^T, forward):           store, residual add, ReLU^2
-//   NN  (dY W, input gradients):    store, ReLU^2 backward
-//   TN  (dY^T X, weight gradients): fp32 gradient, split-K partial
+//   NT  (x W^T, forward):           store, residual add, ReLU^2, CE statistics, dz, RoPE + QK-norm, split-K
+//                                   partials (decode)
+//   NN  (dY W, input gradients):    store, ReLU^2 backward, alpha in + beta v (Newton-Schulz)
+//   TN  (dY^T X, weight gradients): fp32 gradient, split-K partial, store (Newton-Schulz X^T X)
 template <typename T, bool AK, bool BK>
 static hipError_t dispatch_epi(const GemmDesc& d, hipStream_t s) {
     auto run = [&](auto e) -> hipError_t {
@@ -1072,6 +1073,7 @@ static hipError_t dispatch_epi(const GemmDesc& d, hipStream_t s) {
         case Epi::StoreCd: return run(EStoreCd<T>{(T*)d.out, d.ldo, d.sOut});
         case Epi::ResidualCd: return run(EResidual<T>{(T*)d.out, (const T*)d.in, d.ldo});
         case Epi::ReluSq: return run(EReluSq<T>{(T*)d.out, d.ldo});
+        case Epi::SplitK: return run(ESplitK{(float*)d.out, d.ldo, d.split_stride});  // B-row decode products
         case Epi::CeStats:
             if constexpr (sizeof(T) == 2)
                 return run(ECeStats{(bf16*)d.out, d.ldo, (float2*)d.part, d.nblk, d.zt, d.targets});

@@ -122,8 +122,10 @@ hipError_t launch_rmsnorm_fwd(Dt dt, const void* x, void* y, float* rstd, int ro
 // dx(f32) = (accumulate ? dx : 0) + rstd*(dy - y*mean(dy*y)); dx_cd = cd(dx) when non-null
 hipError_t launch_rmsnorm_bwd(Dt dt, const void* y, const float* rstd, const void* dy, float* dx, void* dx_cd,
                               int rows, int C, int accumulate, hipStream_t s);
+// pos >= 0: every row is one token at position pos (decode); else row n is at position n mod T
 hipError_t launch_rope_qknorm_fwd(Dt dt, void* qkv, float* rstdq, float* rstdk, const float* cosv,
-                                  const float* sinv, int N, int T, int H, int Hkv, int D, float eps, hipStream_t s);
+                                  const float* sinv, int N, int T, int H, int Hkv, int D, float eps, hipStream_t s,
+                                  int pos = -1);
 hipError_t launch_rope_qknorm_bwd(Dt dt, void* dqkv, const void* qkv, const float* rstdq, const float* rstdk,
                                   const float* cosv, const float* sinv, int N, int T, int H, int Hkv, int D,
                                   hipStream_t s);
@@ -144,6 +146,20 @@ hipError_t launch_embed_bwd(const int32_t* ids, const float* dx, float* dwte, in
                             int32_t* iscratch, float* partial, hipStream_t s);
 hipError_t launch_to_f32(Dt dt, const void* src, float* dst, size_t n, hipStream_t s);
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);
+
+// ---------------------------------------------------------------- KV-cache decode (decode.hip)
+// cache of one layer: [2][B][Hkv][Tc][D]; stores k and v heads of qkv rows b * rb + (t - t0), t in [t0, t0 + nt)
+hipError_t launch_kv_store(Dt dt, const void* qkv, void* cache, int B, int H, int Hkv, int D, int Tc, int t0, int nt,
+                           int rb, hipStream_t s);
+// y [B, H*D] = attention of the q heads of qkv rows b (one token per sequence, at position pos) over cache
+// positions 0..pos; part: decode_attn_part_floats(B, H, D, Tc) floats of scratch
+size_t decode_attn_part_floats(int B, int H, int D, int Tc);
+hipError_t launch_decode_attn(Dt dt, const void* qkv, const void* cache, float* part, void* y, int B, int H, int Hkv,
+                              int D, int Tc, int pos, hipStream_t s);
+// sum of split-K partials part[s][m][n] (s < splits, stride = elements per split) over rows m < rows:
+// mode 0 store, 1 residual add (out = in + v), 2 the MLP activation relu(v)^2, 3 fp32 store
+hipError_t launch_decode_finish(Dt dt, const float* part, int splits, size_t stride, int rows, int N, int mode,
+                                void* out, const void* in, hipStream_t s);
 
 // ---------------------------------------------------------------- optimizer step (optim.hip)
 // The six matrices of a layer (Wq, Wk, Wv, Wo, Wfc, Wproj) inside the packed matrix range: layer stride,

@@ -287,7 +287,7 @@ template <typename T, int D>
 __global__ void __launch_bounds__(256)
 rope_qknorm_fwd_kernel(T* __restrict__ qkv, float* __restrict__ rstdq, float* __restrict__ rstdk,
                        const float* __restrict__ cosv, const float* __restrict__ sinv, int N, int T_, int H, int Hkv,
-                       float eps)
+                       float eps, int pos)
 {
     constexpr int G = D / 2, L = D / 16;      // half width, lanes per head
     const int gid = blockIdx.x * (256 / L) + threadIdx.x / L;  // (n, head) with head in [0, H+Hkv)
@@ -295,7 +295,7 @@ rope_qknorm_fwd_kernel(T* __restrict__ qkv, float* __restrict__ rstdq, float* __
     const int nh = H + Hkv;
     if (gid >= N * nh) return;                // whole heads leave together (L divides 64)
     const int n = gid / nh, hd = gid % nh;
-    const int t = n % T_;
+    const int t = pos >= 0 ? pos : n % T_;      // pos >= 0: every row is a token at that position (decode)
     const int QKV = (H + 2 * Hkv) * D;
     T* v = qkv + (size_t)n * QKV + hd * D + 8 * j;   // k heads follow the q heads
     float x1[8], x2[8], c[8], sn[8];
@@ -364,14 +364,14 @@ rope_qknorm_bwd_kernel(T* __restrict__ dqkv, const T* __restrict__ qkv, const fl
 
 template <typename T>
 static hipError_t rope_fwd_t(T* qkv, float* rq, float* rk, const float* c, const float* sn, int N, int T_, int H,
-                             int Hkv, int D, float eps, hipStream_t s) {
+                             int Hkv, int D, float eps, int pos, hipStream_t s) {
     const size_t heads = (size_t)N * (H + Hkv);
     if (D == 128) {
         hipLaunchKernelGGL((rope_qknorm_fwd_kernel<T, 128>), dim3((unsigned)((heads + 31) / 32)), dim3(256), 0, s, qkv,
-                           rq, rk, c, sn, N, T_, H, Hkv, eps);
+                           rq, rk, c, sn, N, T_, H, Hkv, eps, pos);
     } else if (D == 64) {
         hipLaunchKernelGGL((rope_qknorm_fwd_kernel<T, 64>), dim3((unsigned)((heads + 63) / 64)), dim3(256), 0, s, qkv,
-                           rq, rk, c, sn, N, T_, H, Hkv, eps);
+                           rq, rk, c, sn, N, T_, H, Hkv, eps, pos);
     } else {
         return hipErrorInvalidValue;
     }
@@ -395,9 +395,9 @@ static hipError_t rope_bwd_t(T* dqkv, const T* qkv, const float* rq, const float
 }
 
 hipError_t launch_rope_qknorm_fwd(Dt dt, void* qkv, float* rstdq, float* rstdk, const float* cosv, const float* sinv,
-                                  int N, int T, int H, int Hkv, int D, float eps, hipStream_t s) {
-    if (dt == Dt::BF16) return rope_fwd_t((bf16*)qkv, rstdq, rstdk, cosv, sinv, N, T, H, Hkv, D, eps, s);
-    return rope_fwd_t((float*)qkv, rstdq, rstdk, cosv, sinv, N, T, H, Hkv, D, eps, s);
+                                  int N, int T, int H, int Hkv, int D, float eps, hipStream_t s, int pos) {
+    if (dt == Dt::BF16) return rope_fwd_t((bf16*)qkv, rstdq, rstdk, cosv, sinv, N, T, H, Hkv, D, eps, pos, s);
+    return rope_fwd_t((float*)qkv, rstdq, rstdk, cosv, sinv, N, T, H, Hkv, D, eps, pos, s);
 }
 
 hipError_t launch_rope_qknorm_bwd(Dt dt, void* dqkv, const void* qkv, const float* rstdq, const float* rstdk,

@@ -34,6 +34,9 @@ struct Plan {
     size_t g_x0[6], g_x1[6], g_a[6], g_b[6];
     int w_group[6];
     MuonShapes shapes;
+    // KV-cache decode buffers (their own region: a decode may follow a forward used as prefill)
+    int Bp;
+    size_t d_x, d_xn, d_rstd, d_qkv, d_rq, d_rk, d_y, d_act, d_part, d_attn;
 };
 
 struct Timed {
@@ -67,6 +70,7 @@ struct ncgpt_ctx {
     bool bound = false;
     int static_dev = -1;  // device whose static scratch holds the workspace (ncgpt_bind_static), else -1
     int lm_mode = NCGPT_LOGITS_STORED;  // ncgpt_set_lm_head_mode
+    bool cast_valid = false;  // the workspace holds a bf16 copy of the weights (a forward or a recasting decode)
     int loss_mode = NCGPT_LOGITS_STORED;  // the mode the last ncgpt_loss ran in
     const int32_t* ids = nullptr;
     const float* params = nullptr;
@@ -180,6 +184,20 @@ GemmDesc lm_head_desc(const ncgpt_ctx* c) {
     return d;
 }
 
+// Split-K of a decode GEMM (B rows x N, reduction K): enough workgroups of 128 x 128 tiles to cover the CUs.
+struct DecSplit {
+    int splits, k_split;
+};
+DecSplit decode_split(int N, int K) {
+    const int tiles = (N + 127) / 128;
+    int s = std::max(1, std::min(K / 64, (2 * kCUs + tiles - 1) / tiles));
+    const int per = (K / 64 + s - 1) / s;
+    DecSplit d;
+    d.k_split = per * 64;
+    d.splits = (K + d.k_split - 1) / d.k_split;
+    return d;
+}
+
 void make_plan(ncgpt_ctx* c) {
     Plan& p = c->pl;
     size_t off = 0;
@@ -268,6 +286,28 @@ void make_plan(ncgpt_ctx* c) {
         p.g_b[g] = A(items * mm * mm * 2);
     }
     p.total = std::max(p.total, off);
+
+    // decode: B rows padded to a multiple of 8 (the GEMMs' row granularity)
+    off = p.total;
+    const size_t Bp = (size_t)((c->B + 7) / 8 * 8);
+    p.Bp = (int)Bp;
+    p.d_x = A(Bp * c->C * e);
+    p.d_xn = A(Bp * c->C * e);
+    p.d_rstd = A(Bp * 4);
+    p.d_qkv = A(Bp * c->QKV * e);
+    p.d_rq = A(Bp * c->H * 4);
+    p.d_rk = A(Bp * c->Hkv * 4);
+    p.d_y = A(Bp * c->HD * e);
+    p.d_act = A(Bp * c->F * e);
+    size_t dp = 0;
+    const int64_t dshape[5][2] = {{c->QKV, c->C}, {c->C, c->HD}, {c->F, c->C}, {c->C, c->F}, {c->V, c->C}};
+    for (auto& d : dshape) {
+        const DecSplit sp = decode_split((int)d[0], (int)d[1]);
+        dp = std::max(dp, (size_t)sp.splits * Bp * d[0] * 4);
+    }
+    p.d_part = A(dp);
+    p.d_attn = A(decode_attn_part_floats((int)c->B, (int)c->H, (int)c->D, (int)c->T) * 4);
+    p.total = off;
 }
 
 // ---------------------------------------------------------------- launch wrapper with optional timing
@@ -426,6 +466,7 @@ ncgpt_status bind_common(ncgpt_ctx* c, uint8_t* ws, size_t bytes, void* stream) 
     if (e != hipSuccess) return hip_fail(c, e, "bind uploads");
     c->bound = true;
     c->state = 0;
+    c->cast_valid = false;
     return NCGPT_OK;
 }
 
@@ -584,6 +625,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
         const size_t n = (size_t)(c->P - c->VC);
         TRY(launch(c, "cast_bf16", 0.0, (double)n * 6,
                    [&] { return launch_cast_bf16(params + c->VC, c->ws + p.wcast, n, c->stream); }));
+        c->cast_valid = true;
     }
     TRY(launch(c, "embed_fwd", 0.0, (double)N * C * (4 + e) + N * 4.0, [&] {
         return launch_embed_fwd(dt, ids, params, c->ws + p.x0, N, C, V, flag, c->stream);
@@ -965,6 +1007,120 @@ ncgpt_status ncgpt_optim_step(ncgpt_ctx* c, float* params, const float* grads, f
         }));
     }
     return NCGPT_OK;
+}
+
+size_t ncgpt_kv_cache_bytes(const ncgpt_ctx* c) {
+    if (!c) return 0;
+    return (size_t)c->L * 2 * c->B * c->Hkv * c->T * c->D * c->esz;
+}
+
+ncgpt_status ncgpt_kv_fill(ncgpt_ctx* c, void* kv_cache, int32_t n) {
+    if (!c) return NCGPT_EINVAL;
+    TRY(check_bound(c));
+    if (c->state < 1) return fail(c, NCGPT_ESTATE, "ncgpt_kv_fill needs the k and v of an ncgpt_forward");
+    if (!kv_cache || n < 0 || n > c->T) return fail(c, NCGPT_EINVAL, "null cache or position count outside [0, seq_len]");
+    const Plan& p = c->pl;
+    const size_t per_layer = (size_t)2 * c->B * c->Hkv * c->T * c->D * c->esz;
+    for (int l = 0; l < c->L; ++l) {
+        TRY(launch(c, "kv_fill", 0.0, (double)per_layer * n / c->T * 2, [&] {
+            return launch_kv_store(c->dt, c->ws + c->lay(l, p.l_qkv), static_cast<uint8_t*>(kv_cache) + l * per_layer,
+                                   (int)c->B, (int)c->H, (int)c->Hkv, (int)c->D, (int)c->T, 0, n, (int)c->T, c->stream);
+        }));
+    }
+    return NCGPT_OK;
+}
+
+ncgpt_status ncgpt_decode_step(ncgpt_ctx* c, const int32_t* ids, const float* params, void* kv_cache, int32_t pos,
+                               float* logits, int recast) {
+    if (!c) return NCGPT_EINVAL;
+    TRY(check_bound(c));
+    if (!ids || !params || !kv_cache || !logits) return fail(c, NCGPT_EINVAL, "null ids, params, cache or logits");
+    if (pos < 0 || pos >= c->T) return fail(c, NCGPT_EINVAL, "position outside [0, seq_len)");
+    const Plan& p = c->pl;
+    const Dt dt = c->dt;
+    const int B = (int)c->B, Bp = p.Bp, C = (int)c->C, F = (int)c->F, QKV = (int)c->QKV, HD = (int)c->HD;
+    const int V = (int)c->V;
+    const float eps = c->cfg.norm_eps;
+    const size_t e = c->esz;
+    // the fp32 weights of this call (weight() reads them); the forward's pointer is restored on return, so a
+    // pending backward still sees its own parameters
+    struct Restore {
+        ncgpt_ctx* c;
+        const float* saved;
+        ~Restore() { c->params = saved; }
+    } restore{c, c->params};
+    c->params = params;
+    if (dt == Dt::BF16) {
+        if (recast) {
+            const size_t n = (size_t)(c->P - c->VC);
+            TRY(launch(c, "cast_bf16", 0.0, (double)n * 6,
+                       [&] { return launch_cast_bf16(params + c->VC, c->ws + p.wcast, n, c->stream); }));
+            c->cast_valid = true;
+        } else if (!c->cast_valid) {
+            return fail(c, NCGPT_ESTATE, "no bf16 weight copy yet: pass recast = 1");
+        }
+    }
+    uint8_t* x = c->ws + p.d_x;
+    uint8_t* xn = c->ws + p.d_xn;
+    uint8_t* qkv = c->ws + p.d_qkv;
+    uint8_t* y = c->ws + p.d_y;
+    uint8_t* act = c->ws + p.d_act;
+    float* part = c->at<float>(p.d_part);
+    uint32_t* flag = c->at<uint32_t>(p.flag);
+    // padding rows stay zero: every row is independent, the padded ones are never read back
+    TRY(launch(c, "decode_zero", 0.0, 0.0, [&] {
+        hipError_t st = launch_zero_u32(reinterpret_cast<uint32_t*>(x), (size_t)Bp * C * e / 4, c->stream);
+        return st == hipSuccess ? launch_zero_u32(reinterpret_cast<uint32_t*>(y), (size_t)Bp * HD * e / 4, c->stream) : st;
+    }));
+    TRY(launch(c, "embed_fwd", 0.0, (double)B * C * (4 + e), [&] {
+        return launch_embed_fwd(dt, ids, params, x, B, C, V, flag, c->stream);
+    }));
+    // one B-row GEMM: split-K partials, then the finish (mode as launch_decode_finish)
+    auto dgemm = [&](const char* tag, const void* A, int lda, const void* W, int N, int K, int mode, void* out,
+                     const void* in, int rows) -> ncgpt_status {
+        const DecSplit sp = decode_split(N, K);
+        GemmDesc d;
+        d.A = A; d.lda = lda; d.B = W; d.ldb = K;
+        d.M = Bp; d.N = N; d.K = K;
+        d.epi = Epi::SplitK; d.out = part; d.ldo = N;
+        d.splits = sp.splits; d.k_split = sp.k_split; d.split_stride = (size_t)Bp * N;
+        d.tile = 2; d.loop = GemmLoop::Ring8;
+        TRY(gemm(c, d, tag));
+        return launch(c, "decode_finish", 0.0, (double)Bp * N * 4 * (sp.splits + 1), [&] {
+            return launch_decode_finish(dt, part, sp.splits, (size_t)Bp * N, rows, N, mode, out, in, c->stream);
+        });
+    };
+    const size_t cache_layer = (size_t)2 * B * c->Hkv * c->T * c->D * e;
+    for (int l = 0; l < c->L; ++l) {
+        uint8_t* cache = static_cast<uint8_t*>(kv_cache) + l * cache_layer;
+        TRY(launch(c, "rmsnorm_fwd", 0.0, (double)Bp * C * 2 * e, [&] {
+            return launch_rmsnorm_fwd(dt, x, xn, c->at<float>(p.d_rstd), Bp, C, eps, c->stream);
+        }));
+        TRY(dgemm("dec_qkv", xn, C, weight(c, l, 0), QKV, C, 0, qkv, nullptr, Bp));
+        TRY(launch(c, "rope_qknorm_fwd", 0.0, (double)B * (c->H + c->Hkv) * c->D * 2 * e, [&] {
+            return launch_rope_qknorm_fwd(dt, qkv, c->at<float>(p.d_rq), c->at<float>(p.d_rk), c->at<float>(p.cosv),
+                                          c->at<float>(p.sinv), B, (int)c->T, (int)c->H, (int)c->Hkv, (int)c->D, eps,
+                                          c->stream, pos);
+        }));
+        TRY(launch(c, "kv_store", 0.0, (double)B * 2 * c->KD * e * 2, [&] {
+            return launch_kv_store(dt, qkv, cache, B, (int)c->H, (int)c->Hkv, (int)c->D, (int)c->T, pos, 1, 1,
+                                   c->stream);
+        }));
+        TRY(launch(c, "decode_attn", 0.0, (double)B * c->Hkv * (pos + 1) * c->D * 2 * e, [&] {
+            return launch_decode_attn(dt, qkv, cache, c->at<float>(p.d_attn), y, B, (int)c->H, (int)c->Hkv,
+                                      (int)c->D, (int)c->T, pos, c->stream);
+        }));
+        TRY(dgemm("dec_attn_out", y, HD, weight(c, l, 3), C, HD, 1, x, x, Bp));
+        TRY(launch(c, "rmsnorm_fwd", 0.0, (double)Bp * C * 2 * e, [&] {
+            return launch_rmsnorm_fwd(dt, x, xn, c->at<float>(p.d_rstd), Bp, C, eps, c->stream);
+        }));
+        TRY(dgemm("dec_fc", xn, C, weight(c, l, 4), F, C, 2, act, nullptr, Bp));
+        TRY(dgemm("dec_proj", act, F, weight(c, l, 5), C, F, 1, x, x, Bp));
+    }
+    TRY(launch(c, "rmsnorm_fwd", 0.0, (double)Bp * C * 2 * e, [&] {
+        return launch_rmsnorm_fwd(dt, x, xn, c->at<float>(p.d_rstd), Bp, C, eps, c->stream);
+    }));
+    return dgemm("dec_lm_head", xn, C, weight(c, -1, 1), V, C, 3, logits, nullptr, B);
 }
 
 ncgpt_status ncgpt_check(ncgpt_ctx* c) {

@@ -100,6 +100,7 @@ _lib = None
 
 EXPORTS = ["ncgpt_num_params", "ncgpt_param_slice", "ncgpt_create", "ncgpt_workspace_size", "ncgpt_bind",
            "ncgpt_bind_static", "ncgpt_set_lm_head_mode", "ncgpt_optim_state_size", "ncgpt_optim_step",
+           "ncgpt_kv_cache_bytes", "ncgpt_kv_fill", "ncgpt_decode_step",
            "ncgpt_forward", "ncgpt_loss", "ncgpt_backward", "ncgpt_check", "ncgpt_probe_numel", "ncgpt_probe",
            "ncgpt_timing_enable", "ncgpt_timing_reset", "ncgpt_timing_count", "ncgpt_timing_get",
            "ncgpt_last_error", "ncgpt_destroy"]
@@ -125,6 +126,10 @@ def lib():
         L.ncgpt_optim_state_size.argtypes = [P(_Config)]
         L.ncgpt_optim_state_size.restype = ct.c_size_t
         L.ncgpt_optim_step.argtypes = [vp, vp, vp, vp, ct.c_int64, P(_OptimConfig)]
+        L.ncgpt_kv_cache_bytes.argtypes = [vp]
+        L.ncgpt_kv_cache_bytes.restype = ct.c_size_t
+        L.ncgpt_kv_fill.argtypes = [vp, vp, ct.c_int32]
+        L.ncgpt_decode_step.argtypes = [vp, vp, vp, vp, ct.c_int32, vp, ct.c_int]
         L.ncgpt_forward.argtypes = [vp, vp, vp]
         L.ncgpt_loss.argtypes = [vp, vp, vp]
         L.ncgpt_backward.argtypes = [vp, vp, ct.c_int, ct.c_float]
@@ -141,7 +146,8 @@ def lib():
         L.ncgpt_destroy.argtypes = [vp]
         L.ncgpt_destroy.restype = None
         for name in EXPORTS:
-            if name not in ("ncgpt_num_params", "ncgpt_last_error", "ncgpt_destroy", "ncgpt_optim_state_size"):
+            if name not in ("ncgpt_num_params", "ncgpt_last_error", "ncgpt_destroy", "ncgpt_optim_state_size",
+                            "ncgpt_kv_cache_bytes"):
                 getattr(L, name).restype = ct.c_int
         _lib = L
     return _lib
@@ -233,6 +239,29 @@ class Model:
         pg = _ptr(grads, torch.float32, self.n_params, "grads")
         ps = _ptr(state, torch.float32, optim_state_size(self.cfg), "state")
         self._check(lib().ncgpt_optim_step(self._ctx, pp, pg, ps, int(step), ct.byref(opt._c())))
+
+    # -- KV-cache decode -------------------------------------------------------------------------
+    def kv_cache(self) -> torch.Tensor:
+        """A zeroed cache of the context's shape, in the compute dtype."""
+        return torch.zeros(self.kv_cache_bytes(), dtype=torch.uint8, device="cuda")
+
+    def kv_cache_bytes(self) -> int:
+        return int(lib().ncgpt_kv_cache_bytes(self._ctx))
+
+    def kv_fill(self, cache: torch.Tensor, n: int):
+        self._check(lib().ncgpt_kv_fill(self._ctx, ct.c_void_p(cache.data_ptr()), int(n)))
+
+    def decode_step(self, ids: torch.Tensor, params: torch.Tensor, cache: torch.Tensor, pos: int,
+                    logits: torch.Tensor = None, recast: bool = True) -> torch.Tensor:
+        """Logits fp32 [batch, vocab] of the tokens ids [batch] at position pos."""
+        if logits is None:
+            logits = torch.empty(self.cfg.batch * self.cfg.vocab_size, dtype=torch.float32, device="cuda")
+        pi = _ptr(ids, torch.int32, self.cfg.batch, "ids")
+        pp = _ptr(params, torch.float32, self.n_params, "params")
+        pl = _ptr(logits, torch.float32, self.cfg.batch * self.cfg.vocab_size, "logits")
+        self._check(lib().ncgpt_decode_step(self._ctx, pi, pp, ct.c_void_p(cache.data_ptr()), int(pos), pl,
+                                            1 if recast else 0))
+        return logits
 
     def set_lm_head_mode(self, mode: int):
         """LOGITS_STORED (default) or LOGITS_RECOMPUTED: where the backward's dz comes from."""

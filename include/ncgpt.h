@@ -167,6 +167,27 @@ size_t ncgpt_optim_state_size(const ncgpt_config* cfg);
 ncgpt_status ncgpt_optim_step(ncgpt_ctx* ctx, float* params, const float* grads, float* state, int64_t step,
                               const ncgpt_optim_config* oc);
 
+/* KV-cache decode ("nanochat 项目深度分析", engine section: a preallocated cache (layers, 2, B, H, T, D) with
+ * a position pointer).  The cache is caller-owned device memory in the compute dtype, laid out
+ * [n_layer][2 (k, v)][batch][n_kv_head][seq_len][head_dim]; k is stored after RoPE and QK-norm, as attention
+ * reads it.  seq_len is the cache capacity. */
+size_t ncgpt_kv_cache_bytes(const ncgpt_ctx* ctx);
+
+/* Prefill: copy k and v of positions [0, n) of every sequence from the last ncgpt_forward into the cache
+ * (a prompt of n tokens run through ncgpt_forward; the forward's positions >= n do not affect positions < n).
+ * ESTATE before ncgpt_forward or after ncgpt_optim_step; EINVAL for n outside [0, seq_len]. */
+ncgpt_status ncgpt_kv_fill(ncgpt_ctx* ctx, void* kv_cache, int32_t n);
+
+/* One decode step: ids int32 [batch] are the tokens at position pos (0 <= pos < seq_len) of each sequence;
+ * positions < pos must already be in the cache (ncgpt_kv_fill or earlier steps).  Runs the block stack on
+ * these batch tokens, stores their k and v at pos, and writes the next-token logits, fp32 [batch, vocab],
+ * to logits.  It equals the causal forward of the sequences at their last position.  recast = 1 casts params
+ * to the bf16 weight copy first (NCGPT_BF16); 0 reuses the copy of the last ncgpt_forward or recasting step
+ * (ESTATE if there is none; params changed since make it stale).  Uses its own scratch: a pending
+ * ncgpt_loss / ncgpt_backward of the last forward is not disturbed. */
+ncgpt_status ncgpt_decode_step(ncgpt_ctx* ctx, const int32_t* ids, const float* params, void* kv_cache, int32_t pos,
+                               float* logits, int recast);
+
 /* Synchronise the bound stream and report device-side errors: EDEVICE if the flag is set (the flag is then
  * cleared), EHIP on an asynchronous HIP error, OK otherwise. */
 ncgpt_status ncgpt_check(ncgpt_ctx* ctx);

@@ -391,3 +391,20 @@ def optim_step(cfg: OracleConfig, params, grads, state, t, opt: OptimConfig = Op
     D = ct.POINTER(ct.c_double)
     lib().orc_optim_step(ct.byref(cfg._c()), p.ctypes.data_as(D), pg, st.ctypes.data_as(D), t, ct.byref(opt._c()))
     return p, st
+
+
+# ---------------------------------------------------------------- decode
+
+def last_logits(cfg: OracleConfig, ids, params):
+    """Next-token logits at the last position of each sequence of ids [B, t]: the causal forward over the
+    whole prefix (a KV-cache decode step must equal it), then the final-norm row times lm_head^T (a numpy
+    matmul).  float64 [B, V]."""
+    ids = np.asarray(ids)
+    B, t = ids.shape
+    c = OracleConfig(cfg.n_layer, cfg.n_embd, cfg.n_head, cfg.n_kv_head, cfg.head_dim, cfg.mlp_dim, cfg.vocab_size,
+                     B, t, cfg.rope_base, cfg.norm_eps)
+    _, acts = forward(c, ids, ids, params)
+    xf = acts["xf"].reshape(B, t, cfg.n_embd)[:, -1]
+    off, r, k = param_slice(c, -1, 1)
+    W = np.asarray(params, dtype=np.float64)[off:off + r * k].reshape(r, k)
+    return xf @ W.T

@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = ncgpt.lib()
     names = declared_functions()
-    assert len(names) >= 21
+    assert len(names) >= 24
     for n in names:
         assert hasattr(L, n), n
     assert sorted(ncgpt.EXPORTS) == names
