@@ -35,6 +35,10 @@
  *  - attention scale 1/sqrt(D); kv head of query head h is h / (H/Hkv);
  *    causal mask j <= t inside one sequence.
  *  - loss is the mean over targets >= 0; negative targets are ignored.
+ *  - block variants (off by default): the "logit stabilisation" woshipm.com
+ *    §三 item 1 names without a formula is read as the tanh soft-cap
+ *    z <- c tanh(z / c); an RMSNorm of the embedding output is the
+ *    embedding-norm variant.
  *
  * Parity: every function here is pinned by tests/test_oracle_*.py (closed
  * forms, invariants, special cases that reduce to library routines, and
@@ -48,6 +52,8 @@
 typedef struct {
     int32_t n_layer, n_embd, n_head, n_kv_head, head_dim, mlp_dim, vocab_size, batch, seq_len;
     double rope_base, norm_eps;
+    double logit_softcap;  /* > 0: logits z become c tanh(z / c) before the loss (a block variant) */
+    int32_t embed_norm;    /* 1: RMSNorm right after the embedding (a block variant) */
 } orc_config;
 
 /* ------------------------------------------------------------------ */
@@ -380,6 +386,23 @@ void orc_cross_entropy_bwd(const double* z, const int32_t* targets, int64_t rows
     }
 }
 
+/* Soft-cap of the logits, z <- c tanh(z / c) (c > 0; c <= 0 leaves z alone), and its backward: with the
+ * uncapped z, dz <- dz (1 - tanh(z / c)^2). */
+void orc_softcap_fwd(double* z, int64_t n, double c)
+{
+    if (c <= 0.0) return;
+    for (int64_t i = 0; i < n; ++i) z[i] = c * tanh(z[i] / c);
+}
+
+void orc_softcap_bwd(const double* z, double* dz, int64_t n, double c)
+{
+    if (c <= 0.0) return;
+    for (int64_t i = 0; i < n; ++i) {
+        const double t = tanh(z[i] / c);
+        dz[i] *= 1.0 - t * t;
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* the whole model                                                     */
 
@@ -389,7 +412,7 @@ void orc_cross_entropy_bwd(const double* z, const int32_t* targets, int64_t rows
  *                QK-norm, v as projected), rstdq [N,H], rstdk [N,Hkv],
  *                y [N,HD], lse_att [B,H,T], xmid [N,C], xn2 [N,C], rstd2 [N],
  *                a [N,F] (= max(0, xn2 Wfc^T)), xout [N,C]
- *   xf [N,C], rstdf [N], lse [N], loss_rows [N]
+ *   xf [N,C], rstdf [N], lse [N], loss_rows [N], x0n [N,C], rstd0 [N]
  * orc_acts_layout fills the element offsets of each piece. */
 enum {
     ORC_A_XN1 = 0, ORC_A_RSTD1, ORC_A_QKV, ORC_A_RSTDQ, ORC_A_RSTDK, ORC_A_Y, ORC_A_LSEATT,
@@ -397,7 +420,7 @@ enum {
 };
 
 typedef struct {
-    int64_t x0, layer0, layer_stride, per_layer[ORC_A_NLAYER], xf, rstdf, lse, loss_rows, total;
+    int64_t x0, layer0, layer_stride, per_layer[ORC_A_NLAYER], xf, rstdf, lse, loss_rows, x0n, rstd0, total;
 } orc_acts_layout;
 
 void orc_get_acts_layout(const orc_config* c, orc_acts_layout* o)
@@ -416,7 +439,9 @@ void orc_get_acts_layout(const orc_config* c, orc_acts_layout* o)
     o->rstdf = end + N * C;
     o->lse = o->rstdf + N;
     o->loss_rows = o->lse + N;
-    o->total = o->loss_rows + N;
+    o->x0n = o->loss_rows + N;        /* the residual stream's start: x0, or rms(x0) with embed_norm */
+    o->rstd0 = o->x0n + N * C;
+    o->total = o->rstd0 + N;
 }
 
 static int check_config(const orc_config* c)
@@ -465,6 +490,8 @@ static int64_t model_forward(const orc_config* c, const int32_t* ids, const int3
         memcpy(x + n * C, p + off + (int64_t)ids[n] * C, sizeof(double) * (size_t)C);
     }
     memcpy(acts + lay.x0, x, sizeof(double) * (size_t)(N * C));
+    if (c->embed_norm) orc_rmsnorm_fwd(acts + lay.x0, N, C, eps, x, acts + lay.rstd0);
+    memcpy(acts + lay.x0n, x, sizeof(double) * (size_t)(N * C));
 
     for (int l = 0; l < c->n_layer; ++l) {
         double* A = acts + lay.layer0 + (int64_t)l * lay.layer_stride;
@@ -520,6 +547,7 @@ static int64_t model_forward(const orc_config* c, const int32_t* ids, const int3
         int64_t nb = N - n0 < blk ? N - n0 : blk;
         double part;
         orc_linear_fwd(xf + n0 * C, p + off, nb, C, V, z);
+        orc_softcap_fwd(z, nb * V, c->logit_softcap);
         int64_t vb = orc_cross_entropy_fwd(z, targets + n0, nb, V, acts + lay.lse + n0, acts + lay.loss_rows + n0, &part);
         if (vb > 0) total += part * (double)vb;
         valid += vb;
@@ -598,7 +626,16 @@ int64_t orc_grad_f64(const orc_config* c, const int32_t* ids, const int32_t* tar
     for (int64_t n0 = 0; n0 < N; n0 += blk) {
         int64_t nb = N - n0 < blk ? N - n0 : blk;
         orc_linear_fwd(xf + n0 * C, p + off, nb, C, V, z);
-        orc_cross_entropy_bwd(z, targets + n0, nb, V, valid, grad_scale, dz);
+        if (c->logit_softcap > 0.0) {
+            double* zc = (double*)malloc(sizeof(double) * (size_t)(nb * V));
+            memcpy(zc, z, sizeof(double) * (size_t)(nb * V));
+            orc_softcap_fwd(zc, nb * V, c->logit_softcap);
+            orc_cross_entropy_bwd(zc, targets + n0, nb, V, valid, grad_scale, dz);
+            orc_softcap_bwd(z, dz, nb * V, c->logit_softcap);
+            free(zc);
+        } else {
+            orc_cross_entropy_bwd(z, targets + n0, nb, V, valid, grad_scale, dz);
+        }
         orc_linear_bwd(xf + n0 * C, p + off, dz, nb, C, V, dxf + n0 * C, grads + off, 1);
     }
     free(z);
@@ -657,7 +694,8 @@ int64_t orc_grad_f64(const orc_config* c, const int32_t* ids, const int32_t* tar
         orc_rmsnorm_bwd(xn1, A + lay.per_layer[ORC_A_RSTD1], dnrm, N, C, dx, 1);
     }
 
-    /* embedding: dwte[ids[n]] += dx0[n] */
+    /* embedding norm, then the embedding: dwte[ids[n]] += dx0[n] */
+    if (c->embed_norm) orc_rmsnorm_bwd(acts + lay.x0n, acts + lay.rstd0, dx, N, C, dx, 0);
     orc_param_slice(c, -1, 0, &off, &rr, &cc);
     for (int64_t n = 0; n < N; ++n)
         for (int64_t i = 0; i < C; ++i) grads[off + (int64_t)ids[n] * C + i] += dx[n * C + i];

@@ -31,9 +31,11 @@
 #include <stdlib.h>
 #include <string.h>
 
-typedef struct {
+typedef struct {   /* the layout of ncgpt_oracle.c's config */
     int32_t n_layer, n_embd, n_head, n_kv_head, head_dim, mlp_dim, vocab_size, batch, seq_len;
     double rope_base, norm_eps;
+    double logit_softcap;
+    int32_t embed_norm;
 } orc_config;
 
 int orc_param_slice(const orc_config* c, int layer, int which, int64_t* offset, int64_t* rows, int64_t* cols);

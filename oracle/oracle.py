@@ -24,13 +24,15 @@ LAYER_ACTS = ["xn1", "rstd1", "qkv", "rstdq", "rstdk", "y", "lse_att", "xmid", "
 class _Cfg(ct.Structure):
     _fields_ = [(n, ct.c_int32) for n in ("n_layer", "n_embd", "n_head", "n_kv_head", "head_dim", "mlp_dim",
                                            "vocab_size", "batch", "seq_len")] + \
-               [("rope_base", ct.c_double), ("norm_eps", ct.c_double)]
+               [("rope_base", ct.c_double), ("norm_eps", ct.c_double), ("logit_softcap", ct.c_double),
+                ("embed_norm", ct.c_int32)]
 
 
 class _Layout(ct.Structure):
     _fields_ = [("x0", ct.c_int64), ("layer0", ct.c_int64), ("layer_stride", ct.c_int64),
                 ("per_layer", ct.c_int64 * len(LAYER_ACTS)), ("xf", ct.c_int64), ("rstdf", ct.c_int64),
-                ("lse", ct.c_int64), ("loss_rows", ct.c_int64), ("total", ct.c_int64)]
+                ("lse", ct.c_int64), ("loss_rows", ct.c_int64), ("x0n", ct.c_int64), ("rstd0", ct.c_int64),
+                ("total", ct.c_int64)]
 
 
 class _Optim(ct.Structure):
@@ -80,10 +82,13 @@ class OracleConfig:
     seq_len: int
     rope_base: float = 10000.0
     norm_eps: float = 2.0 ** -23
+    logit_softcap: float = 0.0   # block variant: logits z -> c tanh(z / c) when c > 0
+    embed_norm: int = 0          # block variant: RMSNorm right after the embedding
 
     def _c(self):
         return _Cfg(self.n_layer, self.n_embd, self.n_head, self.n_kv_head, self.head_dim, self.mlp_dim,
-                    self.vocab_size, self.batch, self.seq_len, self.rope_base, self.norm_eps)
+                    self.vocab_size, self.batch, self.seq_len, self.rope_base, self.norm_eps, self.logit_softcap,
+                    self.embed_norm)
 
 
 def lib():
@@ -325,6 +330,7 @@ def forward(cfg: OracleConfig, ids, targets, params):
     acts["rstdf"] = buf[lay.rstdf:lay.rstdf + N]
     acts["lse"] = buf[lay.lse:lay.lse + N]
     acts["loss_rows"] = buf[lay.loss_rows:lay.loss_rows + N]
+    acts["x0n"] = buf[lay.x0n:lay.x0n + N * C].reshape(N, C)
     return loss.value, acts
 
 
@@ -402,9 +408,10 @@ def last_logits(cfg: OracleConfig, ids, params):
     ids = np.asarray(ids)
     B, t = ids.shape
     c = OracleConfig(cfg.n_layer, cfg.n_embd, cfg.n_head, cfg.n_kv_head, cfg.head_dim, cfg.mlp_dim, cfg.vocab_size,
-                     B, t, cfg.rope_base, cfg.norm_eps)
+                     B, t, cfg.rope_base, cfg.norm_eps, cfg.logit_softcap, cfg.embed_norm)
     _, acts = forward(c, ids, ids, params)
     xf = acts["xf"].reshape(B, t, cfg.n_embd)[:, -1]
     off, r, k = param_slice(c, -1, 1)
     W = np.asarray(params, dtype=np.float64)[off:off + r * k].reshape(r, k)
-    return xf @ W.T
+    z = xf @ W.T
+    return cfg.logit_softcap * np.tanh(z / cfg.logit_softcap) if cfg.logit_softcap > 0 else z

@@ -167,6 +167,8 @@ def torch_model_loss(cfg, ids, tg, params64):
 
     idx = torch.tensor(ids, dtype=torch.long)
     x = W(-1, 0)[idx]
+    if cfg.embed_norm:          # block variant: RMSNorm right after the embedding
+        x = norm(x)
     for l in range(cfg.n_layer):
         u = norm(x)
         q = F.linear(u, W(l, 0)).view(B, T, H, D)
@@ -179,6 +181,8 @@ def torch_model_loss(cfg, ids, tg, params64):
         u = norm(x)
         x = x + F.linear(F.linear(u, W(l, 4)).clamp_min(0.0) ** 2, W(l, 5))  # ReLU^2 (§2.1 item 4)
     z = F.linear(norm(x), W(-1, 1))
+    if cfg.logit_softcap > 0:   # block variant: tanh soft-cap of the logits
+        z = cfg.logit_softcap * torch.tanh(z / cfg.logit_softcap)
     t = torch.tensor(tg, dtype=torch.long)
     t = torch.where(t < 0, torch.full_like(t, -100), t)
     loss = F.cross_entropy(z.view(-1, z.size(-1)), t.view(-1), ignore_index=-100)
