@@ -59,6 +59,17 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// ---- logit soft-cap: c tanh(z / c) = c - 2c / (e^{2z/c} + 1), one exp and one reciprocal; saturates at +-c
+// (e^{2z/c} -> inf gives c, -> 0 gives -c) without a NaN ----
+__device__ __forceinline__ float softcap_fwd(float z, const SoftCap& s) {
+    return fmaf(-s.c2, __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(z * s.k) + 1.0f), s.c);
+}
+// d(capped) / dz from the capped value zc: 1 - tanh^2 = 1 - (zc / c)^2
+__device__ __forceinline__ float softcap_grad(float zc, const SoftCap& s) {
+    const float q = zc * s.ic;
+    return fmaf(-q, q, 1.0f);
+}
+
 __device__ __forceinline__ void raise_error(uint32_t* flag, uint32_t bit) { atomicOr(flag, bit); }
 
 }  // namespace ncgpt

@@ -181,11 +181,12 @@ hipError_t launch_decode_attn(Dt dt, const void* qkv, const void* cache, float* 
 // ---------------------------------------------------------------- split-K finish of B-row GEMMs
 // v = sum over splits of part[s][m][n] (in split order); rows m < rows only.
 //   mode 0: out = cd(v);  1: out = cd(in + v) (residual; in may equal out);
-//   mode 2: out = cd(a * a), a = cd(max(v, 0)) (the MLP activation);  3: out(f32) = v.
+//   mode 2: out = cd(a * a), a = cd(max(v, 0)) (the MLP activation);  3: out(f32) = v, or c tanh(v / c)
+//   with a soft-cap (the logits).
 template <typename T>
 __global__ void __launch_bounds__(256)
 decode_finish_kernel(const float* __restrict__ part, int splits, size_t stride, int rows, int N, int mode,
-                     void* __restrict__ out, const T* in)
+                     void* __restrict__ out, const T* in, SoftCap cap)
 {
     const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= (size_t)rows * N) return;
@@ -197,6 +198,10 @@ decode_finish_kernel(const float* __restrict__ part, int splits, size_t stride, 
         for (int e = 0; e < 4; ++e) v[e] += p[e];
     }
     if (mode == 3) {
+        if (cap.c > 0.0f) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = softcap_fwd(v[e], cap);
+        }
         Vec4<float>::store((float*)out + i, v);
         return;
     }
@@ -216,17 +221,17 @@ decode_finish_kernel(const float* __restrict__ part, int splits, size_t stride, 
 }
 
 hipError_t launch_decode_finish(Dt dt, const float* part, int splits, size_t stride, int rows, int N, int mode,
-                                void* out, const void* in, hipStream_t s) {
+                                void* out, const void* in, hipStream_t s, const SoftCap& cap) {
     if (N % 4) return hipErrorInvalidValue;
     const size_t n4 = (size_t)rows * N / 4;
     if (n4 == 0) return hipSuccess;
     const dim3 grid((unsigned)((n4 + 255) / 256));
     if (dt == Dt::BF16)
         hipLaunchKernelGGL(decode_finish_kernel<bf16>, grid, dim3(256), 0, s, part, splits, stride, rows, N, mode, out,
-                           (const bf16*)in);
+                           (const bf16*)in, cap);
     else
         hipLaunchKernelGGL(decode_finish_kernel<float>, grid, dim3(256), 0, s, part, splits, stride, rows, N, mode, out,
-                           (const float*)in);
+                           (const float*)in, cap);
     return hipGetLastError();
 }
 

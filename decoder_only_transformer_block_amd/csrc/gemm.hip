@@ -330,10 +330,20 @@ struct ECeStats {
     int nblk;
     float* zt;               // [M]
     const int32_t* targets;  // [M]
+    SoftCap cap;
 
+    // acc is the kernel's accumulator of this tile, dead after the epilogue: a soft-cap rewrites it in place
     template <int FM, int FN>
-    __device__ void tile(const f32x16 (&acc)[FM][FN], int m0, int n0, int M, int N, int lane) const {
+    __device__ void tile(f32x16 (&acc)[FM][FN], int m0, int n0, int M, int N, int lane) const {
         const int h = lane >> 5, l32 = lane & 31;
+        if (cap.c > 0.0f) {                       // uniform: the soft-capped variant
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] = softcap_fwd(acc[i][j][r], cap);
+        }
         // the rounded logits leave first, so their stores drain while the statistics are formed
         if (out) store_tile<FM, FN>(acc, m0, n0, 0, M, N, lane, EStoreCd<bf16>{out, ldo});
         if (n0 >= N) return;                      // wave-uniform: the block lies past a ragged vocab edge
@@ -394,10 +404,20 @@ struct EDz {
     const int32_t* targets;
     const float* inv_valid;
     float grad_scale;
+    SoftCap cap;
 
     template <int FM, int FN>
-    __device__ void tile(const f32x16 (&acc)[FM][FN], int m0, int n0, int M, int N, int lane) const {
+    __device__ void tile(f32x16 (&acc)[FM][FN], int m0, int n0, int M, int N, int lane) const {
         const int h = lane >> 5, l32 = lane & 31;
+        const bool capped = cap.c > 0.0f;         // uniform
+        if (capped) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] = softcap_fwd(acc[i][j][r], cap);
+        }
         // every row's target and log2-domain lse first (one memory wait per tile)
         int tv[FM];
         float l2v[FM];
@@ -438,6 +458,10 @@ struct EDz {
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
                             if (n + e == t) r[e] = k * (__builtin_amdgcn_exp2f(z[e] * kLog2eF - l2) - 1.0f);
+                    }
+                    if (capped) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) r[e] = r[e] * softcap_grad(z[e], cap);
                     }
                     if (m < M && n < N) st8(out + (size_t)m * ldo + n, r);
                 }
@@ -537,7 +561,7 @@ struct ERopeNorm {
 };
 
 template <int FM, int FN, class E, int RG = FM>
-__device__ __forceinline__ void epilogue(const f32x16 (&acc)[FM][FN], int m0, int n0, int split, int M, int N,
+__device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], int m0, int n0, int split, int M, int N,
                                          int lane, const E& epi) {
     if constexpr (TileEpi<E>::value) epi.template tile<FM, FN>(acc, m0, n0, M, N, lane);
     else store_tile<FM, FN, E, RG>(acc, m0, n0, split, M, N, lane, epi);
@@ -1076,11 +1100,11 @@ static hipError_t dispatch_epi(const GemmDesc& d, hipStream_t s) {
         case Epi::SplitK: return run(ESplitK{(float*)d.out, d.ldo, d.split_stride});  // B-row decode products
         case Epi::CeStats:
             if constexpr (sizeof(T) == 2)
-                return run(ECeStats{(bf16*)d.out, d.ldo, (float2*)d.part, d.nblk, d.zt, d.targets});
+                return run(ECeStats{(bf16*)d.out, d.ldo, (float2*)d.part, d.nblk, d.zt, d.targets, d.cap});
             break;
         case Epi::Dz:
             if constexpr (sizeof(T) == 2)
-                return run(EDz{(bf16*)d.out, d.ldo, d.lse, d.targets, d.inv_valid, d.grad_scale});
+                return run(EDz{(bf16*)d.out, d.ldo, d.lse, d.targets, d.inv_valid, d.grad_scale, d.cap});
             break;
         case Epi::RopeNorm:
             if constexpr (sizeof(T) == 2) {

@@ -13,6 +13,22 @@ enum class Dt : int { F32 = 0, BF16 = 1 };
 // the host in ncgpt_check.
 enum : uint32_t { kErrBadToken = 1u, kErrNoTargets = 2u, kErrBadTarget = 4u };
 
+// Logit soft-cap z -> c tanh(z / c) (off when c == 0).  The constants are formed once on the host, so every
+// kernel that caps or differentiates a logit uses the same float values: k = 2 log2(e) / c, ic = 1 / c.
+struct SoftCap {
+    float c = 0.0f, c2 = 0.0f, k = 0.0f, ic = 0.0f;
+};
+inline SoftCap make_softcap(float c) {
+    SoftCap s;
+    if (c > 0.0f) {
+        s.c = c;
+        s.c2 = 2.0f * c;
+        s.k = (float)(2.0 * 1.4426950408889634 / (double)c);
+        s.ic = (float)(1.0 / (double)c);
+    }
+    return s;
+}
+
 // ---------------------------------------------------------------- GEMM
 // C[m][n] = sum_k A(m,k) * B(n,k), fp32 accumulation.
 //   a_kcontig: A(m,k) = A[m*lda + k]  else A(m,k) = A[k*lda + m]
@@ -27,9 +43,11 @@ enum class Epi : int {
     Grad,        // out(f32) = (accumulate ? out : 0) + v
     SplitK,      // out(f32)[split*split_stride + m*ldo + n] = v
     CeStats,     // bf16 LM head: per row and wave column block the (max, sum) of the softmax in the log2
-                 // domain (part), the logit at the row's target (zt); the rounded logits too when out != 0
+                 // domain (part), the logit at the row's target (zt); the rounded logits too when out != 0;
+                 // with a soft-cap every logit is capped first (and stored capped)
     Dz,          // bf16 LM head recomputed in the backward: out = bf16(scale (softmax(z) - onehot(target))),
-                 // scale = grad_scale * inv_valid on rows with a valid target, 0 elsewhere
+                 // scale = grad_scale * inv_valid on rows with a valid target, 0 elsewhere; with a soft-cap
+                 // z is the capped logit and the result is multiplied by 1 - (z / c)^2
     Axpby,       // bf16: out = cd(alpha in + beta v) (the Newton-Schulz steps); NN layout, batches allowed
     RopeNorm,    // bf16 qkv projection (head_dim 128, Persist8Heads, 256 x 256 tiles): q and k heads rotated
                  // (RoPE) and RMS-normalised over the head, 1/rms saved; v heads stored as they are
@@ -66,6 +84,7 @@ struct GemmDesc {
     const float* lse = nullptr;      // [M] natural-log LSE (Dz)
     const float* inv_valid = nullptr;
     float grad_scale = 1.0f;
+    SoftCap cap;                     // logit soft-cap (CeStats, Dz)
     // RopeNorm epilogue
     const float* cosv = nullptr;     // [T, 64] rotation tables
     const float* sinv = nullptr;
@@ -136,8 +155,11 @@ hipError_t launch_ce_merge(const void* part, int nblk, const float* zt, const in
                            float* loss_rows, int N, int V, uint32_t* err, hipStream_t s);
 hipError_t launch_loss_reduce(const float* loss_rows, const int32_t* targets, int N, int V, float* loss,
                               float* inv_valid, uint32_t* err, hipStream_t s);
+// logits already capped when cap.c > 0: the gradient is multiplied by 1 - (z / c)^2
 hipError_t launch_ce_bwd(Dt dt, void* logits, const float* lse, const int32_t* targets, const float* inv_valid,
-                         float grad_scale, int N, int V, hipStream_t s);
+                         float grad_scale, const SoftCap& cap, int N, int V, hipStream_t s);
+// z = c tanh(z / c) in place (n % 4 == 0)
+hipError_t launch_softcap(Dt dt, void* z, size_t n, const SoftCap& cap, hipStream_t s);
 // dwte = (accumulate ? dwte : 0) + segment sums of dx rows by token id; deterministic.
 // scratch: 4*N int32 + N*C f32 (the latter may alias any free [N,C] f32 buffer)
 // iscratch: embed_bwd_scratch_ints(N, V) ints; partial: N x C floats; V <= 65536
@@ -157,9 +179,10 @@ size_t decode_attn_part_floats(int B, int H, int D, int Tc);
 hipError_t launch_decode_attn(Dt dt, const void* qkv, const void* cache, float* part, void* y, int B, int H, int Hkv,
                               int D, int Tc, int pos, hipStream_t s);
 // sum of split-K partials part[s][m][n] (s < splits, stride = elements per split) over rows m < rows:
-// mode 0 store, 1 residual add (out = in + v), 2 the MLP activation relu(v)^2, 3 fp32 store
+// mode 0 store, 1 residual add (out = in + v), 2 the MLP activation relu(v)^2, 3 fp32 store (soft-capped
+// when cap.c > 0: the logits)
 hipError_t launch_decode_finish(Dt dt, const float* part, int splits, size_t stride, int rows, int N, int mode,
-                                void* out, const void* in, hipStream_t s);
+                                void* out, const void* in, hipStream_t s, const SoftCap& cap = SoftCap());
 
 // ---------------------------------------------------------------- optimizer step (optim.hip)
 // The six matrices of a layer (Wq, Wk, Wv, Wo, Wfc, Wproj) inside the packed matrix range: layer stride,

@@ -552,12 +552,13 @@ hipError_t launch_loss_reduce(const float* loss_rows, const int32_t* targets, in
 }
 
 // dz = grad_scale * inv_valid * (exp(z - lse) - onehot(target)) on valid rows,
-// 0 on ignored rows; written over the logits.  One workgroup per row, 8
-// consecutive logits per thread and step.
+// 0 on ignored rows; written over the logits.  With a soft-cap the logits are
+// the capped ones and dz is taken back through the cap: times 1 - (z / c)^2.
+// One workgroup per row, 8 consecutive logits per thread and step.
 template <typename T>
 __global__ void __launch_bounds__(256)
 ce_bwd_kernel(T* __restrict__ z, const float* __restrict__ lse, const int32_t* __restrict__ targets,
-              const float* __restrict__ inv_valid, float grad_scale, int V)
+              const float* __restrict__ inv_valid, float grad_scale, SoftCap cap, int V)
 {
     constexpr float kL2e = 1.4426950408889634f;
     const int n = blockIdx.x;
@@ -570,8 +571,11 @@ ce_bwd_kernel(T* __restrict__ z, const float* __restrict__ lse, const int32_t* _
         if (valid) {
             load8(zr + c, v);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                v[e] = k * (__builtin_amdgcn_exp2f(v[e] * kL2e - l2) - (c + e == t ? 1.0f : 0.0f));
+            for (int e = 0; e < 8; ++e) {
+                const float zc = v[e];
+                v[e] = k * (__builtin_amdgcn_exp2f(zc * kL2e - l2) - (c + e == t ? 1.0f : 0.0f));
+                if (cap.c > 0.0f) v[e] = v[e] * softcap_grad(zc, cap);
+            }
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = 0.0f;
@@ -581,14 +585,41 @@ ce_bwd_kernel(T* __restrict__ z, const float* __restrict__ lse, const int32_t* _
 }
 
 hipError_t launch_ce_bwd(Dt dt, void* logits, const float* lse, const int32_t* targets, const float* inv_valid,
-                         float grad_scale, int N, int V, hipStream_t s) {
+                         float grad_scale, const SoftCap& cap, int N, int V, hipStream_t s) {
     if (V % 8) return hipErrorInvalidValue;
     if (dt == Dt::BF16)
         hipLaunchKernelGGL(ce_bwd_kernel<bf16>, dim3(N), dim3(256), 0, s, (bf16*)logits, lse, targets, inv_valid,
-                           grad_scale, V);
+                           grad_scale, cap, V);
     else
         hipLaunchKernelGGL(ce_bwd_kernel<float>, dim3(N), dim3(256), 0, s, (float*)logits, lse, targets, inv_valid,
-                           grad_scale, V);
+                           grad_scale, cap, V);
+    return hipGetLastError();
+}
+
+// z = c tanh(z / c) in place: the fp32 LM head's logits before the cross-entropy of the soft-capped variant.
+template <typename T>
+__global__ void __launch_bounds__(256)
+softcap_kernel(T* __restrict__ z, size_t n4, SoftCap cap)
+{
+    const size_t stride = (size_t)gridDim.x * 256;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+        float v[4];
+        Vec4<T>::load(z + 4 * i, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = softcap_fwd(v[e], cap);
+        Vec4<T>::store(z + 4 * i, v);
+    }
+}
+
+hipError_t launch_softcap(Dt dt, void* z, size_t n, const SoftCap& cap, hipStream_t s) {
+    if (n % 4 || !(cap.c > 0.0f)) return hipErrorInvalidValue;
+    const size_t n4 = n / 4;
+    if (n4 == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)std::min<size_t>((n4 + 255) / 256, 256 * 32);
+    if (dt == Dt::BF16)
+        hipLaunchKernelGGL(softcap_kernel<bf16>, dim3(blocks), dim3(256), 0, s, (bf16*)z, n4, cap);
+    else
+        hipLaunchKernelGGL(softcap_kernel<float>, dim3(blocks), dim3(256), 0, s, (float*)z, n4, cap);
     return hipGetLastError();
 }
 

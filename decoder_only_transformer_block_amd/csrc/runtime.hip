@@ -22,7 +22,7 @@ constexpr int kCUs = 256;
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
-    size_t flag, cosv, sinv, wcast, x0, x, layer0, layer_stride;
+    size_t flag, cosv, sinv, wcast, x0, rstd0, x, layer0, layer_stride;
     size_t l_xn1, l_rstd1, l_qkv, l_rstdq, l_rstdk, l_y, l_lse, l_xn2, l_rstd2, l_act;
     size_t xf, rstdf, logits, cepart, zt, lse, loss_rows, dxn, dx, dx_cd, dh, dy, dqkv, delta, splitk, iscr, total;
     int ce_nblk;
@@ -70,6 +70,7 @@ struct ncgpt_ctx {
     bool bound = false;
     int static_dev = -1;  // device whose static scratch holds the workspace (ncgpt_bind_static), else -1
     int lm_mode = NCGPT_LOGITS_STORED;  // ncgpt_set_lm_head_mode
+    SoftCap cap;                        // the logit soft-cap of cfg (off when cfg.logit_softcap == 0)
     bool cast_valid = false;  // the workspace holds a bf16 copy of the weights (a forward or a recasting decode)
     int loss_mode = NCGPT_LOGITS_STORED;  // the mode the last ncgpt_loss ran in
     const int32_t* ids = nullptr;
@@ -207,7 +208,8 @@ void make_plan(ncgpt_ctx* c) {
     p.cosv = A((size_t)c->T * (c->D / 2) * 4);
     p.sinv = A((size_t)c->T * (c->D / 2) * 4);
     p.wcast = A(c->dt == Dt::BF16 ? (size_t)(c->P - c->VC) * 2 : 0);
-    p.x0 = A(N * c->C * e);
+    p.x0 = A(N * c->C * e);      // the residual stream's start: the embedding, or its RMS norm (embed_norm)
+    p.rstd0 = A(c->cfg.embed_norm ? N * 4 : 0);
     p.x = A(N * c->C * e);
     // one layer's saved activations
     size_t lo = 0;
@@ -537,6 +539,8 @@ ncgpt_status ncgpt_create(const ncgpt_config* g, ncgpt_dtype dtype, ncgpt_ctx** 
     if (bf ? g->seq_len % 128 : g->seq_len % 64) return NCGPT_EUNSUPPORTED;
     if ((double)g->batch * g->seq_len * g->vocab_size > 4.0e12) return NCGPT_EUNSUPPORTED;
     if (!(g->norm_eps >= 0.0f) || !(g->rope_base > 0.0f)) return NCGPT_EINVAL;
+    if (!(g->logit_softcap >= 0.0f) || !std::isfinite(g->logit_softcap)) return NCGPT_EINVAL;
+    if (g->embed_norm != 0 && g->embed_norm != 1) return NCGPT_EINVAL;
     ncgpt_ctx* c = new (std::nothrow) ncgpt_ctx();
     if (!c) return NCGPT_ENOMEM;
     c->cfg = *g;
@@ -548,6 +552,7 @@ ncgpt_status ncgpt_create(const ncgpt_config* g, ncgpt_dtype dtype, ncgpt_ctx** 
     c->P = (int64_t)ncgpt_num_params(g);
     c->VC = c->V * c->C;
     c->esz = bf ? 2 : 4;
+    c->cap = make_softcap(g->logit_softcap);
     make_plan(c);
     // RoPE tables: angle t * base^(-2i/D), evaluated in double, stored fp32
     const int half = (int)(c->D / 2);
@@ -627,10 +632,18 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
                    [&] { return launch_cast_bf16(params + c->VC, c->ws + p.wcast, n, c->stream); }));
         c->cast_valid = true;
     }
-    TRY(launch(c, "embed_fwd", 0.0, (double)N * C * (4 + e) + N * 4.0, [&] {
-        return launch_embed_fwd(dt, ids, params, c->ws + p.x0, N, C, V, flag, c->stream);
-    }));
     const double norm_bytes = (double)N * C * 2 * e + N * 4.0;
+    // the embedding; with embed_norm it passes through an RMSNorm before it enters the first block (the raw
+    // rows go through x, which the first block overwrites)
+    uint8_t* emb = c->ws + (c->cfg.embed_norm ? p.x : p.x0);
+    TRY(launch(c, "embed_fwd", 0.0, (double)N * C * (4 + e) + N * 4.0, [&] {
+        return launch_embed_fwd(dt, ids, params, emb, N, C, V, flag, c->stream);
+    }));
+    if (c->cfg.embed_norm) {
+        TRY(launch(c, "rmsnorm_fwd", 0.0, norm_bytes, [&] {
+            return launch_rmsnorm_fwd(dt, emb, c->ws + p.x0, c->at<float>(p.rstd0), N, C, eps, c->stream);
+        }));
+    }
     for (int l = 0; l < c->L; ++l) {
         uint8_t* xin = c->ws + (l == 0 ? p.x0 : p.x);
         uint8_t* xn1 = c->ws + c->lay(l, p.l_xn1);
@@ -730,6 +743,7 @@ ncgpt_status ncgpt_loss(ncgpt_ctx* c, const int32_t* targets, float* loss) {
         d.out = c->lm_mode == NCGPT_LOGITS_STORED ? (void*)(c->ws + p.logits) : nullptr;
         d.part = c->ws + p.cepart; d.nblk = p.ce_nblk;
         d.zt = c->at<float>(p.zt); d.targets = targets;
+        d.cap = c->cap;
         TRY(gemm(c, d, c->lm_mode == NCGPT_LOGITS_STORED ? "lm_head" : "lm_head_nostore"));
         TRY(launch(c, "ce_merge", 0.0, (double)N * p.ce_nblk * 8 + N * 16.0, [&] {
             return launch_ce_merge(c->ws + p.cepart, p.ce_nblk, c->at<float>(p.zt), targets, c->at<float>(p.lse),
@@ -738,6 +752,11 @@ ncgpt_status ncgpt_loss(ncgpt_ctx* c, const int32_t* targets, float* loss) {
     } else {
         d.epi = Epi::StoreCd; d.out = c->ws + p.logits;
         TRY(gemm(c, d, "lm_head"));
+        if (c->cap.c > 0.0f) {
+            TRY(launch(c, "softcap", 0.0, (double)N * V * c->esz * 2, [&] {
+                return launch_softcap(c->dt, c->ws + p.logits, (size_t)N * V, c->cap, c->stream);
+            }));
+        }
         TRY(launch(c, "ce_fwd_rows", 0.0, (double)N * V * c->esz + N * 12.0, [&] {
             return launch_ce_fwd_rows(c->dt, c->ws + p.logits, targets, c->at<float>(p.lse), c->at<float>(p.loss_rows),
                                       N, V, flag, c->stream);
@@ -791,12 +810,13 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
         d.epi = Epi::Dz; d.out = logits;
         d.lse = c->at<float>(p.lse); d.targets = c->targets; d.inv_valid = c->at<float>(p.flag + 4);
         d.grad_scale = grad_scale;
+        d.cap = c->cap;
         TRY(gemm(c, d, "lm_head_dz"));
     } else {
         // cross-entropy -> dz (in place over the logits)
         TRY(launch(c, "ce_bwd", 0.0, (double)N * V * 2 * e, [&] {
-            return launch_ce_bwd(dt, logits, c->at<float>(p.lse), c->targets, c->at<float>(p.flag + 4), grad_scale, N,
-                                 V, c->stream);
+            return launch_ce_bwd(dt, logits, c->at<float>(p.lse), c->targets, c->at<float>(p.flag + 4), grad_scale,
+                                 c->cap, N, V, c->stream);
         }));
     }
     {   // dxf = dz Wlm
@@ -890,8 +910,20 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             return launch_rmsnorm_bwd(dt, xn1, c->at<float>(c->lay(l, p.l_rstd1)), dxn, dx, dx_cd, N, C, 1, c->stream);
         }));
     }
+    float* demb = dx;    // the gradient at the embedding's output
+    float* escr = dxn;   // embed_bwd's [N, C] scratch
+    if (c->cfg.embed_norm) {
+        // through the embedding norm: its input gradient into dxn (from dx in the compute dtype, as every norm's
+        // backward takes it), then dx serves as the scratch
+        const void* dy = dt == Dt::BF16 ? (const void*)(c->ws + p.dx_cd) : (const void*)dx;
+        TRY(launch(c, "rmsnorm_bwd", 0.0, nb, [&] {
+            return launch_rmsnorm_bwd(dt, c->ws + p.x0, c->at<float>(p.rstd0), dy, dxn, nullptr, N, C, 0, c->stream);
+        }));
+        demb = dxn;
+        escr = dx;
+    }
     TRY(launch(c, "embed_bwd", 0.0, (double)N * C * 8 + (double)V * C * (4 + 4 * acc), [&] {
-        return launch_embed_bwd(c->ids, dx, gslice(-1, 0), N, C, V, acc, c->at<int32_t>(p.iscr), dxn, c->stream);
+        return launch_embed_bwd(c->ids, demb, gslice(-1, 0), N, C, V, acc, c->at<int32_t>(p.iscr), escr, c->stream);
     }));
     c->state = 3;
     return NCGPT_OK;
@@ -1073,8 +1105,13 @@ ncgpt_status ncgpt_decode_step(ncgpt_ctx* c, const int32_t* ids, const float* pa
         return st == hipSuccess ? launch_zero_u32(reinterpret_cast<uint32_t*>(y), (size_t)Bp * HD * e / 4, c->stream) : st;
     }));
     TRY(launch(c, "embed_fwd", 0.0, (double)B * C * (4 + e), [&] {
-        return launch_embed_fwd(dt, ids, params, x, B, C, V, flag, c->stream);
+        return launch_embed_fwd(dt, ids, params, c->cfg.embed_norm ? xn : x, B, C, V, flag, c->stream);
     }));
+    if (c->cfg.embed_norm) {
+        TRY(launch(c, "rmsnorm_fwd", 0.0, (double)B * C * 2 * e, [&] {
+            return launch_rmsnorm_fwd(dt, xn, x, c->at<float>(p.d_rstd), B, C, eps, c->stream);
+        }));
+    }
     // one B-row GEMM: split-K partials, then the finish (mode as launch_decode_finish)
     auto dgemm = [&](const char* tag, const void* A, int lda, const void* W, int N, int K, int mode, void* out,
                      const void* in, int rows) -> ncgpt_status {
@@ -1087,7 +1124,8 @@ ncgpt_status ncgpt_decode_step(ncgpt_ctx* c, const int32_t* ids, const float* pa
         d.tile = 2; d.loop = GemmLoop::Ring8;
         TRY(gemm(c, d, tag));
         return launch(c, "decode_finish", 0.0, (double)Bp * N * 4 * (sp.splits + 1), [&] {
-            return launch_decode_finish(dt, part, sp.splits, (size_t)Bp * N, rows, N, mode, out, in, c->stream);
+            return launch_decode_finish(dt, part, sp.splits, (size_t)Bp * N, rows, N, mode, out, in, c->stream,
+                                        mode == 3 ? c->cap : SoftCap());
         });
     };
     const size_t cache_layer = (size_t)2 * B * c->Hkv * c->T * c->D * e;
@@ -1179,7 +1217,7 @@ ncgpt_status ncgpt_probe(ncgpt_ctx* c, int what, int layer, float* dst) {
     case 7: src = c->ws + p.xf; break;
     case 8: src = c->ws + p.lse; dt = Dt::F32; break;
     case 9: src = c->ws + p.loss_rows; dt = Dt::F32; break;
-    case 10: src = c->ws + p.dx; dt = Dt::F32; break;
+    case 10: src = c->ws + (c->cfg.embed_norm ? p.dxn : p.dx); dt = Dt::F32; break;
     }
     hipError_t e = launch_to_f32(dt, src, dst, n, c->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(c->stream);

@@ -35,7 +35,8 @@ class NcgptError(RuntimeError):
 class _Config(ct.Structure):
     _fields_ = [(n, ct.c_int32) for n in ("n_layer", "n_embd", "n_head", "n_kv_head", "head_dim", "mlp_dim",
                                            "vocab_size", "batch", "seq_len")] + \
-               [("rope_base", ct.c_float), ("norm_eps", ct.c_float)]
+               [("rope_base", ct.c_float), ("norm_eps", ct.c_float), ("logit_softcap", ct.c_float),
+                ("embed_norm", ct.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -51,6 +52,8 @@ class Config:
     seq_len: int
     rope_base: float = 10000.0
     norm_eps: float = 2.0 ** -23
+    logit_softcap: float = 0.0   # c > 0: logits z -> c tanh(z / c)
+    embed_norm: int = 0          # 1: RMSNorm right after the embedding
 
     @classmethod
     def from_workload(cls, w, **kw):
@@ -61,7 +64,8 @@ class Config:
 
     def _c(self):
         return _Config(self.n_layer, self.n_embd, self.n_head, self.n_kv_head, self.head_dim, self.mlp_dim,
-                       self.vocab_size, self.batch, self.seq_len, self.rope_base, self.norm_eps)
+                       self.vocab_size, self.batch, self.seq_len, self.rope_base, self.norm_eps, self.logit_softcap,
+                       self.embed_norm)
 
 
 class _OptimConfig(ct.Structure):

@@ -4,6 +4,7 @@
  *
  * What is computed (sources by page and section):
  *   x0 = wte[ids]                                   untied embedding ("nanochat 项目深度分析" §2.1 item 3)
+ *        (embed_norm = 1: x0 = rmsnorm(wte[ids]), a block variant)
  *   per layer l:                                    pre-norm block (devpress.csdn.net guide §4.1)
  *     u   = rmsnorm(x)                              parameter-free RMSNorm (§2.1 item 5)
  *     q,k,v = u Wq^T, u Wk^T, u Wv^T                bias-free linears, n_head / n_kv_head (§2.1 items 5, 6)
@@ -12,6 +13,8 @@
  *     x   = x + y Wo^T
  *     x   = x + relu(rmsnorm(x) Wfc^T)^2 Wproj^T    ReLU^2 MLP of width 4 n_embd (§2.1 item 4; woshipm.com §五.1)
  *   z = rmsnorm(x) Wlm^T                            untied lm_head
+ *        (logit_softcap = c > 0: z = c tanh(z / c), the reading given to the logit stabilisation that
+ *        woshipm.com §三 item 1 names without a formula)
  *   loss = mean over targets >= 0 of (logsumexp(z) - z[target])
  * The compute dtype mirrors the pages' COMPUTE_DTYPE scheme ("nanochat：低成本跑通大模型训练全流程",
  * precision paragraph): weights are fp32 masters, cast to the compute dtype for every linear, no autocast;
@@ -58,8 +61,10 @@ typedef enum { NCGPT_F32 = 0, NCGPT_BF16 = 1 } ncgpt_dtype;
 
 typedef struct {
     int32_t n_layer, n_embd, n_head, n_kv_head, head_dim, mlp_dim, vocab_size, batch, seq_len;
-    float rope_base; /* 10000 */
-    float norm_eps;  /* 2^-23, the epsilon F.rms_norm uses when none is given */
+    float rope_base;     /* 10000 */
+    float norm_eps;      /* 2^-23, the epsilon F.rms_norm uses when none is given */
+    float logit_softcap; /* 0 (off), or c > 0: the logits become c tanh(z / c) before the loss and in decode */
+    int32_t embed_norm;  /* 0 (off), or 1: an RMSNorm right after the embedding */
 } ncgpt_config;
 
 typedef struct ncgpt_ctx ncgpt_ctx;
@@ -78,7 +83,9 @@ ncgpt_status ncgpt_param_slice(const ncgpt_config* cfg, int layer, int which, si
 /* Create a context (host memory only; no device work).  EUNSUPPORTED unless head_dim is 64 or 128
  * (128 for NCGPT_BF16), n_head % n_kv_head == 0, n_embd, mlp_dim and vocab_size are multiples of 64,
  * vocab_size <= 65536, seq_len is a multiple of 128 for NCGPT_BF16 (of 64 for NCGPT_F32), and
- * batch*seq_len*vocab fits the workspace plan.  *out receives the context; free it with ncgpt_destroy. */
+ * batch*seq_len*vocab fits the workspace plan.  EINVAL for a null pointer or non-positive size, a negative
+ * norm_eps, rope_base <= 0, a negative or non-finite logit_softcap, or embed_norm other than 0 or 1.
+ * *out receives the context; free it with ncgpt_destroy. */
 ncgpt_status ncgpt_create(const ncgpt_config* cfg, ncgpt_dtype dtype, ncgpt_ctx** out);
 
 /* Bytes of device workspace the context needs (saved activations, cast weights, logits, scratch). */
@@ -194,11 +201,13 @@ ncgpt_status ncgpt_check(ncgpt_ctx* ctx);
 
 /* Saved-activation readout (for tests).  Copies one activation of the last forward, converted to fp32,
  * into dst (device, fp32, ncgpt_probe_numel elements) and synchronises the stream.  what:
- *   0 x0 [N,C] embedding output          1 xn1 [N,C] pre-attention norm (layer)
+ *   0 x0 [N,C] the first block's input   1 xn1 [N,C] pre-attention norm (layer)
  *   2 qkv [N,(H+2Hkv)D] after RoPE/QK-norm (layer)   3 y [N,H*D] attention output (layer)
  *   4 lse_att [B,H,T] attention log-sum-exp (layer)  5 xn2 [N,C] pre-MLP norm (layer)
  *   6 act [N,F] relu(xn2 Wfc^T)^2 (layer)  7 xf [N,C] final norm    8 lse [N] logits log-sum-exp
- *   9 loss_rows [N] per-token loss (0 when ignored)  10 dx0 [N,C] gradient w.r.t. x0 (after backward)
+ *   9 loss_rows [N] per-token loss (0 when ignored)
+ *  10 demb [N,C] gradient w.r.t. the embedding rows wte[ids] (after backward; x0's gradient taken back
+ *     through the embedding norm when embed_norm = 1)
  * EINVAL for an unknown what or layer, ESTATE before the forward that produces it. */
 ncgpt_status ncgpt_probe_numel(const ncgpt_ctx* ctx, int what, size_t* numel);
 ncgpt_status ncgpt_probe(ncgpt_ctx* ctx, int what, int layer, float* dst);

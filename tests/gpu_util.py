@@ -22,18 +22,19 @@ def make_inputs(w, seed=1, param_seed=0):
     return ids, tg, params
 
 
-def ocfg(w):
+def ocfg(w, **variants):
+    """The oracle's config of workload w; variants: logit_softcap, embed_norm."""
     return orc.OracleConfig(w.n_layer, w.n_embd, w.n_head, w.n_kv_head, w.head_dim, w.mlp_dim, w.vocab_size,
-                            w.batch, w.seq_len)
+                            w.batch, w.seq_len, **variants)
 
 
 class GpuStep:
     """One ncgpt context plus device copies of the inputs."""
 
-    def __init__(self, w, dtype, ids, params):
+    def __init__(self, w, dtype, ids, params, **variants):
         self.w = w
-        self.cfg = ncgpt.Config.from_workload(w)
-        say(f"[gpu] create {w.name} dtype={dtype} B={w.batch} T={w.seq_len}")
+        self.cfg = ncgpt.Config.from_workload(w, **variants)
+        say(f"[gpu] create {w.name} dtype={dtype} B={w.batch} T={w.seq_len} {variants or ''}")
         self.m = ncgpt.Model(self.cfg, dtype)
         self.ids = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32).reshape(-1)).cuda()
         self.params = torch.from_numpy(np.ascontiguousarray(params, dtype=np.float32)).cuda()

@@ -90,6 +90,10 @@ def test_create_validates_shapes_and_plans_workspace():
         (dict(vocab_size=65536 + 64), ncgpt.F32, ncgpt.EUNSUPPORTED),  # the embedding-gradient sort's limit
         (dict(seq_len=192), ncgpt.BF16, ncgpt.EUNSUPPORTED),
         (dict(batch=0), ncgpt.BF16, ncgpt.EINVAL),
+        (dict(logit_softcap=-1.0), ncgpt.BF16, ncgpt.EINVAL),
+        (dict(logit_softcap=float("inf")), ncgpt.F32, ncgpt.EINVAL),
+        (dict(logit_softcap=float("nan")), ncgpt.F32, ncgpt.EINVAL),
+        (dict(embed_norm=2), ncgpt.BF16, ncgpt.EINVAL),
     ]
     for kw, dt, want in bad:
         d = dict(base.__dict__)
@@ -99,6 +103,13 @@ def test_create_validates_shapes_and_plans_workspace():
         assert not ctx.value
     st, _ = create(base, 7)
     assert st == ncgpt.EINVAL
+    # the block variants: the embedding norm's rstd adds to the plan
+    st, ctx = create(ncgpt.Config(**dict(base.__dict__, logit_softcap=15.0, embed_norm=1)), ncgpt.BF16)
+    assert st == ncgpt.OK
+    m = ct.c_size_t()
+    assert L.ncgpt_workspace_size(ctx, ct.byref(m)) == ncgpt.OK
+    assert m.value > n.value
+    L.ncgpt_destroy(ctx)
 
 
 def test_lm_head_mode_validation():
