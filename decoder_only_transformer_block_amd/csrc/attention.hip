@@ -21,6 +21,7 @@
 // atomics are used and results are bitwise reproducible.
 //
 // fp32 path: plain SIMT kernels, one wave per row, for the fp32 compute mode.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -29,6 +30,24 @@
 namespace ncgpt {
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- workgroup order
+// A stream is the set of workgroups that read the same K / V rows (forward, dQ: one (sequence, kv head) with
+// its r query heads) or the same Q / dO rows (dK/dV: one (sequence, kv head)); a stream has npos workgroups,
+// position 0 the heaviest.  Each XCD runs a contiguous range of the order below (xcd_remap), which walks
+// groups of G streams -- G chosen so one group fills the XCD's resident slots -- and inside a group takes
+// the positions heaviest first, streams fastest.  The group's workgroups start together and stream the same
+// rows at about the same time, so those rows come from the XCD's L2 rather than from HBM, while the
+// heaviest-first order inside each group keeps the tail short.
+__device__ __forceinline__ void attn_order(int bid, int nwg, int npos, int nstream, int G, int& stream, int& pos) {
+    const int L = xcd_remap(bid, nwg);
+    const int grp = L / (G * npos), in = L % (G * npos);
+    const int g0 = grp * G, gn = min(G, nstream - g0);
+    pos = in / gn;
+    stream = g0 + in % gn;
+}
+// G for kernels with per_cu resident workgroups per CU (32 CUs per XCD)
+inline int attn_group(int npos, int per_cu) { return std::max(1, 32 * per_cu / npos); }
 
 // ---------------------------------------------------------------- LDS tiles
 // Every tile is [64 rows][128] bf16 in its natural memory layout (256-byte
@@ -213,7 +232,7 @@ __device__ __forceinline__ void rope_qknorm_bwd_row(float (&v)[4][16], const bf1
 template <int QB>
 __global__ void __launch_bounds__(256, QB == 1 ? 2 : 1)
 attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restrict__ lse, int T, int H, int Hkv,
-              int B)
+              int B, int G)
 {
     constexpr int D = 128, QW = 32 * QB, QBLK = 4 * QW;
     __shared__ __attribute__((aligned(1024))) bf16 sK0[64 * 128];
@@ -222,11 +241,12 @@ attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restr
     __shared__ __attribute__((aligned(1024))) bf16 sV1[64 * 128];
     const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // late (heavy) query blocks first; (head, sequence) varies fastest
-    const int nqb = (T + QBLK - 1) / QBLK;
-    const int hb = blockIdx.x % (H * B), qblk = nqb - 1 - blockIdx.x / (H * B);
-    const int hq = hb / B, b = hb % B;
-    const int g = hq / (H / Hkv);
+    // stream (sequence, kv head); positions: late (heavy) query blocks first, the group's query heads fastest
+    const int nqb = (T + QBLK - 1) / QBLK, r = H / Hkv;
+    int st, pos;
+    attn_order(blockIdx.x, gridDim.x, nqb * r, B * Hkv, G, st, pos);
+    const int b = st / Hkv, g = st % Hkv;
+    const int hq = g * r + pos % r, qblk = nqb - 1 - pos / r;
     const int QKV = (H + 2 * Hkv) * D, HD = H * D, KD = Hkv * D;
     const int q0 = qblk * QBLK;
     const int qw = q0 + QW * w;                 // first query of this wave
@@ -359,7 +379,7 @@ __global__ void __launch_bounds__(256, OCC)
 attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const bf16* __restrict__ dy,
                  const float* __restrict__ lse, float* __restrict__ delta, bf16* __restrict__ dqkv,
                  const float* __restrict__ rstdq, const float* __restrict__ cosv, const float* __restrict__ sinv,
-                 int T, int H, int Hkv, int B)
+                 int T, int H, int Hkv, int B, int G)
 {
     constexpr int D = 128, QB = 128;
     __shared__ __attribute__((aligned(1024))) bf16 sK0[64 * 128];
@@ -368,11 +388,12 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
     __shared__ __attribute__((aligned(1024))) bf16 sV1[64 * 128];
     const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // late (heavy) query blocks first; (head, sequence) varies fastest
-    const int nqb = (T + QB - 1) / QB;
-    const int hb = blockIdx.x % (H * B), qblk = nqb - 1 - blockIdx.x / (H * B);
-    const int hq = hb / B, b = hb % B;
-    const int g = hq / (H / Hkv);
+    // stream (sequence, kv head); positions: late (heavy) query blocks first, the group's query heads fastest
+    const int nqb = (T + QB - 1) / QB, r = H / Hkv;
+    int st, pos;
+    attn_order(blockIdx.x, gridDim.x, nqb * r, B * Hkv, G, st, pos);
+    const int b = st / Hkv, g = st % Hkv;
+    const int hq = g * r + pos % r, qblk = nqb - 1 - pos / r;
     const int QKV = (H + 2 * Hkv) * D, HD = H * D, KD = Hkv * D;
     const int q0 = qblk * QB;
     const int qw = q0 + 32 * w;                 // first query of this wave
@@ -505,7 +526,7 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
 __global__ void __launch_bounds__(512, 1)
 attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, const float* __restrict__ delta,
                    bf16* __restrict__ dqkv, const float* __restrict__ rstdk, const float* __restrict__ cosv,
-                   const float* __restrict__ sinv, int T, int H, int Hkv, int B)
+                   const float* __restrict__ sinv, int T, int H, int Hkv, int B, int G)
 {
     constexpr int D = 128, KB = 128, NW = 8;
     __shared__ __attribute__((aligned(1024))) bf16 sK[KB * 128];
@@ -519,10 +540,10 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
     const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kq = w & 3, qh = w >> 2;            // key block of the wave, query half of each tile
-    // key blocks early in the sequence see the most queries: they come first, and the
-    // (head, sequence) index varies fastest so one kv head's blocks share an XCD
-    const int gb = blockIdx.x % (Hkv * B), kblk = blockIdx.x / (Hkv * B);
-    const int g = gb / B, b = gb % B;
+    // stream (sequence, kv head); key blocks early in the sequence see the most queries: they come first
+    int st, kblk;
+    attn_order(blockIdx.x, gridDim.x, (T + KB - 1) / KB, B * Hkv, G, st, kblk);
+    const int b = st / Hkv, g = st % Hkv;
     const int r = H / Hkv;
     const int QKV = (H + 2 * Hkv) * D, HD = H * D, KD = Hkv * D;
     const int k0 = kblk * KB;
@@ -550,9 +571,13 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
     const int zq = rz(32 * qh + l32, hh), zk = rz(32 * kq + l32, hh), tq = tz(lane) + 32 * 256 * qh;
     const int total = r * nqt;
     const unsigned voq = dma_voff(QKV, lane, w), vod = dma_voff(HD, lane, w);
-    // loads of tile it (query head g r + it / nqt, queries from (qt0 + it % nqt) 64) into one stage
+    // tile it: query tiles from the sequence's end backwards, the group's r query heads fastest -- every key
+    // block of a (sequence, kv head) starts at the last tile, so blocks that run together read the same Q and
+    // dO rows at about the same time (L2 hits)
+    auto qtile = [&](int it) { return qt0 + nqt - 1 - it / r; };
+    // loads of tile it (query head g r + it % r, queries from qtile(it) 64) into one stage
     auto issue = [&](int it, bf16* Qs, bf16* Os, float* Ls, float* Ds) {
-        const int hq = g * r + it / nqt, q0 = (qt0 + it % nqt) * 64;
+        const int hq = g * r + it % r, q0 = qtile(it) * 64;
         dma_rows<64, NW>(buf_rsrc(qkv + (rowbase + q0) * QKV + hq * D, (unsigned)((63 * QKV + 128) * 2)), voq, QKV,
                          Qs, w);
         dma_rows<64, NW>(buf_rsrc(dy + (rowbase + q0) * HD + hq * D, (unsigned)((63 * HD + 128) * 2)), vod, HD, Os, w);
@@ -569,7 +594,7 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
     };
     // one tile: S and dP for the wave's 32 keys x 32 queries, then dV += P^T dO, dK += dS^T Q
     auto compute = [&](int it, const bf16* Qs, const bf16* Os, const float* Ls, const float* Ds) {
-        const int q0 = (qt0 + it % nqt) * 64 + 32 * qh;  // the wave's 32 queries
+        const int q0 = qtile(it) * 64 + 32 * qh;  // the wave's 32 queries
         if (!active || q0 + 31 < kw) return;  // wave-uniform: every query precedes every key of the wave
         const bool diag = q0 < kw + 31;
         f32x16 s, dp;
@@ -801,8 +826,9 @@ hipError_t launch_attn_fwd(const AttnDesc& a, hipStream_t s) {
         if (a.D != 128 || a.T % 64) return hipErrorInvalidValue;
         // one 32-query block per wave: two workgroups per CU (softmax under the other's MFMAs)
         // measured faster than two blocks per wave at one workgroup per CU
-        hipLaunchKernelGGL(attn_fwd_bf16<1>, dim3(((a.T + 127) / 128) * a.H * a.B), dim3(256), 0, s,
-                           (const bf16*)a.qkv, (bf16*)a.y, a.lse, a.T, a.H, a.Hkv, a.B);
+        const int npos = (a.T + 127) / 128 * (a.H / a.Hkv);
+        hipLaunchKernelGGL(attn_fwd_bf16<1>, dim3(npos * a.Hkv * a.B), dim3(256), 0, s, (const bf16*)a.qkv,
+                           (bf16*)a.y, a.lse, a.T, a.H, a.Hkv, a.B, attn_group(npos, 2));
         return hipGetLastError();
     }
     dim3 grid((unsigned)(((size_t)a.B * a.T * a.H + 3) / 4));
@@ -826,11 +852,12 @@ hipError_t launch_attn_bwd(const AttnDesc& a, hipStream_t s, int part) {
         if (part == 0)
             hipLaunchKernelGGL(attn_bwd_dq_bf16<2>, dim3(((a.T + 127) / 128) * a.H * a.B), dim3(256), 0, s,
                                (const bf16*)a.qkv, (const bf16*)a.y, (const bf16*)a.dy, (const float*)a.lse, a.delta,
-                               (bf16*)a.dqkv, a.rstdq, a.cosv, a.sinv, a.T, a.H, a.Hkv, a.B);
+                               (bf16*)a.dqkv, a.rstdq, a.cosv, a.sinv, a.T, a.H, a.Hkv, a.B,
+                               attn_group((a.T + 127) / 128 * (a.H / a.Hkv), 2));
         else
             hipLaunchKernelGGL(attn_bwd_dkdv_bf16, dim3(((a.T + 127) / 128) * a.Hkv * a.B), dim3(512), 0, s,
                                (const bf16*)a.qkv, (const bf16*)a.dy, (const float*)a.delta, (bf16*)a.dqkv, a.rstdk,
-                               a.cosv, a.sinv, a.T, a.H, a.Hkv, a.B);
+                               a.cosv, a.sinv, a.T, a.H, a.Hkv, a.B, attn_group((a.T + 127) / 128, 1));
         return hipGetLastError();
     }
     dim3 gq((unsigned)(((size_t)N * a.H + 3) / 4)), gk((unsigned)(((size_t)N * a.Hkv + 3) / 4));

@@ -59,6 +59,19 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// ---- workgroup order: workgroups are dealt round-robin to the 8 XCDs (each with its own L2), and an XCD
+// starts its share in dispatch order; renumber them so XCD x runs one contiguous range of the logical order
+// (a bijection on [0, nwg)) ----
+__device__ __forceinline__ int xcd_remap(int wg, int nwg) {
+    constexpr int NX = 8;
+    int per = (nwg + NX - 1) / NX;
+    int xcd = wg % NX, local = wg / NX;
+    int tall = nwg % NX;
+    if (tall == 0) tall = NX;
+    if (xcd < tall) return xcd * per + local;
+    return tall * per + (xcd - tall) * (per - 1) + local;
+}
+
 // ---- logit soft-cap: c tanh(z / c) = c - 2c / (e^{2z/c} + 1), one exp and one reciprocal; saturates at +-c
 // (e^{2z/c} -> inf gives c, -> 0 gives -c) without a NaN ----
 __device__ __forceinline__ float softcap_fwd(float z, const SoftCap& s) {

@@ -568,18 +568,8 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[FM][FN], int m0, int n0, 
 }
 
 // ------------------------------------------------------------------ tile order
-// Workgroups are dealt round-robin to the 8 XCDs; renumber them so each XCD
-// gets a contiguous range of tiles (shared A / B tiles stay in one L2), then
-// walk tiles in bands of group_m tile-rows (a per-call choice: GemmDesc::group_m).
-__device__ __forceinline__ int xcd_remap(int wg, int nwg) {
-    constexpr int NX = 8;
-    int per = (nwg + NX - 1) / NX;
-    int xcd = wg % NX, local = wg / NX;
-    int tall = nwg % NX;
-    if (tall == 0) tall = NX;
-    if (xcd < tall) return xcd * per + local;
-    return tall * per + (xcd - tall) * (per - 1) + local;
-}
+// Each XCD takes a contiguous range of tiles (xcd_remap, so shared A / B tiles stay in
+// one L2), walked in bands of group_m tile-rows (a per-call choice: GemmDesc::group_m).
 
 __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
     int in_group = group_m * tiles_n;
