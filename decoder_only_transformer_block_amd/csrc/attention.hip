@@ -32,13 +32,12 @@ namespace ncgpt {
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------- workgroup order
-// A stream is the set of workgroups that read the same K / V rows (forward, dQ: one (sequence, kv head) with
-// its r query heads) or the same Q / dO rows (dK/dV: one (sequence, kv head)); a stream has npos workgroups,
-// position 0 the heaviest.  Each XCD runs a contiguous range of the order below (xcd_remap), which walks
-// groups of G streams -- G chosen so one group fills the XCD's resident slots -- and inside a group takes
-// the positions heaviest first, streams fastest.  The group's workgroups start together and stream the same
-// rows at about the same time, so those rows come from the XCD's L2 rather than from HBM, while the
-// heaviest-first order inside each group keeps the tail short.
+// Forward: a stream is the set of workgroups that read the same K / V rows, one (sequence, kv head) with its
+// r query heads; a stream has npos workgroups, position 0 the heaviest.  Each XCD runs a contiguous range of
+// the order below (xcd_remap), which walks groups of G streams -- G chosen so one group fills the XCD's
+// resident slots -- and inside a group takes the positions heaviest first, streams fastest.  The group's
+// workgroups start together and stream the same rows at about the same time, so those rows come from the
+// XCD's L2 rather than from HBM, while the heaviest-first order inside each group keeps the tail short.
 __device__ __forceinline__ void attn_order(int bid, int nwg, int npos, int nstream, int G, int& stream, int& pos) {
     const int L = xcd_remap(bid, nwg);
     const int grp = L / (G * npos), in = L % (G * npos);
@@ -379,7 +378,7 @@ __global__ void __launch_bounds__(256, OCC)
 attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const bf16* __restrict__ dy,
                  const float* __restrict__ lse, float* __restrict__ delta, bf16* __restrict__ dqkv,
                  const float* __restrict__ rstdq, const float* __restrict__ cosv, const float* __restrict__ sinv,
-                 int T, int H, int Hkv, int B, int G)
+                 int T, int H, int Hkv, int B)
 {
     constexpr int D = 128, QB = 128;
     __shared__ __attribute__((aligned(1024))) bf16 sK0[64 * 128];
@@ -388,12 +387,12 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
     __shared__ __attribute__((aligned(1024))) bf16 sV1[64 * 128];
     const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // stream (sequence, kv head); positions: late (heavy) query blocks first, the group's query heads fastest
-    const int nqb = (T + QB - 1) / QB, r = H / Hkv;
-    int st, pos;
-    attn_order(blockIdx.x, gridDim.x, nqb * r, B * Hkv, G, st, pos);
-    const int b = st / Hkv, g = st % Hkv;
-    const int hq = g * r + pos % r, qblk = nqb - 1 - pos / r;
+    // late (heavy) query blocks first; (head, sequence) varies fastest (grouping one stream's blocks on an
+    // XCD, as the forward does, measured 2 % slower here)
+    const int nqb = (T + QB - 1) / QB;
+    const int hb = blockIdx.x % (H * B), qblk = nqb - 1 - blockIdx.x / (H * B);
+    const int hq = hb / B, b = hb % B;
+    const int g = hq / (H / Hkv);
     const int QKV = (H + 2 * Hkv) * D, HD = H * D, KD = Hkv * D;
     const int q0 = qblk * QB;
     const int qw = q0 + 32 * w;                 // first query of this wave
@@ -526,7 +525,7 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
 __global__ void __launch_bounds__(512, 1)
 attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, const float* __restrict__ delta,
                    bf16* __restrict__ dqkv, const float* __restrict__ rstdk, const float* __restrict__ cosv,
-                   const float* __restrict__ sinv, int T, int H, int Hkv, int B, int G)
+                   const float* __restrict__ sinv, int T, int H, int Hkv, int B)
 {
     constexpr int D = 128, KB = 128, NW = 8;
     __shared__ __attribute__((aligned(1024))) bf16 sK[KB * 128];
@@ -540,10 +539,10 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
     const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kq = w & 3, qh = w >> 2;            // key block of the wave, query half of each tile
-    // stream (sequence, kv head); key blocks early in the sequence see the most queries: they come first
-    int st, kblk;
-    attn_order(blockIdx.x, gridDim.x, (T + KB - 1) / KB, B * Hkv, G, st, kblk);
-    const int b = st / Hkv, g = st % Hkv;
+    // key blocks early in the sequence see the most queries: they come first, and the (head, sequence)
+    // index varies fastest (grouping one stream's blocks on an XCD, as the forward does, measured 3 % slower)
+    const int gb = blockIdx.x % (Hkv * B), kblk = blockIdx.x / (Hkv * B);
+    const int g = gb / B, b = gb % B;
     const int r = H / Hkv;
     const int QKV = (H + 2 * Hkv) * D, HD = H * D, KD = Hkv * D;
     const int k0 = kblk * KB;
@@ -571,13 +570,9 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
     const int zq = rz(32 * qh + l32, hh), zk = rz(32 * kq + l32, hh), tq = tz(lane) + 32 * 256 * qh;
     const int total = r * nqt;
     const unsigned voq = dma_voff(QKV, lane, w), vod = dma_voff(HD, lane, w);
-    // tile it: query tiles from the sequence's end backwards, the group's r query heads fastest -- every key
-    // block of a (sequence, kv head) starts at the last tile, so blocks that run together read the same Q and
-    // dO rows at about the same time (L2 hits)
-    auto qtile = [&](int it) { return qt0 + nqt - 1 - it / r; };
-    // loads of tile it (query head g r + it % r, queries from qtile(it) 64) into one stage
+    // loads of tile it (query head g r + it / nqt, queries from (qt0 + it % nqt) 64) into one stage
     auto issue = [&](int it, bf16* Qs, bf16* Os, float* Ls, float* Ds) {
-        const int hq = g * r + it % r, q0 = qtile(it) * 64;
+        const int hq = g * r + it / nqt, q0 = (qt0 + it % nqt) * 64;
         dma_rows<64, NW>(buf_rsrc(qkv + (rowbase + q0) * QKV + hq * D, (unsigned)((63 * QKV + 128) * 2)), voq, QKV,
                          Qs, w);
         dma_rows<64, NW>(buf_rsrc(dy + (rowbase + q0) * HD + hq * D, (unsigned)((63 * HD + 128) * 2)), vod, HD, Os, w);
@@ -594,7 +589,7 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
     };
     // one tile: S and dP for the wave's 32 keys x 32 queries, then dV += P^T dO, dK += dS^T Q
     auto compute = [&](int it, const bf16* Qs, const bf16* Os, const float* Ls, const float* Ds) {
-        const int q0 = qtile(it) * 64 + 32 * qh;  // the wave's 32 queries
+        const int q0 = (qt0 + it % nqt) * 64 + 32 * qh;  // the wave's 32 queries
         if (!active || q0 + 31 < kw) return;  // wave-uniform: every query precedes every key of the wave
         const bool diag = q0 < kw + 31;
         f32x16 s, dp;
@@ -852,12 +847,11 @@ hipError_t launch_attn_bwd(const AttnDesc& a, hipStream_t s, int part) {
         if (part == 0)
             hipLaunchKernelGGL(attn_bwd_dq_bf16<2>, dim3(((a.T + 127) / 128) * a.H * a.B), dim3(256), 0, s,
                                (const bf16*)a.qkv, (const bf16*)a.y, (const bf16*)a.dy, (const float*)a.lse, a.delta,
-                               (bf16*)a.dqkv, a.rstdq, a.cosv, a.sinv, a.T, a.H, a.Hkv, a.B,
-                               attn_group((a.T + 127) / 128 * (a.H / a.Hkv), 2));
+                               (bf16*)a.dqkv, a.rstdq, a.cosv, a.sinv, a.T, a.H, a.Hkv, a.B);
         else
             hipLaunchKernelGGL(attn_bwd_dkdv_bf16, dim3(((a.T + 127) / 128) * a.Hkv * a.B), dim3(512), 0, s,
                                (const bf16*)a.qkv, (const bf16*)a.dy, (const float*)a.delta, (bf16*)a.dqkv, a.rstdk,
-                               a.cosv, a.sinv, a.T, a.H, a.Hkv, a.B, attn_group((a.T + 127) / 128, 1));
+                               a.cosv, a.sinv, a.T, a.H, a.Hkv, a.B);
         return hipGetLastError();
     }
     dim3 gq((unsigned)(((size_t)N * a.H + 3) / 4)), gk((unsigned)(((size_t)N * a.Hkv + 3) / 4));
