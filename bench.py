@@ -115,6 +115,8 @@ def main():
     ap.add_argument("--workload", default="d12")
     ap.add_argument("--dtype", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8", action="store_true",
+                    help="forward linears on E4M3 operands with per-row scales (bf16 workloads)")
     ap.add_argument("--lm-head", choices=["stored", "recomputed"], default="stored",
                     help="where the backward's dz comes from: stored logits (default) or a second LM-head GEMM")
     ap.add_argument("--kernels", action="store_true", help="print the per-kernel table to stderr")
@@ -137,6 +139,8 @@ def main():
     m = ncgpt.Model(cfg, dtype)
     if args.lm_head == "recomputed":
         m.set_lm_head_mode(ncgpt.LOGITS_RECOMPUTED)
+    if args.fp8:
+        m.set_fp8(True)
     ids, tg = split_stream(token_stream(w.vocab_size, w.batch, w.seq_len, w.tokens, 1))
     ids_d = torch.from_numpy(ids.reshape(-1)).to(dev)
     tg_d = torch.from_numpy(tg.reshape(-1)).to(dev)
@@ -278,7 +282,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if dtype == "bf16" else "f32",
+        "dtype": ("fp8e4m3+bf16" if args.fp8 else "bf16") if dtype == "bf16" else "f32",
         "data": "synthetic",
         "mfu": round(step_mfu, 4),
         "flops_per_token": fpt,

@@ -682,10 +682,48 @@ __device__ __forceinline__ bf16x8 frag32(const bf16* S, int r0, int kk, int lane
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, bool AK, bool BK, class E>
+// ------------------------------------------------------------------ fp8 operands (F8 kernels)
+// An fp8 (OCP E4M3) operand row is moved and laid out in LDS exactly as a bf16 row of half the length: a
+// 64-byte stage row holds 64 k.  v_mfma_scale_f32_32x32x64_f8f6f4 takes per lane the 16-byte chunks hh and
+// 2 + hh of its row (hh the lane half) -- the two fragments the bf16 k-steps 0 and 1 read -- so one MFMA
+// covers the stage.  Its block scales are left at 1 (E8M0 127); the per-row scales of both operands multiply
+// the accumulators before the epilogue (dequant_rows).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ i32x8 cat_frag(bf16x8 lo, bf16x8 hi) {
+    const u32x4 a = __builtin_bit_cast(u32x4, lo), b = __builtin_bit_cast(u32x4, hi);
+    const i32x8 r = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+    return r;
+}
+__device__ __forceinline__ f32x16 mfma_f8(const i32x8& x, const i32x8& y, const f32x16& c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, 127, 0, 127);
+}
+// acc[i][j][e] (row m0 + 32 i + l32, column n0 + 32 j + 8 (e >> 2) + 4 h + (e & 3)) *= sa[row] sb[column]
+template <int FM, int FN>
+__device__ __forceinline__ void dequant_rows(f32x16 (&acc)[FM][FN], int m0, int n0, int M, int N, int lane,
+                                             const float* __restrict__ sa, const float* __restrict__ sb) {
+    const int h = lane >> 5, l32 = lane & 31;
+    float ra[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) ra[i] = m0 + 32 * i + l32 < M ? sa[m0 + 32 * i + l32] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int n = n0 + 32 * j + 8 * g + 4 * h;   // N is a multiple of 4: a group is all in or all out
+            float cb[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (n < N) Vec4<float>::load(sb + n, cb);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] *= ra[i] * cb[e];
+        }
+}
+
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BK, class E, bool F8 = false>
 __global__ void __launch_bounds__(64 * WGM * WGN, 1)
 gemm_bf16_mfma_ring(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
-                    int k_split, int group_m, E epi_, int64_t sA, int64_t sB)
+                    int k_split, int group_m, E epi_, int64_t sA, int64_t sB, const float* __restrict__ rsa,
+                    const float* __restrict__ rsb)
 {
     // batched GEMMs: item blockIdx.z reads A + z sA and B + z sB and writes through its shifted epilogue
     A += blockIdx.z * sA;
@@ -777,18 +815,59 @@ gemm_bf16_mfma_ring(const bf16* __restrict__ A, const bf16* __restrict__ B, int 
         interleave(std::false_type{});
     };
 
-    dma(0, sA0, sB0);
-    dma(1, sA1, sB1);
-    dma(2, sA2, sB2);
-    sync_next();
-    lfrag(0, sA0, sB0, 0);
-    for (int kt = 0; kt < nk; kt += 4) {
-        stage(kt, sA0, sB0, sA1, sB1, sA3, sB3);
-        stage(kt + 1, sA1, sB1, sA2, sB2, sA0, sB0);
-        stage(kt + 2, sA2, sB2, sA3, sB3, sA1, sB1);
-        stage(kt + 3, sA3, sB3, sA0, sB0, sA2, sB2);
+    if constexpr (F8) {
+        // fp8: one MFMA per (i, j) and stage.  The stage's A fragments are reloaded with the next stage's
+        // right after their last MFMA; the B fragments alternate between two buffers.
+        i32x8 a8[FM], b8[2][FN];
+        auto lfa8 = [&](int i, const bf16* S) {
+            a8[i] = cat_frag(frag32<BM, AK>(S, wm * WM + 32 * i, 0, lane), frag32<BM, AK>(S, wm * WM + 32 * i, 1, lane));
+        };
+        auto lfb8 = [&](int buf, const bf16* S) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                b8[buf][j] = cat_frag(frag32<BN, BK>(S, wn * WN + 32 * j, 0, lane),
+                                      frag32<BN, BK>(S, wn * WN + 32 * j, 1, lane));
+        };
+        auto stage8 = [&](int kt, int cb, const bf16* nA, const bf16* nB, bf16* xA, bf16* xB) {
+            dma(kt + 3, xA, xB);
+            sync_next();
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma_f8(b8[cb][j], a8[i], acc[i][j]);
+                lfa8(i, nA);
+            }
+            lfb8(cb ^ 1, nB);
+        };
+        dma(0, sA0, sB0);
+        dma(1, sA1, sB1);
+        dma(2, sA2, sB2);
+        sync_next();
+#pragma unroll
+        for (int i = 0; i < FM; ++i) lfa8(i, sA0);
+        lfb8(0, sB0);
+        for (int kt = 0; kt < nk; kt += 4) {
+            stage8(kt, 0, sA1, sB1, sA3, sB3);
+            stage8(kt + 1, 1, sA2, sB2, sA0, sB0);
+            stage8(kt + 2, 0, sA3, sB3, sA1, sB1);
+            stage8(kt + 3, 1, sA0, sB0, sA2, sB2);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        dequant_rows<FM, FN>(acc, m0 + wm * WM, n0 + wn * WN, M, N, lane, rsa, rsb);
+    } else {
+        dma(0, sA0, sB0);
+        dma(1, sA1, sB1);
+        dma(2, sA2, sB2);
+        sync_next();
+        lfrag(0, sA0, sB0, 0);
+        for (int kt = 0; kt < nk; kt += 4) {
+            stage(kt, sA0, sB0, sA1, sB1, sA3, sB3);
+            stage(kt + 1, sA1, sB1, sA2, sB2, sA0, sB0);
+            stage(kt + 2, sA2, sB2, sA3, sB3, sA1, sB1);
+            stage(kt + 3, sA3, sB3, sA0, sB0, sA2, sB2);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the loads past the end before the stores
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the loads past the end before the stores
 
     epilogue<FM, FN>(acc, m0 + wm * WM, n0 + wn * WN, split, M, N, lane, epi);
 }
@@ -1033,7 +1112,7 @@ static hipError_t run_mfma(const GemmDesc& d, E e, hipStream_t s) {
         if (d.batch > 1 && !BatchEpi<E>::value) return hipErrorInvalidValue;
         hipLaunchKernelGGL((gemm_bf16_mfma_ring<BM, BN, 2, 4, AK, BK, E>), dim3(tiles, splits, d.batch), dim3(512), 0,
                            s, (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, d.K, d.lda, d.ldb, d.k_split, d.group_m, e,
-                           (int64_t)d.sA, (int64_t)d.sB);
+                           (int64_t)d.sA, (int64_t)d.sB, nullptr, nullptr);
         return hipGetLastError();
     }
     const bool eight = d.loop == GemmLoop::Persist8;
@@ -1051,6 +1130,22 @@ static hipError_t run_mfma(const GemmDesc& d, E e, hipStream_t s) {
                        d.ldb, d.k_split, splits, d.group_m, e);
     return hipGetLastError();
     }
+}
+
+// fp8 operands (NT, 256 x 256 tiles, no split): d.K, d.lda and d.ldb count fp8 elements; the kernels move the
+// rows as bf16 rows of half the length.  Always the non-persistent eight-wave ring (the persistent kernels
+// spill with the fp8 fragments), in the 4 x 2 wave grid for the RoPE epilogue (a wave owns a head).
+template <class E>
+static hipError_t run_f8(const GemmDesc& d, E e, hipStream_t s) {
+    if (!d.rsa || !d.rsb || d.K % 128 || d.lda % 2 || d.ldb % 2 || d.tile != 0 || d.splits != 1 || d.batch != 1)
+        return hipErrorInvalidValue;
+    const int K = d.K / 2, lda = d.lda / 2, ldb = d.ldb / 2;
+    const int tiles = ((d.M + 255) / 256) * ((d.N + 255) / 256);
+    constexpr bool heads = std::is_same<E, ERopeNorm>::value;
+    hipLaunchKernelGGL((gemm_bf16_mfma_ring<256, 256, heads ? 4 : 2, heads ? 2 : 4, true, true, E, true>),
+                       dim3(tiles, 1, 1), dim3(512), 0, s, (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, K, lda, ldb,
+                       K, d.group_m, e, (int64_t)0, (int64_t)0, d.rsa, d.rsb);
+    return hipGetLastError();
 }
 
 template <bool AK, bool BK, class E>
@@ -1079,8 +1174,16 @@ static hipError_t run_f32(const GemmDesc& d, E e, hipStream_t s) {
 template <typename T, bool AK, bool BK>
 static hipError_t dispatch_epi(const GemmDesc& d, hipStream_t s) {
     auto run = [&](auto e) -> hipError_t {
-        if constexpr (sizeof(T) == 2) return run_bf16<AK, BK>(d, e, s);
-        else return run_f32<AK, BK>(d, e, s);
+        if constexpr (sizeof(T) == 2) {
+            if constexpr (AK && BK && !std::is_same<decltype(e), ESplitK>::value) {
+                if (d.fp8) return run_f8(d, e, s);
+            }
+            if (d.fp8) return hipErrorInvalidValue;
+            return run_bf16<AK, BK>(d, e, s);
+        } else {
+            if (d.fp8) return hipErrorInvalidValue;
+            return run_f32<AK, BK>(d, e, s);
+        }
     };
     if constexpr (AK && BK) {
         switch (d.epi) {
@@ -1159,6 +1262,7 @@ int gemm_wave_cols(const GemmDesc& d) {
 const char* gemm_kernel_name(const GemmDesc& d) {
     int li = (d.a_kcontig ? 2 : 0) + (d.b_kcontig ? 1 : 0);
     if (d.dt == Dt::F32) return li == 3 ? "gemm_f32_nt" : (li == 2 ? "gemm_f32_nn" : "gemm_f32_tn");
+    if (d.fp8) return "gemm_fp8_nt_256x256";
     static const char* names[3][3] = {
         {"gemm_bf16_nt_256x256", "gemm_bf16_nt_256x128", "gemm_bf16_nt_128x128"},
         {"gemm_bf16_nn_256x256", "gemm_bf16_nn_256x128", "gemm_bf16_nn_128x128"},

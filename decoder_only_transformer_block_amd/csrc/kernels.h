@@ -98,6 +98,11 @@ struct GemmDesc {
     // writes out + z sOut (reading in + z sIn); strides in elements
     int batch = 1;
     int64_t sA = 0, sB = 0, sOut = 0, sIn = 0;
+    // fp8 operands (bf16 mode, NT layout, the forward epilogues): A [M, K] and B [N, K] hold OCP E4M3 bytes, K,
+    // lda and ldb count bytes; the product is multiplied by rsa[m] rsb[n] (per-row scales) before the epilogue
+    bool fp8 = false;
+    const float* rsa = nullptr;
+    const float* rsb = nullptr;
     int tile = -1;    // MFMA tile: 0 = 256x256, 1 = 256x128, 2 = 128x128; -1 = chosen from the shape
     int group_m = 4;  // tiles are walked in bands of group_m tile-rows (L2 reuse of the B tiles)
     GemmLoop loop = GemmLoop::Persist8;
@@ -167,6 +172,10 @@ size_t embed_bwd_scratch_ints(int N, int V);
 hipError_t launch_embed_bwd(const int32_t* ids, const float* dx, float* dwte, int N, int C, int V, int accumulate,
                             int32_t* iscratch, float* partial, hipStream_t s);
 hipError_t launch_to_f32(Dt dt, const void* src, float* dst, size_t n, hipStream_t s);
+// fp8 (E4M3) rows with per-row scales: q[l][r][:] = x[l][r][:] / s[l][r], s = amax / 448, for `layers` matrices of
+// rows x cols at element strides x_layer, q_layer, s_layer; src is the element type of x (BF16 or F32)
+hipError_t launch_quant_rows_fp8(Dt src, const void* x, size_t x_layer, void* q, size_t q_layer, float* s,
+                                 size_t s_layer, int rows, int cols, int layers, hipStream_t st);
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);
 
 // ---------------------------------------------------------------- KV-cache decode (decode.hip)

@@ -623,6 +623,58 @@ hipError_t launch_softcap(Dt dt, void* z, size_t n, const SoftCap& cap, hipStrea
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ fp8 row quantisation
+// Row r of x -> q (OCP E4M3 bytes, the same layout) and the scale s[r] = amax / 448 with x ~ s q: every
+// |x| / s <= 448, the largest finite E4M3 value (v_cvt_pk_fp8_f32 rounds to nearest even and does not
+// saturate: 464 and beyond become NaN, so the scale keeps the row inside).  An all-zero row gets s = 1.
+// One wave per row; blockIdx.y walks `layers` matrices at the given strides.
+template <typename T>
+__global__ void __launch_bounds__(256)
+quant_rows_fp8_kernel(const T* __restrict__ x, size_t x_layer, uint8_t* __restrict__ q, size_t q_layer,
+                      float* __restrict__ s, size_t s_layer, int rows, int cols)
+{
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const T* xr = x + blockIdx.y * x_layer + (size_t)row * cols;
+    uint8_t* qr = q + blockIdx.y * q_layer + (size_t)row * cols;
+    float amax = 0.0f;
+    for (int c = lane * 8; c < cols; c += 512) {
+        float v[8];
+        load8(xr + c, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    }
+    amax = wave_max(amax);
+    const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+    for (int c = lane * 8; c < cols; c += 512) {
+        float v[8];
+        load8(xr + c, v);
+        uint32_t w[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            int t = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * h] * inv, v[4 * h + 1] * inv, 0, false);
+            t = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * h + 2] * inv, v[4 * h + 3] * inv, t, true);
+            w[h] = (uint32_t)t;
+        }
+        *reinterpret_cast<uint2*>(qr + c) = make_uint2(w[0], w[1]);
+    }
+    if (lane == 0) s[blockIdx.y * s_layer + row] = amax > 0.0f ? amax / 448.0f : 1.0f;
+}
+
+hipError_t launch_quant_rows_fp8(Dt src, const void* x, size_t x_layer, void* q, size_t q_layer, float* s,
+                                 size_t s_layer, int rows, int cols, int layers, hipStream_t st) {
+    if (cols % 8 || rows < 0 || layers < 1) return hipErrorInvalidValue;
+    if (rows == 0) return hipSuccess;
+    const dim3 grid((unsigned)((rows + 3) / 4), (unsigned)layers);
+    if (src == Dt::BF16)
+        hipLaunchKernelGGL(quant_rows_fp8_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)x, x_layer, (uint8_t*)q,
+                           q_layer, s, s_layer, rows, cols);
+    else
+        hipLaunchKernelGGL(quant_rows_fp8_kernel<float>, grid, dim3(256), 0, st, (const float*)x, x_layer,
+                           (uint8_t*)q, q_layer, s, s_layer, rows, cols);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ embedding backward
 // dwte[v] = sum of dx rows of the tokens with id v, summed in a fixed order so
 // the result is bitwise reproducible (no float atomics):

@@ -22,7 +22,7 @@ constexpr int kCUs = 256;
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
-    size_t flag, cosv, sinv, wcast, x0, rstd0, x, layer0, layer_stride;
+    size_t flag, cosv, sinv, wcast, w8, w8s, a8, a8s, x0, rstd0, x, layer0, layer_stride;
     size_t l_xn1, l_rstd1, l_qkv, l_rstdq, l_rstdk, l_y, l_lse, l_xn2, l_rstd2, l_act;
     size_t xf, rstdf, logits, cepart, zt, lse, loss_rows, dxn, dx, dx_cd, dh, dy, dqkv, delta, splitk, iscr, total;
     int ce_nblk;
@@ -70,6 +70,8 @@ struct ncgpt_ctx {
     bool bound = false;
     int static_dev = -1;  // device whose static scratch holds the workspace (ncgpt_bind_static), else -1
     int lm_mode = NCGPT_LOGITS_STORED;  // ncgpt_set_lm_head_mode
+    bool fp8 = false;                   // ncgpt_set_fp8: forward linears on E4M3 operands
+    bool loss_fp8 = false;              // the last ncgpt_loss ran its LM head on E4M3 operands
     SoftCap cap;                        // the logit soft-cap of cfg (off when cfg.logit_softcap == 0)
     bool cast_valid = false;  // the workspace holds a bf16 copy of the weights (a forward or a recasting decode)
     int loss_mode = NCGPT_LOGITS_STORED;  // the mode the last ncgpt_loss ran in
@@ -208,6 +210,17 @@ void make_plan(ncgpt_ctx* c) {
     p.cosv = A((size_t)c->T * (c->D / 2) * 4);
     p.sinv = A((size_t)c->T * (c->D / 2) * 4);
     p.wcast = A(c->dt == Dt::BF16 ? (size_t)(c->P - c->VC) * 2 : 0);
+    // fp8 forward linears (bf16 mode): E4M3 weights at the bf16 copy's element offsets, their per-row scales
+    // (layer-major rows: qkv, Wo, Wfc, Wproj; then lm_head), and one activation's rows with their scales
+    {
+        const bool bf = c->dt == Dt::BF16;
+        const size_t rows = (size_t)c->L * (c->QKV + 2 * c->C + c->F) + c->V;
+        const size_t widest = (size_t)std::max(c->C, std::max(c->HD, c->F));
+        p.w8 = A(bf ? (size_t)(c->P - c->VC) : 0);
+        p.w8s = A(bf ? rows * 4 : 0);
+        p.a8 = A(bf ? N * widest : 0);
+        p.a8s = A(bf ? N * 4 : 0);
+    }
     p.x0 = A(N * c->C * e);      // the residual stream's start: the embedding, or its RMS norm (embed_norm)
     p.rstd0 = A(c->cfg.embed_norm ? N * 4 : 0);
     p.x = A(N * c->C * e);
@@ -407,7 +420,7 @@ ncgpt_status gemm(ncgpt_ctx* c, GemmDesc d, const char* tag, bool bf16_always = 
     case Epi::SplitK: out = 4.0 * std::max(1, d.splits); break;
     default: break;
     }
-    const double by = (((double)d.M * d.K + (double)d.N * d.K) * e + mn * out) * d.batch;
+    const double by = (((double)d.M * d.K + (double)d.N * d.K) * (d.fp8 ? 1.0 : e) + mn * out) * d.batch;
     return launch(c, nm, fl, by, [&] { return launch_gemm(d, c->stream); });
 }
 
@@ -450,6 +463,66 @@ const void* weight(ncgpt_ctx* c, int layer, int which) {
     ncgpt_param_slice(&c->cfg, layer, which, &off, &r, &cc);
     if (c->dt == Dt::BF16) return c->at<uint8_t>(c->pl.wcast) + (off - c->VC) * 2;
     return c->params + off;
+}
+
+// fp8 copy of a forward weight (layer -1: lm_head; which 0: the whole qkv weight, 3: Wo, 4: Wfc, 5: Wproj) and
+// the scales of its rows
+const void* weight8(ncgpt_ctx* c, int layer, int which) {
+    size_t off;
+    int64_t r, cc;
+    ncgpt_param_slice(&c->cfg, layer, which, &off, &r, &cc);
+    return c->at<uint8_t>(c->pl.w8) + (off - c->VC);
+}
+int64_t w8_row(const ncgpt_ctx* c, int layer, int which) {
+    const int64_t rpl = c->QKV + 2 * c->C + c->F;
+    if (layer < 0) return c->L * rpl;
+    const int64_t first[6] = {0, 0, 0, c->QKV, c->QKV + c->C, c->QKV + c->C + c->F};
+    return layer * rpl + first[which];
+}
+const float* wscale8(ncgpt_ctx* c, int layer, int which) { return c->at<float>(c->pl.w8s) + w8_row(c, layer, which); }
+
+// E4M3 copies of every forward weight with their row scales, from the fp32 parameters: one launch per matrix
+// kind over all layers, and the lm_head
+ncgpt_status quantize_weights(ncgpt_ctx* c) {
+    const int64_t lp = layer_params(&c->cfg), rpl = c->QKV + 2 * c->C + c->F;
+    struct Kind { int which; int64_t rows, cols; } kinds[4] = {
+        {0, c->QKV, c->C}, {3, c->C, c->HD}, {4, c->F, c->C}, {5, c->C, c->F}};
+    for (const Kind& k : kinds) {
+        size_t off;
+        int64_t r, cc;
+        ncgpt_param_slice(&c->cfg, 0, k.which, &off, &r, &cc);
+        TRY(launch(c, "quant_fp8_w", 0.0, (double)c->L * k.rows * k.cols * 5, [&] {
+            return launch_quant_rows_fp8(Dt::F32, c->params + off, (size_t)lp, c->at<uint8_t>(c->pl.w8) + (off - c->VC),
+                                         (size_t)lp, c->at<float>(c->pl.w8s) + w8_row(c, 0, k.which), (size_t)rpl,
+                                         (int)k.rows, (int)k.cols, (int)c->L, c->stream);
+        }));
+    }
+    size_t off;
+    int64_t r, cc;
+    ncgpt_param_slice(&c->cfg, -1, 1, &off, &r, &cc);
+    return launch(c, "quant_fp8_w", 0.0, (double)c->VC * 5, [&] {
+        return launch_quant_rows_fp8(Dt::F32, c->params + off, 0, c->at<uint8_t>(c->pl.w8) + (off - c->VC), 0,
+                                     c->at<float>(c->pl.w8s) + w8_row(c, -1, 1), 0, (int)c->V, (int)c->C, 1, c->stream);
+    });
+}
+
+// E4M3 rows of one [N, cols] activation (compute dtype bf16) into the shared fp8 activation buffer
+ncgpt_status quantize_act(ncgpt_ctx* c, const void* x, int cols) {
+    return launch(c, "quant_fp8", 0.0, (double)c->N * cols * 3 + c->N * 4.0, [&] {
+        return launch_quant_rows_fp8(Dt::BF16, x, 0, c->at<uint8_t>(c->pl.a8), 0, c->at<float>(c->pl.a8s), 0,
+                                     (int)c->N, cols, 1, c->stream);
+    });
+}
+
+// turn a forward GEMM (A = the activation last quantised, B = weight (layer, which)) into its fp8 form
+void use_fp8(ncgpt_ctx* c, GemmDesc& d, int layer, int which) {
+    d.fp8 = true;
+    d.A = c->at<uint8_t>(c->pl.a8);
+    d.B = weight8(c, layer, which);
+    d.rsa = c->at<float>(c->pl.a8s);
+    d.rsb = wscale8(c, layer, which);
+    d.tile = 0;
+    d.loop = GemmLoop::Ring8;
 }
 
 // Attach a workspace and stream: upload the RoPE tables, clear the device error flag (a kernel, not a
@@ -631,6 +704,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
         TRY(launch(c, "cast_bf16", 0.0, (double)n * 6,
                    [&] { return launch_cast_bf16(params + c->VC, c->ws + p.wcast, n, c->stream); }));
         c->cast_valid = true;
+        if (c->fp8) TRY(quantize_weights(c));
     }
     const double norm_bytes = (double)N * C * 2 * e + N * 4.0;
     // the embedding; with embed_norm it passes through an RMSNorm before it enters the first block (the raw
@@ -666,6 +740,10 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
                 d.cosv = c->at<float>(p.cosv); d.sinv = c->at<float>(p.sinv);
                 d.rstdq = c->at<float>(c->lay(l, p.l_rstdq)); d.rstdk = c->at<float>(c->lay(l, p.l_rstdk));
                 d.T = (int)c->T; d.H = (int)c->H; d.Hkv = (int)c->Hkv; d.eps = eps;
+                if (c->fp8) {
+                    TRY(quantize_act(c, xn1, C));
+                    use_fp8(c, d, l, 0);
+                }
                 TRY(gemm(c, d, "qkv"));
             } else {
                 d.epi = Epi::StoreCd;
@@ -695,6 +773,10 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.epi = Epi::ResidualCd; d.out = c->ws + p.x; d.in = xin; d.ldo = C;
             d.loop = GemmLoop::Ring8;  // epilogue reads the residual: the eight-wave ring without spills
             d.group_m = 8;
+            if (c->fp8) {
+                TRY(quantize_act(c, y, HD));
+                use_fp8(c, d, l, 3);
+            }
             TRY(gemm(c, d, "attn_out"));
         }
         TRY(launch(c, "rmsnorm_fwd", 0.0, norm_bytes, [&] {
@@ -706,6 +788,10 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.M = N; d.N = F; d.K = C;
             d.epi = Epi::ReluSq; d.out = act; d.ldo = F;
             d.loop = GemmLoop::Ring8;  // the non-persistent eight-wave ring measured fastest for this shape
+            if (c->fp8) {
+                TRY(quantize_act(c, xn2, C));
+                use_fp8(c, d, l, 4);
+            }
             TRY(gemm(c, d, "fc"));
         }
         {
@@ -714,6 +800,10 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.M = N; d.N = C; d.K = F;
             d.epi = Epi::ResidualCd; d.out = c->ws + p.x; d.in = c->ws + p.x; d.ldo = C;
             d.loop = GemmLoop::Persist8;  // measured faster than the non-persistent ring despite a small spill
+            if (c->fp8) {
+                TRY(quantize_act(c, act, F));
+                use_fp8(c, d, l, 5);
+            }
             TRY(gemm(c, d, "proj"));
         }
     }
@@ -744,9 +834,15 @@ ncgpt_status ncgpt_loss(ncgpt_ctx* c, const int32_t* targets, float* loss) {
         d.part = c->ws + p.cepart; d.nblk = p.ce_nblk;
         d.zt = c->at<float>(p.zt); d.targets = targets;
         d.cap = c->cap;
+        if (c->fp8) {
+            TRY(quantize_act(c, c->ws + p.xf, (int)c->C));
+            use_fp8(c, d, -1, 1);
+        }
+        const int nblk = (int)((V + gemm_wave_cols(d) - 1) / gemm_wave_cols(d));  // <= p.ce_nblk
+        d.nblk = nblk;
         TRY(gemm(c, d, c->lm_mode == NCGPT_LOGITS_STORED ? "lm_head" : "lm_head_nostore"));
-        TRY(launch(c, "ce_merge", 0.0, (double)N * p.ce_nblk * 8 + N * 16.0, [&] {
-            return launch_ce_merge(c->ws + p.cepart, p.ce_nblk, c->at<float>(p.zt), targets, c->at<float>(p.lse),
+        TRY(launch(c, "ce_merge", 0.0, (double)N * nblk * 8 + N * 16.0, [&] {
+            return launch_ce_merge(c->ws + p.cepart, nblk, c->at<float>(p.zt), targets, c->at<float>(p.lse),
                                    c->at<float>(p.loss_rows), N, V, flag, c->stream);
         }));
     } else {
@@ -767,7 +863,19 @@ ncgpt_status ncgpt_loss(ncgpt_ctx* c, const int32_t* targets, float* loss) {
                                   c->stream);
     }));
     c->loss_mode = c->dt == Dt::BF16 ? c->lm_mode : NCGPT_LOGITS_STORED;
+    c->loss_fp8 = c->fp8;
     c->state = 2;
+    return NCGPT_OK;
+}
+
+ncgpt_status ncgpt_set_fp8(ncgpt_ctx* c, int on) {
+    if (!c) return NCGPT_EINVAL;
+    if (on != 0 && on != 1) return fail(c, NCGPT_EINVAL, "fp8 switch is 0 or 1");
+    if (on && c->dt != Dt::BF16) return fail(c, NCGPT_EUNSUPPORTED, "fp8 linears are built for the bf16 compute dtype");
+    if (on && (c->C % 128 || c->HD % 128 || c->F % 128))
+        return fail(c, NCGPT_EUNSUPPORTED, "fp8 linears need n_embd, n_head * head_dim and mlp_dim multiples of 128");
+    c->fp8 = on != 0;
+    c->state = 0;  // the saved activations of an earlier forward do not match the new setting
     return NCGPT_OK;
 }
 
@@ -811,6 +919,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
         d.lse = c->at<float>(p.lse); d.targets = c->targets; d.inv_valid = c->at<float>(p.flag + 4);
         d.grad_scale = grad_scale;
         d.cap = c->cap;
+        if (c->loss_fp8) use_fp8(c, d, -1, 1);  // the loss left xf's E4M3 rows in the activation buffer
         TRY(gemm(c, d, "lm_head_dz"));
     } else {
         // cross-entropy -> dz (in place over the logits)

@@ -103,7 +103,8 @@ class OptimConfig:
 _lib = None
 
 EXPORTS = ["ncgpt_num_params", "ncgpt_param_slice", "ncgpt_create", "ncgpt_workspace_size", "ncgpt_bind",
-           "ncgpt_bind_static", "ncgpt_set_lm_head_mode", "ncgpt_optim_state_size", "ncgpt_optim_step",
+           "ncgpt_bind_static", "ncgpt_set_lm_head_mode", "ncgpt_set_fp8", "ncgpt_optim_state_size",
+           "ncgpt_optim_step",
            "ncgpt_kv_cache_bytes", "ncgpt_kv_fill", "ncgpt_decode_step",
            "ncgpt_forward", "ncgpt_loss", "ncgpt_backward", "ncgpt_check", "ncgpt_probe_numel", "ncgpt_probe",
            "ncgpt_timing_enable", "ncgpt_timing_reset", "ncgpt_timing_count", "ncgpt_timing_get",
@@ -127,6 +128,7 @@ def lib():
         L.ncgpt_bind.argtypes = [vp, vp, ct.c_size_t, vp]
         L.ncgpt_bind_static.argtypes = [vp, vp]
         L.ncgpt_set_lm_head_mode.argtypes = [vp, ct.c_int]
+        L.ncgpt_set_fp8.argtypes = [vp, ct.c_int]
         L.ncgpt_optim_state_size.argtypes = [P(_Config)]
         L.ncgpt_optim_state_size.restype = ct.c_size_t
         L.ncgpt_optim_step.argtypes = [vp, vp, vp, vp, ct.c_int64, P(_OptimConfig)]
@@ -270,6 +272,10 @@ class Model:
     def set_lm_head_mode(self, mode: int):
         """LOGITS_STORED (default) or LOGITS_RECOMPUTED: where the backward's dz comes from."""
         self._check(lib().ncgpt_set_lm_head_mode(self._ctx, int(mode)))
+
+    def set_fp8(self, on: bool):
+        """Forward linears on E4M3 operands with per-row scales (bf16 contexts)."""
+        self._check(lib().ncgpt_set_fp8(self._ctx, int(bool(on))))
 
     def check(self):
         self._check(lib().ncgpt_check(self._ctx))

@@ -140,6 +140,16 @@ ncgpt_status ncgpt_set_lm_head_mode(ncgpt_ctx* ctx, int mode);
  * ESTATE unless ncgpt_loss followed the last ncgpt_forward. */
 ncgpt_status ncgpt_backward(ncgpt_ctx* ctx, float* grads, int accumulate, float grad_scale);
 
+/* FP8 forward linears (NCGPT_BF16 only; off by default).  With on = 1 the five forward products -- qkv,
+ * attention output, MLP up and down, and the LM head (also its recomputation in NCGPT_LOGITS_RECOMPUTED) --
+ * take OCP E4M3 operands ("supports FP8" on woshipm §一 and §六 and on the devpress.csdn.net guide, which give no
+ * recipe): every weight row and every activation row (token) is scaled by its own amax / 448 and rounded to
+ * nearest even, the products accumulate in fp32 and are multiplied back by both row scales before the
+ * epilogue.  Weights are quantised from the fp32 parameters in every ncgpt_forward; the backward and the
+ * decode step stay bf16.  EUNSUPPORTED for NCGPT_F32 or when n_embd, n_head * head_dim or mlp_dim is not a
+ * multiple of 128; EINVAL for on outside {0, 1}.  The next call on the context must be ncgpt_forward. */
+ncgpt_status ncgpt_set_fp8(ncgpt_ctx* ctx, int on);
+
 /* The optimizer step that follows the backward ("nanochat 项目深度分析" §2.2 and §4.2): Muon for every layer
  * matrix (Wq, Wk, Wv, Wo, Wfc, Wproj), AdamW for wte and lm_head, each group at its own learning rate.
  * Muon is taken in the form of the published Muon description (the pages leave the iteration out):

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     src = open(os.path.join(ROOT, "include", "ncgpt.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(ncgpt_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(ncgpt_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_function():
@@ -109,6 +109,24 @@ def test_create_validates_shapes_and_plans_workspace():
     m = ct.c_size_t()
     assert L.ncgpt_workspace_size(ctx, ct.byref(m)) == ncgpt.OK
     assert m.value > n.value
+    L.ncgpt_destroy(ctx)
+
+
+def test_fp8_switch_validation():
+    L = ncgpt.lib()
+    st, ctx = create(ncgpt.Config.from_workload(WORKLOADS["tiny"]), ncgpt.F32)
+    assert L.ncgpt_set_fp8(ctx, 1) == ncgpt.EUNSUPPORTED            # bf16 contexts only
+    assert L.ncgpt_set_fp8(ctx, 0) == ncgpt.OK
+    L.ncgpt_destroy(ctx)
+    base = ncgpt.Config.from_workload(WORKLOADS["small"])
+    st, ctx = create(base, ncgpt.BF16)
+    assert L.ncgpt_set_fp8(ctx, 1) == ncgpt.OK
+    assert L.ncgpt_set_fp8(ctx, 2) == ncgpt.EINVAL
+    assert L.ncgpt_set_fp8(None, 1) == ncgpt.EINVAL
+    L.ncgpt_destroy(ctx)
+    st, ctx = create(ncgpt.Config(**dict(base.__dict__, n_embd=192, mlp_dim=768)), ncgpt.BF16)
+    assert st == ncgpt.OK
+    assert L.ncgpt_set_fp8(ctx, 1) == ncgpt.EUNSUPPORTED            # K = 192 is not a multiple of 128
     L.ncgpt_destroy(ctx)
 
 
