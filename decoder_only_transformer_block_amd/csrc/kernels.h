@@ -141,8 +141,10 @@ hipError_t launch_attn_bwd(const AttnDesc& a, hipStream_t s, int part);
 hipError_t launch_cast_bf16(const float* src, void* dst, size_t n, hipStream_t s);
 hipError_t launch_embed_fwd(Dt dt, const int32_t* ids, const float* wte, void* x, int N, int C, int V,
                             uint32_t* err, hipStream_t s);
+// q8 non-null (bf16, C a multiple of 256 up to 2048): the stored rows also as E4M3 bytes with scales qs (the
+// row quantiser's result for y)
 hipError_t launch_rmsnorm_fwd(Dt dt, const void* x, void* y, float* rstd, int rows, int C, float eps,
-                              hipStream_t s);
+                              hipStream_t s, void* q8 = nullptr, float* qs = nullptr);
 // dx(f32) = (accumulate ? dx : 0) + rstd*(dy - y*mean(dy*y)); dx_cd = cd(dx) when non-null
 hipError_t launch_rmsnorm_bwd(Dt dt, const void* y, const float* rstd, const void* dy, float* dx, void* dx_cd,
                               int rows, int C, int accumulate, hipStream_t s);

@@ -65,6 +65,25 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// 8 values -> 8 E4M3 bytes (x inv), round to nearest even
+__device__ __forceinline__ uint2 fp8x8(const float (&v)[8], float inv) {
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        int t = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * h] * inv, v[4 * h + 1] * inv, 0, false);
+        t = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * h + 2] * inv, v[4 * h + 3] * inv, t, true);
+        w[h] = (uint32_t)t;
+    }
+    return make_uint2(w[0], w[1]);
+}
+
 __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
     const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
@@ -118,10 +137,12 @@ rmsnorm_fwd_kernel(const T* __restrict__ x, T* __restrict__ y, float* __restrict
 // The same map with each row held in registers (C = 256 NCH): 32 lanes per row, two rows
 // per wave; lane j holds the 8-element chunks j, j + 32, ..., j + 32 (NCH - 1), so every
 // access is 16 bytes wide in bf16, every load is issued before the reduction, and x is
-// read once.
+// read once.  With q non-null the stored row (as rounded to T) also leaves as E4M3 bytes with
+// the row scale qs = amax / 448, exactly as the row quantiser below would make them from y.
 template <typename T, int NCH>
 __global__ void __launch_bounds__(256)
-rmsnorm_fwd_rows(const T* __restrict__ x, T* __restrict__ y, float* __restrict__ rstd, int rows, int C, float eps)
+rmsnorm_fwd_rows(const T* __restrict__ x, T* __restrict__ y, float* __restrict__ rstd, int rows, int C, float eps,
+                 uint8_t* __restrict__ q, float* __restrict__ qs)
 {
     const int row = blockIdx.x * 8 + (threadIdx.x >> 5), j = threadIdx.x & 31;
     const bool live = row < rows;               // no early return: the lane-group sums stay uniform
@@ -136,6 +157,29 @@ rmsnorm_fwd_rows(const T* __restrict__ x, T* __restrict__ y, float* __restrict__
         for (int e = 0; e < 8; ++e) ss += v[i][e] * v[i][e];
     ss = group_sum<32>(ss);
     const float rs = 1.0f / sqrtf(ss / (float)C + eps);
+    if (q) {                                     // uniform
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                v[i][e] = to_f32(from_f32<T>(v[i][e] * rs));   // the value y stores
+                amax = fmaxf(amax, fabsf(v[i][e]));
+            }
+        amax = group_max<32>(amax);
+        if (!live) return;
+        const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            store8(y + base + 256 * i, v[i]);
+            *reinterpret_cast<uint2*>(q + base + 256 * i) = fp8x8(v[i], inv);
+        }
+        if (j == 0) {
+            rstd[row] = rs;
+            qs[row] = amax > 0.0f ? amax / 448.0f : 1.0f;
+        }
+        return;
+    }
     if (!live) return;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
@@ -147,12 +191,14 @@ rmsnorm_fwd_rows(const T* __restrict__ x, T* __restrict__ y, float* __restrict__
 }
 
 template <typename T>
-static bool rmsnorm_fwd_rows_launch(const void* x, void* y, float* rstd, int rows, int C, float eps, hipStream_t s) {
+static bool rmsnorm_fwd_rows_launch(const void* x, void* y, float* rstd, int rows, int C, float eps, uint8_t* q,
+                                    float* qs, hipStream_t s) {
     const dim3 grid((rows + 7) / 8);
     switch (C % 256 ? 0 : C / 256) {
 #define NCGPT_RMS_F(n)                                                                                              \
     case n:                                                                                                          \
-        hipLaunchKernelGGL((rmsnorm_fwd_rows<T, n>), grid, dim3(256), 0, s, (const T*)x, (T*)y, rstd, rows, C, eps); \
+        hipLaunchKernelGGL((rmsnorm_fwd_rows<T, n>), grid, dim3(256), 0, s, (const T*)x, (T*)y, rstd, rows, C, eps,  \
+                           q, qs);                                                                                   \
         return true;
     NCGPT_RMS_F(1) NCGPT_RMS_F(2) NCGPT_RMS_F(3) NCGPT_RMS_F(4) NCGPT_RMS_F(5) NCGPT_RMS_F(6) NCGPT_RMS_F(8)
 #undef NCGPT_RMS_F
@@ -160,10 +206,13 @@ static bool rmsnorm_fwd_rows_launch(const void* x, void* y, float* rstd, int row
     }
 }
 
-hipError_t launch_rmsnorm_fwd(Dt dt, const void* x, void* y, float* rstd, int rows, int C, float eps, hipStream_t s) {
-    if (dt == Dt::BF16 ? rmsnorm_fwd_rows_launch<bf16>(x, y, rstd, rows, C, eps, s)
-                       : rmsnorm_fwd_rows_launch<float>(x, y, rstd, rows, C, eps, s))
+hipError_t launch_rmsnorm_fwd(Dt dt, const void* x, void* y, float* rstd, int rows, int C, float eps, hipStream_t s,
+                              void* q8, float* qs) {
+    if (q8 && (dt != Dt::BF16 || !qs)) return hipErrorInvalidValue;
+    if (dt == Dt::BF16 ? rmsnorm_fwd_rows_launch<bf16>(x, y, rstd, rows, C, eps, (uint8_t*)q8, qs, s)
+                       : rmsnorm_fwd_rows_launch<float>(x, y, rstd, rows, C, eps, nullptr, nullptr, s))
         return hipGetLastError();
+    if (q8) return hipErrorInvalidValue;       // the E4M3 copy comes only from the register-row kernel
     dim3 grid((rows + 3) / 4);
     if (dt == Dt::BF16)
         hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)x, (bf16*)y, rstd, rows, C, eps);
@@ -661,10 +710,53 @@ quant_rows_fp8_kernel(const T* __restrict__ x, size_t x_layer, uint8_t* __restri
     if (lane == 0) s[blockIdx.y * s_layer + row] = amax > 0.0f ? amax / 448.0f : 1.0f;
 }
 
+// The same quantisation with the row held in registers (cols = 8 G NCH): G lanes per row, 256 / G rows per
+// workgroup, lane j holding the 8-element chunks j, j + G, ...; x is read once.
+template <typename T, int G, int NCH>
+__global__ void __launch_bounds__(256)
+quant_rows_fp8_regs(const T* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ s, int rows)
+{
+    constexpr int cols = 8 * G * NCH;
+    const int row = blockIdx.x * (256 / G) + threadIdx.x / G, j = threadIdx.x % G;
+    const bool live = row < rows;                // no early return before the lane-group maximum
+    const size_t base = (size_t)(live ? row : 0) * cols + 8 * j;
+    float v[NCH][8];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) load8(x + base + 8 * G * i, v[i]);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
+    amax = group_max<G>(amax);
+    if (!live) return;
+    const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) *reinterpret_cast<uint2*>(q + base + 8 * G * i) = fp8x8(v[i], inv);
+    if (j == 0) s[row] = amax > 0.0f ? amax / 448.0f : 1.0f;
+}
+
+template <typename T>
+static bool quant_rows_regs_launch(const T* x, uint8_t* q, float* s, int rows, int cols, hipStream_t st) {
+#define NCGPT_QR(g, n)                                                                                            \
+    if (cols == 8 * g * n) {                                                                                       \
+        hipLaunchKernelGGL((quant_rows_fp8_regs<T, g, n>), dim3((rows + 256 / g - 1) / (256 / g)), dim3(256), 0, \
+                           st, x, q, s, rows);                                                                     \
+        return true;                                                                                               \
+    }
+    NCGPT_QR(32, 1) NCGPT_QR(32, 2) NCGPT_QR(32, 3) NCGPT_QR(32, 5) NCGPT_QR(32, 6)
+    NCGPT_QR(64, 2) NCGPT_QR(64, 4) NCGPT_QR(64, 6) NCGPT_QR(64, 8) NCGPT_QR(64, 10) NCGPT_QR(64, 12)
+#undef NCGPT_QR
+    return false;
+}
+
 hipError_t launch_quant_rows_fp8(Dt src, const void* x, size_t x_layer, void* q, size_t q_layer, float* s,
                                  size_t s_layer, int rows, int cols, int layers, hipStream_t st) {
     if (cols % 8 || rows < 0 || layers < 1) return hipErrorInvalidValue;
     if (rows == 0) return hipSuccess;
+    // one bf16 matrix (the activations): rows in registers where the width has a kernel
+    if (src == Dt::BF16 && layers == 1 && quant_rows_regs_launch((const bf16*)x, (uint8_t*)q, s, rows, cols, st))
+        return hipGetLastError();
     const dim3 grid((unsigned)((rows + 3) / 4), (unsigned)layers);
     if (src == Dt::BF16)
         hipLaunchKernelGGL(quant_rows_fp8_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)x, x_layer, (uint8_t*)q,

@@ -514,6 +514,26 @@ ncgpt_status quantize_act(ncgpt_ctx* c, const void* x, int cols) {
     });
 }
 
+// the RMSNorm kernel that holds rows in registers also writes the E4M3 copy (n_embd = 256 k, k in 1..6 or 8)
+bool norm_writes_fp8(const ncgpt_ctx* c) {
+    const int64_t k = c->C / 256;
+    return c->C % 256 == 0 && k >= 1 && k <= 8 && k != 7;
+}
+
+// RMSNorm of [N, C] rows; in fp8 mode the E4M3 rows land in the activation buffer (from the norm kernel
+// itself when it can, else from the row quantiser)
+ncgpt_status norm_fwd(ncgpt_ctx* c, const void* x, void* y, float* rstd, bool to_fp8) {
+    const Plan& p = c->pl;
+    const bool fused = to_fp8 && norm_writes_fp8(c);
+    const double bytes = (double)c->N * c->C * (2 * c->esz + (fused ? 1 : 0)) + c->N * 4.0;
+    TRY(launch(c, "rmsnorm_fwd", 0.0, bytes, [&] {
+        return launch_rmsnorm_fwd(c->dt, x, y, rstd, (int)c->N, (int)c->C, c->cfg.norm_eps, c->stream,
+                                  fused ? (void*)c->at<uint8_t>(p.a8) : nullptr, fused ? c->at<float>(p.a8s) : nullptr);
+    }));
+    if (to_fp8 && !fused) TRY(quantize_act(c, y, (int)c->C));
+    return NCGPT_OK;
+}
+
 // turn a forward GEMM (A = the activation last quantised, B = weight (layer, which)) into its fp8 form
 void use_fp8(ncgpt_ctx* c, GemmDesc& d, int layer, int which) {
     d.fp8 = true;
@@ -725,9 +745,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
         uint8_t* y = c->ws + c->lay(l, p.l_y);
         uint8_t* xn2 = c->ws + c->lay(l, p.l_xn2);
         uint8_t* act = c->ws + c->lay(l, p.l_act);
-        TRY(launch(c, "rmsnorm_fwd", 0.0, norm_bytes, [&] {
-            return launch_rmsnorm_fwd(dt, xin, xn1, c->at<float>(c->lay(l, p.l_rstd1)), N, C, eps, c->stream);
-        }));
+        TRY(norm_fwd(c, xin, xn1, c->at<float>(c->lay(l, p.l_rstd1)), c->fp8));
         {
             GemmDesc d;
             d.A = xn1; d.lda = C; d.B = weight(c, l, 0); d.ldb = C;
@@ -740,10 +758,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
                 d.cosv = c->at<float>(p.cosv); d.sinv = c->at<float>(p.sinv);
                 d.rstdq = c->at<float>(c->lay(l, p.l_rstdq)); d.rstdk = c->at<float>(c->lay(l, p.l_rstdk));
                 d.T = (int)c->T; d.H = (int)c->H; d.Hkv = (int)c->Hkv; d.eps = eps;
-                if (c->fp8) {
-                    TRY(quantize_act(c, xn1, C));
-                    use_fp8(c, d, l, 0);
-                }
+                if (c->fp8) use_fp8(c, d, l, 0);   // xn1's E4M3 rows came with the norm
                 TRY(gemm(c, d, "qkv"));
             } else {
                 d.epi = Epi::StoreCd;
@@ -779,19 +794,14 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             }
             TRY(gemm(c, d, "attn_out"));
         }
-        TRY(launch(c, "rmsnorm_fwd", 0.0, norm_bytes, [&] {
-            return launch_rmsnorm_fwd(dt, c->ws + p.x, xn2, c->at<float>(c->lay(l, p.l_rstd2)), N, C, eps, c->stream);
-        }));
+        TRY(norm_fwd(c, c->ws + p.x, xn2, c->at<float>(c->lay(l, p.l_rstd2)), c->fp8));
         {
             GemmDesc d;
             d.A = xn2; d.lda = C; d.B = weight(c, l, 4); d.ldb = C;
             d.M = N; d.N = F; d.K = C;
             d.epi = Epi::ReluSq; d.out = act; d.ldo = F;
             d.loop = GemmLoop::Ring8;  // the non-persistent eight-wave ring measured fastest for this shape
-            if (c->fp8) {
-                TRY(quantize_act(c, xn2, C));
-                use_fp8(c, d, l, 4);
-            }
+            if (c->fp8) use_fp8(c, d, l, 4);      // xn2's E4M3 rows came with the norm
             TRY(gemm(c, d, "fc"));
         }
         {
@@ -807,9 +817,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             TRY(gemm(c, d, "proj"));
         }
     }
-    TRY(launch(c, "rmsnorm_fwd", 0.0, norm_bytes, [&] {
-        return launch_rmsnorm_fwd(dt, c->ws + p.x, c->ws + p.xf, c->at<float>(p.rstdf), N, C, eps, c->stream);
-    }));
+    TRY(norm_fwd(c, c->ws + p.x, c->ws + p.xf, c->at<float>(p.rstdf), c->fp8));  // xf's E4M3 rows for the LM head
     c->state = 1;
     return NCGPT_OK;
 }
@@ -834,10 +842,7 @@ ncgpt_status ncgpt_loss(ncgpt_ctx* c, const int32_t* targets, float* loss) {
         d.part = c->ws + p.cepart; d.nblk = p.ce_nblk;
         d.zt = c->at<float>(p.zt); d.targets = targets;
         d.cap = c->cap;
-        if (c->fp8) {
-            TRY(quantize_act(c, c->ws + p.xf, (int)c->C));
-            use_fp8(c, d, -1, 1);
-        }
+        if (c->fp8) use_fp8(c, d, -1, 1);   // the forward's final norm left xf's E4M3 rows
         const int nblk = (int)((V + gemm_wave_cols(d) - 1) / gemm_wave_cols(d));  // <= p.ce_nblk
         d.nblk = nblk;
         TRY(gemm(c, d, c->lm_mode == NCGPT_LOGITS_STORED ? "lm_head" : "lm_head_nostore"));

@@ -84,17 +84,20 @@ def test_fp8_product_matches_e4m3_emulation(name):
         assert e_plain > 5 * e
 
 
-CASES = [("small", WORKLOADS["small"]), ("gqa3", GQA3), ("d12_prefix256", D12P)]
+# small and depth 12 take the E4M3 rows of the norms from the norm kernel itself, gqa3 (n_embd 384) from the
+# row quantiser; the last case adds the block variants (soft-cap 0.2 and the embedding norm)
+CASES = [("small", WORKLOADS["small"], {}), ("gqa3", GQA3, {}), ("d12_prefix256", D12P, {}),
+         ("small_variants", WORKLOADS["small"], dict(logit_softcap=0.2, embed_norm=1))]
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("key,w", CASES, ids=[c[0] for c in CASES])
-def test_fp8_step_close_to_oracle(key, w):
+@pytest.mark.parametrize("key,w,var", CASES, ids=[c[0] for c in CASES])
+def test_fp8_step_close_to_oracle(key, w, var):
     ids, tg, params = make_inputs(w)
-    say(f"[oracle] grad {w.name}")
-    lo, go = orc.grad(ocfg(w), ids, tg, params)
-    _, acts = orc.forward(ocfg(w), ids, tg, params)
-    s = GpuStep(w, "bf16", ids, params)
+    say(f"[oracle] grad {w.name} {var}")
+    lo, go = orc.grad(ocfg(w, **var), ids, tg, params)
+    _, acts = orc.forward(ocfg(w, **var), ids, tg, params)
+    s = GpuStep(w, "bf16", ids, params, **var)
     s.m.set_fp8(True)
     loss, st = s.run(tg)
     assert st == ncgpt.OK
