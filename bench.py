@@ -21,6 +21,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, 256 CUs at 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 COPY_MIB = 256              # size of the calibration copy (see copy_calibration)
+LOSS_SCALE = 2.0 ** 16      # the fp16 setting's gradient scale (grad_scale of the backward)
 
 
 def flops_per_token(w):
@@ -113,7 +114,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="d12")
-    ap.add_argument("--dtype", default=None)
+    ap.add_argument("--dtype", default=None, choices=[None, "bf16", "f16", "f32"],
+                    help="compute dtype (default: the workload's); f16 runs with a loss scale of 2^16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fp8", action="store_true",
                     help="forward linears on E4M3 operands with per-row scales (bf16 workloads)")
@@ -152,7 +154,7 @@ def main():
     def step():
         m.forward(ids_d, params)
         m.loss(tg_d, loss)
-        m.backward(grads)
+        m.backward(grads, grad_scale=LOSS_SCALE if dtype == "f16" else 1.0)
 
     for _ in range(args.warmup):
         step()
@@ -282,7 +284,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("fp8e4m3+bf16" if args.fp8 else "bf16") if dtype == "bf16" else "f32",
+        "dtype": ("fp8e4m3+bf16" if args.fp8 else "bf16") if dtype == "bf16" else dtype,
         "data": "synthetic",
         "mfu": round(step_mfu, 4),
         "flops_per_token": fpt,

@@ -116,11 +116,13 @@ __device__ __forceinline__ bf16x8 trfrag_at(const bf16* S, int t, int db) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// 8 accumulator values rounded to the 16-bit operand type H, as an MFMA fragment (bit pattern)
+template <typename HT>
 __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
-    bf16x8 r;
+    typename V8<HT>::type r;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = (bf16)s[base + e];
-    return r;
+    for (int e = 0; e < 8; ++e) r[e] = (HT)s[base + e];
+    return __builtin_bit_cast(bf16x8, r);
 }
 
 __device__ __forceinline__ void zero16(f32x16& a) {
@@ -185,6 +187,7 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, unsigned vo,
 // rotation's transpose then maps the pair (i, i + D/2):
 // out_i = r_i cos - r_{i+D/2} sin, out_{i+D/2} = r_i sin + r_{i+D/2} cos.
 // Dims d and d + 64 sit in the same lane (db and db + 2).
+template <typename HT>
 __device__ __forceinline__ void rope_qknorm_bwd_row(float (&v)[4][16], const bf16* __restrict__ yrow, float rs,
                                                     const float* __restrict__ cs, const float* __restrict__ sn,
                                                     int hh) {
@@ -194,7 +197,7 @@ __device__ __forceinline__ void rope_qknorm_bwd_row(float (&v)[4][16], const bf1
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
             float t[4];
-            Vec4<bf16>::load(yrow + 32 * db + 8 * gg + 4 * hh, t);
+            Vec4<HT>::load(reinterpret_cast<const HT*>(yrow + 32 * db + 8 * gg + 4 * hh), t);
 #pragma unroll
             for (int e = 0; e < 4; ++e) yv[db][4 * gg + e] = t[e];
         }
@@ -228,7 +231,7 @@ __device__ __forceinline__ void rope_qknorm_bwd_row(float (&v)[4][16], const bf1
 // fragment read from LDS for two 32-query blocks at one wave per SIMD; QB = 1
 // fits two workgroups per CU, so one wave's softmax runs under the other's
 // MFMAs.
-template <int QB>
+template <int QB, typename HT>
 __global__ void __launch_bounds__(256, QB == 1 ? 2 : 1)
 attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restrict__ lse, int T, int H, int Hkv,
               int B, int G)
@@ -270,7 +273,10 @@ attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restr
 #pragma unroll
         for (int db = 0; db < 4; ++db) zero16(o[qq][db]);
     }
-    const float c1 = kLog2e * rsqrtf((float)D), c2 = sqrtf((float)D) * kLog2e;
+    // fp16 keeps P = exp(s - sqrt(D)) away from its subnormals by carrying it as 2^15 P (the row sum and the
+    // LSE take the factor out again); the largest value, 2^15, stays inside fp16's range
+    constexpr float kPow = std::is_same<HT, f16>::value ? 15.0f : 0.0f;
+    const float c1 = kLog2e * rsqrtf((float)D), c2 = sqrtf((float)D) * kLog2e - kPow;
 
     const int nkt = min(q0 + QBLK, T) / 64;     // key tiles at or before the block's last query
     const int zk = rz(l32, hh), tl = tz(lane);  // fragment offsets (rows l32 + 32 kb share them)
@@ -300,7 +306,7 @@ attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restr
                 const bf16x8 kf = frag_at(Ks + 32 * 128 * kb, zk ^ (kk << 5));
 #pragma unroll
                 for (int qq = 0; qq < QB; ++qq)
-                    sc[qq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qq][kk], sc[qq], 0, 0, 0);
+                    sc[qq] = mfma16<HT>(kf, qf[qq][kk], sc[qq]);
             }
             // lane holds S[q = qw + 32qq + l32][key = kv0 + 32kb + 8(e>>2) + 4hh + (e&3)] in sc[qq][e]
             auto softmax = [&](auto masked) {
@@ -323,13 +329,13 @@ attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restr
             for (int j = 0; j < 2; ++j) {
                 bf16x8 pf[QB];
 #pragma unroll
-                for (int qq = 0; qq < QB; ++qq) pf[qq] = pack8(sc[qq], 8 * j);
+                for (int qq = 0; qq < QB; ++qq) pf[qq] = pack8<HT>(sc[qq], 8 * j);
 #pragma unroll
                 for (int db = 0; db < 4; ++db) {
                     const bf16x8 vf = trfrag_at(Vs + 128 * (32 * kb + 16 * j), tl, db);
 #pragma unroll
                     for (int qq = 0; qq < QB; ++qq)
-                        o[qq][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qq], o[qq][db], 0, 0, 0);
+                        o[qq][db] = mfma16<HT>(vf, pf[qq], o[qq][db]);
                 }
             }
         }
@@ -360,9 +366,9 @@ attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restr
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = o[qq][db][4 * gg + e] * inv;
-                Vec4<bf16>::store(yp + 32 * db + 8 * gg + 4 * hh, v);
+                Vec4<HT>::store(reinterpret_cast<HT*>(yp + 32 * db + 8 * gg + 4 * hh), v);
             }
-        if (hh == 0) lse[((size_t)b * H + hq) * T + q] = sqrtf((float)D) + logf(ltot);
+        if (hh == 0) lse[((size_t)b * H + hq) * T + q] = sqrtf((float)D) + logf(ltot) - kPow * 0.6931471805599453f;
     }
 }
 
@@ -373,7 +379,7 @@ attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restr
 // in registers, then for every 64-key tile recomputes S and dP, forms dS =
 // P (dP - delta) and accumulates dQ = dS K (scaled by 1/sqrt(D) at the end).
 // K and V tiles travel straight from memory into LDS, double-buffered.
-template <int OCC>
+template <int OCC, typename HT>
 __global__ void __launch_bounds__(256, OCC)
 attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const bf16* __restrict__ dy,
                  const float* __restrict__ lse, float* __restrict__ delta, bf16* __restrict__ dqkv,
@@ -412,9 +418,10 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
         for (int kk = 0; kk < 8; ++kk) {
             qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
             dof[kk] = *reinterpret_cast<const bf16x8*>(gp + 16 * kk);
-            const bf16x8 yv = *reinterpret_cast<const bf16x8*>(yp + 16 * kk);
+            const auto yv = *reinterpret_cast<const typename V8<HT>::type*>(yp + 16 * kk);
+            const auto dv8 = __builtin_bit_cast(typename V8<HT>::type, dof[kk]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) part += (float)dof[kk][e] * (float)yv[e];
+            for (int e = 0; e < 8; ++e) part += (float)dv8[e] * (float)yv[e];
         }
         dl = part + __shfl_xor(part, 32, kWave);
         const size_t li = ((size_t)b * H + hq) * T + q;
@@ -453,10 +460,8 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
             zero16(dp);
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_at(Ks + 32 * 128 * kb, zk ^ (kk << 5)), qf[kk], s, 0,
-                                                            0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_at(Vs + 32 * 128 * kb, zk ^ (kk << 5)), dof[kk], dp,
-                                                             0, 0, 0);
+                s = mfma16<HT>(frag_at(Ks + 32 * 128 * kb, zk ^ (kk << 5)), qf[kk], s);
+                dp = mfma16<HT>(frag_at(Vs + 32 * 128 * kb, zk ^ (kk << 5)), dof[kk], dp);
             }
             // lane holds S[q][key = kv0 + 32kb + 8(e>>2) + 4hh + (e&3)] in s[e]
             auto softmax = [&](auto masked) {
@@ -474,11 +479,11 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
                 softmax(std::false_type{});
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const bf16x8 dsf = pack8(dp, 8 * j);
+                const bf16x8 dsf = pack8<HT>(dp, 8 * j);
 #pragma unroll
                 for (int db = 0; db < 4; ++db)
-                    dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        trfrag_at(Ks + 128 * (32 * kb + 16 * j), tl, db), dsf, dq[db], 0, 0, 0);
+                    dq[db] = mfma16<HT>(
+                        trfrag_at(Ks + 128 * (32 * kb + 16 * j), tl, db), dsf, dq[db]);
             }
         }
     };
@@ -499,7 +504,7 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) gq[db][i] = dq[db][i] * scale;
-    rope_qknorm_bwd_row(gq, qkv + (rowbase + q) * QKV + hq * D, rstdq[(rowbase + q) * H + hq], cosv + q * (D / 2),
+    rope_qknorm_bwd_row<HT>(gq, qkv + (rowbase + q) * QKV + hq * D, rstdq[(rowbase + q) * H + hq], cosv + q * (D / 2),
                         sinv + q * (D / 2), hh);
     bf16* qout = dqkv + (rowbase + q) * QKV + hq * D;
 #pragma unroll
@@ -507,7 +512,7 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
             const float a[4] = {gq[db][4 * gg], gq[db][4 * gg + 1], gq[db][4 * gg + 2], gq[db][4 * gg + 3]};
-            Vec4<bf16>::store(qout + 32 * db + 8 * gg + 4 * hh, a);
+            Vec4<HT>::store(reinterpret_cast<HT*>(qout + 32 * db + 8 * gg + 4 * hh), a);
         }
 }
 
@@ -522,6 +527,7 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
 // first key.  Q, dO, lse and delta tiles travel straight from memory into LDS
 // (buffer_load ... lds), double-buffered: the loads of tile i+1 run under the
 // MFMAs of tile i.
+template <typename HT>
 __global__ void __launch_bounds__(512, 1)
 attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, const float* __restrict__ delta,
                    bf16* __restrict__ dqkv, const float* __restrict__ rstdk, const float* __restrict__ cosv,
@@ -597,10 +603,8 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
         zero16(dp);
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_at(Qs, zq ^ (kk << 5)), frag_at(sK, zk ^ (kk << 5)), s,
-                                                        0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_at(Os, zq ^ (kk << 5)), frag_at(sV, zk ^ (kk << 5)), dp,
-                                                         0, 0, 0);
+            s = mfma16<HT>(frag_at(Qs, zq ^ (kk << 5)), frag_at(sK, zk ^ (kk << 5)), s);
+            dp = mfma16<HT>(frag_at(Os, zq ^ (kk << 5)), frag_at(sV, zk ^ (kk << 5)), dp);
         }
         // lane holds S[q = q0 + 8(e>>2) + 4hh + (e&3)][key = kw + l32] in s[e]; P = exp2(S c1 - lse2),
         // dS / scale = P (dP - delta) (dK is scaled at the end); the mask only on diagonal tiles
@@ -627,13 +631,11 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
             softmax(std::false_type{});
 #pragma unroll
         for (int j2 = 0; j2 < 2; ++j2) {
-            const bf16x8 pf = pack8(s, 8 * j2), dsf = pack8(dp, 8 * j2);
+            const bf16x8 pf = pack8<HT>(s, 8 * j2), dsf = pack8<HT>(dp, 8 * j2);
 #pragma unroll
             for (int db = 0; db < 4; ++db) {
-                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag_at(Os + 128 * 16 * j2, tq, db), pf, dv[db],
-                                                                  0, 0, 0);
-                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trfrag_at(Qs + 128 * 16 * j2, tq, db), dsf, dk[db],
-                                                                  0, 0, 0);
+                dv[db] = mfma16<HT>(trfrag_at(Os + 128 * 16 * j2, tq, db), pf, dv[db]);
+                dk[db] = mfma16<HT>(trfrag_at(Qs + 128 * 16 * j2, tq, db), dsf, dk[db]);
             }
         }
     };
@@ -690,16 +692,16 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
                 gk[db][4 * gg + e] = (dk[db][4 * gg + e] + ok[e]) * scale;
                 c[e] = dv[db][4 * gg + e] + ov[e];
             }
-            Vec4<bf16>::store(kout + KD + 32 * db + 8 * gg + 4 * hh, c);
+            Vec4<HT>::store(reinterpret_cast<HT*>(kout + KD + 32 * db + 8 * gg + 4 * hh), c);
         }
-    rope_qknorm_bwd_row(gk, qkv + (rowbase + key) * QKV + HD + g * D, rstdk[(rowbase + key) * Hkv + g],
+    rope_qknorm_bwd_row<HT>(gk, qkv + (rowbase + key) * QKV + HD + g * D, rstdk[(rowbase + key) * Hkv + g],
                         cosv + key * (D / 2), sinv + key * (D / 2), hh);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
             const float a[4] = {gk[db][4 * gg], gk[db][4 * gg + 1], gk[db][4 * gg + 2], gk[db][4 * gg + 3]};
-            Vec4<bf16>::store(kout + 32 * db + 8 * gg + 4 * hh, a);
+            Vec4<HT>::store(reinterpret_cast<HT*>(kout + 32 * db + 8 * gg + 4 * hh), a);
         }
 }
 
@@ -817,13 +819,14 @@ attn_bwd_dkdv_f32(const float* __restrict__ qkv, const float* __restrict__ dy, c
 
 // ======================================================================== host
 hipError_t launch_attn_fwd(const AttnDesc& a, hipStream_t s) {
-    if (a.dt == Dt::BF16) {
+    if (mfma_dt(a.dt)) {
         if (a.D != 128 || a.T % 64) return hipErrorInvalidValue;
         // one 32-query block per wave: two workgroups per CU (softmax under the other's MFMAs)
         // measured faster than two blocks per wave at one workgroup per CU
         const int npos = (a.T + 127) / 128 * (a.H / a.Hkv);
-        hipLaunchKernelGGL(attn_fwd_bf16<1>, dim3(npos * a.Hkv * a.B), dim3(256), 0, s, (const bf16*)a.qkv,
-                           (bf16*)a.y, a.lse, a.T, a.H, a.Hkv, a.B, attn_group(npos, 2));
+        auto k = a.dt == Dt::F16 ? attn_fwd_bf16<1, f16> : attn_fwd_bf16<1, bf16>;
+        hipLaunchKernelGGL(k, dim3(npos * a.Hkv * a.B), dim3(256), 0, s, (const bf16*)a.qkv, (bf16*)a.y, a.lse, a.T,
+                           a.H, a.Hkv, a.B, attn_group(npos, 2));
         return hipGetLastError();
     }
     dim3 grid((unsigned)(((size_t)a.B * a.T * a.H + 3) / 4));
@@ -840,18 +843,21 @@ hipError_t launch_attn_fwd(const AttnDesc& a, hipStream_t s) {
 
 hipError_t launch_attn_bwd(const AttnDesc& a, hipStream_t s, int part) {
     const int N = a.B * a.T;
-    const bool bf = a.dt == Dt::BF16;
+    const bool bf = mfma_dt(a.dt), h16 = a.dt == Dt::F16;
     if (bf ? (a.D != 128 || a.T % 64 || !a.rstdq || !a.rstdk || !a.cosv || !a.sinv) : (a.D != 128 && a.D != 64))
         return hipErrorInvalidValue;
     if (bf) {
-        if (part == 0)
-            hipLaunchKernelGGL(attn_bwd_dq_bf16<2>, dim3(((a.T + 127) / 128) * a.H * a.B), dim3(256), 0, s,
-                               (const bf16*)a.qkv, (const bf16*)a.y, (const bf16*)a.dy, (const float*)a.lse, a.delta,
-                               (bf16*)a.dqkv, a.rstdq, a.cosv, a.sinv, a.T, a.H, a.Hkv, a.B);
-        else
-            hipLaunchKernelGGL(attn_bwd_dkdv_bf16, dim3(((a.T + 127) / 128) * a.Hkv * a.B), dim3(512), 0, s,
-                               (const bf16*)a.qkv, (const bf16*)a.dy, (const float*)a.delta, (bf16*)a.dqkv, a.rstdk,
+        if (part == 0) {
+            auto k = h16 ? attn_bwd_dq_bf16<2, f16> : attn_bwd_dq_bf16<2, bf16>;
+            hipLaunchKernelGGL(k, dim3(((a.T + 127) / 128) * a.H * a.B), dim3(256), 0, s, (const bf16*)a.qkv,
+                               (const bf16*)a.y, (const bf16*)a.dy, (const float*)a.lse, a.delta, (bf16*)a.dqkv, a.rstdq,
                                a.cosv, a.sinv, a.T, a.H, a.Hkv, a.B);
+        } else {
+            auto k = h16 ? attn_bwd_dkdv_bf16<f16> : attn_bwd_dkdv_bf16<bf16>;
+            hipLaunchKernelGGL(k, dim3(((a.T + 127) / 128) * a.Hkv * a.B), dim3(512), 0, s, (const bf16*)a.qkv,
+                               (const bf16*)a.dy, (const float*)a.delta, (bf16*)a.dqkv, a.rstdk, a.cosv, a.sinv, a.T,
+                               a.H, a.Hkv, a.B);
+        }
         return hipGetLastError();
     }
     dim3 gq((unsigned)(((size_t)N * a.H + 3) / 4)), gk((unsigned)(((size_t)N * a.Hkv + 3) / 4));

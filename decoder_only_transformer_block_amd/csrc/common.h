@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace ncgpt {
@@ -10,6 +12,9 @@ namespace ncgpt {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -20,9 +25,43 @@ constexpr int kWave = 64;
 // ---- scalar conversions (fp32 -> bf16 is round-to-nearest-even in hardware) ----
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(f16 x) { return (float)x; }
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }
+
+// 16-byte vector of eight 16-bit values of type T (bf16 or f16)
+template <typename T> struct V8 { typedef bf16x8 type; };
+template <> struct V8<f16> { typedef f16x8 type; };
+
+// Round a and b to the 16-bit type H and back (the values a store of H keeps), with one packed conversion.
+template <typename H>
+__device__ __forceinline__ void round2(float a, float b, float& ra, float& rb) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 f = {a, b};
+    if constexpr (std::is_same<H, f16>::value) {
+        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+        const f16x2 h = __builtin_convertvector(f, f16x2);
+        ra = (float)h[0];
+        rb = (float)h[1];
+    } else {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+        ra = __uint_as_float(u << 16);
+        rb = __uint_as_float(u & 0xffff0000u);
+    }
+}
+
+// One 32x32x16 product of 16-bit operands held as 16-byte fragments (bit patterns): bf16, or fp16 when H is f16.
+template <typename H>
+__device__ __forceinline__ f32x16 mfma16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    if constexpr (std::is_same<H, f16>::value)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
 
 // ---- 4-element vector load/store of T (8 B for bf16, 16 B for fp32) ----
 template <typename T> struct Vec4;
@@ -44,6 +83,17 @@ template <> struct Vec4<bf16> {
         bf16x4 t;
         t[0] = (bf16)v[0]; t[1] = (bf16)v[1]; t[2] = (bf16)v[2]; t[3] = (bf16)v[3];
         *reinterpret_cast<bf16x4*>(p) = t;
+    }
+};
+template <> struct Vec4<f16> {
+    __device__ static __forceinline__ void load(const f16* p, float (&v)[4]) {
+        f16x4 t = *reinterpret_cast<const f16x4*>(p);
+        v[0] = (float)t[0]; v[1] = (float)t[1]; v[2] = (float)t[2]; v[3] = (float)t[3];
+    }
+    __device__ static __forceinline__ void store(f16* p, const float (&v)[4]) {
+        f16x4 t;
+        t[0] = (f16)v[0]; t[1] = (f16)v[1]; t[2] = (f16)v[2]; t[3] = (f16)v[3];
+        *reinterpret_cast<f16x4*>(p) = t;
     }
 };
 

@@ -39,6 +39,9 @@ hipError_t launch_kv_store(Dt dt, const void* qkv, void* cache, int B, int H, in
     if (dt == Dt::BF16)
         hipLaunchKernelGGL(kv_store_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)qkv, (bf16*)cache, B, H, Hkv, D, Tc,
                            t0, nt, rb);
+    else if (dt == Dt::F16)
+        hipLaunchKernelGGL(kv_store_kernel<f16>, grid, dim3(256), 0, s, (const f16*)qkv, (f16*)cache, B, H, Hkv, D, Tc,
+                           t0, nt, rb);
     else
         hipLaunchKernelGGL(kv_store_kernel<float>, grid, dim3(256), 0, s, (const float*)qkv, (float*)cache, B, H, Hkv,
                            D, Tc, t0, nt, rb);
@@ -171,6 +174,8 @@ hipError_t launch_decode_attn(Dt dt, const void* qkv, const void* cache, float* 
     if (dt == Dt::BF16) {
         if (D == 128) return decode_attn_t<bf16, 128>(qkv, cache, part, y, B, H, Hkv, Tc, pos, s);
         if (D == 64) return decode_attn_t<bf16, 64>(qkv, cache, part, y, B, H, Hkv, Tc, pos, s);
+    } else if (dt == Dt::F16) {
+        if (D == 128) return decode_attn_t<f16, 128>(qkv, cache, part, y, B, H, Hkv, Tc, pos, s);
     } else {
         if (D == 128) return decode_attn_t<float, 128>(qkv, cache, part, y, B, H, Hkv, Tc, pos, s);
         if (D == 64) return decode_attn_t<float, 64>(qkv, cache, part, y, B, H, Hkv, Tc, pos, s);
@@ -229,6 +234,9 @@ hipError_t launch_decode_finish(Dt dt, const float* part, int splits, size_t str
     if (dt == Dt::BF16)
         hipLaunchKernelGGL(decode_finish_kernel<bf16>, grid, dim3(256), 0, s, part, splits, stride, rows, N, mode, out,
                            (const bf16*)in, cap);
+    else if (dt == Dt::F16)
+        hipLaunchKernelGGL(decode_finish_kernel<f16>, grid, dim3(256), 0, s, part, splits, stride, rows, N, mode, out,
+                           (const f16*)in, cap);
     else
         hipLaunchKernelGGL(decode_finish_kernel<float>, grid, dim3(256), 0, s, part, splits, stride, rows, N, mode, out,
                            (const float*)in, cap);

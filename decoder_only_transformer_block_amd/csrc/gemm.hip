@@ -29,20 +29,22 @@ namespace ncgpt {
 // The bf16 ones also take 8 consecutive values (put8): the MFMA kernels
 // exchange half-tiles between lanes l and l+32 so that a lane owns 8
 // consecutive columns and stores 16 bytes at once.
-__device__ __forceinline__ void ld8(const bf16* p, float (&v)[8]) {
-    const bf16x8 t = *reinterpret_cast<const bf16x8*>(p);
+template <typename T>
+__device__ __forceinline__ void ld8(const T* p, float (&v)[8]) {
+    const typename V8<T>::type t = *reinterpret_cast<const typename V8<T>::type*>(p);
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = (float)t[e];
 }
-__device__ __forceinline__ void st8(bf16* p, const float (&v)[8]) {
-    bf16x8 t;
+template <typename T>
+__device__ __forceinline__ void st8(T* p, const float (&v)[8]) {
+    typename V8<T>::type t;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) t[e] = (bf16)v[e];
-    *reinterpret_cast<bf16x8*>(p) = t;
+    for (int e = 0; e < 8; ++e) t[e] = (T)v[e];
+    *reinterpret_cast<typename V8<T>::type*>(p) = t;
 }
 
 template <typename T> struct EStoreCd {
-    static constexpr bool kWide = std::is_same<T, bf16>::value, kLoads = false;
+    static constexpr bool kWide = sizeof(T) == 2, kLoads = false;
     T* out; int ldo;
     int64_t sOut = 0;  // batch stride (elements) of a batched GEMM
     __device__ EStoreCd at(int z) const { EStoreCd e = *this; e.out += z * sOut; return e; }
@@ -52,10 +54,11 @@ template <typename T> struct EStoreCd {
     __device__ void put8(int m, int n, int, const float (&v)[8]) const { st8(out + (size_t)m * ldo + n, v); }
 };
 template <typename T> struct EResidual {
-    static constexpr bool kWide = std::is_same<T, bf16>::value, kLoads = true;
+    static constexpr bool kWide = sizeof(T) == 2, kLoads = true;
+    typedef typename V8<T>::type vec8;
     T* out; const T* in; int ldo;
-    __device__ bf16x8 fetch8(int m, int n) const { return *reinterpret_cast<const bf16x8*>(in + (size_t)m * ldo + n); }
-    __device__ void put8(int m, int n, int, const float (&v)[8], const bf16x8& x) const {
+    __device__ vec8 fetch8(int m, int n) const { return *reinterpret_cast<const vec8*>(in + (size_t)m * ldo + n); }
+    __device__ void put8(int m, int n, int, const float (&v)[8], const vec8& x) const {
         float r[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) r[i] = (float)x[i] + v[i];
@@ -112,7 +115,7 @@ template <class E> __device__ __forceinline__ E epi_at(const E& e, int z) {
 // act = a^2 with a = relu(v) rounded to the compute dtype: the only stored output of
 // the MLP's first linear; the backward recovers a as sqrt(act)
 template <typename T> struct EReluSq {
-    static constexpr bool kWide = std::is_same<T, bf16>::value, kLoads = false;
+    static constexpr bool kWide = sizeof(T) == 2, kLoads = false;
     T* act; int ldo;
     __device__ void operator()(int m, int n, int, const float (&v)[4]) const {
         float s[4];
@@ -127,7 +130,7 @@ template <typename T> struct EReluSq {
         float s[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float r = (float)(bf16)fmaxf(v[i], 0.0f);
+            const float r = to_f32(from_f32<T>(fmaxf(v[i], 0.0f)));
             s[i] = r * r;
         }
         st8(act + (size_t)m * ldo + n, s);
@@ -135,10 +138,11 @@ template <typename T> struct EReluSq {
 };
 // dh = dact * d(relu(h)^2)/dh = dact * 2 relu(h), with relu(h) = sqrt(act)
 template <typename T> struct EReluSqBwd {
-    static constexpr bool kWide = std::is_same<T, bf16>::value, kLoads = true;
+    static constexpr bool kWide = sizeof(T) == 2, kLoads = true;
+    typedef typename V8<T>::type vec8;
     T* out; const T* act; int ldo;
-    __device__ bf16x8 fetch8(int m, int n) const { return *reinterpret_cast<const bf16x8*>(act + (size_t)m * ldo + n); }
-    __device__ void put8(int m, int n, int, const float (&v)[8], const bf16x8& x) const {
+    __device__ vec8 fetch8(int m, int n) const { return *reinterpret_cast<const vec8*>(act + (size_t)m * ldo + n); }
+    __device__ void put8(int m, int n, int, const float (&v)[8], const vec8& x) const {
         float r[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) r[i] = v[i] * 2.0f * __builtin_amdgcn_sqrtf((float)x[i]);
@@ -214,7 +218,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], int m0, 
         static_assert(FM % RG == 0, "row groups must divide the row blocks");
 #pragma unroll
         for (int i0 = 0; i0 < FM; i0 += RG) {
-            bf16x8 in[RG][FN][2];
+            decltype(epi.fetch8(0, 0)) in[RG][FN][2];
 #pragma unroll
             for (int ii = 0; ii < RG; ++ii)
 #pragma unroll
@@ -283,7 +287,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], int m0, 
     }
 }
 
-// ------------------------------------------------------------------ LM-head epilogues (bf16)
+// ------------------------------------------------------------------ LM-head epilogues (16-bit compute dtypes)
 // The cross-entropy needs, per row of logits z, lse = log sum exp z and z[target].  The LM-head GEMM
 // forms them from its accumulators, so no pass over the [N, V] logits is needed for the loss: per row and
 // per wave column block (32 FN columns), the max of z log2(e) and the sum of 2^(z log2(e) - max), and the
@@ -291,8 +295,6 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], int m0, 
 // the backward turns into dz, so loss and gradient see the same logits (the shift is the max of the
 // unrounded values: any shift near the max keeps the sum in range, and the merge is exact for any shift).
 constexpr float kLog2eF = 1.4426950408889634f;
-
-__device__ __forceinline__ float rnd_bf16(float v) { return (float)(bf16)v; }
 
 // Max and sum over lanes l and l ^ 32 (the two halves of one accumulator row).  The swap leaves lanes
 // 0..31 with (own, partner) and lanes 32..63 with (partner, own); both orders give the same result.
@@ -309,22 +311,17 @@ __device__ __forceinline__ float pair_sum(float v) {
 template <class E, class = void> struct TileEpi : std::false_type {};
 template <class E> struct TileEpi<E, std::void_t<decltype(E::kTile)>> : std::bool_constant<E::kTile> {};
 
-// Round the 16 accumulators of one 32x32 block to bf16 and back (v_cvt_pk_bf16_f32 rounds two at once).
+// Round the 16 accumulators of one 32x32 block to T and back (one packed conversion per pair).
+template <typename T>
 __device__ __forceinline__ void round16(const f32x16& a, float (&z)[16]) {
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-        typedef float f32x2_t __attribute__((ext_vector_type(2)));
-        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-        const f32x2_t f = {a[r], a[r + 1]};
-        const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-        z[r] = __uint_as_float(u << 16);
-        z[r + 1] = __uint_as_float(u & 0xffff0000u);
-    }
+    for (int r = 0; r < 16; r += 2) round2<T>(a[r], a[r + 1], z[r], z[r + 1]);
 }
 
+template <typename T>
 struct ECeStats {
     static constexpr bool kTile = true;
-    bf16* out;               // [M][ldo] rounded logits, or null (not stored)
+    T* out;                  // [M][ldo] rounded logits, or null (not stored)
     int ldo;
     float2* part;            // [nblk][M]: a wave's 32 rows of one block are 256 contiguous bytes
     int nblk;
@@ -345,7 +342,7 @@ struct ECeStats {
                     for (int r = 0; r < 16; ++r) acc[i][j][r] = softcap_fwd(acc[i][j][r], cap);
         }
         // the rounded logits leave first, so their stores drain while the statistics are formed
-        if (out) store_tile<FM, FN>(acc, m0, n0, 0, M, N, lane, EStoreCd<bf16>{out, ldo});
+        if (out) store_tile<FM, FN>(acc, m0, n0, 0, M, N, lane, EStoreCd<T>{out, ldo});
         if (n0 >= N) return;                      // wave-uniform: the block lies past a ragged vocab edge
         const bool full = n0 + 32 * FN <= N;      // wave-uniform: no column of the block is past the edge
         const int blk = n0 / (32 * FN);
@@ -357,7 +354,7 @@ struct ECeStats {
             const int m = m0 + 32 * i + l32;
             float z[FN][16];
 #pragma unroll
-            for (int j = 0; j < FN; ++j) round16(acc[i][j], z[j]);
+            for (int j = 0; j < FN; ++j) round16<T>(acc[i][j], z[j]);
             if (!full) {
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
@@ -394,11 +391,12 @@ struct ECeStats {
     }
 };
 
-// dz = grad_scale * inv_valid * (softmax(z) - onehot(target)) from recomputed logits, rounded to bf16
+// dz = grad_scale * inv_valid * (softmax(z) - onehot(target)) from recomputed logits, rounded to T
 // first exactly as the stored logits are, so the result equals the stored-logit backward's.
+template <typename T>
 struct EDz {
     static constexpr bool kTile = true;
-    bf16* out;
+    T* out;
     int ldo;
     const float* lse;
     const int32_t* targets;
@@ -442,14 +440,7 @@ struct EDz {
                     const int n = n0 + 32 * j + 16 * p + 8 * h;
                     float z[8];
 #pragma unroll
-                    for (int e = 0; e < 8; e += 2) {
-                        typedef float f32x2_t __attribute__((ext_vector_type(2)));
-                        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-                        const f32x2_t f = {v[e], v[e + 1]};
-                        const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-                        z[e] = __uint_as_float(u << 16);
-                        z[e + 1] = __uint_as_float(u & 0xffff0000u);
-                    }
+                    for (int e = 0; e < 8; e += 2) round2<T>(v[e], v[e + 1], z[e], z[e + 1]);
                     float r[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) r[e] = valid ? k * __builtin_amdgcn_exp2f(z[e] * kLog2eF - l2) : 0.0f;
@@ -469,7 +460,7 @@ struct EDz {
     }
 };
 
-// ------------------------------------------------------------------ qkv epilogue: RoPE + QK-norm (bf16)
+// ------------------------------------------------------------------ qkv epilogue: RoPE + QK-norm (16-bit)
 // The qkv projection's output leaves already rotated and normalised ("nanochat 项目深度分析" §2.1 items 1-2):
 // for token m (position t = m mod T) and each q or k head, pair (i, i + 64) is rotated by the angle of
 // (t, i) as y_i = x_i cos + x_{i+64} sin, y_{i+64} = -x_i sin + x_{i+64} cos, and the head is divided by
@@ -478,9 +469,10 @@ struct EDz {
 // is saved for the backward.  With the 4 x 2 wave grid a wave owns 128 columns = one head, and in the
 // accumulator layout the pair (i, i + 64) sits in one lane (column blocks j and j + 2), so everything is
 // lane-local except the head sum, which adds the two lane halves of a row.
+template <typename O>  // the stored type (bf16 or f16)
 struct ERopeNorm {
     static constexpr bool kTile = true;
-    bf16* out;
+    O* out;
     int ldo;
     const float* cosv;   // [T][64]
     const float* sinv;
@@ -507,7 +499,7 @@ struct ERopeNorm {
         if (n0 >= N) return;                 // wave-uniform: past the last head
         const int head = n0 >> 7;
         if (head >= H + Hkv) {               // v head: stored as computed
-            store_tile<FM, FN>(acc, m0, n0, 0, M, N, lane, EStoreCd<bf16>{out, ldo});
+            store_tile<FM, FN>(acc, m0, n0, 0, M, N, lane, EStoreCd<O>{out, ldo});
             return;
         }
         const int h = lane >> 5, l32 = lane & 31;
@@ -550,7 +542,7 @@ struct ERopeNorm {
                     swap8(y1, p, v1);
                     swap8(y2, p, v2);
                     if (live) {
-                        bf16* row = out + (size_t)m * ldo + n0 + 16 * p + 8 * h;
+                        O* row = out + (size_t)m * ldo + n0 + 16 * p + 8 * h;
                         st8(row + 32 * j, v1);
                         st8(row + 32 * (j + 2), v2);
                     }
@@ -719,7 +711,7 @@ __device__ __forceinline__ void dequant_rows(f32x16 (&acc)[FM][FN], int m0, int 
         }
 }
 
-template <int BM, int BN, int WGM, int WGN, bool AK, bool BK, class E, bool F8 = false>
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BK, class E, bool F8 = false, typename H = bf16>
 __global__ void __launch_bounds__(64 * WGM * WGN, 1)
 gemm_bf16_mfma_ring(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
                     int k_split, int group_m, E epi_, int64_t sA, int64_t sB, const float* __restrict__ rsa,
@@ -779,7 +771,7 @@ gemm_bf16_mfma_ring(const bf16* __restrict__ A, const bf16* __restrict__ B, int 
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+                acc[i][j] = mfma16<H>(fb[buf][j], fa[buf][i], acc[i][j]);
     };
     // Instruction order inside one k-step's region: each MFMA is followed by at most one
     // load and one fragment read, so neither memory queue receives a burst.  None of the
@@ -881,7 +873,7 @@ gemm_bf16_mfma_ring(const bf16* __restrict__ A, const bf16* __restrict__ B, int 
 // a multiple of four stages (stages past its k range read zeros).  Loads and
 // stores share the vector-memory counter and may complete out of order, so the
 // first wait after an epilogue waits for everything.
-template <int BM, int BN, int WGM, int WGN, bool AK, bool BK, class E>
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BK, class E, typename H = bf16>
 __global__ void __launch_bounds__(64 * WGM * WGN, 1)
 gemm_bf16_mfma_pring(const bf16* __restrict__ A, const bf16* __restrict__ B, int M, int N, int K, int lda, int ldb,
                      int k_split, int splits, int group_m, E epi)
@@ -947,7 +939,7 @@ gemm_bf16_mfma_pring(const bf16* __restrict__ A, const bf16* __restrict__ B, int
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+                acc[i][j] = mfma16<H>(fb[buf][j], fa[buf][i], acc[i][j]);
     };
     // Instruction order inside one k-step's region: each MFMA is followed by at most one
     // load and one fragment read, so neither memory queue receives a burst.  None of the
@@ -1084,14 +1076,18 @@ static int num_cus() {
     return n;
 }
 
-template <int BM, int BN, bool AK, bool BK, class E>
+template <class E> struct IsRope : std::false_type {};
+template <typename T> struct IsRope<ERopeNorm<T>> : std::true_type {};
+
+// H: the 16-bit operand type (bf16, or f16 in the fp16 compute mode)
+template <int BM, int BN, bool AK, bool BK, typename H, class E>
 static hipError_t run_mfma(const GemmDesc& d, E e, hipStream_t s) {
     const int splits = (d.K + d.k_split - 1) / d.k_split;
     const int tiles = ((d.M + BM - 1) / BM) * ((d.N + BN - 1) / BN);
-    if constexpr (std::is_same<E, ERopeNorm>::value) {
+    if constexpr (IsRope<E>::value) {
         if constexpr (BM == 256 && BN == 256) {
             if (d.loop != GemmLoop::Persist8Heads) return hipErrorInvalidValue;
-            auto pk = gemm_bf16_mfma_pring<256, 256, 4, 2, AK, BK, E>;
+            auto pk = gemm_bf16_mfma_pring<256, 256, 4, 2, AK, BK, E, H>;
             static int occ = 0;
             if (occ == 0) {
                 hipError_t st = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(pk), 512, 0);
@@ -1110,13 +1106,14 @@ static hipError_t run_mfma(const GemmDesc& d, E e, hipStream_t s) {
     if (d.batch > 1 && d.loop != GemmLoop::Ring8) return hipErrorInvalidValue;  // batches run on the ring only
     if (d.loop == GemmLoop::Ring8) {
         if (d.batch > 1 && !BatchEpi<E>::value) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((gemm_bf16_mfma_ring<BM, BN, 2, 4, AK, BK, E>), dim3(tiles, splits, d.batch), dim3(512), 0,
+        hipLaunchKernelGGL((gemm_bf16_mfma_ring<BM, BN, 2, 4, AK, BK, E, false, H>), dim3(tiles, splits, d.batch),
+                           dim3(512), 0,
                            s, (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, d.K, d.lda, d.ldb, d.k_split, d.group_m, e,
                            (int64_t)d.sA, (int64_t)d.sB, nullptr, nullptr);
         return hipGetLastError();
     }
     const bool eight = d.loop == GemmLoop::Persist8;
-    auto pk = eight ? gemm_bf16_mfma_pring<BM, BN, 2, 4, AK, BK, E> : gemm_bf16_mfma_pring<BM, BN, 2, 2, AK, BK, E>;
+    auto pk = eight ? gemm_bf16_mfma_pring<BM, BN, 2, 4, AK, BK, E, H> : gemm_bf16_mfma_pring<BM, BN, 2, 2, AK, BK, E, H>;
     const int nt = eight ? 512 : 256;
     static int resident[2] = {0, 0};  // workgroups per CU, from the occupancy query
     int& occ = resident[eight ? 1 : 0];
@@ -1141,19 +1138,19 @@ static hipError_t run_f8(const GemmDesc& d, E e, hipStream_t s) {
         return hipErrorInvalidValue;
     const int K = d.K / 2, lda = d.lda / 2, ldb = d.ldb / 2;
     const int tiles = ((d.M + 255) / 256) * ((d.N + 255) / 256);
-    constexpr bool heads = std::is_same<E, ERopeNorm>::value;
+    constexpr bool heads = IsRope<E>::value;
     hipLaunchKernelGGL((gemm_bf16_mfma_ring<256, 256, heads ? 4 : 2, heads ? 2 : 4, true, true, E, true>),
                        dim3(tiles, 1, 1), dim3(512), 0, s, (const bf16*)d.A, (const bf16*)d.B, d.M, d.N, K, lda, ldb,
                        K, d.group_m, e, (int64_t)0, (int64_t)0, d.rsa, d.rsb);
     return hipGetLastError();
 }
 
-template <bool AK, bool BK, class E>
+template <bool AK, bool BK, typename H, class E>
 static hipError_t run_bf16(const GemmDesc& d, E e, hipStream_t s) {
     switch (d.tile) {
-    case 0: return run_mfma<256, 256, AK, BK>(d, e, s);
-    case 1: return run_mfma<256, 128, AK, BK>(d, e, s);
-    default: return run_mfma<128, 128, AK, BK>(d, e, s);
+    case 0: return run_mfma<256, 256, AK, BK, H>(d, e, s);
+    case 1: return run_mfma<256, 128, AK, BK, H>(d, e, s);
+    default: return run_mfma<128, 128, AK, BK, H>(d, e, s);
     }
 }
 
@@ -1175,11 +1172,11 @@ template <typename T, bool AK, bool BK>
 static hipError_t dispatch_epi(const GemmDesc& d, hipStream_t s) {
     auto run = [&](auto e) -> hipError_t {
         if constexpr (sizeof(T) == 2) {
-            if constexpr (AK && BK && !std::is_same<decltype(e), ESplitK>::value) {
+            if constexpr (AK && BK && std::is_same<T, bf16>::value && !std::is_same<decltype(e), ESplitK>::value) {
                 if (d.fp8) return run_f8(d, e, s);
             }
             if (d.fp8) return hipErrorInvalidValue;
-            return run_bf16<AK, BK>(d, e, s);
+            return run_bf16<AK, BK, T>(d, e, s);
         } else {
             if (d.fp8) return hipErrorInvalidValue;
             return run_f32<AK, BK>(d, e, s);
@@ -1193,18 +1190,18 @@ static hipError_t dispatch_epi(const GemmDesc& d, hipStream_t s) {
         case Epi::SplitK: return run(ESplitK{(float*)d.out, d.ldo, d.split_stride});  // B-row decode products
         case Epi::CeStats:
             if constexpr (sizeof(T) == 2)
-                return run(ECeStats{(bf16*)d.out, d.ldo, (float2*)d.part, d.nblk, d.zt, d.targets, d.cap});
+                return run(ECeStats<T>{(T*)d.out, d.ldo, (float2*)d.part, d.nblk, d.zt, d.targets, d.cap});
             break;
         case Epi::Dz:
             if constexpr (sizeof(T) == 2)
-                return run(EDz{(bf16*)d.out, d.ldo, d.lse, d.targets, d.inv_valid, d.grad_scale, d.cap});
+                return run(EDz<T>{(T*)d.out, d.ldo, d.lse, d.targets, d.inv_valid, d.grad_scale, d.cap});
             break;
         case Epi::RopeNorm:
             if constexpr (sizeof(T) == 2) {
                 if (d.T <= 0 || d.H <= 0 || d.Hkv <= 0 || !d.cosv || !d.sinv || !d.rstdq || !d.rstdk ||
                     d.N != (d.H + 2 * d.Hkv) * 128 || d.tile != 0)
                     return hipErrorInvalidValue;
-                return run(ERopeNorm{(bf16*)d.out, d.ldo, d.cosv, d.sinv, d.rstdq, d.rstdk, d.T, d.H, d.Hkv, d.eps});
+                return run(ERopeNorm<T>{(T*)d.out, d.ldo, d.cosv, d.sinv, d.rstdq, d.rstdk, d.T, d.H, d.Hkv, d.eps});
             }
             break;
         default: break;
@@ -1214,15 +1211,15 @@ static hipError_t dispatch_epi(const GemmDesc& d, hipStream_t s) {
         case Epi::StoreCd: return run(EStoreCd<T>{(T*)d.out, d.ldo, d.sOut});
         case Epi::ReluSqBwd: return run(EReluSqBwd<T>{(T*)d.out, (const T*)d.in, d.ldo});
         case Epi::Axpby:
-            if constexpr (sizeof(T) == 2)
+            if constexpr (std::is_same<T, bf16>::value)
                 return run(EAxpby{(bf16*)d.out, (const bf16*)d.in, d.ldo, d.alpha, d.beta, d.sOut, d.sIn});
             break;
         default: break;
         }
     } else if constexpr (!AK && !BK) {
         switch (d.epi) {
-        case Epi::StoreCd:
-            if constexpr (sizeof(T) == 2) return run(EStoreCd<T>{(T*)d.out, d.ldo, d.sOut});
+        case Epi::StoreCd:  // the Newton-Schulz X^T X (bf16)
+            if constexpr (std::is_same<T, bf16>::value) return run(EStoreCd<T>{(T*)d.out, d.ldo, d.sOut});
             break;
         case Epi::Grad: return run(EGrad{(float*)d.out, d.ldo, d.accumulate});
         case Epi::SplitK: return run(ESplitK{(float*)d.out, d.ldo, d.split_stride});
@@ -1250,6 +1247,7 @@ hipError_t launch_gemm(const GemmDesc& in, hipStream_t s) {
     if (d.k_split % 64) return hipErrorInvalidValue;
     if (d.epi != Epi::SplitK && d.k_split < d.K) return hipErrorInvalidValue;  // only SplitK writes partials
     if (d.dt == Dt::BF16) return dispatch_layout<bf16>(d, s);
+    if (d.dt == Dt::F16) return dispatch_layout<f16>(d, s);
     return dispatch_layout<float>(d, s);
 }
 
@@ -1263,13 +1261,16 @@ const char* gemm_kernel_name(const GemmDesc& d) {
     int li = (d.a_kcontig ? 2 : 0) + (d.b_kcontig ? 1 : 0);
     if (d.dt == Dt::F32) return li == 3 ? "gemm_f32_nt" : (li == 2 ? "gemm_f32_nn" : "gemm_f32_tn");
     if (d.fp8) return "gemm_fp8_nt_256x256";
-    static const char* names[3][3] = {
-        {"gemm_bf16_nt_256x256", "gemm_bf16_nt_256x128", "gemm_bf16_nt_128x128"},
-        {"gemm_bf16_nn_256x256", "gemm_bf16_nn_256x128", "gemm_bf16_nn_128x128"},
-        {"gemm_bf16_tn_256x256", "gemm_bf16_tn_256x128", "gemm_bf16_tn_128x128"}};
+    static const char* names[2][3][3] = {
+        {{"gemm_bf16_nt_256x256", "gemm_bf16_nt_256x128", "gemm_bf16_nt_128x128"},
+         {"gemm_bf16_nn_256x256", "gemm_bf16_nn_256x128", "gemm_bf16_nn_128x128"},
+         {"gemm_bf16_tn_256x256", "gemm_bf16_tn_256x128", "gemm_bf16_tn_128x128"}},
+        {{"gemm_f16_nt_256x256", "gemm_f16_nt_256x128", "gemm_f16_nt_128x128"},
+         {"gemm_f16_nn_256x256", "gemm_f16_nn_256x128", "gemm_f16_nn_128x128"},
+         {"gemm_f16_tn_256x256", "gemm_f16_tn_256x128", "gemm_f16_tn_128x128"}}};
     int r = li == 3 ? 0 : (li == 2 ? 1 : 2);
     int t = d.tile < 0 ? 0 : (d.tile > 2 ? 2 : d.tile);
-    return names[r][t];
+    return names[d.dt == Dt::F16 ? 1 : 0][r][t];
 }
 
 // ------------------------------------------------------------------ split-K reduction

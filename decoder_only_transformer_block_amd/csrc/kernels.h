@@ -7,7 +7,9 @@
 
 namespace ncgpt {
 
-enum class Dt : int { F32 = 0, BF16 = 1 };
+enum class Dt : int { F32 = 0, BF16 = 1, F16 = 2 };
+// the 16-bit compute dtypes share the MFMA path (bf16, or fp16 with loss scaling)
+inline bool mfma_dt(Dt d) { return d != Dt::F32; }
 
 // Device-side error bits, OR-ed into a flag word in the workspace and read by
 // the host in ncgpt_check.
@@ -138,7 +140,8 @@ hipError_t launch_attn_fwd(const AttnDesc& a, hipStream_t s);
 hipError_t launch_attn_bwd(const AttnDesc& a, hipStream_t s, int part);
 
 // ---------------------------------------------------------------- row-wise / elementwise
-hipError_t launch_cast_bf16(const float* src, void* dst, size_t n, hipStream_t s);
+// fp32 -> the 16-bit compute dtype (bf16, or fp16 for Dt::F16), round to nearest even
+hipError_t launch_cast_bf16(const float* src, void* dst, size_t n, hipStream_t s, Dt dt = Dt::BF16);
 hipError_t launch_embed_fwd(Dt dt, const int32_t* ids, const float* wte, void* x, int N, int C, int V,
                             uint32_t* err, hipStream_t s);
 // q8 non-null (bf16, C a multiple of 256 up to 2048): the stored rows also as E4M3 bytes with scales qs (the
@@ -179,6 +182,8 @@ hipError_t launch_to_f32(Dt dt, const void* src, float* dst, size_t n, hipStream
 hipError_t launch_quant_rows_fp8(Dt src, const void* x, size_t x_layer, void* q, size_t q_layer, float* s,
                                  size_t s_layer, int rows, int cols, int layers, hipStream_t st);
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);
+// *ok = 1 if all n values are finite, else 0
+hipError_t launch_finite(const float* x, size_t n, int32_t* ok, hipStream_t s);
 
 // ---------------------------------------------------------------- KV-cache decode (decode.hip)
 // cache of one layer: [2][B][Hkv][Tc][D]; stores k and v heads of qkv rows b * rb + (t - t0), t in [t0, t0 + nt)

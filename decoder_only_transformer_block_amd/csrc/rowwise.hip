@@ -1,6 +1,6 @@
 // Bandwidth-bound kernels of the step: weight cast, embedding gather and its
 // gradient, parameter-free RMSNorm, RoPE + QK-norm, and the cross-entropy
-// pieces.  Storage type T is the compute dtype (float or bf16); all
+// pieces.  Storage type T is the compute dtype (float, bf16 or fp16); all
 // arithmetic is fp32.
 #include "common.h"
 #include "kernels.h"
@@ -21,10 +21,24 @@ __global__ void __launch_bounds__(256) cast_bf16_kernel(const float* __restrict_
     }
 }
 
-hipError_t launch_cast_bf16(const float* src, void* dst, size_t n, hipStream_t s) {
+__global__ void __launch_bounds__(256) cast_f16_kernel(const float* __restrict__ src, f16* __restrict__ dst, size_t n4)
+{
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (; i < n4; i += stride) {
+        float v[4];
+        Vec4<float>::load(src + 4 * i, v);
+        Vec4<f16>::store(dst + 4 * i, v);
+    }
+}
+
+hipError_t launch_cast_bf16(const float* src, void* dst, size_t n, hipStream_t s, Dt dt) {
     size_t n4 = n / 4;
     unsigned blocks = (unsigned)std::min<size_t>((n4 + 255) / 256, 256 * 64);
-    hipLaunchKernelGGL(cast_bf16_kernel, dim3(blocks), dim3(256), 0, s, src, (bf16*)dst, n4);
+    if (dt == Dt::F16)
+        hipLaunchKernelGGL(cast_f16_kernel, dim3(blocks), dim3(256), 0, s, src, (f16*)dst, n4);
+    else
+        hipLaunchKernelGGL(cast_bf16_kernel, dim3(blocks), dim3(256), 0, s, src, (bf16*)dst, n4);
     return hipGetLastError();
 }
 
@@ -52,6 +66,8 @@ hipError_t launch_embed_fwd(Dt dt, const int32_t* ids, const float* wte, void* x
     dim3 grid((N + 3) / 4);
     if (dt == Dt::BF16)
         hipLaunchKernelGGL(embed_fwd_kernel<bf16>, grid, dim3(256), 0, s, ids, wte, (bf16*)x, N, C, V, err);
+    else if (dt == Dt::F16)
+        hipLaunchKernelGGL(embed_fwd_kernel<f16>, grid, dim3(256), 0, s, ids, wte, (f16*)x, N, C, V, err);
     else
         hipLaunchKernelGGL(embed_fwd_kernel<float>, grid, dim3(256), 0, s, ids, wte, (float*)x, N, C, V, err);
     return hipGetLastError();
@@ -97,6 +113,17 @@ __device__ __forceinline__ void load8(const bf16* p, float (&v)[8]) {
 __device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
     *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ void load8(const f16* p, float (&v)[8]) {
+    const f16x8 a = *reinterpret_cast<const f16x8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)a[e];
+}
+__device__ __forceinline__ void store8(f16* p, const float (&v)[8]) {
+    f16x8 a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = (f16)v[e];
+    *reinterpret_cast<f16x8*>(p) = a;
 }
 __device__ __forceinline__ void store8(bf16* p, const float (&v)[8]) {
     bf16x8 a;
@@ -209,13 +236,16 @@ static bool rmsnorm_fwd_rows_launch(const void* x, void* y, float* rstd, int row
 hipError_t launch_rmsnorm_fwd(Dt dt, const void* x, void* y, float* rstd, int rows, int C, float eps, hipStream_t s,
                               void* q8, float* qs) {
     if (q8 && (dt != Dt::BF16 || !qs)) return hipErrorInvalidValue;
-    if (dt == Dt::BF16 ? rmsnorm_fwd_rows_launch<bf16>(x, y, rstd, rows, C, eps, (uint8_t*)q8, qs, s)
-                       : rmsnorm_fwd_rows_launch<float>(x, y, rstd, rows, C, eps, nullptr, nullptr, s))
+    if (dt == Dt::BF16  ? rmsnorm_fwd_rows_launch<bf16>(x, y, rstd, rows, C, eps, (uint8_t*)q8, qs, s)
+        : dt == Dt::F16 ? rmsnorm_fwd_rows_launch<f16>(x, y, rstd, rows, C, eps, nullptr, nullptr, s)
+                        : rmsnorm_fwd_rows_launch<float>(x, y, rstd, rows, C, eps, nullptr, nullptr, s))
         return hipGetLastError();
     if (q8) return hipErrorInvalidValue;       // the E4M3 copy comes only from the register-row kernel
     dim3 grid((rows + 3) / 4);
     if (dt == Dt::BF16)
         hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)x, (bf16*)y, rstd, rows, C, eps);
+    else if (dt == Dt::F16)
+        hipLaunchKernelGGL(rmsnorm_fwd_kernel<f16>, grid, dim3(256), 0, s, (const f16*)x, (f16*)y, rstd, rows, C, eps);
     else
         hipLaunchKernelGGL(rmsnorm_fwd_kernel<float>, grid, dim3(256), 0, s, (const float*)x, (float*)y, rstd, rows, C,
                            eps);
@@ -311,13 +341,17 @@ static bool rmsnorm_bwd_rows_launch(const void* y, const float* rstd, const void
 
 hipError_t launch_rmsnorm_bwd(Dt dt, const void* y, const float* rstd, const void* dy, float* dx, void* dx_cd,
                               int rows, int C, int accumulate, hipStream_t s) {
-    if (dt == Dt::BF16 ? rmsnorm_bwd_rows_launch<bf16>(y, rstd, dy, dx, dx_cd, rows, C, accumulate, s)
-                       : rmsnorm_bwd_rows_launch<float>(y, rstd, dy, dx, dx_cd, rows, C, accumulate, s))
+    if (dt == Dt::BF16  ? rmsnorm_bwd_rows_launch<bf16>(y, rstd, dy, dx, dx_cd, rows, C, accumulate, s)
+        : dt == Dt::F16 ? rmsnorm_bwd_rows_launch<f16>(y, rstd, dy, dx, dx_cd, rows, C, accumulate, s)
+                        : rmsnorm_bwd_rows_launch<float>(y, rstd, dy, dx, dx_cd, rows, C, accumulate, s))
         return hipGetLastError();
     dim3 grid((rows + 3) / 4);
     if (dt == Dt::BF16)
         hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)y, rstd, (const bf16*)dy, dx,
                            (bf16*)dx_cd, rows, C, accumulate);
+    else if (dt == Dt::F16)
+        hipLaunchKernelGGL(rmsnorm_bwd_kernel<f16>, grid, dim3(256), 0, s, (const f16*)y, rstd, (const f16*)dy, dx,
+                           (f16*)dx_cd, rows, C, accumulate);
     else
         hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, grid, dim3(256), 0, s, (const float*)y, rstd, (const float*)dy,
                            dx, (float*)dx_cd, rows, C, accumulate);
@@ -446,6 +480,7 @@ static hipError_t rope_bwd_t(T* dqkv, const T* qkv, const float* rq, const float
 hipError_t launch_rope_qknorm_fwd(Dt dt, void* qkv, float* rstdq, float* rstdk, const float* cosv, const float* sinv,
                                   int N, int T, int H, int Hkv, int D, float eps, hipStream_t s, int pos) {
     if (dt == Dt::BF16) return rope_fwd_t((bf16*)qkv, rstdq, rstdk, cosv, sinv, N, T, H, Hkv, D, eps, pos, s);
+    if (dt == Dt::F16) return rope_fwd_t((f16*)qkv, rstdq, rstdk, cosv, sinv, N, T, H, Hkv, D, eps, pos, s);
     return rope_fwd_t((float*)qkv, rstdq, rstdk, cosv, sinv, N, T, H, Hkv, D, eps, pos, s);
 }
 
@@ -454,6 +489,8 @@ hipError_t launch_rope_qknorm_bwd(Dt dt, void* dqkv, const void* qkv, const floa
                                   hipStream_t s) {
     if (dt == Dt::BF16)
         return rope_bwd_t((bf16*)dqkv, (const bf16*)qkv, rstdq, rstdk, cosv, sinv, N, T, H, Hkv, D, s);
+    if (dt == Dt::F16)
+        return rope_bwd_t((f16*)dqkv, (const f16*)qkv, rstdq, rstdk, cosv, sinv, N, T, H, Hkv, D, s);
     return rope_bwd_t((float*)dqkv, (const float*)qkv, rstdq, rstdk, cosv, sinv, N, T, H, Hkv, D, s);
 }
 
@@ -515,6 +552,9 @@ hipError_t launch_ce_fwd_rows(Dt dt, const void* logits, const int32_t* targets,
                               int V, uint32_t* err, hipStream_t s) {
     if (dt == Dt::BF16)
         hipLaunchKernelGGL(ce_fwd_rows_kernel<bf16>, dim3(N), dim3(256), 0, s, (const bf16*)logits, targets, lse,
+                           loss_rows, V, err);
+    else if (dt == Dt::F16)
+        hipLaunchKernelGGL(ce_fwd_rows_kernel<f16>, dim3(N), dim3(256), 0, s, (const f16*)logits, targets, lse,
                            loss_rows, V, err);
     else
         hipLaunchKernelGGL(ce_fwd_rows_kernel<float>, dim3(N), dim3(256), 0, s, (const float*)logits, targets, lse,
@@ -639,6 +679,9 @@ hipError_t launch_ce_bwd(Dt dt, void* logits, const float* lse, const int32_t* t
     if (dt == Dt::BF16)
         hipLaunchKernelGGL(ce_bwd_kernel<bf16>, dim3(N), dim3(256), 0, s, (bf16*)logits, lse, targets, inv_valid,
                            grad_scale, cap, V);
+    else if (dt == Dt::F16)
+        hipLaunchKernelGGL(ce_bwd_kernel<f16>, dim3(N), dim3(256), 0, s, (f16*)logits, lse, targets, inv_valid,
+                           grad_scale, cap, V);
     else
         hipLaunchKernelGGL(ce_bwd_kernel<float>, dim3(N), dim3(256), 0, s, (float*)logits, lse, targets, inv_valid,
                            grad_scale, cap, V);
@@ -667,6 +710,8 @@ hipError_t launch_softcap(Dt dt, void* z, size_t n, const SoftCap& cap, hipStrea
     const unsigned blocks = (unsigned)std::min<size_t>((n4 + 255) / 256, 256 * 32);
     if (dt == Dt::BF16)
         hipLaunchKernelGGL(softcap_kernel<bf16>, dim3(blocks), dim3(256), 0, s, (bf16*)z, n4, cap);
+    else if (dt == Dt::F16)
+        hipLaunchKernelGGL(softcap_kernel<f16>, dim3(blocks), dim3(256), 0, s, (f16*)z, n4, cap);
     else
         hipLaunchKernelGGL(softcap_kernel<float>, dim3(blocks), dim3(256), 0, s, (float*)z, n4, cap);
     return hipGetLastError();
@@ -761,9 +806,31 @@ hipError_t launch_quant_rows_fp8(Dt src, const void* x, size_t x_layer, void* q,
     if (src == Dt::BF16)
         hipLaunchKernelGGL(quant_rows_fp8_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)x, x_layer, (uint8_t*)q,
                            q_layer, s, s_layer, rows, cols);
+    else if (src == Dt::F16)
+        hipLaunchKernelGGL(quant_rows_fp8_kernel<f16>, grid, dim3(256), 0, st, (const f16*)x, x_layer, (uint8_t*)q,
+                           q_layer, s, s_layer, rows, cols);
     else
         hipLaunchKernelGGL(quant_rows_fp8_kernel<float>, grid, dim3(256), 0, st, (const float*)x, x_layer,
                            (uint8_t*)q, q_layer, s, s_layer, rows, cols);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ loss-scaling check
+// ok = 1, then any thread that meets a non-finite value stores 0 (every writer stores the same value).
+__global__ void __launch_bounds__(64) set_one_kernel(int32_t* ok) { if (threadIdx.x == 0) *ok = 1; }
+__global__ void __launch_bounds__(256) finite_kernel(const float* __restrict__ x, size_t n, int32_t* ok)
+{
+    const size_t stride = (size_t)gridDim.x * 256;
+    bool bad = false;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) bad |= !__builtin_isfinite(x[i]);
+    if (__any(bad) && bad) *ok = 0;
+}
+
+hipError_t launch_finite(const float* x, size_t n, int32_t* ok, hipStream_t s) {
+    hipLaunchKernelGGL(set_one_kernel, dim3(1), dim3(64), 0, s, ok);
+    if (n == 0) return hipGetLastError();
+    const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 256 * 16);
+    hipLaunchKernelGGL(finite_kernel, dim3(blocks), dim3(256), 0, s, x, n, ok);
     return hipGetLastError();
 }
 
@@ -965,6 +1032,8 @@ hipError_t launch_to_f32(Dt dt, const void* src, float* dst, size_t n, hipStream
     if (blocks == 0) return hipSuccess;
     if (dt == Dt::BF16)
         hipLaunchKernelGGL(to_f32_kernel<bf16>, dim3(blocks), dim3(256), 0, s, (const bf16*)src, dst, n);
+    else if (dt == Dt::F16)
+        hipLaunchKernelGGL(to_f32_kernel<f16>, dim3(blocks), dim3(256), 0, s, (const f16*)src, dst, n);
     else
         hipLaunchKernelGGL(to_f32_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)src, dst, n);
     return hipGetLastError();

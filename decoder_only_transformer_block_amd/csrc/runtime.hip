@@ -73,7 +73,7 @@ struct ncgpt_ctx {
     bool fp8 = false;                   // ncgpt_set_fp8: forward linears on E4M3 operands
     bool loss_fp8 = false;              // the last ncgpt_loss ran its LM head on E4M3 operands
     SoftCap cap;                        // the logit soft-cap of cfg (off when cfg.logit_softcap == 0)
-    bool cast_valid = false;  // the workspace holds a bf16 copy of the weights (a forward or a recasting decode)
+    bool cast_valid = false;  // the workspace holds a 16-bit copy of the weights (a forward or a recasting decode)
     int loss_mode = NCGPT_LOGITS_STORED;  // the mode the last ncgpt_loss ran in
     const int32_t* ids = nullptr;
     const float* params = nullptr;
@@ -172,7 +172,7 @@ WGrad pick_wgrad(Dt dt, int64_t M, int64_t N, int64_t K) {
     return w;
 }
 
-// The bf16 LM-head GEMM z = xf Wlm^T (tokens x vocab, K = n_embd): its tile, loop and band height are
+// The 16-bit LM-head GEMM z = xf Wlm^T (tokens x vocab, K = n_embd): its tile, loop and band height are
 // fixed here so that the workspace plan (the CeStats column blocks) and the launches agree.
 GemmDesc lm_head_desc(const ncgpt_ctx* c) {
     GemmDesc d;
@@ -209,7 +209,7 @@ void make_plan(ncgpt_ctx* c) {
     p.flag = A(256);
     p.cosv = A((size_t)c->T * (c->D / 2) * 4);
     p.sinv = A((size_t)c->T * (c->D / 2) * 4);
-    p.wcast = A(c->dt == Dt::BF16 ? (size_t)(c->P - c->VC) * 2 : 0);
+    p.wcast = A(mfma_dt(c->dt) ? (size_t)(c->P - c->VC) * 2 : 0);
     // fp8 forward linears (bf16 mode): E4M3 weights at the bf16 copy's element offsets, their per-row scales
     // (layer-major rows: qkv, Wo, Wfc, Wproj; then lm_head), and one activation's rows with their scales
     {
@@ -244,13 +244,13 @@ void make_plan(ncgpt_ctx* c) {
     p.logits = A(N * c->V * e);
     const GemmDesc lm = lm_head_desc(c);
     p.ce_nblk = (int)((c->V + gemm_wave_cols(lm) - 1) / gemm_wave_cols(lm));
-    p.cepart = A(c->dt == Dt::BF16 ? N * p.ce_nblk * 8 : 0);
+    p.cepart = A(mfma_dt(c->dt) ? N * p.ce_nblk * 8 : 0);
     p.zt = A(N * 4);
     p.lse = A(N * 4);
     p.loss_rows = A(N * 4);
     p.dxn = A(N * c->C * 4);
     p.dx = A(N * c->C * 4);
-    p.dx_cd = A(c->dt == Dt::BF16 ? N * c->C * 2 : 0);
+    p.dx_cd = A(mfma_dt(c->dt) ? N * c->C * 2 : 0);
     p.dh = A(N * c->F * e);
     p.dy = A(N * c->HD * e);
     p.dqkv = A(N * c->QKV * e);
@@ -410,7 +410,7 @@ ncgpt_status gemm(ncgpt_ctx* c, GemmDesc d, const char* tag, bool bf16_always = 
     const char* nm = intern(std::string(gemm_kernel_name(d)) + ":" + epi_name(d.epi) + ":" + tag);
     const double fl = 2.0 * d.M * d.N * d.K * d.batch;
     // algorithmic bytes: both operands once, the output (and what the epilogue reads) once
-    const double e = d.dt == Dt::BF16 ? 2.0 : 4.0, mn = (double)d.M * d.N;
+    const double e = mfma_dt(d.dt) ? 2.0 : 4.0, mn = (double)d.M * d.N;
     double out = e;
     switch (d.epi) {
     case Epi::ResidualCd: case Epi::ReluSqBwd: out = 2.0 * e; break;
@@ -461,7 +461,7 @@ const void* weight(ncgpt_ctx* c, int layer, int which) {
     size_t off;
     int64_t r, cc;
     ncgpt_param_slice(&c->cfg, layer, which, &off, &r, &cc);
-    if (c->dt == Dt::BF16) return c->at<uint8_t>(c->pl.wcast) + (off - c->VC) * 2;
+    if (mfma_dt(c->dt)) return c->at<uint8_t>(c->pl.wcast) + (off - c->VC) * 2;
     return c->params + off;
 }
 
@@ -623,8 +623,8 @@ ncgpt_status ncgpt_param_slice(const ncgpt_config* g, int layer, int which, size
 ncgpt_status ncgpt_create(const ncgpt_config* g, ncgpt_dtype dtype, ncgpt_ctx** out) {
     if (!out) return NCGPT_EINVAL;
     *out = nullptr;
-    if (!valid_cfg(g) || (dtype != NCGPT_F32 && dtype != NCGPT_BF16)) return NCGPT_EINVAL;
-    const bool bf = dtype == NCGPT_BF16;
+    if (!valid_cfg(g) || (dtype != NCGPT_F32 && dtype != NCGPT_BF16 && dtype != NCGPT_F16)) return NCGPT_EINVAL;
+    const bool bf = dtype != NCGPT_F32;   // the 16-bit MFMA path (bf16 or fp16)
     if (g->n_head % g->n_kv_head) return NCGPT_EUNSUPPORTED;
     if (bf ? g->head_dim != 128 : (g->head_dim != 64 && g->head_dim != 128)) return NCGPT_EUNSUPPORTED;
     if (g->n_embd % 64 || g->mlp_dim % 64 || g->vocab_size % 64) return NCGPT_EUNSUPPORTED;
@@ -638,7 +638,7 @@ ncgpt_status ncgpt_create(const ncgpt_config* g, ncgpt_dtype dtype, ncgpt_ctx** 
     if (!c) return NCGPT_ENOMEM;
     c->cfg = *g;
     c->dtype = dtype;
-    c->dt = bf ? Dt::BF16 : Dt::F32;
+    c->dt = dtype == NCGPT_BF16 ? Dt::BF16 : (dtype == NCGPT_F16 ? Dt::F16 : Dt::F32);
     c->L = g->n_layer; c->C = g->n_embd; c->H = g->n_head; c->Hkv = g->n_kv_head; c->D = g->head_dim;
     c->F = g->mlp_dim; c->V = g->vocab_size; c->B = g->batch; c->T = g->seq_len;
     c->N = c->B * c->T; c->HD = c->H * c->D; c->KD = c->Hkv * c->D; c->QKV = c->HD + 2 * c->KD;
@@ -719,10 +719,10 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
     const size_t e = c->esz;
     uint32_t* flag = c->at<uint32_t>(p.flag);
 
-    if (dt == Dt::BF16) {
+    if (mfma_dt(dt)) {
         const size_t n = (size_t)(c->P - c->VC);
         TRY(launch(c, "cast_bf16", 0.0, (double)n * 6,
-                   [&] { return launch_cast_bf16(params + c->VC, c->ws + p.wcast, n, c->stream); }));
+                   [&] { return launch_cast_bf16(params + c->VC, c->ws + p.wcast, n, c->stream, dt); }));
         c->cast_valid = true;
         if (c->fp8) TRY(quantize_weights(c));
     }
@@ -752,7 +752,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.M = N; d.N = QKV; d.K = C;
             d.out = qkv; d.ldo = QKV;
             d.group_m = 8;  // bands of 8 tile-rows measured faster than bands of 4 for this shape
-            if (dt == Dt::BF16) {
+            if (mfma_dt(dt)) {
                 // RoPE + QK-norm in the epilogue: each wave of the 4 x 2 grid owns one head
                 d.epi = Epi::RopeNorm; d.loop = GemmLoop::Persist8Heads; d.tile = 0;
                 d.cosv = c->at<float>(p.cosv); d.sinv = c->at<float>(p.sinv);
@@ -778,7 +778,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             const double pairs = (double)c->B * c->H * c->T * (c->T + 1) / 2.0;
             // algorithmic bytes: read q, k, v; write y and the row log-sum-exp
             const double qb = (double)N * c->H * c->D * e, kb = (double)N * c->Hkv * c->D * e;
-            TRY(launch(c, dt == Dt::BF16 ? "attn_fwd_bf16" : "attn_fwd_f32", 4.0 * c->D * pairs,
+            TRY(launch(c, mfma_dt(dt) ? "attn_fwd_bf16" : "attn_fwd_f32", 4.0 * c->D * pairs,
                        2 * qb + 2 * kb + (double)N * c->H * 4, [&] { return launch_attn_fwd(ad, c->stream); }));
         }
         {
@@ -834,7 +834,7 @@ ncgpt_status ncgpt_loss(ncgpt_ctx* c, const int32_t* targets, float* loss) {
     c->state = 1;
     GemmDesc d = lm_head_desc(c);
     d.A = c->ws + p.xf; d.B = weight(c, -1, 1);
-    if (c->dt == Dt::BF16) {
+    if (mfma_dt(c->dt)) {
         // logits, their softmax statistics and the target logit in one pass; the logits are stored for the
         // backward only in the stored-logit mode
         d.epi = Epi::CeStats;
@@ -867,7 +867,7 @@ ncgpt_status ncgpt_loss(ncgpt_ctx* c, const int32_t* targets, float* loss) {
         return launch_loss_reduce(c->at<float>(p.loss_rows), targets, N, V, loss, c->at<float>(p.flag + 4), flag,
                                   c->stream);
     }));
-    c->loss_mode = c->dt == Dt::BF16 ? c->lm_mode : NCGPT_LOGITS_STORED;
+    c->loss_mode = mfma_dt(c->dt) ? c->lm_mode : NCGPT_LOGITS_STORED;
     c->loss_fp8 = c->fp8;
     c->state = 2;
     return NCGPT_OK;
@@ -887,8 +887,8 @@ ncgpt_status ncgpt_set_fp8(ncgpt_ctx* c, int on) {
 ncgpt_status ncgpt_set_lm_head_mode(ncgpt_ctx* c, int mode) {
     if (!c) return NCGPT_EINVAL;
     if (mode != NCGPT_LOGITS_STORED && mode != NCGPT_LOGITS_RECOMPUTED) return fail(c, NCGPT_EINVAL, "unknown mode");
-    if (mode == NCGPT_LOGITS_RECOMPUTED && c->dt != Dt::BF16)
-        return fail(c, NCGPT_EUNSUPPORTED, "the recomputed-logit mode is built for the bf16 compute dtype");
+    if (mode == NCGPT_LOGITS_RECOMPUTED && !mfma_dt(c->dt))
+        return fail(c, NCGPT_EUNSUPPORTED, "the recomputed-logit mode is built for the 16-bit compute dtypes");
     c->lm_mode = mode;
     return NCGPT_OK;
 }
@@ -906,8 +906,8 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
     uint8_t* logits = c->ws + p.logits;
     float* dxn = c->at<float>(p.dxn);
     float* dx = c->at<float>(p.dx);
-    uint8_t* dxg = dt == Dt::BF16 ? c->ws + p.dx_cd : c->ws + p.dx;  // GEMM operand copy of dx
-    void* dx_cd = dt == Dt::BF16 ? (void*)(c->ws + p.dx_cd) : nullptr;
+    uint8_t* dxg = mfma_dt(dt) ? c->ws + p.dx_cd : c->ws + p.dx;  // GEMM operand copy of dx
+    void* dx_cd = mfma_dt(dt) ? (void*)(c->ws + p.dx_cd) : nullptr;
 
     auto gslice = [&](int layer, int which) {
         size_t off;
@@ -944,7 +944,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
     // dWlm = dz^T xf: vocab x n_embd output over all tokens; 256 x 128 tiles, the four-wave persistent ring
     // measured fastest
     TRY(wgrad(c, "dWlm", logits, V, c->ws + p.xf, C, V, C, gslice(-1, 1), acc, 1));
-    const double nb = (double)N * C * (e + e + 4 + (dt == Dt::BF16 ? 2 : 0)) + N * 4.0;
+    const double nb = (double)N * C * (e + e + 4 + (mfma_dt(dt) ? 2 : 0)) + N * 4.0;
     TRY(launch(c, "rmsnorm_bwd", 0.0, nb, [&] {
         return launch_rmsnorm_bwd(dt, c->ws + p.xf, c->at<float>(p.rstdf), dxn, dx, dx_cd, N, C, 0, c->stream);
     }));
@@ -991,7 +991,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             ad.rstdq = c->at<float>(c->lay(l, p.l_rstdq)); ad.rstdk = c->at<float>(c->lay(l, p.l_rstdk));
             ad.cosv = c->at<float>(p.cosv); ad.sinv = c->at<float>(p.sinv);
             const double pairs = (double)c->B * c->H * c->T * (c->T + 1) / 2.0;
-            const bool bf = dt == Dt::BF16;
+            const bool bf = mfma_dt(dt);
             // algorithmic backward FLOPs: dV, dK and the dP product (6 D per pair) in the key-outer kernel,
             // dQ (2 D per pair) in the query-outer one; the recomputed S and dP products are not counted
             // algorithmic bytes: dQ reads q, k, v, y, dy and lse, writes dq and delta; dK/dV reads q, k, v,
@@ -1003,7 +1003,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             TRY(launch(c, bf ? "attn_bwd_dkdv_bf16" : "attn_bwd_dkdv_f32", 6.0 * c->D * pairs,
                        2 * qb + 4 * kb + 2 * rows, [&] { return launch_attn_bwd(ad, c->stream, 1); }));
         }
-        if (dt != Dt::BF16) {  // the bf16 attention backward applies it in its epilogues
+        if (!mfma_dt(dt)) {  // the 16-bit attention backward applies it in its epilogues
             TRY(launch(c, "rope_qknorm_bwd", 0.0, (double)N * (c->H + c->Hkv) * c->D * 3 * e, [&] {
                 return launch_rope_qknorm_bwd(dt, c->ws + p.dqkv, qkv, c->at<float>(c->lay(l, p.l_rstdq)),
                                               c->at<float>(c->lay(l, p.l_rstdk)), c->at<float>(p.cosv),
@@ -1029,7 +1029,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
     if (c->cfg.embed_norm) {
         // through the embedding norm: its input gradient into dxn (from dx in the compute dtype, as every norm's
         // backward takes it), then dx serves as the scratch
-        const void* dy = dt == Dt::BF16 ? (const void*)(c->ws + p.dx_cd) : (const void*)dx;
+        const void* dy = mfma_dt(dt) ? (const void*)(c->ws + p.dx_cd) : (const void*)dx;
         TRY(launch(c, "rmsnorm_bwd", 0.0, nb, [&] {
             return launch_rmsnorm_bwd(dt, c->ws + p.x0, c->at<float>(p.rstd0), dy, dxn, nullptr, N, C, 0, c->stream);
         }));
@@ -1196,14 +1196,14 @@ ncgpt_status ncgpt_decode_step(ncgpt_ctx* c, const int32_t* ids, const float* pa
         ~Restore() { c->params = saved; }
     } restore{c, c->params};
     c->params = params;
-    if (dt == Dt::BF16) {
+    if (mfma_dt(dt)) {
         if (recast) {
             const size_t n = (size_t)(c->P - c->VC);
             TRY(launch(c, "cast_bf16", 0.0, (double)n * 6,
-                       [&] { return launch_cast_bf16(params + c->VC, c->ws + p.wcast, n, c->stream); }));
+                       [&] { return launch_cast_bf16(params + c->VC, c->ws + p.wcast, n, c->stream, dt); }));
             c->cast_valid = true;
         } else if (!c->cast_valid) {
-            return fail(c, NCGPT_ESTATE, "no bf16 weight copy yet: pass recast = 1");
+            return fail(c, NCGPT_ESTATE, "no 16-bit weight copy yet: pass recast = 1");
         }
     }
     uint8_t* x = c->ws + p.d_x;
@@ -1292,6 +1292,13 @@ ncgpt_status ncgpt_check(ncgpt_ctx* c) {
         return fail(c, NCGPT_EDEVICE, m);
     }
     return NCGPT_OK;
+}
+
+ncgpt_status ncgpt_grads_finite(ncgpt_ctx* c, const float* x, size_t n, int32_t* ok) {
+    if (!c) return NCGPT_EINVAL;
+    TRY(check_bound(c));
+    if (!x || !ok) return fail(c, NCGPT_EINVAL, "null values or flag");
+    return launch(c, "grads_finite", 0.0, (double)n * 4, [&] { return launch_finite(x, n, ok, c->stream); });
 }
 
 ncgpt_status ncgpt_probe_numel(const ncgpt_ctx* c, int what, size_t* numel) {

@@ -15,7 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libncgpt.so")
 
 OK, EINVAL, EUNSUPPORTED, ENOMEM, EHIP, ESTATE, EDEVICE = 0, -1, -2, -3, -4, -5, -6
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 STATIC_SCRATCH_BYTES = 64 << 20   # NCGPT_STATIC_SCRATCH_BYTES
 LOGITS_STORED, LOGITS_RECOMPUTED = 0, 1
 _STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "ENOMEM", -4: "EHIP", -5: "ESTATE", -6: "EDEVICE"}
@@ -106,7 +106,8 @@ EXPORTS = ["ncgpt_num_params", "ncgpt_param_slice", "ncgpt_create", "ncgpt_works
            "ncgpt_bind_static", "ncgpt_set_lm_head_mode", "ncgpt_set_fp8", "ncgpt_optim_state_size",
            "ncgpt_optim_step",
            "ncgpt_kv_cache_bytes", "ncgpt_kv_fill", "ncgpt_decode_step",
-           "ncgpt_forward", "ncgpt_loss", "ncgpt_backward", "ncgpt_check", "ncgpt_probe_numel", "ncgpt_probe",
+           "ncgpt_forward", "ncgpt_loss", "ncgpt_backward", "ncgpt_check", "ncgpt_grads_finite",
+           "ncgpt_probe_numel", "ncgpt_probe",
            "ncgpt_timing_enable", "ncgpt_timing_reset", "ncgpt_timing_count", "ncgpt_timing_get",
            "ncgpt_last_error", "ncgpt_destroy"]
 
@@ -140,6 +141,7 @@ def lib():
         L.ncgpt_loss.argtypes = [vp, vp, vp]
         L.ncgpt_backward.argtypes = [vp, vp, ct.c_int, ct.c_float]
         L.ncgpt_check.argtypes = [vp]
+        L.ncgpt_grads_finite.argtypes = [vp, vp, ct.c_size_t, vp]
         L.ncgpt_probe_numel.argtypes = [vp, ct.c_int, P(ct.c_size_t)]
         L.ncgpt_probe.argtypes = [vp, ct.c_int, ct.c_int, vp]
         L.ncgpt_timing_enable.argtypes = [vp, ct.c_int]
@@ -186,14 +188,15 @@ def _ptr(t: torch.Tensor, dtype, numel, name):
 class Model:
     """One context of the library bound to a workspace and a stream.
 
-    dtype: "bf16" (bf16 compute, fp32 master weights) or "f32".
+    dtype: "bf16" (bf16 compute, fp32 master weights), "f16" (fp16 compute: scale the loss through
+    backward's grad_scale) or "f32".
     static_scratch: bind to the library's own per-GPU scratch array (ncgpt_bind_static) instead of a
     workspace allocated here; only workspaces up to STATIC_SCRATCH_BYTES fit."""
 
     def __init__(self, cfg: Config, dtype: str = "bf16", stream: torch.cuda.Stream = None,
                  static_scratch: bool = False):
         self.cfg = cfg
-        self.dtype = {"bf16": BF16, "f32": F32}[dtype]
+        self.dtype = {"bf16": BF16, "f16": F16, "f32": F32}[dtype]
         self._ctx = ct.c_void_p()
         st = lib().ncgpt_create(ct.byref(cfg._c()), self.dtype, ct.byref(self._ctx))
         if st != OK:
@@ -272,6 +275,14 @@ class Model:
     def set_lm_head_mode(self, mode: int):
         """LOGITS_STORED (default) or LOGITS_RECOMPUTED: where the backward's dz comes from."""
         self._check(lib().ncgpt_set_lm_head_mode(self._ctx, int(mode)))
+
+    def grads_finite(self, x: torch.Tensor, ok: torch.Tensor = None) -> torch.Tensor:
+        """Device int32 flag: 1 when every value of the fp32 tensor x is finite (ncgpt_grads_finite)."""
+        if ok is None:
+            ok = torch.empty(1, dtype=torch.int32, device="cuda")
+        px = _ptr(x, torch.float32, x.numel(), "x")
+        self._check(lib().ncgpt_grads_finite(self._ctx, px, x.numel(), ct.c_void_p(ok.data_ptr())))
+        return ok
 
     def set_fp8(self, on: bool):
         """Forward linears on E4M3 operands with per-row scales (bf16 contexts)."""

@@ -56,8 +56,12 @@ typedef enum {
     NCGPT_EDEVICE = -6       /* device-side error flag set (reported by ncgpt_check) */
 } ncgpt_status;
 
-/* Compute dtype: mirrors COMPUTE_DTYPE (fp32, or bf16 with fp32 master weights). */
-typedef enum { NCGPT_F32 = 0, NCGPT_BF16 = 1 } ncgpt_dtype;
+/* Compute dtype: mirrors COMPUTE_DTYPE (fp32, or bf16 with fp32 master weights; "nanochat：低成本跑通大模型训练全流程",
+ * precision paragraph).  NCGPT_F16 is the float16 setting for GPUs without bf16 ([poetries] tuning tips; the
+ * devpress.csdn.net guide's precision notes): the same scheme in fp16, whose small range makes gradients underflow
+ * unless the loss is scaled -- pass the scale as ncgpt_backward's grad_scale (the returned fp32 gradients carry
+ * it), check them with ncgpt_grads_finite and divide before the optimizer step. */
+typedef enum { NCGPT_F32 = 0, NCGPT_BF16 = 1, NCGPT_F16 = 2 } ncgpt_dtype;
 
 typedef struct {
     int32_t n_layer, n_embd, n_head, n_kv_head, head_dim, mlp_dim, vocab_size, batch, seq_len;
@@ -81,8 +85,8 @@ ncgpt_status ncgpt_param_slice(const ncgpt_config* cfg, int layer, int which, si
                                int64_t* cols);
 
 /* Create a context (host memory only; no device work).  EUNSUPPORTED unless head_dim is 64 or 128
- * (128 for NCGPT_BF16), n_head % n_kv_head == 0, n_embd, mlp_dim and vocab_size are multiples of 64,
- * vocab_size <= 65536, seq_len is a multiple of 128 for NCGPT_BF16 (of 64 for NCGPT_F32), and
+ * (128 for NCGPT_BF16 and NCGPT_F16), n_head % n_kv_head == 0, n_embd, mlp_dim and vocab_size are multiples
+ * of 64, vocab_size <= 65536, seq_len is a multiple of 128 for the 16-bit dtypes (of 64 for NCGPT_F32), and
  * batch*seq_len*vocab fits the workspace plan.  EINVAL for a null pointer or non-positive size, a negative
  * norm_eps, rope_base <= 0, a negative or non-finite logit_softcap, or embed_norm other than 0 or 1.
  * *out receives the context; free it with ncgpt_destroy. */
@@ -208,6 +212,11 @@ ncgpt_status ncgpt_decode_step(ncgpt_ctx* ctx, const int32_t* ids, const float* 
 /* Synchronise the bound stream and report device-side errors: EDEVICE if the flag is set (the flag is then
  * cleared), EHIP on an asynchronous HIP error, OK otherwise. */
 ncgpt_status ncgpt_check(ncgpt_ctx* ctx);
+
+/* Loss-scaling check (the GradScaler step of the fp16 setting): *ok (device int32) = 1 when all n values of x
+ * (device fp32, e.g. the gradients of a scaled backward) are finite, else 0.  Enqueued on the bound stream; no
+ * synchronisation.  EINVAL for null pointers. */
+ncgpt_status ncgpt_grads_finite(ncgpt_ctx* ctx, const float* x, size_t n, int32_t* ok);
 
 /* Saved-activation readout (for tests).  Copies one activation of the last forward, converted to fp32,
  * into dst (device, fp32, ncgpt_probe_numel elements) and synchronises the stream.  what:

@@ -84,6 +84,8 @@ def test_create_validates_shapes_and_plans_workspace():
     bad = [
         (dict(head_dim=96), ncgpt.F32, ncgpt.EUNSUPPORTED),
         (dict(head_dim=64), ncgpt.BF16, ncgpt.EUNSUPPORTED),      # bf16 attention is built for D = 128
+        (dict(head_dim=64), ncgpt.F16, ncgpt.EUNSUPPORTED),       # so is the fp16 one
+        (dict(seq_len=192), ncgpt.F16, ncgpt.EUNSUPPORTED),
         (dict(n_kv_head=3, n_head=2), ncgpt.BF16, ncgpt.EUNSUPPORTED),
         (dict(n_embd=200), ncgpt.BF16, ncgpt.EUNSUPPORTED),
         (dict(vocab_size=8200), ncgpt.BF16, ncgpt.EUNSUPPORTED),
@@ -103,6 +105,13 @@ def test_create_validates_shapes_and_plans_workspace():
         assert not ctx.value
     st, _ = create(base, 7)
     assert st == ncgpt.EINVAL
+    st, ctx = create(base, ncgpt.F16)                                  # fp16 plans like bf16
+    assert st == ncgpt.OK
+    m16 = ct.c_size_t()
+    assert L.ncgpt_workspace_size(ctx, ct.byref(m16)) == ncgpt.OK and m16.value > 0
+    assert L.ncgpt_set_fp8(ctx, 1) == ncgpt.EUNSUPPORTED                # fp8 linears are bf16-only
+    assert L.ncgpt_set_lm_head_mode(ctx, ncgpt.LOGITS_RECOMPUTED) == ncgpt.OK
+    L.ncgpt_destroy(ctx)
     # the block variants: the embedding norm's rstd adds to the plan
     st, ctx = create(ncgpt.Config(**dict(base.__dict__, logit_softcap=15.0, embed_norm=1)), ncgpt.BF16)
     assert st == ncgpt.OK
