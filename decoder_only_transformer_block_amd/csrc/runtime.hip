@@ -140,6 +140,23 @@ int pick_tile(int64_t M, int64_t N) {
     return best;
 }
 
+// Tile for the layer GEMMs: fewest rounds of the 256 CUs weighted by each tile's time, with the tiles' measured
+// relative rates -- a 256 x 128 tile loads 50 % more operand bytes per FLOP and runs at about 0.75 of the
+// 256 x 256 rate, a 128 x 128 one at about 0.5 -- so a half-empty last round of large tiles can still beat
+// full rounds of smaller ones.  Ties go to the larger tile.
+int pick_tile_rounds(int64_t M, int64_t N) {
+    static const int bm[3] = {256, 256, 128}, bn[3] = {256, 128, 128};
+    static const double cost[3] = {1.0, 0.5 / 0.75, 0.25 / 0.5};   // time of one tile, 256 x 256 = 1
+    int best = 0;
+    double best_t = 1e300;
+    for (int t = 0; t < 3; ++t) {
+        const int64_t tiles = ((M + bm[t] - 1) / bm[t]) * ((N + bn[t] - 1) / bn[t]);
+        const double time = (double)((tiles + kCUs - 1) / kCUs) * cost[t];
+        if (time < best_t - 1e-9) { best_t = time; best = t; }
+    }
+    return best;
+}
+
 // Weight gradient dW[M,N] = sum over K tokens.  The output alone has few
 // tiles (e.g. 9 for 768 x 768) while K is the whole batch of tokens, so K is
 // split until one round of workgroups covers the CUs; large outputs use the
@@ -406,7 +423,7 @@ const char* intern(const std::string& s) {
 // tag: the call site (qkv, lm_head, dWfc, ...), so every timing row is one shape
 ncgpt_status gemm(ncgpt_ctx* c, GemmDesc d, const char* tag, bool bf16_always = false) {
     d.dt = bf16_always ? Dt::BF16 : c->dt;
-    if (d.tile < 0) d.tile = pick_tile(d.M, d.N);
+    if (d.tile < 0) d.tile = pick_tile_rounds(d.M, d.N);
     const char* nm = intern(std::string(gemm_kernel_name(d)) + ":" + epi_name(d.epi) + ":" + tag);
     const double fl = 2.0 * d.M * d.N * d.K * d.batch;
     // algorithmic bytes: both operands once, the output (and what the epilogue reads) once
