@@ -178,9 +178,19 @@ WGrad pick_wgrad(Dt dt, int64_t M, int64_t N, int64_t K) {
             w.tile = pick_tile(M, N);
         }
         int64_t tiles = ((M + bm[w.tile] - 1) / bm[w.tile]) * ((N + bn[w.tile] - 1) / bn[w.tile]);
-        int64_t s = tiles >= kCUs ? 1 : kCUs / tiles;
-        s = std::min<int64_t>(s, K / 512);
-        w.splits = (int)std::max<int64_t>(1, s);
+        // splits s: rounds of the (split, tile) items times the time of a 1/s-deep tile, plus the fixed-order
+        // reduce of s fp32 partials; the rates are the measured ones of these kernels (about 4.7 TFLOP/s per CU
+        // for the split-K GEMMs, 6 TB/s for the reduce)
+        const double tile_s = 2.0 * bm[w.tile] * bn[w.tile] * (double)K / 4.7e12, out_bytes = 4.0 * M * N;
+        int64_t best = 1;
+        double best_t = 1e300;
+        const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(K / 512, 64));
+        for (int64_t s = 1; s <= smax; ++s) {
+            const double t = (double)((tiles * s + kCUs - 1) / kCUs) / (double)s * tile_s +
+                             (s > 1 ? (double)(s + 1) * out_bytes / 6.0e12 : 0.0);
+            if (t < best_t * 0.999) { best_t = t; best = s; }
+        }
+        w.splits = (int)best;
     }
     int64_t kb = K / 64;
     int64_t per = (kb + w.splits - 1) / w.splits;
