@@ -61,7 +61,7 @@ inline int attn_group(int npos, int per_cu) { return std::max(1, 32 * per_cu / n
 // high bits differ across 4 consecutive rows (transposed reads hit 4 distinct
 // 64-byte bank groups), so neither read conflicts on the 64-bank LDS.
 // rfrag / trfrag below are the definitional forms; the kernels read through the
-// closed-form offsets further down (rz, tz, frag_at, trfrag_at).
+// closed-form offsets further down (rz, tz, frag_at, trfrag_at; frag_lds, trfrag_lds).
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -113,6 +113,21 @@ __device__ __forceinline__ bf16x8 trfrag_at(const bf16* S, int t, int db) {
     s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 2048 + (t ^ (db << 6) ^ 32)));
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// LDS byte addresses as plain 32-bit integers: a tile base that is a multiple of 16 KB has zeros in every bit a
+// fragment offset XOR touches, so base + (off ^ x) = (base + off) ^ x and one register per lane and tile serves
+// every fragment of the tile, the other tiles at fixed distances riding in the instruction's offset field
+typedef __attribute__((address_space(3))) const char lds_cchar;
+typedef __attribute__((address_space(3))) const bf16x8 lds_frag;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(size_t)(lds_cchar*)p; }
+__device__ __forceinline__ bf16x8 frag_lds(uint32_t a) { return *(lds_frag*)(size_t)a; }
+__device__ __forceinline__ bf16x8 trfrag_lds(uint32_t lo, uint32_t hi) {
+    s16x4 l = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)lo);
+    s16x4 h = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)hi);
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 v = {l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
     return __builtin_bit_cast(bf16x8, v);
 }
 
@@ -534,13 +549,19 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
                    const float* __restrict__ sinv, int T, int H, int Hkv, int B)
 {
     constexpr int D = 128, KB = 128, NW = 8;
-    __shared__ __attribute__((aligned(1024))) bf16 sK[KB * 128];
-    __shared__ __attribute__((aligned(1024))) bf16 sV[KB * 128];
-    __shared__ __attribute__((aligned(1024))) bf16 sQ0[64 * 128];
-    __shared__ __attribute__((aligned(1024))) bf16 sO0[64 * 128];
-    __shared__ __attribute__((aligned(1024))) bf16 sQ1[64 * 128];
-    __shared__ __attribute__((aligned(1024))) bf16 sO1[64 * 128];
-    __shared__ __attribute__((aligned(16))) float sL0[64], sD0[64], sL1[64], sD1[64];
+    // one LDS block at fixed offsets: K 0, V 32 KB, then per stage Q and dO 16 KB apart (stage 0 at 64 KB,
+    // stage 1 at 96 KB), then the LSE / delta rows
+    __shared__ __attribute__((aligned(16384))) bf16 smem[4 * KB * 128 + 4 * 256];
+    bf16* const sK = smem;
+    bf16* const sV = smem + KB * 128;
+    bf16* const sQ0 = smem + 2 * KB * 128;
+    bf16* const sO0 = sQ0 + 64 * 128;
+    bf16* const sQ1 = sO0 + 64 * 128;
+    bf16* const sO1 = sQ1 + 64 * 128;
+    float* const sL0 = reinterpret_cast<float*>(smem + 4 * KB * 128);
+    float* const sD0 = sL0 + 64;
+    float* const sL1 = sD0 + 64;
+    float* const sD1 = sL1 + 64;
 
     const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -573,7 +594,7 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
     const int qt0 = k0 / 64, nqt = T / 64 - qt0;
     // fragment offsets: the wave's query half (32 qh + l32) in the Q / dO tiles, its keys
     // (32 kq + l32) in K / V, and the transposed reads of the query half
-    const int zq = rz(32 * qh + l32, hh), zk = rz(32 * kq + l32, hh), tq = tz(lane) + 32 * 256 * qh;
+    const int zq0 = rz(32 * qh + l32, hh), zk0 = rz(32 * kq + l32, hh), tq0 = tz(lane) + 32 * 256 * qh;
     const int total = r * nqt;
     const unsigned voq = dma_voff(QKV, lane, w), vod = dma_voff(HD, lane, w);
     // loads of tile it (query head g r + it / nqt, queries from (qt0 + it % nqt) 64) into one stage
@@ -597,15 +618,29 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
     auto compute = [&](int it, const bf16* Qs, const bf16* Os, const float* Ls, const float* Ds) {
         const int q0 = (qt0 + it % nqt) * 64 + 32 * qh;  // the wave's 32 queries
         if (!active || q0 + 31 < kw) return;  // wave-uniform: every query precedes every key of the wave
+        // fragment offsets re-formed per tile (one XOR per fragment) instead of held in registers
+        uint32_t aq = lds_addr(Qs) + zq0, ak = lds_addr(sK) + zk0, at = lds_addr(Qs) + tq0;
+        asm volatile("" : "+v"(aq), "+v"(ak), "+v"(at));   // formed per tile, not hoisted into registers
+        constexpr uint32_t OQ = 64 * 128 * 2, OV = KB * 128 * 2;   // dO past Q, V past K (bytes)
         const bool diag = q0 < kw + 31;
         f32x16 s, dp;
         zero16(s);
         zero16(dp);
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-            s = mfma16<HT>(frag_at(Qs, zq ^ (kk << 5)), frag_at(sK, zk ^ (kk << 5)), s);
-            dp = mfma16<HT>(frag_at(Os, zq ^ (kk << 5)), frag_at(sV, zk ^ (kk << 5)), dp);
+            const uint32_t xq = aq ^ (kk << 5), xk = ak ^ (kk << 5);
+            s = mfma16<HT>(frag_lds(xq), frag_lds(xk), s);
+            dp = mfma16<HT>(frag_lds(xq + OQ), frag_lds(xk + OV), dp);
         }
+        // issue order: the fragments of the first two k-steps, then per k-step its two MFMAs and the reads of
+        // the k-step two ahead
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int kk = 0; kk < 6; ++kk) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         // lane holds S[q = q0 + 8(e>>2) + 4hh + (e&3)][key = kw + l32] in s[e]; P = exp2(S c1 - lse2),
         // dS / scale = P (dP - delta) (dK is scaled at the end); the mask only on diagonal tiles
         auto softmax = [&](auto masked) {
@@ -634,10 +669,19 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
             const bf16x8 pf = pack8<HT>(s, 8 * j2), dsf = pack8<HT>(dp, 8 * j2);
 #pragma unroll
             for (int db = 0; db < 4; ++db) {
-                dv[db] = mfma16<HT>(trfrag_at(Os + 128 * 16 * j2, tq, db), pf, dv[db]);
-                dk[db] = mfma16<HT>(trfrag_at(Qs + 128 * 16 * j2, tq, db), dsf, dk[db]);
+                const uint32_t lo = (at ^ (db << 6)) + 4096 * j2, hi = (at ^ (db << 6) ^ 32) + 4096 * j2 + 2048;
+                dv[db] = mfma16<HT>(trfrag_lds(lo + OQ, hi + OQ), pf, dv[db]);
+                dk[db] = mfma16<HT>(trfrag_lds(lo, hi), dsf, dk[db]);
             }
         }
+        // issue order: transposed fragments (two reads each) two MFMAs ahead of their use
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int m = 0; m < 12; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     };
 
     // two tiles per iteration on the two static stages (so the compiler sees that
