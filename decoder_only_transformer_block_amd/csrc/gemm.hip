@@ -1281,7 +1281,16 @@ splitk_reduce_kernel(const float* __restrict__ part, int splits, size_t stride, 
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n4) return;
     float4 acc = accumulate ? reinterpret_cast<const float4*>(g)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sidx = 0; sidx < splits; ++sidx) {
+    // partials added in split order; four loads in flight at a time
+    int sidx = 0;
+    for (; sidx + 4 <= splits; sidx += 4) {
+        float4 p[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) p[u] = reinterpret_cast<const float4*>(part + (size_t)(sidx + u) * stride)[i];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) { acc.x += p[u].x; acc.y += p[u].y; acc.z += p[u].z; acc.w += p[u].w; }
+    }
+    for (; sidx < splits; ++sidx) {
         float4 p = reinterpret_cast<const float4*>(part + (size_t)sidx * stride)[i];
         acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
     }

@@ -643,32 +643,50 @@ hipError_t launch_loss_reduce(const float* loss_rows, const int32_t* targets, in
 // dz = grad_scale * inv_valid * (exp(z - lse) - onehot(target)) on valid rows,
 // 0 on ignored rows; written over the logits.  With a soft-cap the logits are
 // the capped ones and dz is taken back through the cap: times 1 - (z / c)^2.
-// One workgroup per row, 8 consecutive logits per thread and step.
+// One workgroup per row, 8 consecutive logits per thread and chunk; a thread loads four chunks before it
+// stores any, so each wave keeps 4 KB of reads in flight (one chunk at a time left HBM latency exposed).
+template <typename T>
+__device__ __forceinline__ void ce_bwd_chunk(float (&v)[8], int c, int t, float k, float l2, const SoftCap& cap) {
+    constexpr float kL2e = 1.4426950408889634f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float zc = v[e];
+        v[e] = k * (__builtin_amdgcn_exp2f(zc * kL2e - l2) - (c + e == t ? 1.0f : 0.0f));
+        if (cap.c > 0.0f) v[e] = v[e] * softcap_grad(zc, cap);
+    }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256)
 ce_bwd_kernel(T* __restrict__ z, const float* __restrict__ lse, const int32_t* __restrict__ targets,
               const float* __restrict__ inv_valid, float grad_scale, SoftCap cap, int V)
 {
     constexpr float kL2e = 1.4426950408889634f;
+    constexpr int U = 4, STEP = 2048;          // 256 threads x 8 logits
     const int n = blockIdx.x;
     const int t = targets[n];
     T* zr = z + (size_t)n * V;
-    const bool valid = t >= 0 && t < V;
-    const float k = valid ? grad_scale * (*inv_valid) : 0.0f, l2 = valid ? lse[n] * kL2e : 0.0f;
-    for (int c = threadIdx.x * 8; c < V; c += 2048) {
-        float v[8];
-        if (valid) {
-            load8(zr + c, v);
+    if (!(t >= 0 && t < V)) {                  // ignored row: zero gradient
+        const float zero[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        for (int c = threadIdx.x * 8; c < V; c += STEP) store8(zr + c, zero);
+        return;
+    }
+    const float k = grad_scale * (*inv_valid), l2 = lse[n] * kL2e;
+    const int full = V / (U * STEP) * (U * STEP);   // columns in whole groups of U chunks
+    for (int c0 = threadIdx.x * 8; c0 < full; c0 += U * STEP) {
+        float v[U][8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float zc = v[e];
-                v[e] = k * (__builtin_amdgcn_exp2f(zc * kL2e - l2) - (c + e == t ? 1.0f : 0.0f));
-                if (cap.c > 0.0f) v[e] = v[e] * softcap_grad(zc, cap);
-            }
-        } else {
+        for (int u = 0; u < U; ++u) load8(zr + c0 + u * STEP, v[u]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+        for (int u = 0; u < U; ++u) {
+            ce_bwd_chunk<T>(v[u], c0 + u * STEP, t, k, l2, cap);
+            store8(zr + c0 + u * STEP, v[u]);
         }
+    }
+    for (int c = full + threadIdx.x * 8; c < V; c += STEP) {
+        float v[8];
+        load8(zr + c, v);
+        ce_bwd_chunk<T>(v, c, t, k, l2, cap);
         store8(zr + c, v);
     }
 }

@@ -837,6 +837,7 @@ ncgpt_status ncgpt_forward(ncgpt_ctx* c, const int32_t* ids, const float* params
             d.M = N; d.N = C; d.K = F;
             d.epi = Epi::ResidualCd; d.out = c->ws + p.x; d.in = c->ws + p.x; d.ldo = C;
             d.loop = GemmLoop::Persist8;  // measured faster than the non-persistent ring despite a small spill
+            d.group_m = 2;                // the n_embd-wide outputs: bands of 2 tile-rows measured fastest
             if (c->fp8) {
                 TRY(quantize_act(c, act, F));
                 use_fp8(c, d, l, 5);
@@ -966,6 +967,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
         d.M = N; d.N = C; d.K = V;
         d.epi = Epi::StoreCd; d.out = dxn; d.ldo = C;  // compute dtype
         d.loop = GemmLoop::Ring8;  // input gradients (NN): the non-persistent eight-wave ring measured fastest
+        d.group_m = 2;             // the n_embd-wide outputs: bands of 2 tile-rows measured fastest
         TRY(gemm(c, d, "dxf"));
     }
     // dWlm = dz^T xf: vocab x n_embd output over all tokens; 256 x 128 tiles, the four-wave persistent ring
@@ -996,6 +998,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             d.M = N; d.N = C; d.K = F;
             d.epi = Epi::StoreCd; d.out = dxn; d.ldo = C;  // compute dtype
             d.loop = GemmLoop::Ring8;  // input gradients (NN): the non-persistent eight-wave ring measured fastest
+            d.group_m = 2;             // the n_embd-wide outputs: bands of 2 tile-rows measured fastest
             TRY(gemm(c, d, "dxn2"));
         }
         TRY(wgrad(c, "dWfc", c->ws + p.dh, F, xn2, C, F, C, gslice(l, 4), acc));  // dWfc = dh^T xn2
@@ -1044,6 +1047,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             d.M = N; d.N = C; d.K = QKV;
             d.epi = Epi::StoreCd; d.out = dxn; d.ldo = C;  // compute dtype
             d.loop = GemmLoop::Ring8;  // input gradients (NN): the non-persistent eight-wave ring measured fastest
+            d.group_m = 2;             // the n_embd-wide outputs: bands of 2 tile-rows measured fastest
             TRY(gemm(c, d, "dxn1"));
         }
         TRY(wgrad(c, "dWqkv", c->ws + p.dqkv, QKV, xn1, C, QKV, C, gslice(l, 0), acc));  // dWqkv = dqkv^T xn1
