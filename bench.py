@@ -45,15 +45,15 @@ def mfu(w, seconds_per_step):
 
 
 def cpu_baseline(w):
-    """The CPU oracle (fp64, OpenMP) on one sequence of the workload's length
-    (same model, same sequence length, batch 1): forward + loss + backward,
-    timed on this host."""
+    """The CPU oracle (fp64, OpenMP) timed on this host, forward + loss +
+    backward: the whole step for workloads of at most 4096 tokens, otherwise
+    one sequence of the workload's length (same model, batch 1)."""
     import oracle as orc
     from decoder_only_transformer_block_amd.inputs import init_params, split_stream, token_stream
-    ws = w.with_(batch=1)
+    ws = w if w.n_tokens <= 4096 else w.with_(batch=1)
     cfg = orc.OracleConfig(ws.n_layer, ws.n_embd, ws.n_head, ws.n_kv_head, ws.head_dim, ws.mlp_dim, ws.vocab_size,
                            ws.batch, ws.seq_len)
-    ids, tg = split_stream(token_stream(ws.vocab_size, 1, ws.seq_len, ws.tokens, 1))
+    ids, tg = split_stream(token_stream(ws.vocab_size, ws.batch, ws.seq_len, ws.tokens, 1))
     params = init_params(orc.num_params(cfg), seed=0)
     orc.lib()
     t0 = time.perf_counter()
@@ -61,9 +61,70 @@ def cpu_baseline(w):
     dt = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     cores = min(cores, len(os.sched_getaffinity(0)))
-    return {"value": round(ws.seq_len / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{w.name} model, 1 sequence x {ws.seq_len} tokens (1/{w.batch} of a step), "
-                      f"forward+loss+backward in fp64, {dt:.1f} s"}
+    what = (f"the whole step, {ws.batch} x {ws.seq_len} tokens" if ws.batch == w.batch else
+            f"1 sequence x {ws.seq_len} tokens (1/{w.batch} of a step)")
+    return {"value": round(ws.n_tokens / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{w.name} model, {what}, forward+loss+backward in fp64, {dt:.2f} s"}
+
+
+class ClockSampler:
+    """Mean shader clock and board power over a timed region, read from the GPU's sysfs entries every 20 ms
+    by a host thread: the current sclk is the starred line of pp_dpm_sclk, the power hwmon's power1_input
+    (microwatts).  Reports None where the entries are absent."""
+
+    def __init__(self):
+        import glob
+        self.sclk = self.power = None
+        for d in sorted(glob.glob("/sys/class/drm/card*/device")):
+            try:
+                with open(os.path.join(d, "vendor")) as f:
+                    if f.read().strip() != "0x1002":
+                        continue
+            except OSError:
+                continue
+            if os.path.exists(os.path.join(d, "pp_dpm_sclk")):
+                self.sclk = os.path.join(d, "pp_dpm_sclk")
+                pw = sorted(glob.glob(os.path.join(d, "hwmon", "hwmon*", "power1_input")))
+                self.power = pw[0] if pw else None
+                break
+        self.mhz, self.watts = [], []
+
+    def _read(self):
+        try:
+            with open(self.sclk) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        self.mhz.append(float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0]))
+            if self.power:
+                with open(self.power) as f:
+                    self.watts.append(float(f.read()) / 1e6)
+        except (OSError, ValueError, IndexError):
+            pass
+
+    def __enter__(self):
+        import threading
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.wait(0.02):
+                self._read()
+        self._t = threading.Thread(target=run, daemon=True)
+        if self.sclk:
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.sclk:
+            self._t.join()
+
+    def summary(self, step_mfu):
+        if not self.mhz:
+            return None
+        mhz = sum(self.mhz) / len(self.mhz)
+        return {"sclk_mhz_mean": round(mhz, 1), "power_w_mean": round(sum(self.watts) / len(self.watts), 1)
+                if self.watts else None, "samples": len(self.mhz),
+                "mfu_at_observed_clock": round(step_mfu * 2400.0 / mhz, 4) if mhz > 0 else None}
 
 
 def copy_calibration(dev):
@@ -160,11 +221,13 @@ def main():
         step()
     m.check()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    clock = ClockSampler()
+    with clock:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     m.check()
     ms = (t1 - t0) * 1e3 / args.steps
     tok_s = w.n_tokens / (ms / 1e3)
@@ -287,6 +350,7 @@ def main():
         "dtype": ("fp8e4m3+bf16" if args.fp8 else "bf16") if dtype == "bf16" else dtype,
         "data": "synthetic",
         "mfu": round(step_mfu, 4),
+        "gpu_clock": clock.summary(step_mfu),
         "flops_per_token": fpt,
         "config": {"workload": f"{w.name}: depth {w.n_layer}, n_embd {w.n_embd}, {w.n_head}x{w.head_dim} heads, "
                                f"{w.n_kv_head} kv heads, MLP {w.mlp_dim}, vocab {w.vocab_size}, "
