@@ -72,10 +72,10 @@ class ClockSampler:
     by a host thread: the current sclk is the starred line of pp_dpm_sclk, the power hwmon's power1_input
     (microwatts).  Reports None where the entries are absent."""
 
-    def __init__(self):
+    def __init__(self, root="/sys/class/drm"):
         import glob
         self.sclk = self.power = None
-        for d in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for d in sorted(glob.glob(os.path.join(root, "card*", "device"))):
             try:
                 with open(os.path.join(d, "vendor")) as f:
                     if f.read().strip() != "0x1002":

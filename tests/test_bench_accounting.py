@@ -60,3 +60,26 @@ def test_mfu_definition():
     step = bench.flops_per_token(w) * w.n_tokens
     assert step / 1e12 == pytest.approx(50.72, abs=0.01)
     assert bench.mfu(w, 50.4e-3) == pytest.approx(0.40, abs=0.001)
+
+
+def test_clock_sampler_reads_the_starred_sclk_and_power(tmp_path):
+    """The sampler takes the starred line of pp_dpm_sclk (a fixed level or the intermediate 'S:' state) and
+    power1_input in microwatts, skips cards of other vendors, and rebases MFU to the observed clock."""
+    import time
+    other = tmp_path / "card0" / "device"
+    other.mkdir(parents=True)
+    (other / "vendor").write_text("0x10de\n")
+    (other / "pp_dpm_sclk").write_text("0: 100Mhz *\n")
+    dev = tmp_path / "card1" / "device"
+    (dev / "hwmon" / "hwmon3").mkdir(parents=True)
+    (dev / "vendor").write_text("0x1002\n")
+    (dev / "pp_dpm_sclk").write_text("S: 2000Mhz *\n0: 500Mhz\n1: 2400Mhz\n")
+    (dev / "hwmon" / "hwmon3" / "power1_input").write_text("1250000000\n")
+    c = bench.ClockSampler(str(tmp_path))
+    with c:
+        time.sleep(0.15)
+    out = c.summary(0.3)
+    assert out["samples"] >= 2
+    assert out["sclk_mhz_mean"] == 2000.0 and out["power_w_mean"] == 1250.0
+    assert out["mfu_at_observed_clock"] == round(0.3 * 2400 / 2000, 4)
+    assert bench.ClockSampler(str(tmp_path / "none")).summary(0.3) is None
