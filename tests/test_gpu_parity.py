@@ -77,6 +77,30 @@ def test_step_matches_oracle(key, w, dtype):
     assert not bad, bad
 
 
+SEED_CASES = [(w, dtype, tok_seed, param_seed)
+              for w, dtype in ((WORKLOADS["tiny"], "f32"), (WORKLOADS["small"], "bf16"), (GQA3, "bf16"))
+              for tok_seed, param_seed in ((0, 1), (2, 2))]
+
+
+@pytest.mark.parametrize("w,dtype,tok_seed,param_seed", SEED_CASES,
+                         ids=[f"{c[0].name}-tokens{c[2]}-params{c[3]}" for c in SEED_CASES])
+def test_step_matches_oracle_other_seeds(w, dtype, tok_seed, param_seed):
+    """The same step on other token streams and weights (the cases above use tokens 1, weights 0): loss and
+    every tensor's gradient to the same bars."""
+    ids, tg, params = make_inputs(w, seed=tok_seed, param_seed=param_seed)
+    say(f"[oracle] grad {w.name} seeds {tok_seed}/{param_seed}")
+    lo, go = orc.grad(ocfg(w), ids, tg, params)
+    s = GpuStep(w, dtype, ids, params)
+    loss, st = s.run(tg)
+    assert st == ncgpt.OK
+    rel = abs(loss - lo) / abs(lo)
+    say(f"  loss gpu {loss:.7f} oracle {lo:.7f} rel {rel:.2e}")
+    assert rel <= (1e-5 if dtype == "f32" else 1e-2)
+    report = []
+    bad = compare_grads(w, s.grads_np(), go, dtype, report)
+    assert not bad, bad
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_ignored_targets_and_error_flags(dtype):
     """Ignored (negative) targets contribute nothing and are excluded from the mean; a whole
