@@ -140,17 +140,17 @@ int pick_tile(int64_t M, int64_t N) {
     return best;
 }
 
-// Tile for the layer GEMMs: fewest rounds of the 256 CUs weighted by each tile's time, with the tiles' measured
-// relative rates -- a 256 x 128 tile loads 50 % more operand bytes per FLOP and runs at about 0.75 of the
-// 256 x 256 rate, a 128 x 128 one at about 0.5 -- so a half-empty last round of large tiles can still beat
-// full rounds of smaller ones.  Ties go to the larger tile.
-int pick_tile_rounds(int64_t M, int64_t N) {
+// Tile for the ring and persistent GEMMs: fewest rounds of the 256 CUs weighted by each tile's time, with the
+// tiles' measured relative rates -- a 256 x 128 tile loads 50 % more operand bytes per FLOP and runs at about
+// 0.75 of the 256 x 256 rate, a 128 x 128 one at about 0.5 -- so a half-empty last round of large tiles can still
+// beat full rounds of smaller ones.  Ties go to the larger tile.  A batched product counts the tiles of all items.
+int pick_tile_rounds(int64_t M, int64_t N, int64_t batch) {
     static const int bm[3] = {256, 256, 128}, bn[3] = {256, 128, 128};
     static const double cost[3] = {1.0, 0.5 / 0.75, 0.25 / 0.5};   // time of one tile, 256 x 256 = 1
     int best = 0;
     double best_t = 1e300;
     for (int t = 0; t < 3; ++t) {
-        const int64_t tiles = ((M + bm[t] - 1) / bm[t]) * ((N + bn[t] - 1) / bn[t]);
+        const int64_t tiles = ((M + bm[t] - 1) / bm[t]) * ((N + bn[t] - 1) / bn[t]) * batch;
         const double time = (double)((tiles + kCUs - 1) / kCUs) * cost[t];
         if (time < best_t - 1e-9) { best_t = time; best = t; }
     }
@@ -433,7 +433,7 @@ const char* intern(const std::string& s) {
 // tag: the call site (qkv, lm_head, dWfc, ...), so every timing row is one shape
 ncgpt_status gemm(ncgpt_ctx* c, GemmDesc d, const char* tag, bool bf16_always = false) {
     d.dt = bf16_always ? Dt::BF16 : c->dt;
-    if (d.tile < 0) d.tile = pick_tile_rounds(d.M, d.N);
+    if (d.tile < 0) d.tile = pick_tile_rounds(d.M, d.N, d.batch);
     const char* nm = intern(std::string(gemm_kernel_name(d)) + ":" + epi_name(d.epi) + ":" + tag);
     const double fl = 2.0 * d.M * d.N * d.K * d.batch;
     // algorithmic bytes: both operands once, the output (and what the epilogue reads) once
@@ -1132,7 +1132,7 @@ ncgpt_status ncgpt_optim_step(ncgpt_ctx* c, float* params, const float* grads, f
                 d.a_kcontig = !tall; d.b_kcontig = !tall;
                 d.M = m; d.N = m; d.K = tall ? R : Cc;
                 d.epi = Epi::StoreCd; d.out = Am; d.ldo = m;
-                d.loop = GemmLoop::Ring8; d.tile = 2;
+                d.loop = GemmLoop::Ring8;
                 d.batch = batch; d.sA = sx; d.sB = sx; d.sOut = sm;
                 TRY(gemm(c, d, "ns_gram", true));
             }
@@ -1141,7 +1141,7 @@ ncgpt_status ncgpt_optim_step(ncgpt_ctx* c, float* params, const float* grads, f
                 d.A = Am; d.B = Am; d.lda = m; d.ldb = m; d.b_kcontig = false;
                 d.M = m; d.N = m; d.K = m;
                 d.epi = Epi::Axpby; d.out = Bm; d.in = Am; d.ldo = m; d.alpha = oc->ns_b; d.beta = oc->ns_c;
-                d.loop = GemmLoop::Ring8; d.tile = 2;
+                d.loop = GemmLoop::Ring8;
                 d.batch = batch; d.sA = sm; d.sB = sm; d.sOut = sm; d.sIn = sm;
                 TRY(gemm(c, d, "ns_poly", true));
             }
@@ -1152,7 +1152,7 @@ ncgpt_status ncgpt_optim_step(ncgpt_ctx* c, float* params, const float* grads, f
                 d.b_kcontig = false;
                 d.M = R; d.N = Cc;
                 d.epi = Epi::Axpby; d.out = xn; d.in = x; d.ldo = Cc; d.alpha = oc->ns_a; d.beta = 1.0f;
-                d.loop = GemmLoop::Ring8; d.tile = pick_tile((int64_t)R * batch, Cc);
+                d.loop = GemmLoop::Ring8;
                 d.batch = batch; d.sOut = sx; d.sIn = sx;
                 TRY(gemm(c, d, "ns_update", true));
             }
