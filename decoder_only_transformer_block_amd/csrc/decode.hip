@@ -138,7 +138,21 @@ decode_combine_kernel(const float* __restrict__ part, T* __restrict__ y, int H, 
     const int bh = blockIdx.x, d = threadIdx.x;
     const float* pp = part + (size_t)bh * nchunk * (D + 1);
     float o = 0.0f, l = 0.0f;
-    for (int c = 0; c < nchunk; ++c) {
+    int c = 0;
+    for (; c + 4 <= nchunk; c += 4) {   // chunk order, four chunks' loads in flight
+        float po[4], pl[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            po[u] = pp[(c + u) * (D + 1) + d];
+            pl[u] = pp[(c + u) * (D + 1) + D];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            o += po[u];
+            l += pl[u];
+        }
+    }
+    for (; c < nchunk; ++c) {
         o += pp[c * (D + 1) + d];
         l += pp[c * (D + 1) + D];
     }
@@ -196,7 +210,19 @@ decode_finish_kernel(const float* __restrict__ part, int splits, size_t stride, 
     const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= (size_t)rows * N) return;
     float v[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < splits; ++sp) {
+    // partials added in split order, four loads in flight at a time (one at a time left the chain of load
+    // latencies exposed: these kernels move little data)
+    int sp = 0;
+    for (; sp + 4 <= splits; sp += 4) {
+        float p[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Vec4<float>::load(part + (sp + u) * stride + i, p[u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += p[u][e];
+    }
+    for (; sp < splits; ++sp) {
         float p[4];
         Vec4<float>::load(part + sp * stride + i, p);
 #pragma unroll
