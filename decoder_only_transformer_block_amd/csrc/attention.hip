@@ -131,6 +131,21 @@ __device__ __forceinline__ bf16x8 trfrag_lds(uint32_t lo, uint32_t hi) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// Row and transposed fragments from byte offsets into tile S.  The reads keep S as their object, so where S is
+// an LDS array of its own the compiler knows they do not touch direct-to-LDS loads in flight into other
+// arrays, and issues them without waiting for those loads (a read it cannot place is made to wait for all).
+__device__ __forceinline__ bf16x8 frag_in(const bf16* S, uint32_t off) {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(S) + off);
+}
+__device__ __forceinline__ bf16x8 trfrag_in(const bf16* S, uint32_t lo, uint32_t hi) {
+    const char* p = reinterpret_cast<const char*>(S);
+    s16x4 l = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + lo));
+    s16x4 h = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + hi));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 v = {l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
 // 8 accumulator values rounded to the 16-bit operand type H, as an MFMA fragment (bit pattern)
 template <typename HT>
 __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
@@ -549,19 +564,24 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
                    const float* __restrict__ sinv, int T, int H, int Hkv, int B)
 {
     constexpr int D = 128, KB = 128, NW = 8;
-    // one LDS block at fixed offsets: K 0, V 32 KB, then per stage Q and dO 16 KB apart (stage 0 at 64 KB,
-    // stage 1 at 96 KB), then the LSE / delta rows
-    __shared__ __attribute__((aligned(16384))) bf16 smem[4 * KB * 128 + 4 * 256];
-    bf16* const sK = smem;
-    bf16* const sV = smem + KB * 128;
-    bf16* const sQ0 = smem + 2 * KB * 128;
-    bf16* const sO0 = sQ0 + 64 * 128;
-    bf16* const sQ1 = sO0 + 64 * 128;
-    bf16* const sO1 = sQ1 + 64 * 128;
-    float* const sL0 = reinterpret_cast<float*>(smem + 4 * KB * 128);
-    float* const sD0 = sL0 + 64;
-    float* const sL1 = sD0 + 64;
-    float* const sD1 = sL1 + 64;
+    // K with V 32 KB past it; per stage Q with dO 16 KB past it, and the LSE / delta rows.  Each stage is an LDS
+    // array of its own: the compiler then knows that the transposed reads of one stage do not touch the loads in
+    // flight into the other, and issues them without waiting for those loads.
+    __shared__ __attribute__((aligned(16384))) bf16 sKV[2 * KB * 128];
+    __shared__ __attribute__((aligned(16384))) bf16 sS0[2 * 64 * 128];
+    __shared__ __attribute__((aligned(16384))) bf16 sS1[2 * 64 * 128];
+    __shared__ __attribute__((aligned(256))) float sLD0[128];
+    __shared__ __attribute__((aligned(256))) float sLD1[128];
+    bf16* const sK = sKV;
+    bf16* const sV = sKV + KB * 128;
+    bf16* const sQ0 = sS0;
+    bf16* const sO0 = sS0 + 64 * 128;
+    bf16* const sQ1 = sS1;
+    bf16* const sO1 = sS1 + 64 * 128;
+    float* const sL0 = sLD0;
+    float* const sD0 = sLD0 + 64;
+    float* const sL1 = sLD1;
+    float* const sD1 = sLD1 + 64;
 
     const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -619,9 +639,8 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
         const int q0 = (qt0 + it % nqt) * 64 + 32 * qh;  // the wave's 32 queries
         if (!active || q0 + 31 < kw) return;  // wave-uniform: every query precedes every key of the wave
         // fragment offsets re-formed per tile (one XOR per fragment) instead of held in registers
-        uint32_t aq = lds_addr(Qs) + zq0, ak = lds_addr(sK) + zk0, at = lds_addr(Qs) + tq0;
+        uint32_t aq = zq0, ak = zk0, at = tq0;
         asm volatile("" : "+v"(aq), "+v"(ak), "+v"(at));   // formed per tile, not hoisted into registers
-        constexpr uint32_t OQ = 64 * 128 * 2, OV = KB * 128 * 2;   // dO past Q, V past K (bytes)
         const bool diag = q0 < kw + 31;
         f32x16 s, dp;
         zero16(s);
@@ -629,8 +648,8 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
             const uint32_t xq = aq ^ (kk << 5), xk = ak ^ (kk << 5);
-            s = mfma16<HT>(frag_lds(xq), frag_lds(xk), s);
-            dp = mfma16<HT>(frag_lds(xq + OQ), frag_lds(xk + OV), dp);
+            s = mfma16<HT>(frag_in(Qs, xq), frag_in(sK, xk), s);
+            dp = mfma16<HT>(frag_in(Os, xq), frag_in(sV, xk), dp);
         }
         // issue order: the fragments of the first two k-steps, then per k-step its two MFMAs and the reads of
         // the k-step two ahead
@@ -647,9 +666,9 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
 #pragma unroll
             for (int gg = 0; gg < 4; ++gg) {
                 const int ql = 32 * qh + 8 * gg + 4 * hh;
-                const float4 l4 = *reinterpret_cast<const float4*>(Ls + ql);
-                const float4 d4 = *reinterpret_cast<const float4*>(Ds + ql);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + ql);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + ql);
+                const float lv[4] = {l4[0], l4[1], l4[2], l4[3]}, dv4[4] = {d4[0], d4[1], d4[2], d4[3]};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int idx = 4 * gg + e;
@@ -670,8 +689,8 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
 #pragma unroll
             for (int db = 0; db < 4; ++db) {
                 const uint32_t lo = (at ^ (db << 6)) + 4096 * j2, hi = (at ^ (db << 6) ^ 32) + 4096 * j2 + 2048;
-                dv[db] = mfma16<HT>(trfrag_lds(lo + OQ, hi + OQ), pf, dv[db]);
-                dk[db] = mfma16<HT>(trfrag_lds(lo, hi), dsf, dk[db]);
+                dv[db] = mfma16<HT>(trfrag_in(Os, lo, hi), pf, dv[db]);
+                dk[db] = mfma16<HT>(trfrag_in(Qs, lo, hi), dsf, dk[db]);
             }
         }
         // issue order: transposed fragments (two reads each) two MFMAs ahead of their use
