@@ -616,6 +616,7 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
     // (32 kq + l32) in K / V, and the transposed reads of the query half
     const int zq0 = rz(32 * qh + l32, hh), zk0 = rz(32 * kq + l32, hh), tq0 = tz(lane) + 32 * 256 * qh;
     const int total = r * nqt;
+    bf16x8 kf[8];                                 // the wave's K fragments, read once (after the first publish)
     const unsigned voq = dma_voff(QKV, lane, w), vod = dma_voff(HD, lane, w);
     // loads of tile it (query head g r + it / nqt, queries from (qt0 + it % nqt) 64) into one stage
     auto issue = [&](int it, bf16* Qs, bf16* Os, float* Ls, float* Ds) {
@@ -648,16 +649,16 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
             const uint32_t xq = aq ^ (kk << 5), xk = ak ^ (kk << 5);
-            s = mfma16<HT>(frag_in(Qs, xq), frag_in(sK, xk), s);
+            s = mfma16<HT>(frag_in(Qs, xq), kf[kk], s);
             dp = mfma16<HT>(frag_in(Os, xq), frag_in(sV, xk), dp);
         }
         // issue order: the fragments of the first two k-steps, then per k-step its two MFMAs and the reads of
-        // the k-step two ahead
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        // the k-step two ahead (Q, dO and V: K is in registers)
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
         for (int kk = 0; kk < 6; ++kk) {
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         // lane holds S[q = q0 + 8(e>>2) + 4hh + (e&3)][key = kw + l32] in s[e]; P = exp2(S c1 - lse2),
@@ -707,6 +708,8 @@ attn_bwd_dkdv_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ dy, co
     // reads of one stage never wait on loads into the other)
     issue(0, sQ0, sO0, sL0, sD0);
     publish();
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) kf[kk] = frag_in(sK, zk0 ^ (kk << 5));
     for (int it = 0; it < total; it += 2) {
         if (it + 1 < total) issue(it + 1, sQ1, sO1, sL1, sD1);
         compute(it, sQ0, sO0, sL0, sD0);

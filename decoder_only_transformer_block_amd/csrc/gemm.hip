@@ -84,6 +84,7 @@ template <typename T> struct EResidual {
 // out = cd(alpha in + beta v): the Newton-Schulz steps B = b A + c A A and X = a X + B X (bf16)
 struct EAxpby {
     static constexpr bool kWide = true, kLoads = true;
+    typedef bf16x8 vec8;
     bf16* out; const bf16* in; int ldo;
     float alpha, beta;
     int64_t sOut, sIn;  // batch strides (elements)
@@ -208,6 +209,48 @@ __device__ __forceinline__ void wide8(const f32x16 (&acc)[FM][FN], int i, int j,
 // 8g + 4(l / 32) + 0..3).  m0, n0: the wave tile's first row and column.
 // RG: row blocks whose epilogue inputs are fetched together (FM by default; the
 // persistent kernels, which keep more registers live, fetch half as many at once).
+// Epilogues that read a tensor 8 values at a time (fetch8 / put8)
+template <class E, class = void> struct WideLoads : std::false_type {};
+template <class E> struct WideLoads<E, std::void_t<decltype(E::kLoads)>> : std::bool_constant<E::kWide && E::kLoads> {};
+// The type of one fetch8 of a loads-epilogue (int where there is none)
+template <class E, bool P> struct EpiIn { typedef int type; };
+template <class E> struct EpiIn<E, true> { typedef typename E::vec8 type; };
+
+// The inputs of a loads-epilogue for RG row blocks from row block i0: in[ii][j][p] holds the 8 values at the
+// columns the lane stores for row block i0 + ii (see wide8).
+template <int RG, int FN, class E>
+__device__ __forceinline__ void fetch_rows(typename E::vec8 (&in)[RG][FN][2], int i0,
+                                           int m0, int n0, int M, int N, int lane, const E& epi) {
+    const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int ii = 0; ii < RG; ++ii)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int m = m0 + 32 * (i0 + ii) + l32, n = n0 + 32 * j + 16 * p + 8 * h;
+                if (m < M && n < N) in[ii][j][p] = epi.fetch8(m, n);
+            }
+}
+// The loads-epilogue of RG row blocks from i0, given their fetched inputs.
+template <int FM, int FN, int RG, class E>
+__device__ __forceinline__ void apply_rows(const f32x16 (&acc)[FM][FN], const typename E::vec8 (&in)[RG][FN][2],
+                                           int i0, int m0, int n0, int split, int M, int N, int lane, const E& epi) {
+    const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int ii = 0; ii < RG; ++ii)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int i = i0 + ii;
+                float v[8];
+                wide8<FM, FN>(acc, i, j, p, v);
+                const int m = m0 + 32 * i + l32, n = n0 + 32 * j + 16 * p + 8 * h;
+                if (m < M && n < N) epi.put8(m, n, split, v, in[ii][j][p]);
+            }
+}
+
 template <int FM, int FN, class E, int RG = FM>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], int m0, int n0, int split, int M, int N,
                                            int lane, const E& epi) {
@@ -218,35 +261,9 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], int m0, 
         static_assert(FM % RG == 0, "row groups must divide the row blocks");
 #pragma unroll
         for (int i0 = 0; i0 < FM; i0 += RG) {
-            decltype(epi.fetch8(0, 0)) in[RG][FN][2];
-#pragma unroll
-            for (int ii = 0; ii < RG; ++ii)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-#pragma unroll
-                    for (int p = 0; p < 2; ++p) {
-                        const int m = m0 + 32 * (i0 + ii) + l32, n = n0 + 32 * j + 16 * p + 8 * h;
-                        if (m < M && n < N) in[ii][j][p] = epi.fetch8(m, n);
-                    }
-#pragma unroll
-            for (int ii = 0; ii < RG; ++ii)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-#pragma unroll
-                    for (int p = 0; p < 2; ++p) {
-                        const int i = i0 + ii;
-                        float v[8];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][j][8 * p + e]),
-                                                                            __float_as_uint(acc[i][j][8 * p + 4 + e]),
-                                                                            false, false);
-                            v[e] = __uint_as_float(r[0]);
-                            v[4 + e] = __uint_as_float(r[1]);
-                        }
-                        const int m = m0 + 32 * i + l32, n = n0 + 32 * j + 16 * p + 8 * h;
-                        if (m < M && n < N) epi.put8(m, n, split, v, in[ii][j][p]);
-                    }
+            typename E::vec8 in[RG][FN][2];
+            fetch_rows<RG, FN, E>(in, i0, m0, n0, M, N, lane, epi);
+            apply_rows<FM, FN, RG, E>(acc, in, i0, m0, n0, split, M, N, lane, epi);
         }
         return;
     }
@@ -790,22 +807,30 @@ gemm_bf16_mfma_ring(const bf16* __restrict__ A, const bf16* __restrict__ B, int 
         if constexpr (NV > NMF) __builtin_amdgcn_sched_group_barrier(0x020, NV - NMF, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
-    // own loads of the next stage done (the two later stages may still fly), own LDS reads done, then the barrier
-    auto sync_next = [&]() {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL) : "memory");
+    // own loads of the next stage done (the two later stages may still fly, and X later loads of the epilogue's
+    // input: vector-memory loads complete in issue order), own LDS reads done, then the barrier
+    auto sync_next = [&](auto X) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL + decltype(X)::value) : "memory");
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
     // one stage: its loads three stages ahead, k-step 0, publish the next stage, k-step 1
-    auto stage = [&](int kt, const bf16* cA, const bf16* cB, const bf16* nA, const bf16* nB, bf16* xA, bf16* xB) {
+    auto stage = [&](int kt, const bf16* cA, const bf16* cB, const bf16* nA, const bf16* nB, bf16* xA, bf16* xB,
+                     auto X) {
         dma(kt + 3, xA, xB);
         lfrag(1, cA, cB, 1);
         mma(0);
         interleave(std::true_type{});
-        sync_next();
+        sync_next(X);
         lfrag(0, nA, nB, 0);
         mma(1);
         interleave(std::false_type{});
     };
+    using X0 = std::integral_constant<int, 0>;
+    // An epilogue that reads a tensor has it fetched into registers under the MFMAs of the last three stages:
+    // FM x FN x 2 loads per lane, every one issued (addresses clamped into the tensor) so the wait counts hold.
+    constexpr bool kPf = WideLoads<E>::value && !F8;
+    using XE = std::integral_constant<int, kPf ? FM * FN * 2 : 0>;
+    typename EpiIn<E, kPf>::type pin[FM][FN][2];
 
     if constexpr (F8) {
         // fp8: one MFMA per (i, j) and stage.  The stage's A fragments are reloaded with the next stage's
@@ -822,7 +847,7 @@ gemm_bf16_mfma_ring(const bf16* __restrict__ A, const bf16* __restrict__ B, int 
         };
         auto stage8 = [&](int kt, int cb, const bf16* nA, const bf16* nB, bf16* xA, bf16* xB) {
             dma(kt + 3, xA, xB);
-            sync_next();
+            sync_next(X0{});
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -834,7 +859,7 @@ gemm_bf16_mfma_ring(const bf16* __restrict__ A, const bf16* __restrict__ B, int 
         dma(0, sA0, sB0);
         dma(1, sA1, sB1);
         dma(2, sA2, sB2);
-        sync_next();
+        sync_next(X0{});
 #pragma unroll
         for (int i = 0; i < FM; ++i) lfa8(i, sA0);
         lfb8(0, sB0);
@@ -850,18 +875,37 @@ gemm_bf16_mfma_ring(const bf16* __restrict__ A, const bf16* __restrict__ B, int 
         dma(0, sA0, sB0);
         dma(1, sA1, sB1);
         dma(2, sA2, sB2);
-        sync_next();
+        sync_next(X0{});
         lfrag(0, sA0, sB0, 0);
-        for (int kt = 0; kt < nk; kt += 4) {
-            stage(kt, sA0, sB0, sA1, sB1, sA3, sB3);
-            stage(kt + 1, sA1, sB1, sA2, sB2, sA0, sB0);
-            stage(kt + 2, sA2, sB2, sA3, sB3, sA1, sB1);
-            stage(kt + 3, sA3, sB3, sA0, sB0, sA2, sB2);
+        const int kl = kPf ? (nk + 3) / 4 * 4 - 4 : nk;   // stages before the last block of four
+        for (int kt = 0; kt < kl; kt += 4) {
+            stage(kt, sA0, sB0, sA1, sB1, sA3, sB3, X0{});
+            stage(kt + 1, sA1, sB1, sA2, sB2, sA0, sB0, X0{});
+            stage(kt + 2, sA2, sB2, sA3, sB3, sA1, sB1, X0{});
+            stage(kt + 3, sA3, sB3, sA0, sB0, sA2, sB2, X0{});
+        }
+        if constexpr (kPf) {
+            stage(kl, sA0, sB0, sA1, sB1, sA3, sB3, X0{});
+            const int mw = m0 + wm * WM, nw = n0 + wn * WN;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int p = 0; p < 2; ++p)
+                        pin[i][j][p] = epi.fetch8(min(mw + 32 * i + l32, M - 1),
+                                                  min(nw + 32 * j + 16 * p + 8 * h, N - 8));
+            stage(kl + 1, sA1, sB1, sA2, sB2, sA0, sB0, XE{});
+            stage(kl + 2, sA2, sB2, sA3, sB3, sA1, sB1, XE{});
+            stage(kl + 3, sA3, sB3, sA0, sB0, sA2, sB2, XE{});
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the loads past the end before the stores
     }
 
-    epilogue<FM, FN>(acc, m0 + wm * WM, n0 + wn * WN, split, M, N, lane, epi);
+    if constexpr (kPf)
+        apply_rows<FM, FN, FM, E>(acc, pin, 0, m0 + wm * WM, n0 + wn * WN, split, M, N, lane, epi);
+    else
+        epilogue<FM, FN>(acc, m0 + wm * WM, n0 + wn * WN, split, M, N, lane, epi);
 }
 
 // ------------------------------------------------------------------ persistent four-stage ring
