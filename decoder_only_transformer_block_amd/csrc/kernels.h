@@ -148,7 +148,8 @@ hipError_t launch_embed_fwd(Dt dt, const int32_t* ids, const float* wte, void* x
 // row quantiser's result for y)
 hipError_t launch_rmsnorm_fwd(Dt dt, const void* x, void* y, float* rstd, int rows, int C, float eps,
                               hipStream_t s, void* q8 = nullptr, float* qs = nullptr);
-// dx(f32) = (accumulate ? dx : 0) + rstd*(dy - y*mean(dy*y)); dx_cd = cd(dx) when non-null
+// g = acc + rstd*(dy - y*mean(dy*y)) with acc = 0 (accumulate 0), the fp32 dx (1) or dx_cd (2); g is written
+// to dx (fp32) and to dx_cd (compute dtype), each when non-null
 hipError_t launch_rmsnorm_bwd(Dt dt, const void* y, const float* rstd, const void* dy, float* dx, void* dx_cd,
                               int rows, int C, int accumulate, hipStream_t s);
 // pos >= 0: every row is one token at position pos (decode); else row n is at position n mod T

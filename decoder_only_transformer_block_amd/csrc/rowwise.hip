@@ -254,7 +254,9 @@ hipError_t launch_rmsnorm_fwd(Dt dt, const void* x, void* y, float* rstd, int ro
 
 // Derivative of the map above, from its saved output y and scale rstd:
 // dx = rstd * (dy - y * mean(dy * y)).
-// dy arrives in the compute dtype; dx (the residual-stream gradient) stays fp32.
+// dy arrives in the compute dtype.  The residual-stream gradient it adds to is read from dx (fp32,
+// accumulate = 1) or dx_cd (the compute dtype, accumulate = 2), or starts at 0 (accumulate = 0); the sum is
+// written to whichever of dx and dx_cd is given.
 template <typename T>
 __global__ void __launch_bounds__(256)
 rmsnorm_bwd_kernel(const T* __restrict__ y, const float* __restrict__ rstd, const T* __restrict__ dy,
@@ -276,10 +278,11 @@ rmsnorm_bwd_kernel(const T* __restrict__ y, const float* __restrict__ rstd, cons
         float a[4], b[4], o[4] = {0.f, 0.f, 0.f, 0.f};
         Vec4<T>::load(y + base + c, a);
         Vec4<T>::load(dy + base + c, b);
-        if (accumulate) Vec4<float>::load(dx + base + c, o);
+        if (accumulate == 1) Vec4<float>::load(dx + base + c, o);
+        else if (accumulate == 2) Vec4<T>::load(dx_cd + base + c, o);
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] += rs * (b[i] - a[i] * dot);
-        Vec4<float>::store(dx + base + c, o);
+        if (dx) Vec4<float>::store(dx + base + c, o);
         if (dx_cd) Vec4<T>::store(dx_cd + base + c, o);
     }
 }
@@ -299,8 +302,10 @@ rmsnorm_bwd_rows(const T* __restrict__ y, const float* __restrict__ rstd, const 
     for (int i = 0; i < NCH; ++i) {
         load8(y + base + 256 * i, a[i]);
         load8(dy + base + 256 * i, b[i]);
-        if (accumulate) {
+        if (accumulate == 1) {
             load8(dx + base + 256 * i, o[i]);
+        } else if (accumulate == 2) {
+            load8(dx_cd + base + 256 * i, o[i]);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[i][e] = 0.0f;
@@ -318,7 +323,7 @@ rmsnorm_bwd_rows(const T* __restrict__ y, const float* __restrict__ rstd, const 
     for (int i = 0; i < NCH; ++i) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[i][e] += rs * (b[i][e] - a[i][e] * dot);
-        store8(dx + base + 256 * i, o[i]);
+        if (dx) store8(dx + base + 256 * i, o[i]);
         if (dx_cd) store8(dx_cd + base + 256 * i, o[i]);
     }
 }

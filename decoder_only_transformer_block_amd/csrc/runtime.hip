@@ -973,9 +973,17 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
     // dWlm = dz^T xf: vocab x n_embd output over all tokens; 256 x 128 tiles, the four-wave persistent ring
     // measured fastest
     TRY(wgrad(c, "dWlm", logits, V, c->ws + p.xf, C, V, C, gslice(-1, 1), acc, 1));
-    const double nb = (double)N * C * (e + e + 4 + (mfma_dt(dt) ? 2 : 0)) + N * 4.0;
-    TRY(launch(c, "rmsnorm_bwd", 0.0, nb, [&] {
-        return launch_rmsnorm_bwd(dt, c->ws + p.xf, c->at<float>(p.rstdf), dxn, dx, dx_cd, N, C, 0, c->stream);
+    // In the 16-bit modes the residual-stream gradient lives in the compute dtype, as the residual stream itself
+    // does (dx_cd, read and written by every norm's backward); only layer 0's also leaves it in fp32 (dx) for the
+    // embedding gradient.  fp32 keeps it in dx.
+    const bool g16 = mfma_dt(dt);
+    float* const dx_acc = g16 ? nullptr : dx;
+    const int acc_from = g16 ? 2 : 1;
+    auto nb_of = [&](int accumulate, bool f32_out) {   // bytes of one norm backward
+        return (double)N * C * (2.0 * e + (accumulate ? e : 0) + (g16 ? 2 : 0) + (f32_out ? 4 : 0)) + N * 4.0;
+    };
+    TRY(launch(c, "rmsnorm_bwd", 0.0, nb_of(0, !g16), [&] {
+        return launch_rmsnorm_bwd(dt, c->ws + p.xf, c->at<float>(p.rstdf), dxn, dx_acc, dx_cd, N, C, 0, c->stream);
     }));
     for (int l = (int)c->L - 1; l >= 0; --l) {
         uint8_t* xn1 = c->ws + c->lay(l, p.l_xn1);
@@ -1002,8 +1010,9 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             TRY(gemm(c, d, "dxn2"));
         }
         TRY(wgrad(c, "dWfc", c->ws + p.dh, F, xn2, C, F, C, gslice(l, 4), acc));  // dWfc = dh^T xn2
-        TRY(launch(c, "rmsnorm_bwd", 0.0, nb + (double)N * C * 4, [&] {
-            return launch_rmsnorm_bwd(dt, xn2, c->at<float>(c->lay(l, p.l_rstd2)), dxn, dx, dx_cd, N, C, 1, c->stream);
+        TRY(launch(c, "rmsnorm_bwd", 0.0, nb_of(1, !g16), [&] {
+            return launch_rmsnorm_bwd(dt, xn2, c->at<float>(c->lay(l, p.l_rstd2)), dxn, dx_acc, dx_cd, N, C, acc_from,
+                                      c->stream);
         }));
         {   // dy = dx Wo
             GemmDesc d;
@@ -1051,8 +1060,9 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
             TRY(gemm(c, d, "dxn1"));
         }
         TRY(wgrad(c, "dWqkv", c->ws + p.dqkv, QKV, xn1, C, QKV, C, gslice(l, 0), acc));  // dWqkv = dqkv^T xn1
-        TRY(launch(c, "rmsnorm_bwd", 0.0, nb + (double)N * C * 4, [&] {
-            return launch_rmsnorm_bwd(dt, xn1, c->at<float>(c->lay(l, p.l_rstd1)), dxn, dx, dx_cd, N, C, 1, c->stream);
+        TRY(launch(c, "rmsnorm_bwd", 0.0, nb_of(1, !g16 || l == 0), [&] {
+            return launch_rmsnorm_bwd(dt, xn1, c->at<float>(c->lay(l, p.l_rstd1)), dxn, l == 0 ? dx : dx_acc, dx_cd,
+                                      N, C, acc_from, c->stream);
         }));
     }
     float* demb = dx;    // the gradient at the embedding's output
@@ -1061,7 +1071,7 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
         // through the embedding norm: its input gradient into dxn (from dx in the compute dtype, as every norm's
         // backward takes it), then dx serves as the scratch
         const void* dy = mfma_dt(dt) ? (const void*)(c->ws + p.dx_cd) : (const void*)dx;
-        TRY(launch(c, "rmsnorm_bwd", 0.0, nb, [&] {
+        TRY(launch(c, "rmsnorm_bwd", 0.0, (double)N * C * (2.0 * e + 4) + N * 4.0, [&] {
             return launch_rmsnorm_bwd(dt, c->ws + p.x0, c->at<float>(p.rstd0), dy, dxn, nullptr, N, C, 0, c->stream);
         }));
         demb = dxn;
