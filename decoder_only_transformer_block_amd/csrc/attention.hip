@@ -61,7 +61,7 @@ inline int attn_group(int npos, int per_cu) { return std::max(1, 32 * per_cu / n
 // high bits differ across 4 consecutive rows (transposed reads hit 4 distinct
 // 64-byte bank groups), so neither read conflicts on the 64-bank LDS.
 // rfrag / trfrag below are the definitional forms; the kernels read through the
-// closed-form offsets further down (rz, tz, frag_at, trfrag_at; frag_lds, trfrag_lds).
+// closed-form offsets further down (rz, tz, frag_at, trfrag_at; frag_in, trfrag_in).
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -116,24 +116,10 @@ __device__ __forceinline__ bf16x8 trfrag_at(const bf16* S, int t, int db) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// LDS byte addresses as plain 32-bit integers: a tile base that is a multiple of 16 KB has zeros in every bit a
-// fragment offset XOR touches, so base + (off ^ x) = (base + off) ^ x and one register per lane and tile serves
-// every fragment of the tile, the other tiles at fixed distances riding in the instruction's offset field
-typedef __attribute__((address_space(3))) const char lds_cchar;
-typedef __attribute__((address_space(3))) const bf16x8 lds_frag;
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(size_t)(lds_cchar*)p; }
-__device__ __forceinline__ bf16x8 frag_lds(uint32_t a) { return *(lds_frag*)(size_t)a; }
-__device__ __forceinline__ bf16x8 trfrag_lds(uint32_t lo, uint32_t hi) {
-    s16x4 l = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)lo);
-    s16x4 h = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)hi);
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-    s16x8 v = {l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
-    return __builtin_bit_cast(bf16x8, v);
-}
-
-// Row and transposed fragments from byte offsets into tile S.  The reads keep S as their object, so where S is
-// an LDS array of its own the compiler knows they do not touch direct-to-LDS loads in flight into other
-// arrays, and issues them without waiting for those loads (a read it cannot place is made to wait for all).
+// Row and transposed fragments from byte offsets into tile S (tiles are 16 KB-aligned, so an offset XOR-ed
+// with a fragment's chunk bits stays inside the tile).  The reads keep S as their object, so where S is an LDS
+// array of its own the compiler knows they do not touch direct-to-LDS loads in flight into other arrays, and
+// issues them without waiting for those loads (a read it cannot place is made to wait for all).
 __device__ __forceinline__ bf16x8 frag_in(const bf16* S, uint32_t off) {
     return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(S) + off);
 }
@@ -552,9 +538,9 @@ attn_bwd_dq_bf16(const bf16* __restrict__ qkv, const bf16* __restrict__ y, const
 // 32 keys (block w % 4) and take the two 32-query halves of every 64-query
 // tile; each accumulates its half's share of dK and dV (32 keys x 128 dims
 // each) in registers, and the two shares are added in a fixed order at the end
-// (deterministic).  K and V rows of the block sit in LDS; the workgroup loops
-// over the r query heads of the group and over the query tiles at or after its
-// first key.  Q, dO, lse and delta tiles travel straight from memory into LDS
+// (deterministic).  V rows of the block sit in LDS, and each wave keeps its
+// 32 keys' K fragments in registers; the workgroup loops over the r query heads
+// of the group and over the query tiles at or after its first key.  Q, dO, lse and delta tiles travel straight from memory into LDS
 // (buffer_load ... lds), double-buffered: the loads of tile i+1 run under the
 // MFMAs of tile i.
 template <typename HT>

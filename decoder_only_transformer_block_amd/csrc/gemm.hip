@@ -204,11 +204,6 @@ __device__ __forceinline__ void wide8(const f32x16 (&acc)[FM][FN], int i, int j,
     }
 }
 
-// Epilogue of an MFMA wave tile: FM x FN accumulators of 32 x 32 (operand-swapped
-// layout: lane l holds row l % 32 and, in registers 4g..4g+3, columns
-// 8g + 4(l / 32) + 0..3).  m0, n0: the wave tile's first row and column.
-// RG: row blocks whose epilogue inputs are fetched together (FM by default; the
-// persistent kernels, which keep more registers live, fetch half as many at once).
 // Epilogues that read a tensor 8 values at a time (fetch8 / put8)
 template <class E, class = void> struct WideLoads : std::false_type {};
 template <class E> struct WideLoads<E, std::void_t<decltype(E::kLoads)>> : std::bool_constant<E::kWide && E::kLoads> {};
@@ -251,6 +246,11 @@ __device__ __forceinline__ void apply_rows(const f32x16 (&acc)[FM][FN], const ty
             }
 }
 
+// Epilogue of an MFMA wave tile: FM x FN accumulators of 32 x 32 (operand-swapped
+// layout: lane l holds row l % 32 and, in registers 4g..4g+3, columns
+// 8g + 4(l / 32) + 0..3).  m0, n0: the wave tile's first row and column.
+// RG: row blocks whose epilogue inputs are fetched together (FM by default; the
+// persistent kernels, which keep more registers live, fetch half as many at once).
 template <int FM, int FN, class E, int RG = FM>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[FM][FN], int m0, int n0, int split, int M, int N,
                                            int lane, const E& epi) {
