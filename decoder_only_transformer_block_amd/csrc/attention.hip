@@ -242,21 +242,22 @@ __device__ __forceinline__ void rope_qknorm_bwd_row(float (&v)[4][16], const bf1
 }
 
 // ======================================================================== bf16 forward
-// Workgroup: 4 waves x 32 QB queries of one head; K/V tiles of 64 keys travel
-// straight from memory into LDS, double-buffered.  QB = 2 reuses every K and V
-// fragment read from LDS for two 32-query blocks at one wave per SIMD; QB = 1
-// fits two workgroups per CU, so one wave's softmax runs under the other's
-// MFMAs.
-template <int QB, typename HT>
-__global__ void __launch_bounds__(256, QB == 1 ? 2 : 1)
+// Workgroup: 4 waves x 32 QB queries of one head; K/V tiles travel
+// straight from memory into LDS, double-buffered, KT keys per tile.  QB = 2
+// reuses every K and V fragment read from LDS for two 32-query blocks at one
+// wave per SIMD; QB = 1 runs several workgroups per CU, so one wave's softmax
+// runs under the others' MFMAs: two with 64-key tiles (64 KB of LDS each),
+// three with 32-key tiles (32 KB each; 158 VGPRs fit three waves per SIMD).
+template <int QB, typename HT, int KT = 64>
+__global__ void __launch_bounds__(256, QB == 1 ? (KT == 32 ? 3 : 2) : 1)
 attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restrict__ lse, int T, int H, int Hkv,
               int B, int G)
 {
     constexpr int D = 128, QW = 32 * QB, QBLK = 4 * QW;
-    __shared__ __attribute__((aligned(1024))) bf16 sK0[64 * 128];
-    __shared__ __attribute__((aligned(1024))) bf16 sV0[64 * 128];
-    __shared__ __attribute__((aligned(1024))) bf16 sK1[64 * 128];
-    __shared__ __attribute__((aligned(1024))) bf16 sV1[64 * 128];
+    __shared__ __attribute__((aligned(1024))) bf16 sK0[KT * 128];
+    __shared__ __attribute__((aligned(1024))) bf16 sV0[KT * 128];
+    __shared__ __attribute__((aligned(1024))) bf16 sK1[KT * 128];
+    __shared__ __attribute__((aligned(1024))) bf16 sV1[KT * 128];
     const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     // stream (sequence, kv head); positions: late (heavy) query blocks first, the group's query heads fastest
@@ -294,26 +295,26 @@ attn_fwd_bf16(const bf16* __restrict__ qkv, bf16* __restrict__ y, float* __restr
     constexpr float kPow = std::is_same<HT, f16>::value ? 15.0f : 0.0f;
     const float c1 = kLog2e * rsqrtf((float)D), c2 = sqrtf((float)D) * kLog2e - kPow;
 
-    const int nkt = min(q0 + QBLK, T) / 64;     // key tiles at or before the block's last query
+    const int nkt = min(q0 + QBLK, T) / KT;     // key tiles at or before the block's last query
     const int zk = rz(l32, hh), tl = tz(lane);  // fragment offsets (rows l32 + 32 kb share them)
     const unsigned vo = dma_voff(QKV, lane, w);
     const bf16* kbase = qkv + rowbase * QKV + HD + g * D;
     auto issue = [&](int kt, bf16* Ks, bf16* Vs) {
-        const bf16* kp = kbase + (size_t)kt * 64 * QKV;
-        const unsigned bytes = (unsigned)((63 * QKV + 128) * 2);
-        dma_rows<64>(buf_rsrc(kp, bytes), vo, QKV, Ks, w);
-        dma_rows<64>(buf_rsrc(kp + KD, bytes), vo, QKV, Vs, w);
+        const bf16* kp = kbase + (size_t)kt * KT * QKV;
+        const unsigned bytes = (unsigned)(((KT - 1) * QKV + 128) * 2);
+        dma_rows<KT>(buf_rsrc(kp, bytes), vo, QKV, Ks, w);
+        dma_rows<KT>(buf_rsrc(kp + KD, bytes), vo, QKV, Vs, w);
     };
     auto publish = [&]() {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     };
     auto compute = [&](int kt, const bf16* Ks, const bf16* Vs) {
-        const int kv0 = kt * 64;
+        const int kv0 = kt * KT;
         if (!active || kv0 > qw + QW - 1) return;  // wave-uniform: the whole tile lies after the wave's queries
-        const bool diag = kv0 + 63 > qw;
+        const bool diag = kv0 + KT - 1 > qw;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KT / 32; ++kb) {
             f32x16 sc[QB];
 #pragma unroll
             for (int qq = 0; qq < QB; ++qq) zero16(sc[qq]);
@@ -873,12 +874,13 @@ attn_bwd_dkdv_f32(const float* __restrict__ qkv, const float* __restrict__ dy, c
 hipError_t launch_attn_fwd(const AttnDesc& a, hipStream_t s) {
     if (mfma_dt(a.dt)) {
         if (a.D != 128 || a.T % 64) return hipErrorInvalidValue;
-        // one 32-query block per wave: two workgroups per CU (softmax under the other's MFMAs)
-        // measured faster than two blocks per wave at one workgroup per CU
+        // one 32-query block per wave, several workgroups per CU (softmax under the others' MFMAs): measured
+        // faster than two blocks per wave at one workgroup per CU, and three workgroups with 32-key tiles
+        // faster than two with 64-key tiles
         const int npos = (a.T + 127) / 128 * (a.H / a.Hkv);
-        auto k = a.dt == Dt::F16 ? attn_fwd_bf16<1, f16> : attn_fwd_bf16<1, bf16>;
+        auto k = a.dt == Dt::F16 ? attn_fwd_bf16<1, f16, 32> : attn_fwd_bf16<1, bf16, 32>;
         hipLaunchKernelGGL(k, dim3(npos * a.Hkv * a.B), dim3(256), 0, s, (const bf16*)a.qkv, (bf16*)a.y, a.lse, a.T,
-                           a.H, a.Hkv, a.B, attn_group(npos, 2));
+                           a.H, a.Hkv, a.B, attn_group(npos, 3));
         return hipGetLastError();
     }
     dim3 grid((unsigned)(((size_t)a.B * a.T * a.H + 3) / 4));
