@@ -18,6 +18,10 @@ using namespace ncgpt;
 namespace {
 
 constexpr int kCUs = 256;
+// dWlm = dz^T xf reads the [tokens, vocab] dz once per column tile of its n_embd-wide output: 256 x 256 tiles
+// (split-K where the tile rounds come out uneven) measured faster than 256 x 128 ones, which read dz twice as
+// often (d12: 2.52 against 3.15 ms per step)
+constexpr int kDWlmTile = 0;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -161,7 +165,8 @@ int pick_tile_rounds(int64_t M, int64_t N, int64_t batch) {
 // tiles (e.g. 9 for 768 x 768) while K is the whole batch of tokens, so K is
 // split until one round of workgroups covers the CUs; large outputs use the
 // forward tile rule.
-WGrad pick_wgrad(Dt dt, int64_t M, int64_t N, int64_t K) {
+// tile >= 0 (16-bit): that tile, with the split count from the same model
+WGrad pick_wgrad(Dt dt, int64_t M, int64_t N, int64_t K, int tile = -1) {
     WGrad w;
     if (dt == Dt::F32) {
         w.tile = 0;
@@ -172,7 +177,9 @@ WGrad pick_wgrad(Dt dt, int64_t M, int64_t N, int64_t K) {
     } else {
         static const int bm[3] = {256, 256, 128}, bn[3] = {256, 128, 128};
         const int64_t tiles0 = ((M + 255) / 256) * ((N + 255) / 256);
-        if (tiles0 < kCUs) {
+        if (tile >= 0) {
+            w.tile = tile;
+        } else if (tiles0 < kCUs) {
             w.tile = (M >= 256 && N >= 256) ? 0 : 2;
         } else {
             w.tile = pick_tile(M, N);
@@ -284,9 +291,10 @@ void make_plan(ncgpt_ctx* c) {
     p.delta = A((size_t)2 * c->B * c->H * c->T * 4);
     // split-K partials: the largest splits * M * N over the weight gradients
     size_t sk = 0;
-    const int64_t shapes[5][2] = {{c->QKV, c->C}, {c->C, c->HD}, {c->F, c->C}, {c->C, c->F}, {c->V, c->C}};
+    const int64_t shapes[5][3] = {{c->QKV, c->C, -1}, {c->C, c->HD, -1}, {c->F, c->C, -1}, {c->C, c->F, -1},
+                                  {c->V, c->C, kDWlmTile}};
     for (auto& s : shapes) {
-        WGrad w = pick_wgrad(c->dt, s[0], s[1], (int64_t)N);
+        WGrad w = pick_wgrad(c->dt, s[0], s[1], (int64_t)N, (int)s[2]);
         if (w.splits > 1) sk = std::max(sk, (size_t)w.splits * s[0] * s[1] * 4);
     }
     p.splitk = A(sk);
@@ -455,8 +463,7 @@ ncgpt_status gemm(ncgpt_ctx* c, GemmDesc d, const char* tag, bool bf16_always = 
 ncgpt_status wgrad(ncgpt_ctx* c, const char* tag, const void* dY, int ldy, const void* X, int ldx, int M, int N,
                    float* g, int accumulate, int tile = -1) {
     const int K = (int)c->N;
-    WGrad w = pick_wgrad(c->dt, M, N, K);
-    if (tile >= 0 && w.splits == 1) w.tile = tile;
+    const WGrad w = pick_wgrad(c->dt, M, N, K, tile);
     GemmDesc d;
     // both operands are read through transposing LDS reads (half rate): the four-wave persistent
     // ring, which reads fewer fragments per MFMA, measured fastest
@@ -970,9 +977,8 @@ ncgpt_status ncgpt_backward(ncgpt_ctx* c, float* grads, int accumulate, float gr
         d.group_m = 2;             // the n_embd-wide outputs: bands of 2 tile-rows measured fastest
         TRY(gemm(c, d, "dxf"));
     }
-    // dWlm = dz^T xf: vocab x n_embd output over all tokens; 256 x 128 tiles, the four-wave persistent ring
-    // measured fastest
-    TRY(wgrad(c, "dWlm", logits, V, c->ws + p.xf, C, V, C, gslice(-1, 1), acc, 1));
+    // dWlm = dz^T xf: vocab x n_embd output over all tokens (the tile: kDWlmTile)
+    TRY(wgrad(c, "dWlm", logits, V, c->ws + p.xf, C, V, C, gslice(-1, 1), acc, kDWlmTile));
     // In the 16-bit modes the residual-stream gradient lives in the compute dtype, as the residual stream itself
     // does (dx_cd, read and written by every norm's backward); only layer 0's also leaves it in fp32 (dx) for the
     // embedding gradient.  fp32 keeps it in dx.
